@@ -1,0 +1,290 @@
+"""CPU oracle for 2:4 structured-sparse GEMM (prune, compress, FP8 quantise, GEMM).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with the
+HIP library and imports nothing from it.  It is deliberately plain and slow:
+NumPy, exact integer work on bit patterns, IEEE float32 where the method fixes
+float32, and float64 for the reference product.
+
+Sources ("the cookbook" = the page "Deploying 2:4 Sparsity with FP8 on Hopper:
+A Production Cookbook"):
+
+* 2:4 pruning: the cookbook, pipeline step 4 "Apply 2:4 structured pruning
+  safely" (keep the two largest-magnitude values of every 4) and step 2
+  "Choose 2:4-eligible layers and orientation" (groups are 4 contiguous values
+  along the inner K dimension); Practical Example 1 "2:4 mask application" (a
+  top-2-of-|w| mask over groups of 4 along the chosen axis; the axis length must
+  be divisible by 4).
+* Compressed form: kept values plus 2-bit positions; the SlideSparse page
+  ("SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity") describes the
+  weights being converted once, offline, into the hardware's compressed format.
+* FP8 scaling: the cookbook, pipeline step 3 "Calibrate for FP8 and sparsity"
+  (per-tensor dynamic scaling to avoid overflow), step 6 "Precision pipeline and
+  post-pruning recalibration" (scales recomputed after pruning) and
+  "Troubleshooting quick hits" (clip the maximum to avoid overflow and NaN).
+* Readings where the pages are silent (each is applied below and nowhere else):
+  ties in |w| go to the lower index; magnitudes are compared exactly on the
+  bfloat16 bit patterns (+0 and -0 equal); dropped positions decompress to +0;
+  kept values are stored in ascending index order; position nibble
+  ``i0 | i1 << 2`` for group g sits at bits ``4*(g % 8)`` of metadata word
+  ``g // 8``; FP8 is OCP E4M3FN (bias 7, max 448, no infinities, NaN = S.1111.111);
+  the scale is ``s = fp32(amax / 448)`` (``s = 1`` when amax is 0) and a value is
+  quantised as ``e4m3_rne(clamp(fp32(v / s), -448, 448))``.
+
+Representation: bfloat16 tensors are passed as ``numpy.uint16`` bit patterns,
+FP8-E4M3 tensors as ``numpy.uint8`` codes, metadata as ``numpy.uint32`` words.
+
+Parity pins live in ``tests/test_oracle_*.py``; every function here is pinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+GROUP = 4          # values per 2:4 group along K
+KEEP = 2           # kept values per group
+GROUPS_PER_WORD = 8  # 4-bit position nibbles per 32-bit metadata word
+
+# ----------------------------------------------------------------------------
+# bfloat16 bit patterns
+# ----------------------------------------------------------------------------
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32 (the high 16 bits)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# 2:4 magnitude pruning (the cookbook, pipeline step 4 and Practical Example 1)
+# ----------------------------------------------------------------------------
+
+
+def prune_mask(w_bits: np.ndarray) -> np.ndarray:
+    """Boolean keep-mask of 2:4 magnitude pruning along the last axis (K).
+
+    In every group of 4 contiguous values along K, value i is kept iff fewer
+    than two values of the group rank above it, where j ranks above i when
+    |w_j| > |w_i|, or |w_j| == |w_i| and j < i (ties go to the lower index).
+    |w| is compared exactly as the unsigned integer ``bits & 0x7FFF``, which
+    orders finite bfloat16 magnitudes exactly and makes +0 equal to -0.
+    Inputs must be finite.
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    n, k = w_bits.shape
+    if k % GROUP:
+        raise ValueError("K must be a multiple of 4")
+    a = (w_bits & np.uint16(0x7FFF)).astype(np.int32).reshape(n, k // GROUP, GROUP)
+    above = np.zeros(a.shape, dtype=np.int32)
+    for i in range(GROUP):
+        for j in range(GROUP):
+            if j == i:
+                continue
+            beats = a[..., j] > a[..., i]
+            if j < i:
+                beats = beats | (a[..., j] == a[..., i])
+            above[..., i] += beats
+    return (above < KEEP).reshape(n, k)
+
+
+def apply_mask(w_bits: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Pruned dense weight: kept values as they are, dropped positions +0."""
+    return np.where(mask, np.asarray(w_bits, dtype=np.uint16), np.uint16(0)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# Compressed 2:4 form: kept values + 2-bit positions
+# ----------------------------------------------------------------------------
+
+
+def compress(w: np.ndarray, mask: np.ndarray):
+    """Pack the kept values of each group and their positions.
+
+    ``w`` is ``[N, K]`` (any element type: bfloat16 bits or FP8 codes), ``mask``
+    the keep-mask with exactly two True per group of 4.  Returns
+    ``values [N, K/2]`` (same element type as ``w``; the two kept values of group
+    g at columns 2g and 2g+1, in ascending position order) and
+    ``meta [N, K/32]`` uint32 (group g's nibble ``i0 | i1 << 2`` with i0 < i1 at
+    bits ``4*(g % 8)`` of word ``g // 8``).
+    """
+    w = np.asarray(w)
+    mask = np.asarray(mask, dtype=bool)
+    n, k = w.shape
+    if k % (GROUP * GROUPS_PER_WORD):
+        raise ValueError("K must be a multiple of 32")
+    g = mask.reshape(n, k // GROUP, GROUP)
+    if not np.all(g.sum(axis=-1) == KEEP):
+        raise ValueError("mask must keep exactly 2 of every 4")
+    i0 = np.argmax(g, axis=-1)                       # first kept position
+    i1 = (GROUP - 1) - np.argmax(g[..., ::-1], axis=-1)  # last kept position
+    wg = w.reshape(n, k // GROUP, GROUP)
+    v0 = np.take_along_axis(wg, i0[..., None], axis=-1)[..., 0]
+    v1 = np.take_along_axis(wg, i1[..., None], axis=-1)[..., 0]
+    values = np.stack([v0, v1], axis=-1).reshape(n, k // 2).astype(w.dtype)
+    nib = (i0 | (i1 << 2)).astype(np.uint32).reshape(n, k // 32, GROUPS_PER_WORD)
+    shifts = (4 * np.arange(GROUPS_PER_WORD, dtype=np.uint32))
+    meta = np.bitwise_or.reduce(nib << shifts, axis=-1).astype(np.uint32)
+    return values, meta
+
+
+def meta_positions(meta: np.ndarray, k: int):
+    """Decode metadata words into the two kept positions (i0, i1) of every group."""
+    meta = np.asarray(meta, dtype=np.uint32)
+    n = meta.shape[0]
+    shifts = (4 * np.arange(GROUPS_PER_WORD, dtype=np.uint32))
+    nib = ((meta[..., None] >> shifts) & np.uint32(0xF)).reshape(n, k // GROUP)
+    return (nib & 3).astype(np.int64), (nib >> 2).astype(np.int64)
+
+
+def mask_from_meta(meta: np.ndarray, k: int) -> np.ndarray:
+    i0, i1 = meta_positions(meta, k)
+    n = i0.shape[0]
+    m = np.zeros((n, k // GROUP, GROUP), dtype=bool)
+    np.put_along_axis(m, i0[..., None], True, axis=-1)
+    np.put_along_axis(m, i1[..., None], True, axis=-1)
+    return m.reshape(n, k)
+
+
+def decompress(values: np.ndarray, meta: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of :func:`compress`: dense ``[N, K]`` with zero bits at dropped positions."""
+    values = np.asarray(values)
+    n = values.shape[0]
+    i0, i1 = meta_positions(meta, k)
+    vg = values.reshape(n, k // GROUP, KEEP)
+    out = np.zeros((n, k // GROUP, GROUP), dtype=values.dtype)
+    np.put_along_axis(out, i0[..., None], vg[..., 0:1], axis=-1)
+    np.put_along_axis(out, i1[..., None], vg[..., 1:2], axis=-1)
+    return out.reshape(n, k)
+
+
+def prune_compress(w_bits: np.ndarray):
+    """Prune then compress a bfloat16 weight: returns (values, meta)."""
+    return compress(np.asarray(w_bits, dtype=np.uint16), prune_mask(w_bits))
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 (OCP "E4M3FN": bias 7, no infinities, max finite 448)
+# ----------------------------------------------------------------------------
+
+
+def e4m3_value_table() -> np.ndarray:
+    """Value of each of the 256 E4M3 codes (NaN for 0x7F and 0xFF).
+
+    Code = s.eeee.mmm; e == 0 is subnormal, m/8 * 2^-6; otherwise
+    (1 + m/8) * 2^(e-7); e == 15 with m == 7 is NaN.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[code] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3 = e4m3_value_table()
+_E4M3_POS = _E4M3[:0x7F]  # codes 0x00..0x7E: the non-negative finite values, ascending
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    """Round float32 values to E4M3 codes: clamp to [-448, 448], then nearest, ties to even.
+
+    The nearest code is found by searching the table of the 127 non-negative
+    finite values; when |t| lies strictly between two neighbours lo < hi it
+    rounds down iff 2|t| < lo + hi, up iff 2|t| > lo + hi, and to the code with
+    an even (zero) last mantissa bit on equality.  Both sides of that comparison
+    are exact in float64.  The sign bit is copied from t (so -0 -> 0x80).
+    Inputs must not be NaN.
+    """
+    t = np.asarray(t, dtype=np.float32)
+    if np.isnan(t).any():
+        raise ValueError("NaN input")
+    a = np.minimum(np.abs(t).astype(np.float64), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # _E4M3_POS[hi] >= a
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    exact = _E4M3_POS[hi] == a
+    lo = np.maximum(hi - 1, 0)
+    twice = 2.0 * a
+    mid = _E4M3_POS[lo] + _E4M3_POS[hi]
+    pick_hi = (twice > mid) | ((twice == mid) & (hi % 2 == 0))
+    code = np.where(exact, hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return code | (np.signbit(t).astype(np.uint8) << np.uint8(7))
+
+
+def fp8_scale(v_bits: np.ndarray) -> np.float32:
+    """Per-tensor dynamic scale ``fp32(amax / 448)``, or 1 when the tensor is all zero.
+
+    amax is the exact maximum of |v| over the whole tensor (the cookbook, step 3:
+    one scale per tensor, from the data, chosen so nothing overflows).
+    """
+    amax = np.float32(np.max(np.abs(bf16_to_f32(v_bits)))) if np.size(v_bits) else np.float32(0)
+    if amax == 0:
+        return np.float32(1.0)
+    return np.float32(amax) / np.float32(E4M3_MAX)
+
+
+def quant_fp8(v_bits: np.ndarray, scale=None):
+    """Quantise bfloat16 values to E4M3 codes with one per-tensor scale.
+
+    ``scale=None`` is the dynamic mode (scale from :func:`fp8_scale`); otherwise
+    the given float32 scale is used as is (static mode, where the clamp at +-448
+    is what keeps out-of-range values finite).  Each value is divided by the
+    scale in IEEE float32 and rounded with :func:`e4m3_encode`.
+    Returns (codes, scale).
+    """
+    s = fp8_scale(v_bits) if scale is None else np.float32(scale)
+    t = bf16_to_f32(v_bits) / s
+    assert t.dtype == np.float32
+    return e4m3_encode(t), s
+
+
+def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
+    """float64 values ``scale * decode(code)`` represented by E4M3 codes."""
+    return np.float64(np.float32(scale)) * e4m3_decode(codes)
+
+
+# ----------------------------------------------------------------------------
+# Reference product Y = X . W^T (float64) and its magnitude sum
+# ----------------------------------------------------------------------------
+
+
+def gemm_ref(x_hat: np.ndarray, w_hat: np.ndarray):
+    """``ref = X W^T`` and ``mag = |X| |W|^T`` in float64.
+
+    ``x_hat`` is ``[M, K]``, ``w_hat`` ``[N, K]`` (dense, pruned, dequantised).
+    ``mag[m, n] = sum_k |x[m,k] w[n,k]|`` scales the accumulation-order part of
+    the tolerance.
+    """
+    x_hat = np.asarray(x_hat, dtype=np.float64)
+    w_hat = np.asarray(w_hat, dtype=np.float64)
+    return x_hat @ w_hat.T, np.abs(x_hat) @ np.abs(w_hat).T
+
+
+def sparse_operands_bf16(x_bits, values, meta, k):
+    """Dense float64 operands of the BF16 path: X as given, W decompressed."""
+    return bf16_to_f64(x_bits), bf16_to_f64(decompress(values, meta, k))
+
+
+def sparse_operands_fp8(xq, x_scale, wq_values, meta, w_scale, k):
+    """Dense float64 operands of the FP8 path: both dequantised, W decompressed."""
+    return dequant_fp8(xq, x_scale), dequant_fp8(decompress(wq_values, meta, k), w_scale)
+
+
+def within_tolerance(y, ref, mag, rel=8e-3, absmag=1e-4):
+    """Elementwise test ``|y - ref| <= rel*|ref| + absmag*mag`` (y: the BF16 output as float)."""
+    y = np.asarray(y, dtype=np.float64)
+    return np.abs(y - ref) <= rel * np.abs(ref) + absmag * mag
