@@ -1,0 +1,361 @@
+"""Benchmark of the 2:4 sparse GEMM path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload up|down|prefill|layers]
+
+Default workload: the decode-shaped FP8 FFN up-projection (K=4096, N=14336) at
+M = 1, 16 and 64 tokens.  One step = one pass of the per-call path for each M:
+dynamic per-tensor E4M3 quantisation of X (sp24_quant_fp8) and the sparse GEMM
+(sp24_gemm, including any split-K reduction), on weights that were pruned,
+compressed and quantised once at load.  The load path (sp24_prune_compress and
+the weight quantisation) is timed separately and reported under "load_path".
+
+Inputs are seeded synthetic tensors (workloads/) resident in HBM before the
+timed region.  Each call reads a different one of R weight copies (> 2x the
+256 MB last-level cache), so weight bytes come from HBM.  Steps are captured
+once per weight copy in HIP graphs and replayed; the graphs' outputs are
+checked bitwise against an eager run.
+
+Prints ONE JSON line with the metric, the roofline of the dominant kernel (the
+sparse GEMM, timed with HIP events on the stream it runs on), the dense-MFMA
+baseline of the same shapes, and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse GEMM TFLOP/s + GB/s and % of roofline vs dense MFMA, decode & prefill"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA; equal to SMFMAC's rate of nonzero MACs
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="up", choices=["up", "down", "prefill", "layers"])
+    ap.add_argument("--dtype", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=0,
+                    help="GEMM launches per M for the per-kernel timing (0: automatic)")
+    return ap.parse_args()
+
+
+def gemm_bytes(m, n, k, fp8):
+    """Algorithmic bytes of one sparse GEMM: compressed values + metadata + X + Y."""
+    es = 1 if fp8 else 2
+    return n * (k // 2) * es + n * (k // 32) * 4 + m * k * es + m * n * 2
+
+
+def dense_bytes(m, n, k, fp8):
+    es = 1 if fp8 else 2
+    return n * k * es + m * k * es + m * n * 2
+
+
+def quant_bytes(m, k):
+    return m * k * 2 + m * k + 4
+
+
+class Events:
+    """HIP events on the current (torch) stream, which is the stream libsp24 launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, reps):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        s.record()
+        for i in range(reps):
+            fn(i)
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / 1e3  # seconds
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bf16_gemm_linear_amd as sp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8 = args.dtype == "fp8"
+    dt = sp.FP8 if fp8 else sp.BF16
+    ev = Events(torch)
+
+    # ---------------------------------------------------------------- workload
+    if args.workload in ("up", "down"):
+        spec = W.UP if args.workload == "up" else W.DOWN
+        K, N, Ms = spec["K"], spec["N"], list(spec["Ms"])
+        w_cpu = W.up_weight() if args.workload == "up" else W.down_weight()
+        xs_cpu = {m: (W.up_x(m) if args.workload == "up" else W.down_x(m)) for m in Ms}
+        desc = ("decode FFN %s-projection, 2:4 sparse %s, M=%s tokens, K=%d, N=%d"
+                % (args.workload, "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16",
+                   "/".join(map(str, Ms)), K, N))
+        bound = "hbm"
+    elif args.workload == "prefill":
+        K, N, Ms = W.PREFILL["K"], W.PREFILL["N"], [W.PREFILL["M"]]
+        w_cpu = W.prefill_weight()
+        xs_cpu = {Ms[0]: W.prefill_x()}
+        desc = "prefill GEMM, 2:4 sparse %s, M=%d, K=%d, N=%d" % (
+            "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16", Ms[0], K, N)
+        bound = "mfma"
+    else:
+        raise SystemExit("--workload layers: use the layer-sweep mode of this script (not yet built)")
+
+    # ---------------------------------------------------------------- load path
+    w = w_cpu.to(dev)
+    xs = {m: xs_cpu[m].to(dev) for m in Ms}
+    values = torch.empty(N, K // 2, dtype=torch.bfloat16, device=dev)
+    meta = torch.empty(N, K // 32, dtype=torch.int32, device=dev)
+    t_prune = ev.time(lambda i: sp.prune_compress(w, values, meta), 5) / 5
+    qv, sw = (sp.quant_fp8(values) if fp8 else (values, None))
+    if fp8:
+        qbuf = torch.empty_like(qv)
+        t_wq = ev.time(lambda i: sp.quant_fp8(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC), 5) / 5
+    else:
+        t_wq = 0.0
+    torch.cuda.synchronize()
+    load_path = {
+        "prune_compress_us": t_prune * 1e6,
+        "prune_compress_GBs": (N * K * 2 + N * K + N * (K // 32) * 4) / t_prune / 1e9,
+        "quant_weight_us": t_wq * 1e6 if fp8 else None,
+        "quant_weight_GBs": (N * K // 2 * 2 + N * K // 2) / t_wq / 1e9 if fp8 else None,
+    }
+    del w
+
+    # weight copies, so that each call reads its weight from HBM
+    wbytes = qv.numel() * qv.element_size() + meta.numel() * 4
+    R = max(2, min(16, int(np.ceil(2.2 * LLC_BYTES / wbytes)))) if bound == "hbm" else 1
+    wq_copies = [qv] + [qv.clone() for _ in range(R - 1)]
+    meta_copies = [meta] + [meta.clone() for _ in range(R - 1)]
+
+    # per-M buffers (allocated once: graphs and timed loops allocate nothing)
+    bufs = {}
+    for m in Ms:
+        b = {"y": torch.empty(m, N, dtype=torch.bfloat16, device=dev)}
+        if fp8:
+            b["xq"] = torch.empty(m, K, dtype=torch.uint8, device=dev)
+            b["sx"] = torch.empty(1, dtype=torch.float32, device=dev)
+            nb = sp.workspace_size(sp.OP_QUANT, sp.BF16, m * K, 1, 1)
+            b["qws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        nb = sp.workspace_size(sp.OP_GEMM, dt, m, N, K)
+        b["gws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        b["plan"] = sp.plan(sp.OP_GEMM, dt, m, N, K)
+        bufs[m] = b
+
+    def call_quant(m):
+        b = bufs[m]
+        if fp8:
+            sp.quant_fp8(xs[m], scale=b["sx"], out=b["xq"], ws=b["qws"], mode=sp.SCALE_DYNAMIC)
+
+    def call_gemm(m, r):
+        b = bufs[m]
+        if fp8:
+            sp.gemm(b["xq"], wq_copies[r], meta_copies[r], x_scale=b["sx"], w_scale=sw, out=b["y"],
+                    ws=b["gws"])
+        else:
+            sp.gemm(xs[m], wq_copies[r], meta_copies[r], out=b["y"], ws=b["gws"])
+
+    def step(r):
+        for j, m in enumerate(Ms):
+            call_quant(m)
+            call_gemm(m, (r * len(Ms) + j) % R)
+
+    # eager reference of every M's output for one rotation index
+    step(0)
+    torch.cuda.synchronize()
+    eager = {m: bufs[m]["y"].clone() for m in Ms}
+
+    # ---------------------------------------------------------------- graphs
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    n_graphs = R  # one graph per rotation start
+    for r in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def replay(i):
+        graphs[i % n_graphs].replay()
+
+    for i in range(args.warmup):
+        replay(i)
+    torch.cuda.synchronize()
+    t_steps = ev.time(replay, args.steps)
+    ms_per_step = t_steps / args.steps * 1e3
+
+    # graphs replayed many times must reproduce the eager outputs bitwise
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    for m in Ms:
+        if not torch.equal(bufs[m]["y"].view(torch.int16), eager[m].view(torch.int16)):
+            raise SystemExit("graph replay output differs from the eager run for M=%d" % m)
+
+    step_bytes = sum(gemm_bytes(m, N, K, fp8) + (quant_bytes(m, K) if fp8 else 0) for m in Ms)
+    step_flops = sum(2 * m * N * K for m in Ms)          # dense-equivalent
+    value_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+
+    # ---------------------------------------------------------------- dominant kernel
+    per_m = {}
+    for m in Ms:
+        reps = args.kernel_reps or (R * 16 if bound == "hbm" else 5)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                call_gemm(m, i % R)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t = ev.time(lambda i: g.replay(), 3) / 3 / reps
+        gb = gemm_bytes(m, N, K, fp8)
+        per_m[m] = {"gemm_us": t * 1e6, "GBs": gb / t / 1e9,
+                    "hbm_frac": gb / t / 1e9 / HBM_PEAK_GBS,
+                    "tflops_dense_equiv": 2 * m * N * K / t / 1e12,
+                    "tflops_effective": m * N * K / t / 1e12,
+                    "plan": {k2: v for k2, v in bufs[m]["plan"].items()
+                             if k2 in ("tile_n", "tile_m", "waves", "split_k")}}
+        del g
+    for m in Ms:  # quantiser alone
+        if fp8:
+            reps = 200
+            t = ev.time(lambda i: call_quant(m), reps) / reps
+            per_m[m]["quant_x_us_eager"] = t * 1e6
+
+    # ---------------------------------------------------------------- dense baseline
+    if not args.no_dense:
+        wd = sp.decompress(qv, meta, K)
+        Rd = max(2, min(16, int(np.ceil(2.2 * LLC_BYTES / (wd.numel() * wd.element_size()))))) \
+            if bound == "hbm" else 1
+        wd_copies = [wd] + [wd.clone() for _ in range(Rd - 1)]
+        for m in Ms:
+            b = bufs[m]
+            xin = b["xq"] if fp8 else xs[m]
+            yd = torch.empty_like(b["y"])
+            nb = sp.workspace_size(sp.OP_DENSE_GEMM, dt, m, N, K)
+            dws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+
+            def dcall(i, m=m, xin=xin, yd=yd, dws=dws):
+                sp.dense_gemm(xin, wd_copies[i % Rd], x_scale=bufs[m].get("sx"), w_scale=sw, out=yd,
+                              ws=dws)
+            reps = args.kernel_reps or (Rd * 16 if bound == "hbm" else 5)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    dcall(i)
+            g.replay()
+            torch.cuda.synchronize()
+            t = ev.time(lambda i: g.replay(), 3) / 3 / reps
+            db = dense_bytes(m, N, K, fp8)
+            per_m[m]["dense_gemm_us"] = t * 1e6
+            per_m[m]["dense_GBs"] = db / t / 1e9
+            per_m[m]["sparse_speedup_vs_dense"] = t / (per_m[m]["gemm_us"] / 1e6)
+            del g
+        del wd_copies, wd
+
+    if bound == "hbm":
+        tot_b = sum(gemm_bytes(m, N, K, fp8) for m in Ms)
+        tot_t = sum(per_m[m]["gemm_us"] for m in Ms) / 1e6
+        achieved = tot_b / tot_t / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "kernel": "gemm_skinny_kernel (sparse %s), mean over M=%s"
+                              % ("fp8" if fp8 else "bf16", "/".join(map(str, Ms)))}
+    else:
+        m = Ms[0]
+        eff = per_m[m]["tflops_effective"]
+        peak = FP8_DENSE_PEAK_TFLOPS if fp8 else BF16_DENSE_PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": eff, "peak": peak, "unit": "TFLOP/s",
+                    "frac": eff / peak, "traffic": None,
+                    "kernel": "sparse GEMM, nonzero MACs x2 per second vs the dense %s MFMA peak"
+                              % ("FP8" if fp8 else "BF16")}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline and bound == "hbm":
+        cpu = cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes)
+
+    out = {
+        "metric": METRIC,
+        "value": value_gbs if bound == "hbm" else step_flops / 2 / (ms_per_step / 1e3) / 1e12,
+        "unit": "GB/s" if bound == "hbm" else "TFLOP/s (nonzero MACs x2)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded, workloads/)",
+        "config": {"workload": desc, "M": Ms, "K": K, "N": N, "weight_copies": R,
+                   "step": "per M: quantise X + sparse GEMM" if fp8 else "per M: sparse GEMM"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_m": {str(m): per_m[m] for m in Ms},
+        "step_GB": step_bytes / 1e9,
+        "step_tflops_dense_equiv": step_flops / (ms_per_step / 1e3) / 1e12,
+        "load_path": load_path,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes):
+    """The CPU oracle's per-call path on the same inputs: quantise X and the float64
+    product over the decompressed weight, one full step (all M) per repetition."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import sp24_ref as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wb = W.bf16_bits(w_cpu)
+    v, meta = O.prune_compress(wb)            # load path, not timed
+    if fp8:
+        vq, sw = O.quant_fp8(v)
+    xb = {m: W.bf16_bits(xs_cpu[m]) for m in Ms}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for m in Ms:
+            if fp8:
+                xq, sx = O.quant_fp8(xb[m])
+                ref, mag = O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, K))
+            else:
+                ref, mag = O.gemm_ref(*O.sparse_operands_bf16(xb[m], v, meta, K))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 20:
+            break
+    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%d full step(s) of the same workload (quantise X, decompress W, float64 "
+                      "product and magnitude sum for M=%s), %.1f s wall" % (
+                          reps, "/".join(map(str, Ms)), el)}
+
+
+if __name__ == "__main__":
+    main()

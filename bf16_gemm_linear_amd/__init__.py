@@ -1,0 +1,287 @@
+"""Python binding of libsp24: 2:4 structured-sparse GEMM for gfx950 (MI355X).
+
+Thin ctypes marshalling over the C ABI declared in include/sp24.h: every call
+checks dtypes, devices, shapes and contiguity of torch tensors, passes their
+device pointers and the current HIP stream, and raises on a non-OK status.
+PyTorch is used only for device memory and streams; all arithmetic runs in the
+library's HIP kernels.  If libsp24.so is missing this module raises on import:
+there is no fallback.
+
+    values, meta = prune_compress(w)                    # w: [n, k] bf16 on the GPU
+    xq, sx = quant_fp8(x)                               # per-tensor dynamic scale
+    y = gemm(xq, values_q, meta, x_scale=sx, w_scale=sw)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM",
+    "Sp24Error", "lib", "lib_path", "version",
+    "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
+    "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
+]
+
+BF16, FP8 = 0, 1
+SCALE_DYNAMIC, SCALE_STATIC = 0, 1
+OP_GEMM, OP_QUANT, OP_DENSE_GEMM = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libsp24.so")
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        "libsp24.so is not built (expected at %s); run `python -m bf16_gemm_linear_amd.build`" % lib_path)
+
+lib = ctypes.CDLL(lib_path)
+
+_vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", _int), ("tile_n", _int), ("tile_m", _int), ("waves", _int),
+                ("split_k", _int), ("grid_x", _int), ("grid_y", _int), ("grid_z", _int),
+                ("workspace_bytes", _sz)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_SIGS = {
+    "sp24_prune_compress": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "sp24_decompress": [_int, _vp, _vp, _i64, _i64, _vp, _vp],
+    "sp24_quant_fp8": [_vp, _i64, _vp, _vp, _int, _vp, _sz, _vp],
+    "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
+    "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
+    "sp24_status_string": [_int],
+    "sp24_version": [],
+    "sp24_probe_mfma_layout": [_int, _vp, _vp, _vp, _vp, _int, _vp],
+    "sp24_probe_mfma_rate": [_int, _int, _int, _int, _vp, _vp],
+    "sp24_probe_copy": [_vp, _vp, _sz, _vp],
+    "sp24_probe_read": [_vp, _sz, _vp, _vp],
+    "sp24_probe_read_blocks": [],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _int
+lib.sp24_workspace_size.restype = _sz
+lib.sp24_status_string.restype = ctypes.c_char_p
+
+
+class Sp24Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, lib.sp24_status_string(status).decode(), status))
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Sp24Error(fn, status)
+
+
+def version() -> int:
+    return lib.sp24_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must be %d-D" % (name, ndim))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+_FP8_T = torch.float8_e4m3fn
+_CODE_T = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _dtype_of(t):
+    return BF16 if t.dtype == torch.bfloat16 else FP8
+
+
+def workspace_size(op: int, dtype: int, m: int, n: int, k: int) -> int:
+    return int(lib.sp24_workspace_size(op, dtype, m, n, k))
+
+
+def plan(op: int, dtype: int, m: int, n: int, k: int) -> dict:
+    p = Plan()
+    _check("sp24_plan_gemm", lib.sp24_plan_gemm(op, dtype, m, n, k, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prune_compress(w: torch.Tensor, values: torch.Tensor | None = None,
+                   meta: torch.Tensor | None = None):
+    """2:4-prune a bf16 weight [n, k] along k and compress it -> (values [n, k/2], meta [n, k/32] int32)."""
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    if values is None:
+        values = torch.empty(n, k // 2, dtype=torch.bfloat16, device=w.device)
+    if meta is None:
+        meta = torch.empty(n, max(k // 32, 1), dtype=torch.int32, device=w.device)
+    _need(values, "values", torch.bfloat16, 2, w.device)
+    _need(meta, "meta", torch.int32, 2, w.device)
+    _check("sp24_prune_compress",
+           lib.sp24_prune_compress(_ptr(w), n, k, _ptr(values), _ptr(meta), _stream(w.device)))
+    return values, meta
+
+
+def decompress(values: torch.Tensor, meta: torch.Tensor, k: int, out: torch.Tensor | None = None):
+    """Dense pruned W [n, k] from (values, meta); bf16 values give bf16, E4M3 codes give uint8 codes."""
+    _need(values, "values", (torch.bfloat16,) + _CODE_T, 2)
+    _need(meta, "meta", torch.int32, 2, values.device)
+    n = values.shape[0]
+    dt = BF16 if values.dtype == torch.bfloat16 else FP8
+    if out is None:
+        out = torch.empty(n, k, dtype=torch.bfloat16 if dt == BF16 else torch.uint8, device=values.device)
+    _need(out, "out", torch.bfloat16 if dt == BF16 else _CODE_T, 2, values.device)
+    _check("sp24_decompress",
+           lib.sp24_decompress(dt, _ptr(values), _ptr(meta), n, k, _ptr(out), _stream(values.device)))
+    return out
+
+
+def quant_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None, mode: int | None = None):
+    """Per-tensor E4M3 quantisation of a bf16 tensor -> (codes uint8, scale fp32[1]).
+
+    mode SCALE_DYNAMIC (the default without `scale`): s = amax/448 is computed on
+    the device and written to `scale` (a new fp32[1] tensor when None).
+    mode SCALE_STATIC (the default with `scale`): the given fp32 device scalar is used.
+    """
+    _need(x, "x", torch.bfloat16)
+    count = x.numel()
+    if mode is None:
+        mode = SCALE_DYNAMIC if scale is None else SCALE_STATIC
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, "out", _CODE_T, None, x.device)
+    if out.numel() != count:
+        raise ValueError("out has the wrong size")
+    if scale is None:
+        if mode == SCALE_STATIC:
+            raise ValueError("static mode needs a scale")
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(scale, "scale", torch.float32, None, x.device)
+    nbytes = workspace_size(OP_QUANT, BF16, count, 1, 1) if mode == SCALE_DYNAMIC else 0
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_quant_fp8",
+           lib.sp24_quant_fp8(_ptr(x), count, _ptr(out), _ptr(scale), mode, _ptr(ws), nbytes,
+                              _stream(x.device)))
+    return out, scale
+
+
+def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
+    _need(x, "x", (torch.bfloat16,) + _CODE_T, 2)
+    dt = BF16 if x.dtype == torch.bfloat16 else FP8
+    m, k = x.shape
+    _need(w, "w", torch.bfloat16 if dt == BF16 else _CODE_T, 2, x.device)
+    n = w.shape[0]
+    if sparse:
+        _need(meta, "meta", torch.int32, 2, x.device)
+        if w.shape[1] * 2 != k or meta.shape != (n, k // 32):
+            raise ValueError("compressed weight shapes do not match k=%d" % k)
+    elif w.shape[1] != k:
+        raise ValueError("w has %d columns, x has %d" % (w.shape[1], k))
+    if dt == FP8:
+        if x_scale is None or w_scale is None:
+            raise ValueError("FP8 operands need x_scale and w_scale")
+        _need(x_scale, "x_scale", torch.float32, None, x.device)
+        _need(w_scale, "w_scale", torch.float32, None, x.device)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    op = OP_GEMM if sparse else OP_DENSE_GEMM
+    nbytes = workspace_size(op, dt, m, n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    xs = _ptr(x_scale) if dt == FP8 else None
+    wsc = _ptr(w_scale) if dt == FP8 else None
+    if sparse:
+        st = lib.sp24_gemm(dt, m, n, k, _ptr(x), xs, _ptr(w), _ptr(meta), wsc, _ptr(out), _ptr(ws),
+                           nbytes, _stream(x.device))
+        _check("sp24_gemm", st)
+    else:
+        st = lib.sp24_dense_gemm(dt, m, n, k, _ptr(x), xs, _ptr(w), wsc, _ptr(out), _ptr(ws), nbytes,
+                                 _stream(x.device))
+        _check("sp24_dense_gemm", st)
+    return out
+
+
+def gemm(x, values, meta, x_scale=None, w_scale=None, out=None, ws=None):
+    """Y = X . W^T with W compressed 2:4 (values, meta); bf16 output [m, n]."""
+    return _gemm(True, x, values, meta, x_scale, w_scale, out, ws)
+
+
+def dense_gemm(x, w, x_scale=None, w_scale=None, out=None, ws=None):
+    """Dense-MFMA baseline Y = X . W^T with an uncompressed W [n, k]."""
+    return _gemm(False, x, w, None, x_scale, w_scale, out, ws)
+
+
+# --------------------------------------------------------------------------- probes
+
+def probe_mfma_layout(variant: int, a: torch.Tensor, b: torch.Tensor, idx: torch.Tensor,
+                      c: torch.Tensor, n_exp: int):
+    for t, nm in ((a, "a"), (b, "b"), (idx, "idx"), (c, "c")):
+        _need(t, nm)
+    if a.numel() * a.element_size() < n_exp * 64 * 32 or b.numel() * b.element_size() < n_exp * 64 * 32:
+        raise ValueError("a/b too small")
+    if idx.numel() * idx.element_size() < n_exp * 64 * 4 or c.numel() * c.element_size() < n_exp * 64 * 64:
+        raise ValueError("idx/c too small")
+    _check("sp24_probe_mfma_layout",
+           lib.sp24_probe_mfma_layout(variant, _ptr(a), _ptr(b), _ptr(idx), _ptr(c), n_exp,
+                                      _stream(a.device)))
+
+
+def probe_mfma_rate(variant: int, iters: int, blocks: int, waves: int, out: torch.Tensor):
+    _need(out, "out", torch.float32)
+    if out.numel() < blocks * waves * 64:
+        raise ValueError("out too small")
+    _check("sp24_probe_mfma_rate",
+           lib.sp24_probe_mfma_rate(variant, iters, blocks, waves, _ptr(out), _stream(out.device)))
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor):
+    _need(src, "src")
+    _need(dst, "dst", None, None, src.device)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check("sp24_probe_copy", lib.sp24_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+
+
+def probe_read(src: torch.Tensor, out: torch.Tensor):
+    _need(src, "src")
+    _need(out, "out", torch.int32, None, src.device)
+    if out.numel() < lib.sp24_probe_read_blocks():
+        raise ValueError("out too small")
+    _check("sp24_probe_read",
+           lib.sp24_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), _stream(src.device)))

@@ -1,0 +1,269 @@
+// Small-m ("decode") GEMM kernels: Y[m, n] = sum_k X[m, k] W[n, k].
+//
+// At decode sizes the product streams the weight once and is bound by HBM
+// bandwidth, so the kernel is organised around coalesced weight loads and as
+// many loads in flight as possible; MFMA throughput is irrelevant here.
+//
+// Instruction mapping.  The sparse matrix instruction takes the compressed
+// operand as "A" and the dense one as "B", so W (compressed, 16 rows) is A and
+// X (16 tokens) is B; the 16x16 accumulator is a tile of Y^T:
+//   lane l, accumulator register i  <->  n = 4*(l/16) + i,  m = l % 16.
+// A lane of A holds row l%16 and, for lane group q = l/16, one 32-wide slice
+// of K with its 8 index nibbles (one metadata word).  B lane l holds token
+// l%16 and two 16-byte halves of K taken from the slices of lane groups
+// q/2 and q/2 + 2 (the B layout measured on gfx950 with one-hot probes).
+//
+// K permutation.  Within a "chunk" of T units (a unit = 128 values of K, one
+// metadata word per lane group), lane group q takes the contiguous K range
+// [kb + 32*T*q, kb + 32*T*(q+1)) and unit u of the chunk reads its u-th
+// 32-slice.  A and B use the same map, so the sum over K is unchanged while
+// every lane reads contiguous weight bytes: 16*T compressed values and T
+// metadata words per lane; activations come in 16-byte pieces.
+//
+// K split.  Chunks are dealt round-robin to the waves of a workgroup (and to
+// grid.z slices when split_k > 1); wave partial tiles are reduced through LDS
+// in a fixed wave order, split-K partials by a second kernel in a fixed slice
+// order, so results are bitwise reproducible.
+//
+// The dense baseline (W uncompressed, dense MFMA) shares the structure.
+#include "sp24_common.hpp"
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+namespace {
+
+// Loads of n 16-byte vectors from p.
+template <int N>
+__device__ __forceinline__ void load16(i32x4 (&dst)[N], const uint8_t* p) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) dst[j] = *reinterpret_cast<const i32x4*>(p + 16 * j);
+}
+
+template <int T>
+__device__ __forceinline__ void load_meta(uint32_t (&dst)[T], const uint32_t* p) {
+  if constexpr (T == 4) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  } else if constexpr (T == 2) {
+    u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else {
+#pragma unroll
+    for (int j = 0; j < T; ++j) dst[j] = p[j];
+  }
+}
+
+__device__ __forceinline__ i32x8 cat(i32x4 a, i32x4 b) {
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x16 as_bf16x16(i32x4 a, i32x4 b) {
+  return __builtin_bit_cast(bf16x16, cat(a, b));
+}
+
+// Element offset (within a row of X) of the v-th 16-byte piece of unit u for a
+// lane of group q.  Dense instructions pair A and B slots one to one, so B
+// mirrors A's contiguous slice.  The sparse instructions' B operand is split
+// in two halves: half h of lane group q holds instruction K
+// [h*Kt/2 + q*Kt/8, +Kt/8) (Kt = 128 for fp8, 64 for bf16), which belongs to
+// the A slice of lane group (q >> 1) + 2h at offset (q & 1) * Kt/8.
+template <int DT, bool SPARSE, int T>
+__device__ __forceinline__ int x_piece(int kb, int q, int u, int v) {
+  if constexpr (SPARSE) {
+    if constexpr (DT == SP24_FP8_E4M3) {
+      return kb + 32 * T * ((q >> 1) + 2 * v) + 32 * u + 16 * (q & 1);
+    } else {
+      const int h = v >> 1, half = v & 1;  // instruction h of the unit, B half
+      return kb + 32 * T * ((q >> 1) + 2 * half) + 32 * u + 16 * h + 8 * (q & 1);
+    }
+  } else {
+    constexpr int ESZ = DT == SP24_BF16 ? 2 : 1;
+    return kb + 32 * T * q + 32 * u + v * (16 / ESZ);
+  }
+}
+
+// One chunk of T units for RB row blocks (16 rows of W each) and MB token
+// blocks (16 rows of X each).  DT: SP24_BF16 or SP24_FP8_E4M3; SPARSE: W in
+// compressed form (values + meta) or dense.
+template <int DT, bool SPARSE, int T, int RB, int MB>
+__device__ __forceinline__ void chunk(f32x4 (&acc)[RB][MB], const uint8_t* __restrict__ w,
+                                      const uint32_t* __restrict__ meta,
+                                      const uint8_t* __restrict__ x, int n0, int m0, int kb,
+                                      int lane, int N, int M, int K) {
+  constexpr int ESZ = DT == SP24_BF16 ? 2 : 1;
+  // bytes per lane per unit: compressed W 16*ESZ (dense 32*ESZ), X 32*ESZ
+  constexpr int WV = (SPARSE ? 16 : 32) * ESZ / 16;  // 16-byte vectors of W per unit
+  constexpr int XV = 32 * ESZ / 16;                  // 16-byte vectors of X per unit
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kq = kb + 32 * T * q;  // first K of this lane group
+
+  i32x4 wv[RB][T * WV];
+  uint32_t mt[RB][T];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int row = n0 + rb * 16 + r16;
+    row = row < N ? row : N - 1;  // ragged n: clamp the load, the store is masked
+    if constexpr (SPARSE) {
+      load_meta<T>(mt[rb], meta + (size_t)row * (K / 32) + kq / 32);
+      load16<T * WV>(wv[rb], w + ((size_t)row * (K / 2) + kq / 2) * ESZ);
+    } else {
+      load16<T * WV>(wv[rb], w + ((size_t)row * K + kq) * ESZ);
+    }
+  }
+  i32x4 xv[MB][T * XV];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + mb * 16 + r16;
+    if (m < M) {
+      const uint8_t* xr = x + (size_t)m * K * ESZ;
+#pragma unroll
+      for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+          xv[mb][u * XV + v] =
+              *reinterpret_cast<const i32x4*>(xr + x_piece<DT, SPARSE, T>(kb, q, u, v) * ESZ);
+    } else {
+#pragma unroll
+      for (int j = 0; j < T * XV; ++j) xv[mb][j] = i32x4{0, 0, 0, 0};
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
+          acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(
+              wv[rb][u], cat(xv[mb][2 * u], xv[mb][2 * u + 1]), acc[rb][mb], (int)mt[rb][u], 0, 0);
+        } else if constexpr (SPARSE && DT == SP24_BF16) {
+          // groups 0..3 of the word (first 16 K of the slice), then groups 4..7
+          acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+              as_bf16x8(wv[rb][2 * u]), as_bf16x16(xv[mb][4 * u], xv[mb][4 * u + 1]), acc[rb][mb],
+              (int)mt[rb][u], 0, 0);
+          acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+              as_bf16x8(wv[rb][2 * u + 1]), as_bf16x16(xv[mb][4 * u + 2], xv[mb][4 * u + 3]),
+              acc[rb][mb], (int)mt[rb][u], 0, 1);
+        } else if constexpr (!SPARSE && DT == SP24_FP8_E4M3) {
+          acc[rb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              cat(wv[rb][2 * u], wv[rb][2 * u + 1]), cat(xv[mb][2 * u], xv[mb][2 * u + 1]),
+              acc[rb][mb], 0, 0, 0, 0, 0, 0);
+        } else {
+          // dense bf16: 4 instructions of K=32 (8 values per lane group each)
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(wv[rb][4 * u + h]), as_bf16x8(xv[mb][4 * u + h]), acc[rb][mb], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <int DT, bool SPARSE, int RB, int MB, int NW, bool PARTIAL>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
+    const uint32_t* __restrict__ meta, const float* __restrict__ x_scale,
+    const float* __restrict__ w_scale, uint16_t* __restrict__ y, float* __restrict__ partial,
+    int M, int N, int K) {
+  constexpr int TILE = RB * MB * 256;  // floats per wave tile
+  __shared__ float red[NW * TILE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * (RB * 16), m0 = blockIdx.y * (MB * 16);
+  const int splits = gridDim.z;
+
+  f32x4 acc[RB][MB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int units = K / 128;
+  const int full = units / 4, tail = units % 4;
+  const int nchunks = full + (tail ? 1 : 0);
+  const int workers = splits * NW;
+  for (int c = blockIdx.z * NW + wave; c < nchunks; c += workers) {
+    const int kb = c * 512;
+    if (c < full) {
+      chunk<DT, SPARSE, 4, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    } else if (tail == 1) {
+      chunk<DT, SPARSE, 1, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    } else if (tail == 2) {
+      chunk<DT, SPARSE, 2, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    } else {
+      chunk<DT, SPARSE, 3, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    }
+  }
+
+  // wave tiles -> LDS, element (rb, mb, i, lane) at ((rb*MB + mb)*4 + i)*64 + lane
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave * TILE + ((rb * MB + mb) * 4 + i) * 64 + lane] = acc[rb][mb][i];
+  __syncthreads();
+
+  float scale = 1.0f;
+  if constexpr (DT == SP24_FP8_E4M3) {
+    if (!PARTIAL) scale = x_scale[0] * w_scale[0];
+  }
+  // Output o = ((rb*MB + mb)*16 + mi)*16 + nj: consecutive threads take
+  // consecutive n of one token row.
+  for (int o = threadIdx.x; o < TILE; o += NW * 64) {
+    const int nj = o & 15, mi = (o >> 4) & 15, blk = o >> 8;  // blk = rb*MB + mb
+    const int rb = blk / MB, mb = blk % MB;
+    const int src = (blk * 4 + (nj & 3)) * 64 + (nj >> 2) * 16 + mi;
+    float s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) s += red[wv * TILE + src];
+    const int n = n0 + rb * 16 + nj, m = m0 + mb * 16 + mi;
+    if (n < N && m < M) {
+      if constexpr (PARTIAL)
+        partial[((size_t)blockIdx.z * M + m) * N + n] = s;
+      else
+        y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s * scale);
+    }
+  }
+}
+
+template <int DT, bool SPARSE, int RB, int MB, int NW>
+hipError_t launch_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(NW * 64);
+  const uint8_t* x = static_cast<const uint8_t*>(a.x);
+  const uint8_t* w = static_cast<const uint8_t*>(a.w);
+  if (p.split_k > 1)
+    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, true>), grid, block, 0, s, x, w,
+                       a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, false>), grid, block, 0, s, x, w,
+                       a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+  return hipGetLastError();
+}
+
+template <int DT, bool SPARSE>
+hipError_t launch_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  const int rb = p.tile_n / 16, mb = p.tile_m / 16, nw = p.waves;
+  // The plan table only produces these shapes (checked by the plan tests).
+  if (rb == 1 && mb == 1 && nw == 4) return launch_cfg<DT, SPARSE, 1, 1, 4>(a, p, s);
+  if (rb == 1 && mb == 1 && nw == 8) return launch_cfg<DT, SPARSE, 1, 1, 8>(a, p, s);
+  if (rb == 2 && mb == 1 && nw == 8) return launch_cfg<DT, SPARSE, 2, 1, 8>(a, p, s);
+  if (rb == 2 && mb == 2 && nw == 8) return launch_cfg<DT, SPARSE, 2, 2, 8>(a, p, s);
+  if (rb == 2 && mb == 4 && nw == 4) return launch_cfg<DT, SPARSE, 2, 4, 4>(a, p, s);
+  if (rb == 4 && mb == 4 && nw == 4) return launch_cfg<DT, SPARSE, 4, 4, 4>(a, p, s);
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  if (a.dtype == SP24_FP8_E4M3)
+    return a.sparse ? launch_dt<SP24_FP8_E4M3, true>(a, p, s) : launch_dt<SP24_FP8_E4M3, false>(a, p, s);
+  return a.sparse ? launch_dt<SP24_BF16, true>(a, p, s) : launch_dt<SP24_BF16, false>(a, p, s);
+}
+
+}  // namespace sp24

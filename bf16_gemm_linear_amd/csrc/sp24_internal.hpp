@@ -1,0 +1,43 @@
+// Host-side launch functions of the libsp24 kernels.  Arguments are already
+// validated by the C ABI layer (sp24_api.hip) when these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sp24.h"
+
+namespace sp24 {
+
+// sp24_format.hip
+hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16_t* values,
+                                 uint32_t* meta, hipStream_t s);
+hipError_t launch_decompress(int dtype, const void* values, const uint32_t* meta, int64_t n,
+                             int64_t k, void* out, hipStream_t s);
+
+// sp24_quant.hip
+size_t quant_workspace_bytes(int64_t count);
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
+                            void* ws, hipStream_t s);
+
+// sp24_gemm_skinny.hip / sp24_gemm_tiled.hip / sp24_reduce.hip
+struct GemmArgs {
+  int dtype;
+  bool sparse;
+  int m, n, k;
+  const void* x;
+  const float* x_scale;
+  const void* w;        // compressed values (sparse) or dense W
+  const uint32_t* meta; // sparse only
+  const float* w_scale;
+  uint16_t* y;
+  float* partial;       // split-K partial sums [split_k][m][n], or nullptr
+};
+hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
+hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
+hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s);
+
+// host plan (sp24_plan.cpp logic lives in sp24_api.hip)
+int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out);
+
+}  // namespace sp24

@@ -1,0 +1,220 @@
+// Layout, issue-rate and bandwidth probes (see include/sp24_probe.h).
+//
+// The layout probe runs one matrix instruction per wave on operands read from
+// memory and writes back the accumulator registers, so the host can map
+// lanes, registers and sparse index bits to matrix coordinates with one-hot
+// inputs.  Every access is at a fixed per-lane stride inside buffers whose
+// size the caller derives from n_exp.
+#include "../../include/sp24_probe.h"
+#include "sp24_common.hpp"
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+namespace {
+
+template <int V>
+__global__ __launch_bounds__(64) void layout_kernel(const uint8_t* __restrict__ a,
+                                                    const uint8_t* __restrict__ b,
+                                                    const uint32_t* __restrict__ idx,
+                                                    float* __restrict__ c) {
+  const int64_t slot = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const i32x4 a0 = *reinterpret_cast<const i32x4*>(a + slot * 32);
+  const i32x4 a1 = *reinterpret_cast<const i32x4*>(a + slot * 32 + 16);
+  const i32x4 b0 = *reinterpret_cast<const i32x4*>(b + slot * 32);
+  const i32x4 b1 = *reinterpret_cast<const i32x4*>(b + slot * 32 + 16);
+  const int ix = (int)idx[slot];
+  const i32x8 bb{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  float* out = c + slot * 16;
+  if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_FP8 || V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0 ||
+                V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID1 || V == SP24_PROBE_MFMA_16x16x128_FP8 ||
+                V == SP24_PROBE_MFMA_16x16x32_BF16) {
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+    if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_FP8)
+      acc = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a0, bb, acc, ix, 0, 0);
+    else if constexpr (V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0)
+      acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                      __builtin_bit_cast(bf16x16, bb), acc, ix, 0, 0);
+    else if constexpr (V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID1)
+      acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                      __builtin_bit_cast(bf16x16, bb), acc, ix, 0, 1);
+    else if constexpr (V == SP24_PROBE_MFMA_16x16x128_FP8) {
+      const i32x8 aa{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc, 0, 0, 0, 0, 0, 0);
+    } else
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                    __builtin_bit_cast(bf16x8, b0), acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = acc[i];
+  } else {
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8)
+      acc = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a0, bb, acc, ix, 0, 0);
+    else if constexpr (V == SP24_PROBE_SMFMAC_32x32x32_BF16_ABID0)
+      acc = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                      __builtin_bit_cast(bf16x16, bb), acc, ix, 0, 0);
+    else
+      acc = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                      __builtin_bit_cast(bf16x16, bb), acc, ix, 0, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = acc[i];
+  }
+}
+
+// Back-to-back instructions on register operands, four independent chains.
+template <int V>
+__global__ void rate_kernel(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  i32x4 a = {lane, lane + 1, lane + 2, lane + 3};
+  i32x8 b = {lane, 1, 2, 3, 4, 5, 6, lane};
+  const int ix = 0x88888888 ^ lane;  // any valid-looking index pattern
+  float r = 0.f;
+  if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8 || V == SP24_PROBE_SMFMAC_32x32x32_BF16_ABID0) {
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+      if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8) {
+        c0 = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c3, ix, 0, 0);
+      } else {
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, a);
+        const bf16x16 bb = __builtin_bit_cast(bf16x16, b);
+        c0 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aa, bb, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aa, bb, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aa, bb, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aa, bb, c3, ix, 0, 0);
+      }
+    }
+    for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  } else {
+    f32x4 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const i32x8 a8 = {lane, 1, 2, 3, 4, 5, 6, 7};
+    for (int it = 0; it < iters; ++it) {
+      if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_FP8) {
+        c0 = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c3, ix, 0, 0);
+      } else if constexpr (V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0) {
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, a);
+        const bf16x16 bb = __builtin_bit_cast(bf16x16, b);
+        c0 = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(aa, bb, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(aa, bb, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(aa, bb, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(aa, bb, c3, ix, 0, 0);
+      } else if constexpr (V == SP24_PROBE_MFMA_16x16x128_FP8) {
+        c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c0, 0, 0, 0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c1, 0, 0, 0, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c2, 0, 0, 0, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c3, 0, 0, 0, 0, 0, 0);
+      } else {
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, a);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, a + 1);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, c3, 0, 0, 0);
+      }
+    }
+    for (int i = 0; i < 4; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  }
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t nvec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride)
+    dst[i] = ld_nt(src + i);
+}
+
+constexpr int kReadBlocks = 256 * 8;
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t nvec,
+                                                   uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    const u32x4 v = ld_nt(src + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
+  __shared__ uint32_t sh[4];
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
+}
+
+}  // namespace
+}  // namespace sp24
+
+using namespace sp24;
+
+extern "C" {
+
+int sp24_probe_mfma_layout(int variant, const void* a, const void* b, const uint32_t* idx, float* c,
+                           int n_exp, void* stream) {
+  if (variant < 0 || variant >= SP24_PROBE_N_VARIANTS) return SP24_ERR_MODE;
+  if (!a || !b || !idx || !c) return SP24_ERR_NULL;
+  if (n_exp < 1 || n_exp > (1 << 20)) return SP24_ERR_SHAPE;
+  if ((((uintptr_t)a | (uintptr_t)b | (uintptr_t)idx | (uintptr_t)c) & 15u) != 0) return SP24_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* pa = static_cast<const uint8_t*>(a);
+  const uint8_t* pb = static_cast<const uint8_t*>(b);
+  switch (variant) {
+#define SP24_LAYOUT_CASE(V) \
+  case V: hipLaunchKernelGGL(layout_kernel<V>, dim3(n_exp), dim3(64), 0, s, pa, pb, idx, c); break;
+    SP24_LAYOUT_CASE(0) SP24_LAYOUT_CASE(1) SP24_LAYOUT_CASE(2) SP24_LAYOUT_CASE(3)
+    SP24_LAYOUT_CASE(4) SP24_LAYOUT_CASE(5) SP24_LAYOUT_CASE(6) SP24_LAYOUT_CASE(7)
+#undef SP24_LAYOUT_CASE
+  }
+  return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
+}
+
+int sp24_probe_mfma_rate(int variant, int iters, int blocks, int waves, float* out, void* stream) {
+  if (variant < 0 || variant >= SP24_PROBE_N_VARIANTS || variant == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID1 ||
+      variant == SP24_PROBE_SMFMAC_32x32x32_BF16_ABID1)
+    return SP24_ERR_MODE;
+  if (!out) return SP24_ERR_NULL;
+  if (iters < 1 || blocks < 1 || waves < 1 || waves > 16 || blocks > (1 << 20)) return SP24_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 g(blocks), blk(waves * 64);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL(rate_kernel<0>, g, blk, 0, s, iters, out); break;
+    case 1: hipLaunchKernelGGL(rate_kernel<1>, g, blk, 0, s, iters, out); break;
+    case 3: hipLaunchKernelGGL(rate_kernel<3>, g, blk, 0, s, iters, out); break;
+    case 4: hipLaunchKernelGGL(rate_kernel<4>, g, blk, 0, s, iters, out); break;
+    case 6: hipLaunchKernelGGL(rate_kernel<6>, g, blk, 0, s, iters, out); break;
+    case 7: hipLaunchKernelGGL(rate_kernel<7>, g, blk, 0, s, iters, out); break;
+  }
+  return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
+}
+
+int sp24_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return SP24_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return SP24_ERR_SHAPE;
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15u) != 0) return SP24_ERR_ALIGN;
+  const uintptr_t a0 = (uintptr_t)src, b0 = (uintptr_t)dst;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return SP24_ERR_ALIAS;
+  const int64_t nvec = (int64_t)(bytes / 16);
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(copy_kernel, dim3((int)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
+  return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
+}
+
+int sp24_probe_read_blocks(void) { return kReadBlocks; }
+
+int sp24_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (!src || !out) return SP24_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return SP24_ERR_SHAPE;
+  if ((((uintptr_t)src | (uintptr_t)out) & 15u) != 0) return SP24_ERR_ALIGN;
+  hipLaunchKernelGGL(read_kernel, dim3(kReadBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), (int64_t)(bytes / 16), out);
+  return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+// Per-tensor FP8-E4M3 quantisation of bf16 tensors.
+//
+// One scale per tensor from the tensor's own maximum magnitude, chosen so no
+// value overflows, with a clip at the format maximum ("Deploying 2:4 Sparsity
+// with FP8 on Hopper", pipeline step 3, step 6 and "Troubleshooting quick
+// hits").  s = fp32(amax / 448) (1 when amax is 0); q = e4m3_rne(clamp(x / s)).
+//
+// amax is order-independent and exact: it is taken on the integer keys
+// (bits & 0x7FFF), which order finite bf16 magnitudes exactly.
+//   small tensors (<= kFusedMax values): one workgroup does amax and the cast
+//                                        in one launch;
+//   larger tensors: kernel 1 writes one partial maximum per workgroup into the
+//                   workspace; kernel 2 re-reduces those partials in every
+//                   workgroup (a few KB from L2), stores the scale from
+//                   workgroup 0 and casts.  No atomics, no memset, no host sync.
+#include "sp24_common.hpp"
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;
+constexpr int64_t kFusedMax = 32768;
+constexpr int kFusedThreads = 1024;
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Block-wide maximum; every thread receives the result.
+template <int NT>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sh) {
+  v = wave_max(v);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) r = max(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint32_t key_max8(u32x4 d) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m = max(m, d[j] & 0x7FFFu);
+    m = max(m, (d[j] >> 16) & 0x7FFFu);
+  }
+  return m;
+}
+
+__device__ __forceinline__ float scale_from_key(uint32_t key) {
+  // amax is the bf16 value with bits `key`; the division is IEEE float32.
+  return key == 0 ? 1.0f : bf16_to_f32(key) / 448.0f;
+}
+
+// 8 bf16 -> 8 E4M3 codes
+__device__ __forceinline__ u32x2 cast8(u32x4 d, float s) {
+  uint32_t b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b[j] = f32x2_to_e4m3(bf16_to_f32(d[j] & 0xFFFFu) / s, bf16_to_f32(d[j] >> 16) / s);
+  return u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+}
+
+__device__ __forceinline__ uint8_t cast1(uint32_t h, float s) {
+  return (uint8_t)(f32x2_to_e4m3(bf16_to_f32(h) / s, 0.0f) & 0xFFu);
+}
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t* __restrict__ x,
+                                                                int64_t count,
+                                                                uint32_t* __restrict__ partial) {
+  __shared__ uint32_t sh[kThreads / kWave];
+  const int64_t nvec = count / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  uint32_t m = 0;
+  for (int64_t i = t0; i < nvec; i += stride) m = max(m, key_max8(ld_nt(xv + i)));
+  for (int64_t i = nvec * 8 + t0; i < count; i += stride) m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+  m = block_max<kThreads>(m, sh);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t count,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale,
+                                                        const uint32_t* __restrict__ partial,
+                                                        int npartial) {
+  __shared__ uint32_t sh[kThreads / kWave];
+  float s;
+  if (partial != nullptr) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npartial; i += kThreads) m = max(m, partial[i]);
+    m = block_max<kThreads>(m, sh);
+    s = scale_from_key(m);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  } else {
+    s = *scale;
+  }
+  const int64_t nvec = count / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x2* qv = reinterpret_cast<u32x2*>(q);
+  for (int64_t i = t0; i < nvec; i += stride) qv[i] = cast8(ld_nt(xv + i), s);
+  for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = cast1(x[i], s);
+}
+
+// Small tensors: amax and cast in one workgroup.
+__global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16_t* __restrict__ x,
+                                                                    int64_t count,
+                                                                    uint8_t* __restrict__ q,
+                                                                    float* __restrict__ scale,
+                                                                    int dynamic) {
+  __shared__ uint32_t sh[kFusedThreads / kWave];
+  const int64_t nvec = count / 8;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  float s;
+  if (dynamic) {
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < nvec; i += kFusedThreads) m = max(m, key_max8(xv[i]));
+    for (int64_t i = nvec * 8 + threadIdx.x; i < count; i += kFusedThreads)
+      m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+    m = block_max<kFusedThreads>(m, sh);
+    s = scale_from_key(m);
+    if (threadIdx.x == 0) *scale = s;
+  } else {
+    s = *scale;
+  }
+  u32x2* qv = reinterpret_cast<u32x2*>(q);
+  for (int64_t i = threadIdx.x; i < nvec; i += kFusedThreads) qv[i] = cast8(xv[i], s);
+  for (int64_t i = nvec * 8 + threadIdx.x; i < count; i += kFusedThreads) q[i] = cast1(x[i], s);
+}
+
+int n_partials(int64_t count) {
+  int64_t g = (count / 8 + kThreads * 4 - 1) / (kThreads * 4);  // >= 4 vectors per thread
+  if (g > kMaxPartials) g = kMaxPartials;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+size_t quant_workspace_bytes(int64_t count) {
+  if (count <= kFusedMax) return 0;
+  return (size_t)n_partials(count) * sizeof(uint32_t);
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
+                            void* ws, hipStream_t s) {
+  const bool dynamic = mode == SP24_SCALE_DYNAMIC;
+  if (count <= kFusedMax) {
+    hipLaunchKernelGGL(fused_quant_kernel, dim3(1), dim3(kFusedThreads), 0, s, x, count, q, scale,
+                       dynamic ? 1 : 0);
+    return hipGetLastError();
+  }
+  int64_t cast_blocks = (count / 8 + kThreads * 2 - 1) / (kThreads * 2);
+  if (cast_blocks > 256 * 8) cast_blocks = 256 * 8;
+  if (cast_blocks < 1) cast_blocks = 1;
+  if (!dynamic) {
+    hipLaunchKernelGGL(cast_kernel, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q,
+                       scale, (const uint32_t*)nullptr, 0);
+    return hipGetLastError();
+  }
+  const int np = n_partials(count);
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(np), dim3(kThreads), 0, s, x, count, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cast_kernel, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q, scale,
+                     (const uint32_t*)partial, np);
+  return hipGetLastError();
+}
+
+}  // namespace sp24

@@ -1,0 +1,169 @@
+/*
+ * sp24.h -- C ABI of libsp24: 2:4 structured-sparse GEMM Y = X . W^T for
+ * gfx950 (AMD Instinct MI355X), BF16 or FP8-E4M3 operands, fp32 accumulation,
+ * BF16 output.
+ *
+ * Operation sources ("the cookbook" = the page "Deploying 2:4 Sparsity with
+ * FP8 on Hopper: A Production Cookbook"):
+ *   - 2:4 magnitude pruning: the cookbook, pipeline step 4 (keep the two
+ *     largest-magnitude values of every group of 4) and step 2 (groups are 4
+ *     contiguous values along the inner dimension K of the [out, in] weight);
+ *     Practical Example 1 (top-2 of |w| per group of 4 along the chosen axis).
+ *   - Compressed form: the SlideSparse page ("SlideSparse: Fast and Flexible
+ *     (2N-2):2N Structured Sparsity") has weights converted once, offline, to
+ *     the hardware's compressed layout; this library defines that layout below.
+ *   - Per-tensor dynamic FP8 scaling with a clip at the format maximum: the
+ *     cookbook, pipeline steps 3 and 6 and "Troubleshooting quick hits".
+ *   - The sparse product on the linear/FFN projections: the cookbook, pipeline
+ *     step 2 and its "What to prune" table.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, contiguous, row-major device buffers owned by the
+ *     caller.  The library never allocates or frees device memory and keeps no
+ *     mutable global state; calls are reentrant.
+ *   - W is [n, k] (the nn.Linear weight layout), X is [m, k], Y is [m, n].
+ *   - bf16 buffers hold IEEE bfloat16 bit patterns; FP8 buffers hold OCP
+ *     E4M3FN byte codes (bias 7, max 448, NaN = 0x7F/0xFF, no infinities).
+ *   - Compressed weight of W [n, k]:
+ *       values [n, k/2]: the two kept values of group g (columns 4g..4g+3) at
+ *                        columns 2g and 2g+1, in ascending position order;
+ *       meta   [n, k/32] uint32: group g's nibble (i0 | i1 << 2), i0 < i1 the
+ *                        kept positions inside the group, at bits 4*(g % 8) of
+ *                        word g / 8.
+ *     The kept pair of a group: the two largest |w|, magnitudes compared
+ *     exactly, ties to the lower index, +0 == -0.  Inputs must be finite.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; results are visible after the stream is synchronised.
+ *   - Every argument is validated before any HIP call.  The return value is
+ *     SP24_OK or a negative sp24_status.  Faults inside a kernel surface at the
+ *     caller's next synchronisation; with the environment variable
+ *     SP24_SYNC_CHECK=1 every call synchronises its stream and reports them.
+ *   - Device pointers must be 16-byte aligned.  Outputs must not overlap inputs.
+ */
+#ifndef SP24_H
+#define SP24_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SP24_VERSION 100 /* 1.0.0 */
+
+typedef enum sp24_status {
+  SP24_OK = 0,
+  SP24_ERR_NULL = -1,      /* a required pointer is NULL */
+  SP24_ERR_SHAPE = -2,     /* a size is out of range (see each call) */
+  SP24_ERR_ALIGN = -3,     /* a device pointer is not 16-byte aligned */
+  SP24_ERR_DTYPE = -4,     /* unknown dtype */
+  SP24_ERR_WORKSPACE = -5, /* workspace missing or smaller than sp24_workspace_size() */
+  SP24_ERR_HIP = -6,       /* a HIP launch or (with SP24_SYNC_CHECK) a kernel failed */
+  SP24_ERR_MODE = -7,      /* unknown scale mode or op */
+  SP24_ERR_ALIAS = -8      /* an output overlaps an input */
+} sp24_status;
+
+typedef enum sp24_dtype {
+  SP24_BF16 = 0,     /* bfloat16 operands, no scales */
+  SP24_FP8_E4M3 = 1  /* OCP E4M3FN codes with one fp32 scale per tensor */
+} sp24_dtype;
+
+typedef enum sp24_scale_mode {
+  SP24_SCALE_DYNAMIC = 0, /* compute s = amax/448 on the device and store it */
+  SP24_SCALE_STATIC = 1   /* use the scale already stored at scale_dev */
+} sp24_scale_mode;
+
+typedef enum sp24_op {
+  SP24_OP_GEMM = 0,       /* sp24_gemm */
+  SP24_OP_QUANT = 1,      /* sp24_quant_fp8 */
+  SP24_OP_DENSE_GEMM = 2  /* sp24_dense_gemm */
+} sp24_op;
+
+typedef enum sp24_kernel {
+  SP24_KERNEL_SKINNY = 0, /* small m: no LDS tiles, K split across waves */
+  SP24_KERNEL_TILED = 1   /* large m: LDS-staged tiles */
+} sp24_kernel;
+
+/* Launch plan chosen by the host from (op, dtype, m, n, k).  Pure host logic:
+ * sp24_plan() makes no HIP call, so it can be inspected without a GPU. */
+typedef struct sp24_plan {
+  int kernel;             /* sp24_kernel */
+  int tile_n;             /* rows of W per workgroup */
+  int tile_m;             /* rows of X per workgroup */
+  int waves;              /* waves (64 lanes) per workgroup */
+  int split_k;            /* number of K slices reduced through the workspace (1: none) */
+  int grid_x, grid_y, grid_z;
+  size_t workspace_bytes; /* bytes of workspace this plan needs */
+} sp24_plan;
+
+/* Prune W [n, k] (bf16) to 2:4 along k and compress it.
+ *   w_bf16      in : [n, k] bf16
+ *   values_bf16 out: [n, k/2] bf16
+ *   meta        out: [n, k/32] uint32
+ * Requires n >= 1, k >= 32, k % 32 == 0.  Dropped values are not stored. */
+int sp24_prune_compress(const void* w_bf16, int64_t n, int64_t k, void* values_bf16,
+                        uint32_t* meta, void* stream);
+
+/* Rebuild the dense pruned W [n, k] from (values, meta): kept values at their
+ * positions, all-zero bit patterns (+0) elsewhere.
+ *   dtype  SP24_BF16 (values and w_out are bf16) or SP24_FP8_E4M3 (byte codes)
+ * Requires n >= 1, k >= 32, k % 32 == 0.  Nibbles are used as given: a nibble
+ * with i0 == i1 (never written by sp24_prune_compress) writes both values to
+ * one position, the second last; every write stays inside the row. */
+int sp24_decompress(int dtype, const void* values, const uint32_t* meta, int64_t n, int64_t k,
+                    void* w_out, void* stream);
+
+/* Quantise count bf16 values to E4M3 codes with one per-tensor scale.
+ *   mode SP24_SCALE_DYNAMIC: amax = max|x| over the tensor (exact), then
+ *        *scale_dev = fp32(amax / 448) (1.0 if amax == 0), written by the
+ *        device (no host synchronisation); needs a workspace.
+ *   mode SP24_SCALE_STATIC : *scale_dev is read, not written; no workspace.
+ *   Each value: q = e4m3_rne(clamp(fp32(x / s), -448, 448)) with an IEEE
+ *   float32 division (values beyond the range saturate to +-448).
+ *   x_bf16 in: [count] bf16; q_out out: [count] bytes; scale_dev: one fp32 on
+ *   the device.  count >= 1.  ws/ws_bytes: sp24_workspace_size(SP24_OP_QUANT, ...). */
+int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Y = X . W^T with W in compressed 2:4 form; fp32 accumulation; bf16 output.
+ *   dtype SP24_BF16    : x is bf16 [m, k], w_values bf16 [n, k/2]; scales ignored (may be NULL).
+ *   dtype SP24_FP8_E4M3: x is E4M3 [m, k] with *x_scale_dev, w_values E4M3 [n, k/2]
+ *                        with *w_scale_dev; y = bf16_rne(acc * fp32(sx * sw)).
+ *   w_meta [n, k/32]; y_bf16 [m, n].
+ * Requires m >= 1, n >= 1, k >= 128, k % 128 == 0.  The sum over k is formed in
+ * a fixed order for a given (m, n, k): results are bitwise reproducible.
+ * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM, dtype, m, n, k)
+ * (may be NULL/0 when that is 0).  Every supported shape runs the sparse
+ * kernels; there is no dense fallback. */
+int sp24_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const float* x_scale_dev,
+              const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Dense baseline for comparison: Y = X . W^T with an uncompressed W [n, k]
+ * (bf16 or E4M3 codes) on dense MFMA; same scales, epilogue and limits as
+ * sp24_gemm. */
+int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
+                    const float* x_scale_dev, const void* w_dense, const float* w_scale_dev,
+                    void* y_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by an op at a shape (0 if none; also 0 for invalid
+ * arguments, which the op itself then rejects). */
+size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k);
+
+/* The launch plan sp24_gemm / sp24_dense_gemm would use (op SP24_OP_GEMM or
+ * SP24_OP_DENSE_GEMM).  Host-only.  Returns SP24_OK or the error the op would
+ * return for these sizes. */
+int sp24_plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out);
+
+/* Human-readable text of a status code (static storage). */
+const char* sp24_status_string(int status);
+
+/* SP24_VERSION of the built library. */
+int sp24_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_H */

@@ -1,0 +1,67 @@
+/*
+ * sp24_probe.h -- measurement and layout probes shipped in libsp24.
+ *
+ * These calls are not part of the GEMM path.  They pin down facts of gfx950
+ * that the sparse kernels rely on and that the pages (written for other
+ * hardware) cannot give: how the sparse matrix-core instructions (SMFMAC) map
+ * lanes and index bits to matrix elements, their issue rate, and the HBM
+ * streaming rate.  Same conventions as sp24.h: caller-owned device buffers,
+ * asynchronous on `stream`, validation before any HIP call, SP24_* status.
+ */
+#ifndef SP24_PROBE_H
+#define SP24_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Instruction variants understood by the probes. */
+typedef enum sp24_probe_variant {
+  SP24_PROBE_SMFMAC_16x16x128_FP8 = 0,  /* v_smfmac_f32_16x16x128_fp8_fp8 */
+  SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0 = 1, /* v_smfmac_f32_16x16x64_bf16, abid 0 */
+  SP24_PROBE_SMFMAC_16x16x64_BF16_ABID1 = 2, /* same, abid 1 */
+  SP24_PROBE_SMFMAC_32x32x64_FP8 = 3,   /* v_smfmac_f32_32x32x64_fp8_fp8 */
+  SP24_PROBE_SMFMAC_32x32x32_BF16_ABID0 = 4,
+  SP24_PROBE_SMFMAC_32x32x32_BF16_ABID1 = 5,
+  SP24_PROBE_MFMA_16x16x128_FP8 = 6,    /* dense v_mfma_f32_16x16x128_f8f6f4 (fp8 x fp8) */
+  SP24_PROBE_MFMA_16x16x32_BF16 = 7,    /* dense v_mfma_f32_16x16x32_bf16 */
+  SP24_PROBE_N_VARIANTS = 8
+} sp24_probe_variant;
+
+/* Run one instruction per experiment, accumulator starting at 0.
+ * Experiment e uses one wave (64 lanes).  Per lane, with fixed strides:
+ *   a   : 32 bytes at a   + (e*64 + lane)*32  (the A operand; 16 bytes used by
+ *         sparse variants and by the dense bf16 variant, 32 by dense fp8)
+ *   b   : 32 bytes at b   + (e*64 + lane)*32  (the B operand; 16 bytes used
+ *         by the dense bf16 variant)
+ *   idx : 4 bytes  at idx + (e*64 + lane)     (sparse index register)
+ *   c   : 16 floats at c + (e*64 + lane)*16   (accumulator registers; 4 used
+ *         by the 16x16 variants)
+ * n_exp >= 1.  Returns SP24_ERR_MODE for an unknown variant. */
+int sp24_probe_mfma_layout(int variant, const void* a, const void* b, const uint32_t* idx,
+                           float* c, int n_exp, void* stream);
+
+/* Issue-rate loop: `blocks` workgroups of `waves` waves each issue `iters`
+ * instructions of `variant` on register operands (4 independent accumulators),
+ * then write one float per lane to out[(block*waves + wave)*64 + lane] so the
+ * work cannot be removed.  The caller times the launch. */
+int sp24_probe_mfma_rate(int variant, int iters, int blocks, int waves, float* out, void* stream);
+
+/* Copy `bytes` (multiple of 16) from src to dst with 16-byte loads and stores:
+ * the reference kernel for HBM bandwidth and for scaling traffic counters. */
+int sp24_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Read `bytes` (multiple of 16) from src, writing one checksum word per
+ * workgroup to out[blockIdx] (out holds >= sp24_probe_read_blocks() words):
+ * the stream-read rate of HBM. */
+int sp24_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+int sp24_probe_read_blocks(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_PROBE_H */

@@ -1,0 +1,121 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the binding
+and the oracle on the CPU, on the same seeded inputs, and compare."""
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import sp24_ref as O
+
+try:  # collection must work on hosts without the built library; GPU tests then fail loudly
+    import bf16_gemm_linear_amd as _sp
+    _IMPORT_ERROR = None
+except ImportError as e:  # pragma: no cover
+    _sp, _IMPORT_ERROR = None, e
+
+DEV = torch.device("cuda:0")
+
+
+def need_sp():
+    """The binding; raises if libsp24.so is missing (there is no fallback path)."""
+    if _sp is None:
+        raise RuntimeError("libsp24.so is not built: %s" % _IMPORT_ERROR)
+    return _sp
+
+
+def announce(*what):
+    """Name the case on stdout before its GPU work, so a failing run says which one."""
+    print("[case]", *what, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor on any device."""
+    return W.bf16_bits(t.detach().cpu())
+
+
+def u32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.uint8).numpy()
+
+
+def f32(t: torch.Tensor) -> np.float32:
+    return np.float32(t.detach().cpu().numpy().reshape(-1)[0])
+
+
+def f32_bits(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+class GpuWeight:
+    """A weight as the HIP path holds it: compressed (and for FP8 quantised)."""
+
+    def __init__(self, w_bf16_cpu: torch.Tensor, fp8: bool):
+        self.n, self.k = w_bf16_cpu.shape
+        w = w_bf16_cpu.to(DEV)
+        sp = need_sp()
+        self.values, self.meta = sp.prune_compress(w)
+        del w
+        self.fp8 = fp8
+        if fp8:
+            self.qvalues, self.scale = sp.quant_fp8(self.values)
+        else:
+            self.qvalues, self.scale = self.values, None
+
+
+class OracleWeight:
+    """The oracle's compressed (and quantised) form of selected rows of a weight.
+
+    Pruning and compression are row-local, so the oracle on a subset of rows
+    is exactly its answer for those rows; the FP8 scale is per tensor and is
+    computed from every value of the weight (the maximum magnitude survives
+    pruning, which the oracle tests pin)."""
+
+    def __init__(self, w_bits: np.ndarray, fp8: bool, rows=None):
+        self.rows = np.arange(w_bits.shape[0]) if rows is None else np.asarray(rows)
+        self.k = w_bits.shape[1]
+        self.values, self.meta = O.prune_compress(w_bits[self.rows])
+        self.fp8 = fp8
+        if fp8:
+            self.scale = O.fp8_scale(w_bits if rows is not None else self.values)
+            self.qvalues, _ = O.quant_fp8(self.values, scale=self.scale)
+        else:
+            self.qvalues, self.scale = self.values, None
+
+
+def gpu_x(x_bf16_cpu: torch.Tensor, fp8: bool):
+    x = x_bf16_cpu.to(DEV)
+    if fp8:
+        q, s = need_sp().quant_fp8(x)
+        return q, s
+    return x, None
+
+
+def oracle_x(x_bits: np.ndarray, fp8: bool):
+    if fp8:
+        return O.quant_fp8(x_bits)
+    return x_bits, None
+
+
+def oracle_ref(xq, xs, ow: OracleWeight):
+    if ow.fp8:
+        xh, wh = O.sparse_operands_fp8(xq, xs, ow.qvalues, ow.meta, ow.scale, ow.k)
+    else:
+        xh, wh = O.sparse_operands_bf16(xq, ow.values, ow.meta, ow.k)
+    return O.gemm_ref(xh, wh)
+
+
+def assert_within_tolerance(y_bits: np.ndarray, ref: np.ndarray, mag: np.ndarray, what=""):
+    y = O.bf16_to_f64(y_bits)
+    ok = O.within_tolerance(y, ref, mag)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i, j = bad[0]
+        excess = np.abs(y - ref) / (8e-3 * np.abs(ref) + 1e-4 * mag)
+        raise AssertionError(
+            "%s: %d of %d outside tolerance; first at %s: y=%r ref=%r mag=%r; worst ratio %.3g"
+            % (what, len(bad), ok.size, (int(i), int(j)), y[i, j], ref[i, j], mag[i, j], excess.max()))

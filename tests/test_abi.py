@@ -1,0 +1,173 @@
+"""Host-only checks of libsp24's C ABI: it loads, exports every declared
+symbol, validates every argument before any HIP call, and plans launches.
+
+No test here launches a kernel; fake device addresses are only ever passed to
+calls that must reject them during validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+sp = pytest.importorskip("bf16_gemm_linear_amd", reason="libsp24.so not built")
+lib = sp.lib
+
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EHIP, EMODE, EALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+A = 0x7F0000000000  # a 16-byte aligned fake device address (never dereferenced)
+
+
+def _declared_functions():
+    names = []
+    for h in ("sp24.h", "sp24_probe.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(sp24_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert sp.version() == 100
+    assert lib.sp24_status_string(0) == b"ok"
+    for code in range(-8, 0):
+        assert lib.sp24_status_string(code) != b"unknown status"
+    assert lib.sp24_status_string(-99) == b"unknown status"
+
+
+def p(x):
+    return ctypes.c_void_p(x)
+
+
+def gemm(dtype=0, m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
+         wsc=A + 0x400000, y=A + 0x500000, ws=None, wsb=0):
+    return lib.sp24_gemm(dtype, m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), p(ws), wsb, None)
+
+
+def test_gemm_validation():
+    assert gemm(dtype=7) == EDTYPE
+    assert gemm(x=None) == ENULL
+    assert gemm(meta=None) == ENULL
+    assert gemm(dtype=1, xs=None) == ENULL
+    assert gemm(m=0) == ESHAPE
+    assert gemm(n=0) == ESHAPE
+    assert gemm(k=64) == ESHAPE
+    assert gemm(k=384 + 32) == ESHAPE
+    assert gemm(k=1 << 31) == ESHAPE
+    assert gemm(x=A + 8) == EALIGN
+    assert gemm(meta=A + 0x300004) == EALIGN
+    assert gemm(dtype=1, xs=A + 0x100002) == EALIGN
+    assert gemm(y=A + 16) == EALIAS                       # y overlaps x
+    assert gemm(y=A + 0x200000 + 32) == EALIAS            # y overlaps values
+    assert gemm(dtype=1, y=A + 0x400000 - 64, m=1, n=64) == EALIAS  # y covers w_scale
+
+
+def test_gemm_workspace_validation():
+    # a shape that splits K: small n, long k
+    m, n, k = 64, 256, 16384
+    need = lib.sp24_workspace_size(0, 1, m, n, k)
+    assert need == sp.plan(sp.OP_GEMM, sp.FP8, m, n, k)["workspace_bytes"]
+    assert need > 0
+    big = 0x10000000
+    args = dict(dtype=1, m=m, n=n, k=k, x=A, xs=A + big, w=A + 2 * big, meta=A + 3 * big,
+                wsc=A + 4 * big, y=A + 5 * big)
+    assert gemm(**args, ws=None, wsb=0) == EWS
+    assert gemm(**args, ws=A + 6 * big, wsb=need - 1) == EWS
+    assert gemm(**args, ws=A + 6 * big + 4, wsb=need) == EALIGN
+    assert gemm(**args, ws=A + 5 * big, wsb=need) == EALIAS
+
+
+def test_dense_gemm_validation():
+    f = lib.sp24_dense_gemm
+    assert f(3, 1, 1, 128, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == EDTYPE
+    assert f(0, 1, 1, 100, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ESHAPE
+    assert f(0, 1, 1, 128, None, None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ENULL
+    assert f(1, 1, 1, 128, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ENULL
+
+
+def test_prune_and_decompress_validation():
+    f = lib.sp24_prune_compress
+    assert f(None, 4, 64, p(A), p(A + 0x1000), None) == ENULL
+    assert f(p(A), 0, 64, p(A + 0x10000), p(A + 0x20000), None) == ESHAPE
+    assert f(p(A), 4, 48, p(A + 0x10000), p(A + 0x20000), None) == ESHAPE
+    assert f(p(A), 4, 64, p(A + 0x10008), p(A + 0x20000), None) == EALIGN
+    assert f(p(A), 4, 64, p(A + 256), p(A + 0x20000), None) == EALIAS
+    d = lib.sp24_decompress
+    assert d(2, p(A), p(A + 0x1000), 4, 64, p(A + 0x2000), None) == EDTYPE
+    assert d(0, p(A), None, 4, 64, p(A + 0x2000), None) == ENULL
+    assert d(1, p(A), p(A + 0x1000), 4, 16, p(A + 0x2000), None) == ESHAPE
+    assert d(1, p(A), p(A + 0x1000), 4, 64, p(A + 0x2004), None) == EALIGN
+    assert d(0, p(A), p(A + 0x1000), 4, 64, p(A + 64), None) == EALIAS
+
+
+def test_quant_validation():
+    f = lib.sp24_quant_fp8
+    big = 1 << 20
+    need = lib.sp24_workspace_size(1, 0, big, 1, 1)
+    assert need > 0
+    assert lib.sp24_workspace_size(1, 0, 1000, 1, 1) == 0     # small tensors need none
+    X, Q, S, W = A, A + 0x1000000, A + 0x2000000, A + 0x3000000
+    assert f(p(X), big, p(Q), p(S), 5, p(W), need, None) == EMODE
+    assert f(None, big, p(Q), p(S), 0, p(W), need, None) == ENULL
+    assert f(p(X), 0, p(Q), p(S), 0, p(W), need, None) == ESHAPE
+    assert f(p(X), big, p(Q), p(S), 0, None, 0, None) == EWS
+    assert f(p(X), big, p(Q), p(S), 0, p(W), need - 1, None) == EWS
+    assert f(p(X + 2), big, p(Q), p(S), 0, p(W), need, None) == EALIGN
+    assert f(p(X), big, p(Q), p(S + 1), 0, p(W), need, None) == EALIGN
+    assert f(p(X), big, p(X + 16), p(S), 0, p(W), need, None) == EALIAS
+    assert f(p(X), big, p(Q), p(Q + 8), 0, p(W), need, None) == EALIAS
+
+
+def test_plan_table_shapes():
+    allowed = {(16, 16, 4), (16, 16, 8), (32, 16, 8), (32, 32, 8), (32, 64, 4), (64, 64, 4)}
+    shapes = [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (1, 4096, 14336),
+              (64, 4096, 14336), (8, 256, 256), (256, 6144, 4096), (256, 4096, 14336),
+              (8192, 28672, 8192), (3, 100, 128), (33, 17, 640)]
+    for dt in (sp.BF16, sp.FP8):
+        for op in (sp.OP_GEMM, sp.OP_DENSE_GEMM):
+            for m, n, k in shapes:
+                pl = sp.plan(op, dt, m, n, k)
+                assert (pl["tile_n"], pl["tile_m"], pl["waves"]) in allowed
+                assert pl["grid_x"] * pl["tile_n"] >= n and (pl["grid_x"] - 1) * pl["tile_n"] < n
+                assert pl["grid_y"] * pl["tile_m"] >= m and (pl["grid_y"] - 1) * pl["tile_m"] < m
+                assert pl["grid_z"] == pl["split_k"] >= 1
+                ws = pl["workspace_bytes"]
+                assert ws == (pl["split_k"] * m * n * 4 if pl["split_k"] > 1 else 0)
+                assert lib.sp24_workspace_size(op, dt, m, n, k) == ws
+
+
+def test_plan_splits_k_only_when_grid_is_small():
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 64, 4096, 14336)   # 128 tiles, 28 chunks of K
+    assert pl["split_k"] == 2
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 1, 14336, 4096)    # 896 tiles
+    assert pl["split_k"] == 1
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 8, 256, 256)       # one chunk of K: nothing to split
+    assert pl["split_k"] == 1
+
+
+def test_plan_rejects_what_the_op_rejects():
+    with pytest.raises(sp.Sp24Error):
+        sp.plan(sp.OP_GEMM, sp.FP8, 1, 1, 100)
+    with pytest.raises(sp.Sp24Error):
+        sp.plan(sp.OP_QUANT, sp.FP8, 1, 1, 128)
+    with pytest.raises(sp.Sp24Error):
+        sp.plan(sp.OP_GEMM, 9, 1, 1, 128)
+
+
+def test_probe_validation():
+    assert lib.sp24_probe_mfma_layout(99, p(A), p(A), p(A), p(A), 1, None) == EMODE
+    assert lib.sp24_probe_mfma_layout(0, None, p(A), p(A), p(A), 1, None) == ENULL
+    assert lib.sp24_probe_mfma_layout(0, p(A), p(A), p(A), p(A), 0, None) == ESHAPE
+    assert lib.sp24_probe_mfma_rate(2, 1, 1, 1, p(A), None) == EMODE
+    assert lib.sp24_probe_copy(p(A), p(A + 16), 64, None) == EALIAS
+    assert lib.sp24_probe_copy(p(A), p(A + 4096), 65, None) == ESHAPE
+    assert lib.sp24_probe_read(p(A), 0, p(A + 4096), None) == ESHAPE
+    assert lib.sp24_probe_read_blocks() > 0
