@@ -44,7 +44,7 @@ _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", _int), ("tile_n", _int), ("tile_m", _int), ("waves", _int),
                 ("split_k", _int), ("grid_x", _int), ("grid_y", _int), ("grid_z", _int),
-                ("workspace_bytes", _sz)]
+                ("config", _int), ("batch", _int), ("workspace_bytes", _sz)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

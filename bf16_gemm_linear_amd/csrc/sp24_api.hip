@@ -47,22 +47,31 @@ int finish(hipError_t launch, hipStream_t s) {
 
 int esize(int dtype) { return dtype == SP24_BF16 ? 2 : 1; }
 
-// SP24_TILE="tile_n,tile_m,waves,split_k" overrides the skinny plan (tuning only).
-bool tile_override(int* tn, int* tm, int* nw, int* sk) {
+// SP24_TILE="config,split_k" overrides the small-m plan (tuning only; split_k 0
+// keeps the automatic choice).
+bool tile_override(int* cfg, int* sk) {
   const char* v = getenv("SP24_TILE");
   if (v == nullptr || v[0] == '\0') return false;
-  int a, b, c, d;
-  if (sscanf(v, "%d,%d,%d,%d", &a, &b, &c, &d) != 4) return false;
-  *tn = a; *tm = b; *nw = c; *sk = d;
+  int a, b;
+  if (sscanf(v, "%d,%d", &a, &b) != 2) return false;
+  if (a < 0 || (a >= kSkinnyConfigs && a != kTiledConfig) || b < 0 || b > 64) return false;
+  *cfg = a;
+  *sk = b;
   return true;
 }
 
-bool skinny_supported(int tn, int tm, int nw) {
-  const int rb = tn / 16, mb = tm / 16;
-  if (tn % 16 || tm % 16) return false;
-  return (rb == 1 && mb == 1 && (nw == 4 || nw == 8)) || (rb == 2 && mb == 1 && nw == 8) ||
-         (rb == 2 && mb == 2 && nw == 8) || (rb == 2 && mb == 4 && nw == 4) ||
-         (rb == 4 && mb == 4 && nw == 4);
+struct Cfg {
+  int rb, mb, nw, batch;
+};
+
+Cfg skinny_cfg(int id) {
+  switch (id) {
+#define SP24_CFG_CASE(ID, RB, MB, NW, BATCH) \
+  case ID: return Cfg{RB, MB, NW, BATCH};
+    SP24_SKINNY_CONFIGS(SP24_CFG_CASE)
+#undef SP24_CFG_CASE
+  }
+  return Cfg{1, 1, 8, 1};
 }
 
 }  // namespace
@@ -75,21 +84,41 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   if (m < 1 || n < 1 || k < 128 || k % 128 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
     return SP24_ERR_SHAPE;
 
-  int tn, tm, nw, sk = 0;
+  // Large m with enough 256 x 256 tiles to fill the chip: LDS-tiled kernel.
+  const int64_t tiles = ((n + 255) / 256) * ((m + 255) / 256);
+  int id, sk = 0;
   if (m <= 16) {
-    tn = 16; tm = 16; nw = 8;
+    id = n >= 8192 ? 5 : 1;
   } else if (m <= 32) {
-    tn = 32; tm = 32; nw = 8;
+    id = 11;
   } else if (m <= 64) {
-    tn = 32; tm = 64; nw = 4;
+    id = n >= 8192 ? 8 : 11;
   } else {
-    tn = 64; tm = 64; nw = 4;
+    id = 8;
   }
-  int otn, otm, onw, osk;
-  if (tile_override(&otn, &otm, &onw, &osk) && skinny_supported(otn, otm, onw) && osk >= 1 &&
-      osk <= 64) {
-    tn = otn; tm = otm; nw = onw; sk = osk;
+  int oid, osk;
+  const bool forced = tile_override(&oid, &osk);
+  if (forced) {
+    id = oid;
+    sk = osk;
   }
+  if ((!forced && m > 256 && tiles >= 128) || (forced && id == kTiledConfig)) {
+    if (tiles > INT_MAX) return SP24_ERR_SHAPE;
+    out->kernel = SP24_KERNEL_TILED;
+    out->tile_n = 256;
+    out->tile_m = 256;
+    out->waves = 4;
+    out->split_k = 1;
+    out->grid_x = (int)tiles;
+    out->grid_y = 1;
+    out->grid_z = 1;
+    out->config = kTiledConfig;
+    out->batch = 1;
+    out->workspace_bytes = 0;
+    return SP24_OK;
+  }
+  const Cfg c = skinny_cfg(id);
+  const int tn = 16 * c.rb, tm = 16 * c.mb, nw = c.nw;
   const int64_t gx = (n + tn - 1) / tn, gy = (m + tm - 1) / tm;
   const int64_t chunks = (k / 128 + 3) / 4;
   if (sk == 0) {
@@ -107,6 +136,8 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   out->grid_x = (int)gx;
   out->grid_y = (int)gy;
   out->grid_z = sk;
+  out->config = id;
+  out->batch = c.batch;
   out->workspace_bytes = sk > 1 ? (size_t)sk * (size_t)m * (size_t)n * sizeof(float) : 0;
   return SP24_OK;
 }
@@ -242,7 +273,7 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   a.y = static_cast<uint16_t*>(y);
   a.partial = p.split_k > 1 ? static_cast<float*>(ws) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_gemm_skinny(a, p, s);
+  hipError_t e = p.kernel == SP24_KERNEL_TILED ? launch_gemm_tiled(a, p, s) : launch_gemm_skinny(a, p, s);
   if (e == hipSuccess && p.split_k > 1) e = launch_splitk_reduce(a, p.split_k, s);
   return finish(e, s);
 }

@@ -38,6 +38,8 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Non-temporal load: for pure streams whose every load instruction covers
+// whole cache lines (the bandwidth probes).
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
   return __builtin_nontemporal_load(p);

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __rest
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
     u32x4 in[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) in[j] = ld_nt(w + t * 4 + j);
+    for (int j = 0; j < 4; ++j) in[j] = *(w + t * 4 + j);
     uint32_t out[8];
     uint32_t word = 0;
 #pragma unroll

@@ -32,27 +32,6 @@
 namespace sp24 {
 namespace {
 
-// Loads of n 16-byte vectors from p.
-template <int N>
-__device__ __forceinline__ void load16(i32x4 (&dst)[N], const uint8_t* p) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) dst[j] = *reinterpret_cast<const i32x4*>(p + 16 * j);
-}
-
-template <int T>
-__device__ __forceinline__ void load_meta(uint32_t (&dst)[T], const uint32_t* p) {
-  if constexpr (T == 4) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(p);
-    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
-  } else if constexpr (T == 2) {
-    u32x2 v = *reinterpret_cast<const u32x2*>(p);
-    dst[0] = v[0]; dst[1] = v[1];
-  } else {
-#pragma unroll
-    for (int j = 0; j < T; ++j) dst[j] = p[j];
-  }
-}
-
 __device__ __forceinline__ i32x8 cat(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -84,35 +63,57 @@ __device__ __forceinline__ int x_piece(int kb, int q, int u, int v) {
   }
 }
 
-// One chunk of T units for RB row blocks (16 rows of W each) and MB token
-// blocks (16 rows of X each).  DT: SP24_BF16 or SP24_FP8_E4M3; SPARSE: W in
-// compressed form (values + meta) or dense.
+// Registers of one chunk of T units for RB row blocks (16 rows of W each) and
+// MB token blocks (16 rows of X each).
 template <int DT, bool SPARSE, int T, int RB, int MB>
-__device__ __forceinline__ void chunk(f32x4 (&acc)[RB][MB], const uint8_t* __restrict__ w,
-                                      const uint32_t* __restrict__ meta,
-                                      const uint8_t* __restrict__ x, int n0, int m0, int kb,
-                                      int lane, int N, int M, int K) {
-  constexpr int ESZ = DT == SP24_BF16 ? 2 : 1;
-  // bytes per lane per unit: compressed W 16*ESZ (dense 32*ESZ), X 32*ESZ
-  constexpr int WV = (SPARSE ? 16 : 32) * ESZ / 16;  // 16-byte vectors of W per unit
-  constexpr int XV = 32 * ESZ / 16;                  // 16-byte vectors of X per unit
-  const int q = lane >> 4, r16 = lane & 15;
-  const int kq = kb + 32 * T * q;  // first K of this lane group
-
+struct Chunk {
+  static constexpr int ESZ = DT == SP24_BF16 ? 2 : 1;
+  // 16-byte vectors per lane per unit: compressed W 16*ESZ bytes (dense 32*ESZ), X 32*ESZ
+  static constexpr int WV = (SPARSE ? 16 : 32) * ESZ / 16;
+  static constexpr int XV = 32 * ESZ / 16;
   i32x4 wv[RB][T * WV];
-  uint32_t mt[RB][T];
+  uint32_t mt[RB][SPARSE ? T : 1];
+  i32x4 xv[MB][T * XV];
+};
+
+// Issue every load of one chunk.  Plain (cached) loads: one load instruction
+// covers only part of each 128-byte line of a weight row and the rest of the
+// line arrives with the chunk's other loads, so the line must stay cached in
+// between (non-temporal loads measured ~1.4x slower here).
+template <int DT, bool SPARSE, int T, int RB, int MB>
+__device__ __forceinline__ void load_chunk(Chunk<DT, SPARSE, T, RB, MB>& r,
+                                           const uint8_t* __restrict__ w,
+                                           const uint32_t* __restrict__ meta,
+                                           const uint8_t* __restrict__ x, int n0, int m0, int kb,
+                                           int lane, int N, int M, int K) {
+  using C = Chunk<DT, SPARSE, T, RB, MB>;
+  constexpr int ESZ = C::ESZ, WV = C::WV, XV = C::XV;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kq = kb + 32 * T * q;  // first K of this lane group's contiguous slice
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     int row = n0 + rb * 16 + r16;
     row = row < N ? row : N - 1;  // ragged n: clamp the load, the store is masked
+    const uint8_t* wp;
     if constexpr (SPARSE) {
-      load_meta<T>(mt[rb], meta + (size_t)row * (K / 32) + kq / 32);
-      load16<T * WV>(wv[rb], w + ((size_t)row * (K / 2) + kq / 2) * ESZ);
+      const uint32_t* mp = meta + (size_t)row * (K / 32) + kq / 32;
+      if constexpr (T == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(mp);
+        r.mt[rb][0] = v[0]; r.mt[rb][1] = v[1]; r.mt[rb][2] = v[2]; r.mt[rb][3] = v[3];
+      } else if constexpr (T == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(mp);
+        r.mt[rb][0] = v[0]; r.mt[rb][1] = v[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < T; ++j) r.mt[rb][j] = mp[j];
+      }
+      wp = w + ((size_t)row * (K / 2) + kq / 2) * ESZ;
     } else {
-      load16<T * WV>(wv[rb], w + ((size_t)row * K + kq) * ESZ);
+      wp = w + ((size_t)row * K + kq) * ESZ;
     }
+#pragma unroll
+    for (int j = 0; j < T * WV; ++j) r.wv[rb][j] = *reinterpret_cast<const i32x4*>(wp + 16 * j);
   }
-  i32x4 xv[MB][T * XV];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + mb * 16 + r16;
@@ -122,14 +123,17 @@ __device__ __forceinline__ void chunk(f32x4 (&acc)[RB][MB], const uint8_t* __res
       for (int u = 0; u < T; ++u)
 #pragma unroll
         for (int v = 0; v < XV; ++v)
-          xv[mb][u * XV + v] =
+          r.xv[mb][u * XV + v] =
               *reinterpret_cast<const i32x4*>(xr + x_piece<DT, SPARSE, T>(kb, q, u, v) * ESZ);
     } else {
 #pragma unroll
-      for (int j = 0; j < T * XV; ++j) xv[mb][j] = i32x4{0, 0, 0, 0};
+      for (int j = 0; j < T * XV; ++j) r.xv[mb][j] = i32x4{0, 0, 0, 0};
     }
   }
+}
 
+template <int DT, bool SPARSE, int T, int RB, int MB>
+__device__ __forceinline__ void mma_chunk(f32x4 (&acc)[RB][MB], const Chunk<DT, SPARSE, T, RB, MB>& r) {
 #pragma unroll
   for (int u = 0; u < T; ++u) {
 #pragma unroll
@@ -138,32 +142,45 @@ __device__ __forceinline__ void chunk(f32x4 (&acc)[RB][MB], const uint8_t* __res
       for (int mb = 0; mb < MB; ++mb) {
         if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
           acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(
-              wv[rb][u], cat(xv[mb][2 * u], xv[mb][2 * u + 1]), acc[rb][mb], (int)mt[rb][u], 0, 0);
+              r.wv[rb][u], cat(r.xv[mb][2 * u], r.xv[mb][2 * u + 1]), acc[rb][mb], (int)r.mt[rb][u], 0,
+              0);
         } else if constexpr (SPARSE && DT == SP24_BF16) {
           // groups 0..3 of the word (first 16 K of the slice), then groups 4..7
           acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-              as_bf16x8(wv[rb][2 * u]), as_bf16x16(xv[mb][4 * u], xv[mb][4 * u + 1]), acc[rb][mb],
-              (int)mt[rb][u], 0, 0);
+              as_bf16x8(r.wv[rb][2 * u]), as_bf16x16(r.xv[mb][4 * u], r.xv[mb][4 * u + 1]),
+              acc[rb][mb], (int)r.mt[rb][u], 0, 0);
           acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-              as_bf16x8(wv[rb][2 * u + 1]), as_bf16x16(xv[mb][4 * u + 2], xv[mb][4 * u + 3]),
-              acc[rb][mb], (int)mt[rb][u], 0, 1);
+              as_bf16x8(r.wv[rb][2 * u + 1]), as_bf16x16(r.xv[mb][4 * u + 2], r.xv[mb][4 * u + 3]),
+              acc[rb][mb], (int)r.mt[rb][u], 0, 1);
         } else if constexpr (!SPARSE && DT == SP24_FP8_E4M3) {
           acc[rb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              cat(wv[rb][2 * u], wv[rb][2 * u + 1]), cat(xv[mb][2 * u], xv[mb][2 * u + 1]),
+              cat(r.wv[rb][2 * u], r.wv[rb][2 * u + 1]), cat(r.xv[mb][2 * u], r.xv[mb][2 * u + 1]),
               acc[rb][mb], 0, 0, 0, 0, 0, 0);
         } else {
           // dense bf16: 4 instructions of K=32 (8 values per lane group each)
 #pragma unroll
           for (int h = 0; h < 4; ++h)
             acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(wv[rb][4 * u + h]), as_bf16x8(xv[mb][4 * u + h]), acc[rb][mb], 0, 0, 0);
+                as_bf16x8(r.wv[rb][4 * u + h]), as_bf16x8(r.xv[mb][4 * u + h]), acc[rb][mb], 0, 0, 0);
         }
       }
     }
   }
 }
 
-template <int DT, bool SPARSE, int RB, int MB, int NW, bool PARTIAL>
+template <int DT, bool SPARSE, int T, int RB, int MB>
+__device__ __forceinline__ void one_chunk(f32x4 (&acc)[RB][MB], const uint8_t* __restrict__ w,
+                                          const uint32_t* __restrict__ meta,
+                                          const uint8_t* __restrict__ x, int n0, int m0, int kb,
+                                          int lane, int N, int M, int K) {
+  Chunk<DT, SPARSE, T, RB, MB> r;
+  load_chunk(r, w, meta, x, n0, m0, kb, lane, N, M, K);
+  mma_chunk(acc, r);
+}
+
+// RB x MB tiles of 16x16 per wave; NW waves per workgroup split K; BATCH
+// chunks of loads are issued before their matrix instructions.
+template <int DT, bool SPARSE, int RB, int MB, int NW, int BATCH, bool PARTIAL>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ meta, const float* __restrict__ x_scale,
@@ -174,7 +191,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * (RB * 16), m0 = blockIdx.y * (MB * 16);
-  const int splits = gridDim.z;
 
   f32x4 acc[RB][MB];
 #pragma unroll
@@ -182,21 +198,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Chunks of 512 K (4 units) are dealt round-robin to the splits*NW waves
+  // working on this tile; a last partial chunk of 1-3 units goes to the next
+  // wave in the rotation.
   const int units = K / 128;
   const int full = units / 4, tail = units % 4;
-  const int nchunks = full + (tail ? 1 : 0);
-  const int workers = splits * NW;
-  for (int c = blockIdx.z * NW + wave; c < nchunks; c += workers) {
-    const int kb = c * 512;
-    if (c < full) {
-      chunk<DT, SPARSE, 4, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
-    } else if (tail == 1) {
-      chunk<DT, SPARSE, 1, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
-    } else if (tail == 2) {
-      chunk<DT, SPARSE, 2, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
-    } else {
-      chunk<DT, SPARSE, 3, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
-    }
+  const int workers = gridDim.z * NW;
+  const int wid = blockIdx.z * NW + wave;
+  for (int c = wid; c < full; c += workers * BATCH) {
+    Chunk<DT, SPARSE, 4, RB, MB> r[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (c + b * workers < full)
+        load_chunk(r[b], w, meta, x, n0, m0, (c + b * workers) * 512, lane, N, M, K);
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b)
+      if (c + b * workers < full) mma_chunk(acc, r[b]);
+  }
+  if (tail != 0 && wid == full % workers) {
+    const int kb = full * 512;
+    if (tail == 1)
+      one_chunk<DT, SPARSE, 1, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    else if (tail == 2)
+      one_chunk<DT, SPARSE, 2, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
+    else
+      one_chunk<DT, SPARSE, 3, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
   }
 
   // wave tiles -> LDS, element (rb, mb, i, lane) at ((rb*MB + mb)*4 + i)*64 + lane
@@ -213,7 +239,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     if (!PARTIAL) scale = x_scale[0] * w_scale[0];
   }
   // Output o = ((rb*MB + mb)*16 + mi)*16 + nj: consecutive threads take
-  // consecutive n of one token row.
+  // consecutive n of one token row; waves are summed in a fixed order.
   for (int o = threadIdx.x; o < TILE; o += NW * 64) {
     const int nj = o & 15, mi = (o >> 4) & 15, blk = o >> 8;  // blk = rb*MB + mb
     const int rb = blk / MB, mb = blk % MB;
@@ -231,31 +257,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
   }
 }
 
-template <int DT, bool SPARSE, int RB, int MB, int NW>
+template <int DT, bool SPARSE, int RB, int MB, int NW, int BATCH>
 hipError_t launch_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(NW * 64);
   const uint8_t* x = static_cast<const uint8_t*>(a.x);
   const uint8_t* w = static_cast<const uint8_t*>(a.w);
   if (p.split_k > 1)
-    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, true>), grid, block, 0, s, x, w,
-                       a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, true>), grid, block, 0, s,
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, false>), grid, block, 0, s, x, w,
-                       a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+    hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, false>), grid, block, 0, s,
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
   return hipGetLastError();
 }
 
 template <int DT, bool SPARSE>
 hipError_t launch_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
-  const int rb = p.tile_n / 16, mb = p.tile_m / 16, nw = p.waves;
-  // The plan table only produces these shapes (checked by the plan tests).
-  if (rb == 1 && mb == 1 && nw == 4) return launch_cfg<DT, SPARSE, 1, 1, 4>(a, p, s);
-  if (rb == 1 && mb == 1 && nw == 8) return launch_cfg<DT, SPARSE, 1, 1, 8>(a, p, s);
-  if (rb == 2 && mb == 1 && nw == 8) return launch_cfg<DT, SPARSE, 2, 1, 8>(a, p, s);
-  if (rb == 2 && mb == 2 && nw == 8) return launch_cfg<DT, SPARSE, 2, 2, 8>(a, p, s);
-  if (rb == 2 && mb == 4 && nw == 4) return launch_cfg<DT, SPARSE, 2, 4, 4>(a, p, s);
-  if (rb == 4 && mb == 4 && nw == 4) return launch_cfg<DT, SPARSE, 4, 4, 4>(a, p, s);
-  return hipErrorInvalidConfiguration;
+  switch (p.config) {
+#define SP24_SKINNY_CASE(ID, RB, MB, NW, BATCH) \
+  case ID: return launch_cfg<DT, SPARSE, RB, MB, NW, BATCH>(a, p, s);
+    SP24_SKINNY_CONFIGS(SP24_SKINNY_CASE)
+#undef SP24_SKINNY_CASE
+    default: return hipErrorInvalidConfiguration;
+  }
 }
 
 }  // namespace

@@ -33,6 +33,30 @@ struct GemmArgs {
   uint16_t* y;
   float* partial;       // split-K partial sums [split_k][m][n], or nullptr
 };
+// Small-m kernel configurations: X(id, row blocks of 16, token blocks of 16,
+// waves per workgroup, chunks of loads issued per batch).
+#define SP24_SKINNY_CONFIGS(X) \
+  X(0, 1, 1, 8, 1)             \
+  X(1, 1, 1, 4, 2)             \
+  X(2, 1, 1, 2, 4)             \
+  X(3, 2, 1, 4, 2)             \
+  X(4, 2, 1, 8, 1)             \
+  X(5, 4, 1, 4, 2)             \
+  X(6, 2, 2, 8, 1)             \
+  X(7, 2, 4, 4, 1)             \
+  X(8, 4, 4, 4, 1)             \
+  X(9, 4, 2, 4, 1)             \
+  X(10, 1, 1, 4, 1)            \
+  X(11, 2, 2, 4, 2)            \
+  X(12, 1, 4, 4, 1)            \
+  X(13, 2, 1, 2, 4)            \
+  X(14, 1, 1, 8, 2)            \
+  X(15, 4, 1, 8, 1)            \
+  X(16, 1, 2, 8, 1)            \
+  X(17, 2, 4, 8, 1)
+constexpr int kSkinnyConfigs = 18;
+constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
+
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s);

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t* 
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   uint32_t m = 0;
-  for (int64_t i = t0; i < nvec; i += stride) m = max(m, key_max8(ld_nt(xv + i)));
+  for (int64_t i = t0; i < nvec; i += stride) m = max(m, key_max8(*(xv + i)));
   for (int64_t i = nvec * 8 + t0; i < count; i += stride) m = max(m, (uint32_t)(x[i] & 0x7FFFu));
   m = block_max<kThreads>(m, sh);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
-  for (int64_t i = t0; i < nvec; i += stride) qv[i] = cast8(ld_nt(xv + i), s);
+  for (int64_t i = t0; i < nvec; i += stride) qv[i] = cast8(*(xv + i), s);
   for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = cast1(x[i], s);
 }
 

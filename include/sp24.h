@@ -94,6 +94,8 @@ typedef struct sp24_plan {
   int waves;              /* waves (64 lanes) per workgroup */
   int split_k;            /* number of K slices reduced through the workspace (1: none) */
   int grid_x, grid_y, grid_z;
+  int config;             /* kernel configuration id inside the kernel family */
+  int batch;              /* chunks of K whose loads are issued together */
   size_t workspace_bytes; /* bytes of workspace this plan needs */
 } sp24_plan;
 

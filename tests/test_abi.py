@@ -127,7 +127,10 @@ def test_quant_validation():
 
 
 def test_plan_table_shapes():
-    allowed = {(16, 16, 4), (16, 16, 8), (32, 16, 8), (32, 32, 8), (32, 64, 4), (64, 64, 4)}
+    src = open(os.path.join(ROOT, "bf16_gemm_linear_amd", "csrc", "sp24_internal.hpp")).read()
+    table = {int(i): (16 * int(rb), 16 * int(mb), int(nw), int(b)) for i, rb, mb, nw, b in
+             re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+    assert len(table) >= 8
     shapes = [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (1, 4096, 14336),
               (64, 4096, 14336), (8, 256, 256), (256, 6144, 4096), (256, 4096, 14336),
               (8192, 28672, 8192), (3, 100, 128), (33, 17, 640)]
@@ -135,7 +138,11 @@ def test_plan_table_shapes():
         for op in (sp.OP_GEMM, sp.OP_DENSE_GEMM):
             for m, n, k in shapes:
                 pl = sp.plan(op, dt, m, n, k)
-                assert (pl["tile_n"], pl["tile_m"], pl["waves"]) in allowed
+                if pl["kernel"] == 1:   # LDS-tiled: one workgroup per 256 x 256 tile
+                    assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (256, 256, 4, 1)
+                    assert pl["grid_x"] == -(-n // 256) * -(-m // 256)
+                    continue
+                assert table[pl["config"]] == (pl["tile_n"], pl["tile_m"], pl["waves"], pl["batch"])
                 assert pl["grid_x"] * pl["tile_n"] >= n and (pl["grid_x"] - 1) * pl["tile_n"] < n
                 assert pl["grid_y"] * pl["tile_m"] >= m and (pl["grid_y"] - 1) * pl["tile_m"] < m
                 assert pl["grid_z"] == pl["split_k"] >= 1
@@ -145,12 +152,19 @@ def test_plan_table_shapes():
 
 
 def test_plan_splits_k_only_when_grid_is_small():
-    pl = sp.plan(sp.OP_GEMM, sp.FP8, 64, 4096, 14336)   # 128 tiles, 28 chunks of K
-    assert pl["split_k"] == 2
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 16, 1024, 16384)   # 64 tiles, 32 chunks of K
+    assert pl["split_k"] > 1
     pl = sp.plan(sp.OP_GEMM, sp.FP8, 1, 14336, 4096)    # 896 tiles
     assert pl["split_k"] == 1
     pl = sp.plan(sp.OP_GEMM, sp.FP8, 8, 256, 256)       # one chunk of K: nothing to split
     assert pl["split_k"] == 1
+
+
+def test_plan_uses_tiled_kernel_for_prefill_only():
+    assert sp.plan(sp.OP_GEMM, sp.FP8, 8192, 28672, 8192)["kernel"] == 1
+    assert sp.plan(sp.OP_DENSE_GEMM, sp.FP8, 8192, 28672, 8192)["kernel"] == 1
+    for m in (1, 16, 64, 256):
+        assert sp.plan(sp.OP_GEMM, sp.FP8, m, 14336, 4096)["kernel"] == 0
 
 
 def test_plan_rejects_what_the_op_rejects():

@@ -59,7 +59,9 @@ def test_tiny_workload_fp8():
 
 
 SHAPES = [(1, 16, 128), (3, 17, 256), (16, 64, 384), (17, 100, 640), (33, 48, 1152),
-          (64, 256, 2048), (65, 40, 512), (100, 33, 1408), (8, 32, 16384), (129, 80, 896)]
+          (64, 256, 2048), (65, 40, 512), (100, 33, 1408), (8, 32, 16384), (129, 80, 896),
+          # LDS-tiled kernel: ragged tiles in m and n, several K steps
+          (1000, 8200, 640), (2048, 8192, 1024), (777, 32784, 256)]
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -89,11 +91,14 @@ def test_dense_baseline(fp8):
     x = W.randn_bf16((33, 640), seed=5)
     w = W.randn_bf16((100, 640), seed=6, std=0.02)
     _full_case(x, w, fp8, "dense ragged", dense=True)
+    x = W.randn_bf16((1000, 640), seed=7)
+    w = W.randn_bf16((8200, 640), seed=8, std=0.02)
+    _full_case(x, w, fp8, "dense tiled ragged", dense=True)
 
 
 def test_bitwise_reproducible_and_split_k():
     sp = need_sp()
-    for m, n, k in ((64, 4096, 14336), (8, 32, 16384)):
+    for m, n, k in ((16, 1024, 16384), (8, 32, 16384)):
         pl = sp.plan(sp.OP_GEMM, sp.FP8, m, n, k)
         assert pl["split_k"] > 1
         x = W.randn_bf16((m, k), seed=m + k)
