@@ -107,7 +107,7 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     out->kernel = SP24_KERNEL_TILED;
     out->tile_n = 256;
     out->tile_m = 256;
-    out->waves = 4;
+    out->waves = 8;
     out->split_k = 1;
     out->grid_x = (int)tiles;
     out->grid_y = 1;

@@ -139,7 +139,7 @@ def test_plan_table_shapes():
             for m, n, k in shapes:
                 pl = sp.plan(op, dt, m, n, k)
                 if pl["kernel"] == 1:   # LDS-tiled: one workgroup per 256 x 256 tile
-                    assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (256, 256, 4, 1)
+                    assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (256, 256, 8, 1)
                     assert pl["grid_x"] == -(-n // 256) * -(-m // 256)
                     continue
                 assert table[pl["config"]] == (pl["tile_n"], pl["tile_m"], pl["waves"], pl["batch"])
