@@ -51,6 +51,33 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_SOURCES = {
+    "hbm": ["bf16_gemm_linear_amd/csrc/sp24_gemm_skinny.hip", "bf16_gemm_linear_amd/csrc/sp24_common.hpp"],
+    "mfma": ["bf16_gemm_linear_amd/csrc/sp24_gemm_tiled.hip", "bf16_gemm_linear_amd/csrc/sp24_common.hpp"],
+}
+
+
+def counted_traffic(workload, bound):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summaries (profiles/*.md, FETCH_SIZE and WRITE_SIZE scaled by a copy of known size),
+    or None when no summary matches the current kernel source."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[bound]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("workload") == workload and rec.get("kernel_source_sha256") == digest:
+                        return rec["traffic_bytes_per_launch"]
+    return None
+
+
 def gemm_bytes(m, n, k, fp8):
     """Algorithmic bytes of one sparse GEMM: compressed values + metadata + X + Y."""
     es = 1 if fp8 else 2
@@ -283,7 +310,8 @@ def main():
         tot_t = sum(per_m[m]["gemm_us"] for m in Ms) / 1e6
         achieved = tot_b / tot_t / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": counted_traffic(args.workload, "hbm") if fp8 else None,
                     "kernel": "gemm_skinny_kernel (sparse %s), mean over M=%s"
                               % ("fp8" if fp8 else "bf16", "/".join(map(str, Ms)))}
     else:
@@ -291,7 +319,8 @@ def main():
         eff = per_m[m]["tflops_effective"]
         peak = FP8_DENSE_PEAK_TFLOPS if fp8 else BF16_DENSE_PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": eff, "peak": peak, "unit": "TFLOP/s",
-                    "frac": eff / peak, "traffic": None,
+                    "frac": eff / peak,
+                    "traffic": counted_traffic(args.workload, "mfma") if fp8 else None,
                     "kernel": "sparse GEMM, nonzero MACs x2 per second vs the dense %s MFMA peak"
                               % ("FP8" if fp8 else "BF16")}
 
