@@ -51,9 +51,13 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = {
-    "hbm": ["bf16_gemm_linear_amd/csrc/sp24_gemm_skinny.hip", "bf16_gemm_linear_amd/csrc/sp24_common.hpp"],
-    "mfma": ["bf16_gemm_linear_amd/csrc/sp24_gemm_tiled.hip", "bf16_gemm_linear_amd/csrc/sp24_common.hpp"],
+_CSRC = "bf16_gemm_linear_amd/csrc/"
+KERNEL_NAMES = {0: "gemm_skinny_kernel", 1: "gemm_tiled_kernel", 2: "gemm_stream_kernel"}
+KERNEL_SOURCES = {  # the dominant kernel's sources and the plan that picks its configuration
+    "hbm": [_CSRC + f for f in ("sp24_gemm_stream.hip", "sp24_dma.hpp", "sp24_common.hpp",
+                                "sp24_internal.hpp", "sp24_api.hip")],
+    "mfma": [_CSRC + f for f in ("sp24_gemm_tiled.hip", "sp24_dma.hpp", "sp24_common.hpp",
+                                 "sp24_internal.hpp", "sp24_api.hip")],
 }
 
 
@@ -312,8 +316,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS,
                     "traffic": counted_traffic(args.workload, "hbm") if fp8 else None,
-                    "kernel": "gemm_skinny_kernel (sparse %s), mean over M=%s"
-                              % ("fp8" if fp8 else "bf16", "/".join(map(str, Ms)))}
+                    "kernel": "%s (sparse %s), mean over M=%s"
+                              % ("/".join(sorted({KERNEL_NAMES[bufs[m]["plan"]["kernel"]] for m in Ms})),
+                                 "fp8" if fp8 else "bf16", "/".join(map(str, Ms)))}
     else:
         m = Ms[0]
         eff = per_m[m]["tflops_effective"]

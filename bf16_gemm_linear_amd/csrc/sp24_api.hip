@@ -47,22 +47,126 @@ int finish(hipError_t launch, hipStream_t s) {
 
 int esize(int dtype) { return dtype == SP24_BF16 ? 2 : 1; }
 
-// SP24_TILE="config,split_k" overrides the small-m plan (tuning only; split_k 0
-// keeps the automatic choice).
-bool tile_override(int* cfg, int* sk) {
+// SP24_TILE="config,split_k[,rows]" overrides the small-m plan (tuning and
+// tests only): split_k 0 keeps the automatic choice; rows (stream kernel
+// only) sets the rows per workgroup.
+bool tile_override(int* cfg, int* sk, int* rows) {
   const char* v = getenv("SP24_TILE");
   if (v == nullptr || v[0] == '\0') return false;
-  int a, b;
-  if (sscanf(v, "%d,%d", &a, &b) != 2) return false;
-  if (a < 0 || (a >= kSkinnyConfigs && a != kTiledConfig) || b < 0 || b > 64) return false;
+  int a, b, r = 0;
+  const int got = sscanf(v, "%d,%d,%d", &a, &b, &r);
+  if (got < 2) return false;
+  const bool known = (a >= 0 && a < kSkinnyConfigs) || a == kTiledConfig ||
+                     (a >= kStreamBase && a < kStreamBase + kStreamConfigs);
+  if (!known || b < 0 || b > 64 || r < 0) return false;
   *cfg = a;
   *sk = b;
+  *rows = got == 3 ? r : 0;
   return true;
 }
 
 struct Cfg {
   int rb, mb, nw, batch;
 };
+
+struct StreamShape {
+  int rbw, kw, mb, u;
+};
+
+struct StreamChoice {
+  int id;
+  int64_t rows;
+};
+
+StreamShape stream_shape(int id) {
+  switch (id) {
+#define SP24_STREAM_SHAPE(ID, RBW, KW, MB, U, SMAX) \
+  case ID: return StreamShape{RBW, KW, MB, U};
+    SP24_STREAM_CONFIGS(SP24_STREAM_SHAPE)
+#undef SP24_STREAM_SHAPE
+  }
+  return StreamShape{1, 1, 1, 1};
+}
+
+// Plan of stream configuration `id` (0-based) for a shape, or false if the
+// configuration cannot run it (K must split into whole steps).  Each
+// workgroup takes one range of rows: the rows are shared equally over about
+// 256 workgroups per token block (a multiple of 4 rows, at least 16, at most
+// the configuration's row blocks), so every CU streams the same amount of W.
+// split_k 0 picks the split automatically: K is split over the grid only when
+// the row ranges alone leave more than half of the CUs idle.
+bool plan_stream(int id, int sk_req, int rows_req, int64_t m, int64_t n, int64_t k, sp24_plan* out) {
+  const StreamShape c = stream_shape(id);
+  const int64_t bn = 16 * c.rbw, bm = 16 * c.mb, ups = (int64_t)c.u * c.kw;
+  const int64_t units = k / 128;
+  if (units % ups != 0) return false;
+  const int64_t gy = (m + bm - 1) / bm;
+  if (gy > 65535) return false;
+  const int64_t shares = gy >= 256 ? 1 : 256 / gy;
+  int64_t rows = ((n + shares - 1) / shares + 3) / 4 * 4;
+  rows = rows < 16 ? 16 : rows;  // below one row block, split K instead: X is re-read per range
+  rows = rows < bn ? rows : bn;
+  if (rows_req > 0) {
+    if (rows_req % 4 != 0 || rows_req > bn) return false;
+    rows = rows_req;
+  }
+  const int64_t gx = (n + rows - 1) / rows;
+  if (gx > INT_MAX) return false;
+  int64_t sk = sk_req > 0 ? sk_req : 1;
+  if (sk_req == 0)
+    while (sk < 16 && gx * gy * sk * 2 <= 256 && units % (2 * sk * ups) == 0) sk *= 2;
+  if (units % (sk * ups) != 0 || sk > 65535) return false;
+  out->kernel = SP24_KERNEL_STREAM;
+  out->tile_n = (int)rows;
+  out->tile_m = (int)bm;
+  out->waves = c.rbw * c.kw;
+  out->split_k = (int)sk;
+  out->grid_x = (int)gx;
+  out->grid_y = (int)gy;
+  out->grid_z = (int)sk;
+  out->config = kStreamBase + id;
+  out->batch = c.u;
+  out->workspace_bytes = sk > 1 ? (size_t)sk * (size_t)m * (size_t)n * sizeof(float) : 0;
+  return true;
+}
+
+// Default stream configuration and rows per workgroup for a shape (rows 0:
+// equal shares over ~256 workgroups per token block).  Chosen from sweeps of
+// every configuration on the decode shapes of a Llama-3-8B-sized layer on
+// MI355X:
+//  * m <= 16: X is negligible and W streams at the HBM rate; short row ranges
+//    want many waves along K (8 waves over 16 rows), ~30-64 rows per CU do
+//    best as two 8-wave workgroups per CU, longer ranges as 8 row blocks.
+//  * m <= 64: X (m*k bytes per workgroup, from L2 into LDS) costs as much as
+//    W's share when a CU has few rows, so few-row shapes take 32 tokens per
+//    workgroup (W read twice, the second time from cache), or, for long K, 64
+//    rows per workgroup with K split over 4 workgroups.
+StreamChoice stream_default(int64_t m, int64_t n, int64_t k) {
+  const int64_t rows_cu = (n + 255) / 256;
+  auto rows_for = [&](int64_t shares, int64_t lo, int64_t hi) {
+    int64_t r = ((n + shares - 1) / shares + 3) / 4 * 4;
+    return r < lo ? lo : (r > hi ? hi : r);
+  };
+  if (m <= 16) {
+    if (rows_cu <= 16) return StreamChoice{k >= 8192 ? 5 : 4, 0};
+    if (rows_cu <= 64) return StreamChoice{15, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
+    return StreamChoice{9, 0};
+  }
+  if (m <= 32) {
+    if (rows_cu <= 16) return StreamChoice{14, 0};
+    if (rows_cu <= 64) return StreamChoice{8, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
+    return StreamChoice{13, 0};
+  }
+  if (m <= 64) {
+    if (rows_cu <= 16) return k >= 8192 ? StreamChoice{3, 64} : StreamChoice{8, 0};
+    if (rows_cu <= 32) return StreamChoice{13, 0};
+    if (rows_cu <= 64) return StreamChoice{3, 0};
+    return StreamChoice{12, 0};
+  }
+  const int64_t gy = (m + 63) / 64;
+  const int64_t shares = gy >= 256 ? 1 : 256 / gy;
+  return StreamChoice{(n + shares - 1) / shares > 64 ? 12 : 3, 0};
+}
 
 Cfg skinny_cfg(int id) {
   switch (id) {
@@ -96,8 +200,8 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   } else {
     id = 8;
   }
-  int oid, osk;
-  const bool forced = tile_override(&oid, &osk);
+  int oid, osk, orows = 0;
+  const bool forced = tile_override(&oid, &osk, &orows);
   if (forced) {
     id = oid;
     sk = osk;
@@ -116,6 +220,14 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     out->batch = 1;
     out->workspace_bytes = 0;
     return SP24_OK;
+  }
+  if (forced && id >= kStreamBase) {
+    if (!plan_stream(id - kStreamBase, sk, orows, m, n, k, out)) return SP24_ERR_SHAPE;
+    return SP24_OK;
+  }
+  if (!forced) {
+    const StreamChoice d = stream_default(m, n, k);
+    if (plan_stream(d.id, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
   }
   const Cfg c = skinny_cfg(id);
   const int tn = 16 * c.rb, tm = 16 * c.mb, nw = c.nw;
@@ -273,7 +385,9 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   a.y = static_cast<uint16_t*>(y);
   a.partial = p.split_k > 1 ? static_cast<float*>(ws) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p.kernel == SP24_KERNEL_TILED ? launch_gemm_tiled(a, p, s) : launch_gemm_skinny(a, p, s);
+  hipError_t e = p.kernel == SP24_KERNEL_TILED    ? launch_gemm_tiled(a, p, s)
+                 : p.kernel == SP24_KERNEL_STREAM ? launch_gemm_stream(a, p, s)
+                                                  : launch_gemm_skinny(a, p, s);
   if (e == hipSuccess && p.split_k > 1) e = launch_splitk_reduce(a, p.split_k, s);
   return finish(e, s);
 }

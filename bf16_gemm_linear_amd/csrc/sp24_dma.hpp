@@ -1,0 +1,29 @@
+// Direct global -> LDS loads and the vector-memory wait used by the kernels
+// that stage operands through an LDS ring (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sp24 {
+
+// global_load_lds_dwordx4 / _dword: lane l of the instruction writes the bytes
+// it loads to LDS at lds_dst + l * size (lds_dst is wave-uniform).  The loads
+// count in vmcnt like ordinary vector-memory loads and complete in issue order.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+
+}  // namespace sp24

@@ -1,0 +1,388 @@
+// Small-m ("decode") GEMM kernels with an LDS ring: Y[m, n] = sum_k X[m, k] W[n, k].
+//
+// At decode sizes the product streams the weight once from HBM and is bound
+// by that stream; X (at most a few hundred KB) is re-read from L2 by every
+// workgroup.  These kernels give each workgroup one contiguous range of W
+// rows (sized by the host so that the grid covers every CU with equal shares,
+// e.g. 56 rows on each of 256 CUs for n = 14336; a multiple of 4 rows) and walk K in steps.  Every
+// operand of a step -- the rows' compressed values and metadata words and the
+// X rows -- goes from global memory straight into one buffer of an LDS ring
+// with global_load_lds, in whole 64..256-byte row segments, STAGES-1 steps
+// ahead of the step being multiplied; the X rows of a step are then read from
+// LDS by every wave that needs them.
+//
+// Waves.  A workgroup has RBW x KW waves: wave (rg, kg) multiplies row block
+// rg (16 W rows) by MB token blocks (16 X rows each) over units
+// [kg*U, (kg+1)*U) of every step (a unit is 128 values of K; a step holds
+// U*KW units).  The KW partial tiles of a row block are summed through LDS in
+// a fixed order at the end, and K slices of the grid (grid.z) through the
+// split-K workspace, so results are bitwise reproducible.
+//
+// Instruction mapping (16 x 16 tiles; measured on gfx950 with one-hot
+// probes).  The compressed operand is A, so W is A and X is B and the
+// accumulator is a tile of Y^T: lane l, register i <-> W row 4*(l/16) + i,
+// token l % 16.  Within a unit, A lane group q = l/16 holds the 32 K values
+// [32q, 32q + 32) of its row (16 bytes of fp8 values and one metadata word);
+// the sparse B operand holds two runs of K (the measured split-half layout),
+// which for fp8 are the unit's bytes [64h + 16q, +16), h = 0, 1.  The bf16
+// and dense variants use the same unit with their own instruction shapes.
+//
+// LDS rows are XOR-swizzled in 16-byte pieces so that the 16 rows read by one
+// instruction fall on distinct bank groups; the LDS-DMA load writes lane i's
+// bytes to slot i, so the swizzle is applied on the global side.
+#include "sp24_common.hpp"
+#include "sp24_dma.hpp"
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+namespace {
+
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int DT, bool SPARSE, int RBW, int KW, int MB, int U, int SMAX>
+struct StreamCfg {
+  static constexpr int DT_ = DT, RBW_ = RBW, KW_ = KW, MB_ = MB, U_ = U;
+  static constexpr bool SPARSE_ = SPARSE;
+  static constexpr bool FP8 = DT == SP24_FP8_E4M3;
+  static constexpr int ESZ = FP8 ? 1 : 2;
+  static constexpr int NW = RBW * KW, NT = NW * 64;
+  static constexpr int BN = RBW * 16, BM = MB * 16;       // W rows, X rows per workgroup
+  static constexpr int UPS = U * KW;                      // units of 128 K per step
+  static constexpr int XU = 128 * ESZ;                    // X bytes per row per unit
+  static constexpr int WU = (SPARSE ? 64 : 128) * ESZ;    // W bytes per row per unit
+  static constexpr int MU = SPARSE ? 4 : 0;               // metadata words per row per unit
+  static constexpr int XB = UPS * XU, WB = UPS * WU, MW = UPS * MU;  // per row per step
+  static constexpr int PX = XB / 16, PW = WB / 16;        // 16-byte pieces per row per step
+  static constexpr int PXU = XU / 16, PWU = WU / 16;      // ... per unit
+  static constexpr int W_OFF = 0, M_OFF = BN * WB, X_OFF = M_OFF + BN * MW * 4;
+  static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
+  static constexpr int STAGES = SMAX < kLdsBytes / STAGE ? SMAX : kLdsBytes / STAGE;
+  // load instructions per step: 1 KB (dwordx4) for values and X, 256 B (dword) for metadata
+  static constexpr int W_TOT = BN * WB / 1024, M_TOT = BN * MW / 64, X_TOT = BM * XB / 1024;
+  static constexpr int W_PER = (W_TOT + NW - 1) / NW, M_PER = (M_TOT + NW - 1) / NW,
+                       X_PER = (X_TOT + NW - 1) / NW;
+  // every wave issues at least this many loads per step
+  static constexpr int MIN_PER_STEP = W_TOT / NW + M_TOT / NW + X_TOT / NW;
+  static constexpr int RED = KW > 1 ? KW * RBW * MB * 1024 : 0;  // epilogue LDS bytes
+  static constexpr int LDS = STAGES * STAGE > RED ? STAGES * STAGE : RED;
+  static_assert(STAGES >= 2, "two LDS buffers at least");
+  static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MW,
+                "whole load instructions");
+  static_assert(MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(LDS <= kLdsBytes, "LDS budget");
+};
+
+// Slot of 16-byte piece c of LDS row r in a row of P pieces: the 16 rows read
+// by one instruction land on the 16 distinct 16-byte bank groups (64 banks).
+// XOR swizzles are their own inverse: slot s of row r holds piece swz(r, s).
+template <int P>
+__device__ __forceinline__ int swz16(int r, int c) {
+  static_assert((P & (P - 1)) == 0, "power of two");
+  if constexpr (P >= 16) return c ^ (r & 15);
+  else return c ^ ((r / (16 / P)) & (P - 1));
+}
+// Metadata words (MW per row): the 16 rows x 4 words of one read land on 64
+// distinct banks.
+template <int MW>
+__device__ __forceinline__ int swzm(int r, int w) {
+  if constexpr (MW <= 4) return w;
+  else return w ^ (4 * ((r / (64 / MW)) & (MW / 4 - 1)));
+}
+
+__device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Per-lane sources of this wave's loads.  Load g of a stream (g = j*NW +
+// wave) fills slots [64g, 64g + 64) of the stream's LDS region; step ks adds
+// ks * UPS units to every source.
+template <class C>
+struct StreamLoader {
+  const uint8_t* wp[C::W_PER];
+  const uint32_t* mp[C::M_PER > 0 ? C::M_PER : 1];
+  const uint8_t* xp[C::X_PER];
+  int wave;
+
+  __device__ __forceinline__ StreamLoader(const uint8_t* __restrict__ w,
+                                          const uint32_t* __restrict__ meta,
+                                          const uint8_t* __restrict__ x, int n0, int n_last,
+                                          int m0, int M, int K, int u0, int wave_, int lane)
+      : wave(wave_) {
+    const size_t wrow = (size_t)(K / 128) * C::WU;
+#pragma unroll
+    for (int j = 0; j < C::W_PER; ++j) {
+      const int p = (j * C::NW + wave) * 64 + lane, row = p / C::PW;
+      const int sp = swz16<C::PW>(row, p % C::PW);
+      const int n = min(n0 + row, n_last);  // rows past the range: clamp the load, never stored
+      wp[j] = w + (size_t)n * wrow + (size_t)(u0 + sp / C::PWU) * C::WU + 16 * (sp % C::PWU);
+    }
+    if constexpr (C::SPARSE_) {
+#pragma unroll
+      for (int j = 0; j < C::M_PER; ++j) {
+        const int p = (j * C::NW + wave) * 64 + lane, row = p / C::MW;
+        const int sw = swzm<C::MW>(row, p % C::MW);
+        const int n = min(n0 + row, n_last);
+        mp[j] = meta + (size_t)n * (K / 32) + (size_t)(u0 + sw / 4) * 4 + (sw % 4);
+      }
+    }
+    const size_t xrow = (size_t)K * C::ESZ;
+#pragma unroll
+    for (int j = 0; j < C::X_PER; ++j) {
+      const int p = (j * C::NW + wave) * 64 + lane, row = p / C::PX;
+      const int sp = swz16<C::PX>(row, p % C::PX);
+      const int m = min(m0 + row, M - 1);  // rows past M: clamp the load, never stored
+      xp[j] = x + (size_t)m * xrow + (size_t)(u0 + sp / C::PXU) * C::XU + 16 * (sp % C::PXU);
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint8_t* buf, int ks) const {
+#pragma unroll
+    for (int j = 0; j < C::W_PER; ++j) {
+      const int g = j * C::NW + wave;
+      if (C::W_TOT % C::NW == 0 || g < C::W_TOT)
+        dma16(wp[j] + (size_t)ks * C::WB, buf + C::W_OFF + g * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < C::M_PER; ++j) {
+      const int g = j * C::NW + wave;
+      if (C::M_TOT % C::NW == 0 || g < C::M_TOT)
+        dma4(mp[j] + (size_t)ks * C::MW, buf + C::M_OFF + g * 256);
+    }
+#pragma unroll
+    for (int j = 0; j < C::X_PER; ++j) {
+      const int g = j * C::NW + wave;
+      if (C::X_TOT % C::NW == 0 || g < C::X_TOT)
+        dma16(xp[j] + (size_t)ks * C::XB, buf + C::X_OFF + g * 1024);
+    }
+  }
+};
+
+// Wait until at most later * PER of this wave's loads are outstanding
+// (`later` is wave-uniform and at most MAXL).
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      wait_vmcnt<MAXL * PER>();
+      return;
+    }
+    wait_later<PER, MAXL - 1>(later);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+__device__ __forceinline__ i32x4 lds16(const uint8_t* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+
+// Units kg*U .. kg*U + U - 1 of one step for row block rg and MB token blocks.
+// All LDS reads of the step are issued before its matrix instructions.
+template <class C>
+__device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::MB_], const uint8_t* __restrict__ buf,
+                                           int rg, int kg, int lane) {
+  constexpr int MB = C::MB_, U = C::U_;
+  constexpr bool FP8 = C::FP8, SPARSE = C::SPARSE_;
+  const int q = lane >> 4, r = lane & 15;
+  const int wrow = 16 * rg + r;
+  const uint8_t* wr = buf + C::W_OFF + wrow * C::WB;
+  // A: sparse fp8 1 piece, sparse bf16 2, dense fp8 2, dense bf16 4 per unit
+  constexpr int AP = SPARSE ? (FP8 ? 1 : 2) : (FP8 ? 2 : 4);
+  // B: sparse fp8 2 pieces, sparse bf16 4, dense fp8 2, dense bf16 4 per unit and token block
+  constexpr int BP = FP8 ? 2 : 4;
+  i32x4 a[U][AP];
+  uint32_t ix[U];
+  i32x4 b[U][MB][BP];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = kg * U + u;  // unit within the step
+#pragma unroll
+    for (int e = 0; e < AP; ++e) {
+      int c;
+      if constexpr (SPARSE && FP8) c = v * C::PWU + q;                 // K [32q, +32)
+      else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
+      else if constexpr (FP8) c = v * C::PWU + 2 * q + e;              // K [32q, +32)
+      else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
+      a[u][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
+    }
+    if constexpr (SPARSE)
+      ix[u] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MW * 4 +
+                                                 4 * swzm<C::MW>(wrow, 4 * v + q));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int xrow = 16 * mb + r;
+      const uint8_t* xr = buf + C::X_OFF + xrow * C::XB;
+#pragma unroll
+      for (int e = 0; e < BP; ++e) {
+        int c;
+        if constexpr (SPARSE && FP8) c = v * C::PXU + 4 * e + q;  // run e: bytes [64e + 16q, +16)
+        else if constexpr (SPARSE) {
+          // instruction h = e >> 1, run hb = e & 1: K 64hb + 32(q>>1) + 16h + 8(q&1)
+          const int h = e >> 1, hb = e & 1;
+          c = v * C::PXU + 8 * hb + 4 * (q >> 1) + 2 * h + (q & 1);
+        } else if constexpr (FP8) c = v * C::PXU + 2 * q + e;
+        else c = v * C::PXU + 4 * e + q;
+        b[u][mb][e] = lds16(xr + 16 * swz16<C::PX>(xrow, c));
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (SPARSE && FP8) {
+        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[u][0], cat8(b[u][mb][0], b[u][mb][1]),
+                                                                acc[mb], (int)ix[u], 0, 0);
+      } else if constexpr (SPARSE) {
+        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+            __builtin_bit_cast(bf16x8, a[u][0]),
+            __builtin_bit_cast(bf16x16, cat8(b[u][mb][0], b[u][mb][1])), acc[mb], (int)ix[u], 0, 0);
+        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+            __builtin_bit_cast(bf16x8, a[u][1]),
+            __builtin_bit_cast(bf16x16, cat8(b[u][mb][2], b[u][mb][3])), acc[mb], (int)ix[u], 0, 1);
+      } else if constexpr (FP8) {
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            cat8(a[u][0], a[u][1]), cat8(b[u][mb][0], b[u][mb][1]), acc[mb], 0, 0, 0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][e]),
+                                                            __builtin_bit_cast(bf16x8, b[u][mb][e]),
+                                                            acc[mb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <class C, bool PARTIAL>
+__global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
+    const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
+    float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice) {
+  constexpr int MB = C::MB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
+  const int rg = wave % RBW, kg = wave / RBW;
+  const int n0 = blockIdx.x * rows_per_wg, m0 = blockIdx.y * C::BM;
+  const int n_end = min(N, n0 + rows_per_wg);
+  const int u0 = blockIdx.z * units_per_slice;
+  const int nks = units_per_slice / C::UPS;  // the host keeps units_per_slice a multiple of UPS
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Ring of STAGES buffers.  At the top of step ks a wave waits for its own
+  // loads of step ks; the barrier then makes every wave's loads visible and
+  // guarantees that every wave has finished reading buffer (ks - 1) % STAGES,
+  // which receives the loads of step ks + STAGES - 1 while step ks is
+  // multiplied.  A bare s_barrier: __syncthreads() adds a release fence that
+  // waits for every outstanding LDS-DMA load and would drain the ring.
+  const StreamLoader<C> ld(w, meta, x, n0, n_end - 1, m0, M, K, u0, wave, lane);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nks) ld.issue(lds + p * C::STAGE, p);
+  for (int ks = 0; ks < nks; ++ks) {
+    wait_later<C::MIN_PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
+    __builtin_amdgcn_s_barrier();
+    const int nxt = ks + STAGES - 1;
+    if (nxt < nks) ld.issue(lds + (nxt % STAGES) * C::STAGE, nxt);
+    stream_mma<C>(acc, lds + (ks % STAGES) * C::STAGE, rg, kg, lane);
+  }
+
+  // Sum the KW partial tiles of each row block in wave order kg = 0, 1, ...
+  if constexpr (KW > 1) {
+    __syncthreads();  // every wave is done reading the ring
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(((kg * RBW + rg) * MB + mb) * 4 + i) * 64 + lane] = acc[mb][i];
+    __syncthreads();
+    if (kg != 0) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s = red[((rg * MB + mb) * 4 + i) * 64 + lane];
+#pragma unroll
+        for (int g = 1; g < KW; ++g) s += red[(((g * RBW + rg) * MB + mb) * 4 + i) * 64 + lane];
+        acc[mb][i] = s;
+      }
+  }
+
+  float scale = 1.0f;
+  if constexpr (C::FP8 && !PARTIAL) scale = x_scale[0] * w_scale[0];
+  const int q = lane >> 4, c = lane & 15;
+  const int n = n0 + 16 * rg + 4 * q;  // accumulator registers 0..3: rows n .. n + 3
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + 16 * mb + c;
+    if (m >= M || n >= n_end) continue;
+    if constexpr (PARTIAL) {
+      float* pr = partial + ((size_t)blockIdx.z * M + m) * N;
+      if (n + 3 < n_end && (N & 3) == 0) {
+        *reinterpret_cast<f32x4*>(pr + n) = acc[mb];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < n_end) pr[n + e] = acc[mb][e];
+      }
+    } else {
+      uint16_t* yr = y + (size_t)m * N;
+      const uint32_t lo = f32_to_bf16_rne(acc[mb][0] * scale) | (f32_to_bf16_rne(acc[mb][1] * scale) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[mb][2] * scale) | (f32_to_bf16_rne(acc[mb][3] * scale) << 16);
+      if (n + 3 < n_end && (N & 3) == 0) {
+        *reinterpret_cast<u32x2*>(yr + n) = u32x2{lo, hi};
+      } else {
+        const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < n_end) yr[n + e] = (uint16_t)v[e];
+      }
+    }
+  }
+}
+
+template <int DT, bool SPARSE, int RBW, int KW, int MB, int U, int SMAX>
+hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  using C = StreamCfg<DT, SPARSE, RBW, KW, MB, U, SMAX>;
+  const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(C::NT);
+  const int units_per_slice = a.k / 128 / p.split_k;
+  if (p.tile_n > C::BN || p.tile_m != C::BM || p.waves != C::NW || units_per_slice % C::UPS != 0)
+    return hipErrorInvalidConfiguration;
+  const uint8_t* x = static_cast<const uint8_t*>(a.x);
+  const uint8_t* w = static_cast<const uint8_t*>(a.w);
+  if (p.split_k > 1)
+    hipLaunchKernelGGL((gemm_stream_kernel<C, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                       a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<C, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                       a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+  return hipGetLastError();
+}
+
+template <int DT, bool SPARSE>
+hipError_t launch_stream_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  switch (p.config - kStreamBase) {
+#define SP24_STREAM_CASE(ID, RBW, KW, MB, U, SMAX) \
+  case ID: return launch_stream_cfg<DT, SPARSE, RBW, KW, MB, U, SMAX>(a, p, s);
+    SP24_STREAM_CONFIGS(SP24_STREAM_CASE)
+#undef SP24_STREAM_CASE
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  if (a.dtype == SP24_FP8_E4M3)
+    return a.sparse ? launch_stream_dt<SP24_FP8_E4M3, true>(a, p, s)
+                    : launch_stream_dt<SP24_FP8_E4M3, false>(a, p, s);
+  return a.sparse ? launch_stream_dt<SP24_BF16, true>(a, p, s) : launch_stream_dt<SP24_BF16, false>(a, p, s);
+}
+
+}  // namespace sp24

@@ -33,6 +33,7 @@
 // tiles XCD by XCD and, inside an XCD, in groups of 8 tile columns, so that
 // workgroups resident at the same time share W and X tiles in their XCD's L2.
 #include "sp24_common.hpp"
+#include "sp24_dma.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -70,17 +71,6 @@ __device__ __forceinline__ int swz_x(int row, int c) { return c ^ ((row >> 1) & 
 // so the 64 lanes of a read (32 rows x words 2s, 2s+1) hit 64 distinct banks.
 __device__ __forceinline__ int swz_m(int row, int w, int words) {
   return words == 4 ? (w ^ (((row >> 4) & 1) * 2)) : w;
-}
-
-// Direct global -> LDS loads (global_load_lds_dwordx4 / _dword): lane l of an
-// instruction writes the bytes it loads to LDS at dst + l * size.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);
 }
 
 template <int DT, bool SPARSE>
@@ -152,13 +142,6 @@ struct Loader {
       dma16(xp[j] + (size_t)ks * L::XB, buf + L::X_OFF + (wave * S::X_INSTR + j) * 1024);
   }
 };
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
-}
 
 __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

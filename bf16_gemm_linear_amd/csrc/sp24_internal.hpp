@@ -20,7 +20,7 @@ size_t quant_workspace_bytes(int64_t count);
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
                             void* ws, hipStream_t s);
 
-// sp24_gemm_skinny.hip / sp24_gemm_tiled.hip / sp24_reduce.hip
+// sp24_gemm_skinny.hip / sp24_gemm_stream.hip / sp24_gemm_tiled.hip / sp24_reduce.hip
 struct GemmArgs {
   int dtype;
   bool sparse;
@@ -57,7 +57,37 @@ struct GemmArgs {
 constexpr int kSkinnyConfigs = 18;
 constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
 
+// Small-m LDS-ring kernel configurations (config id = kStreamBase + id):
+// X(id, row blocks of 16 = waves along n, waves along K, token blocks of 16,
+//   128-K units per wave per step, LDS buffers at most).  Every entry fits
+// the 160 KB of LDS with at least two buffers for all four operand types:
+// (row blocks + token blocks) * units per step <= 20.
+#define SP24_STREAM_CONFIGS(X) \
+  X(0, 4, 1, 1, 2, 6)          \
+  X(1, 4, 2, 1, 1, 6)          \
+  X(2, 4, 1, 4, 2, 4)          \
+  X(3, 4, 2, 4, 1, 4)          \
+  X(4, 1, 4, 1, 1, 6)          \
+  X(5, 1, 8, 1, 1, 4)          \
+  X(6, 1, 4, 4, 1, 3)          \
+  X(7, 2, 2, 1, 1, 6)          \
+  X(8, 2, 4, 2, 1, 3)          \
+  X(9, 8, 1, 1, 2, 4)          \
+  X(10, 4, 1, 2, 2, 4)         \
+  X(11, 2, 2, 4, 1, 4)         \
+  X(12, 8, 1, 4, 1, 3)         \
+  X(13, 4, 2, 2, 1, 4)         \
+  X(14, 1, 4, 2, 1, 4)         \
+  X(15, 2, 4, 1, 1, 4)         \
+  X(16, 4, 2, 1, 1, 10)        \
+  X(17, 2, 4, 1, 1, 8)         \
+  X(18, 4, 4, 1, 1, 6)         \
+  X(19, 1, 8, 1, 1, 8)
+constexpr int kStreamConfigs = 20;
+constexpr int kStreamBase = 100;
+
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
+hipError_t launch_gemm_stream(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s);
 

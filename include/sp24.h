@@ -81,21 +81,23 @@ typedef enum sp24_op {
 } sp24_op;
 
 typedef enum sp24_kernel {
-  SP24_KERNEL_SKINNY = 0, /* small m: no LDS tiles, K split across waves */
-  SP24_KERNEL_TILED = 1   /* large m: LDS-staged tiles */
+  SP24_KERNEL_SKINNY = 0, /* small m: operands straight to registers, K split across waves */
+  SP24_KERNEL_TILED = 1,  /* large m: 256 x 256 tiles staged through an LDS ring */
+  SP24_KERNEL_STREAM = 2  /* small m: one row range per workgroup, operands through an LDS ring */
 } sp24_kernel;
 
 /* Launch plan chosen by the host from (op, dtype, m, n, k).  Pure host logic:
  * sp24_plan() makes no HIP call, so it can be inspected without a GPU. */
 typedef struct sp24_plan {
   int kernel;             /* sp24_kernel */
-  int tile_n;             /* rows of W per workgroup */
+  int tile_n;             /* rows of W per workgroup (stream kernel: the rows of its range) */
   int tile_m;             /* rows of X per workgroup */
   int waves;              /* waves (64 lanes) per workgroup */
   int split_k;            /* number of K slices reduced through the workspace (1: none) */
   int grid_x, grid_y, grid_z;
   int config;             /* kernel configuration id inside the kernel family */
-  int batch;              /* chunks of K whose loads are issued together */
+  int batch;              /* skinny: chunks of K whose loads are issued together;
+                             stream: 128-K units per wave per step */
   size_t workspace_bytes; /* bytes of workspace this plan needs */
 } sp24_plan;
 

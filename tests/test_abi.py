@@ -130,7 +130,9 @@ def test_plan_table_shapes():
     src = open(os.path.join(ROOT, "bf16_gemm_linear_amd", "csrc", "sp24_internal.hpp")).read()
     table = {int(i): (16 * int(rb), 16 * int(mb), int(nw), int(b)) for i, rb, mb, nw, b in
              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
-    assert len(table) >= 8
+    stream = {100 + int(i): tuple(int(v) for v in t) for i, *t in
+              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+    assert len(table) >= 8 and len(stream) >= 8
     shapes = [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (1, 4096, 14336),
               (64, 4096, 14336), (8, 256, 256), (256, 6144, 4096), (256, 4096, 14336),
               (8192, 28672, 8192), (3, 100, 128), (33, 17, 640)]
@@ -142,7 +144,15 @@ def test_plan_table_shapes():
                     assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (256, 256, 8, 1)
                     assert pl["grid_x"] == -(-n // 256) * -(-m // 256)
                     continue
-                assert table[pl["config"]] == (pl["tile_n"], pl["tile_m"], pl["waves"], pl["batch"])
+                if pl["kernel"] == 2:   # LDS ring: one range of rows per workgroup
+                    rbw, kw, mb, u, smax = stream[pl["config"]]
+                    assert (pl["tile_m"], pl["waves"], pl["batch"]) == (16 * mb, rbw * kw, u)
+                    assert 0 < pl["tile_n"] <= 16 * rbw
+                    assert pl["tile_n"] % 4 == 0
+                    assert (k // 128) % (pl["split_k"] * u * kw) == 0
+                else:
+                    assert pl["kernel"] == 0
+                    assert table[pl["config"]] == (pl["tile_n"], pl["tile_m"], pl["waves"], pl["batch"])
                 assert pl["grid_x"] * pl["tile_n"] >= n and (pl["grid_x"] - 1) * pl["tile_n"] < n
                 assert pl["grid_y"] * pl["tile_m"] >= m and (pl["grid_y"] - 1) * pl["tile_m"] < m
                 assert pl["grid_z"] == pl["split_k"] >= 1
@@ -164,7 +174,23 @@ def test_plan_uses_tiled_kernel_for_prefill_only():
     assert sp.plan(sp.OP_GEMM, sp.FP8, 8192, 28672, 8192)["kernel"] == 1
     assert sp.plan(sp.OP_DENSE_GEMM, sp.FP8, 8192, 28672, 8192)["kernel"] == 1
     for m in (1, 16, 64, 256):
-        assert sp.plan(sp.OP_GEMM, sp.FP8, m, 14336, 4096)["kernel"] == 0
+        assert sp.plan(sp.OP_GEMM, sp.FP8, m, 14336, 4096)["kernel"] != 1
+
+
+def test_plan_stream_rows_cover_every_cu_equally():
+    # equal row ranges over all 256 CUs: 14336 rows as 512 ranges of 28 (two
+    # workgroups per CU), 56 per CU at m = 64, 16 per CU for 4096 rows
+    for m, n, k, rows, gx, gz in ((1, 14336, 4096, 28, 512, 1), (64, 14336, 4096, 56, 256, 1),
+                                  (1, 4096, 14336, 16, 256, 1), (64, 4096, 14336, 64, 64, 4)):
+        pl = sp.plan(sp.OP_GEMM, sp.FP8, m, n, k)
+        assert (pl["kernel"], pl["tile_n"], pl["grid_x"], pl["split_k"]) == (2, rows, gx, gz)
+        assert (gx * gz) % 256 == 0
+
+
+def test_plan_falls_back_to_skinny_kernel_for_odd_k():
+    # 31 units of 128 K: the default stream step (2 units) does not divide K
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 1, 14336, 31 * 128)
+    assert pl["kernel"] == 0
 
 
 def test_plan_rejects_what_the_op_rejects():

@@ -12,40 +12,12 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import (DEV, GpuWeight, OracleWeight, announce, assert_within_tolerance, bits,
-                         codes, f32, f32_bits, gpu_x, need_sp, oracle_ref, oracle_x, u32)
+from gpu_helpers import (GpuWeight, OracleWeight, announce, assert_within_tolerance, bits, codes,
+                         f32, f32_bits, gpu_x, need_sp, oracle_ref, oracle_x, u32)
+from gpu_helpers import full_case as _full_case
 from oracle import sp24_ref as O
 
 pytestmark = pytest.mark.gpu
-
-
-def _full_case(x_cpu, w_cpu, fp8, what, dense=False):
-    """Whole pipeline on both sides; compare codes, scales and every output."""
-    sp = need_sp()
-    announce("gemm", what, "fp8" if fp8 else "bf16", tuple(x_cpu.shape), tuple(w_cpu.shape),
-             "dense" if dense else "sparse")
-    gw = GpuWeight(w_cpu, fp8)
-    xq, xs = gpu_x(x_cpu, fp8)
-    if dense:
-        wd = sp.decompress(gw.qvalues, gw.meta, gw.k)
-        y = sp.dense_gemm(xq, wd, x_scale=xs, w_scale=gw.scale)
-    else:
-        y = sp.gemm(xq, gw.qvalues, gw.meta, x_scale=xs, w_scale=gw.scale)
-    torch.cuda.synchronize()
-    ow = OracleWeight(W.bf16_bits(w_cpu), fp8)
-    oxq, oxs = oracle_x(W.bf16_bits(x_cpu), fp8)
-    assert np.array_equal(u32(gw.meta), ow.meta)
-    if fp8:
-        assert f32_bits(f32(gw.scale)) == f32_bits(ow.scale)
-        assert f32_bits(f32(xs)) == f32_bits(oxs)
-        assert np.array_equal(codes(gw.qvalues), ow.qvalues)
-        assert np.array_equal(codes(xq), oxq)
-    else:
-        assert np.array_equal(bits(gw.values), ow.values)
-    ref, mag = oracle_ref(oxq, oxs, ow)
-    yb = bits(y)
-    assert_within_tolerance(yb, ref, mag, what)
-    return y, yb
 
 
 def test_tiny_workload_bf16():
