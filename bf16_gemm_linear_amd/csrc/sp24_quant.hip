@@ -7,8 +7,11 @@
 //
 // amax is order-independent and exact: it is taken on the integer keys
 // (bits & 0x7FFF), which order finite bf16 magnitudes exactly.
-//   small tensors (<= kFusedMax values): one workgroup does amax and the cast
-//                                        in one launch;
+//   small tensors (<= kFusedMax values): one launch; every workgroup takes
+//                   amax over the whole tensor (at most 256 KB, from L2) and
+//                   casts its own slice of kFusedSlice values, so the division
+//                   (the costly part) is spread over the CUs while the
+//                   reduction needs no second launch (a launch costs ~2 us);
 //   larger tensors: kernel 1 writes one partial maximum per workgroup into the
 //                   workspace; kernel 2 re-reduces those partials in every
 //                   workgroup (a few KB from L2), stores the scale from
@@ -21,8 +24,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;
-constexpr int64_t kFusedMax = 32768;
-constexpr int kFusedThreads = 1024;
+constexpr int kFusedThreads = 512;
+constexpr int64_t kFusedMax = 131072;  // values
+constexpr int kFusedSlice = 4096;      // values cast per workgroup (8 per thread)
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
@@ -112,30 +116,40 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = cast1(x[i], s);
 }
 
-// Small tensors: amax and cast in one workgroup.
+// Small tensors in one launch: workgroup b takes amax over the whole tensor,
+// then casts values [b * kFusedSlice, (b + 1) * kFusedSlice).
 __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16_t* __restrict__ x,
                                                                     int64_t count,
                                                                     uint8_t* __restrict__ q,
                                                                     float* __restrict__ scale,
                                                                     int dynamic) {
   __shared__ uint32_t sh[kFusedThreads / kWave];
-  const int64_t nvec = count / 8;
+  const int nvec = (int)(count / 8);
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   float s;
   if (dynamic) {
     uint32_t m = 0;
-    for (int64_t i = threadIdx.x; i < nvec; i += kFusedThreads) m = max(m, key_max8(xv[i]));
-    for (int64_t i = nvec * 8 + threadIdx.x; i < count; i += kFusedThreads)
-      m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+    int i = threadIdx.x;
+    for (; i + 3 * kFusedThreads < nvec; i += 4 * kFusedThreads) {  // four loads in flight
+      const u32x4 a = xv[i], b = xv[i + kFusedThreads], c = xv[i + 2 * kFusedThreads],
+                  d = xv[i + 3 * kFusedThreads];
+      m = max(m, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+    }
+    for (; i < nvec; i += kFusedThreads) m = max(m, key_max8(xv[i]));
+    const int tail = nvec * 8 + threadIdx.x;
+    if (tail < count) m = max(m, (uint32_t)(x[tail] & 0x7FFFu));
     m = block_max<kFusedThreads>(m, sh);
     s = scale_from_key(m);
-    if (threadIdx.x == 0) *scale = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
   } else {
     s = *scale;
   }
+  const int v0 = blockIdx.x * (kFusedSlice / 8);
+  const int v1 = min(nvec, v0 + kFusedSlice / 8);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
-  for (int64_t i = threadIdx.x; i < nvec; i += kFusedThreads) qv[i] = cast8(xv[i], s);
-  for (int64_t i = nvec * 8 + threadIdx.x; i < count; i += kFusedThreads) q[i] = cast1(x[i], s);
+  for (int i = v0 + threadIdx.x; i < v1; i += kFusedThreads) qv[i] = cast8(xv[i], s);
+  const int tail = nvec * 8 + threadIdx.x;  // the last workgroup casts the 0..7 trailing values
+  if (blockIdx.x == gridDim.x - 1 && tail < count) q[tail] = cast1(x[tail], s);
 }
 
 int n_partials(int64_t count) {
@@ -156,7 +170,8 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float*
                             void* ws, hipStream_t s) {
   const bool dynamic = mode == SP24_SCALE_DYNAMIC;
   if (count <= kFusedMax) {
-    hipLaunchKernelGGL(fused_quant_kernel, dim3(1), dim3(kFusedThreads), 0, s, x, count, q, scale,
+    const int blocks = (int)((count + kFusedSlice - 1) / kFusedSlice);
+    hipLaunchKernelGGL(fused_quant_kernel, dim3(blocks), dim3(kFusedThreads), 0, s, x, count, q, scale,
                        dynamic ? 1 : 0);
     return hipGetLastError();
   }

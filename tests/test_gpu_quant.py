@@ -65,7 +65,8 @@ def test_dynamic_decode_activations(m):
     _dynamic(W.down_x(m), "down x")
 
 
-@pytest.mark.parametrize("count", [1, 7, 8, 4095, 32768, 32769, 100003, 1 << 20, (1 << 22) + 5])
+@pytest.mark.parametrize("count", [1, 7, 8, 4095, 16391, 16392, 32768, 65543, 65544, 100003, 131072,
+                                   131073, 1 << 20, (1 << 22) + 5])
 def test_dynamic_sizes_and_tails(count):
     _dynamic(W.randn_bf16((count,), seed=count % 1000 + 1, std=3.0), "count")
 
