@@ -9,6 +9,11 @@ dynamic per-tensor E4M3 quantisation of X (sp24_quant_fp8) and the sparse GEMM
 compressed and quantised once at load.  The load path (sp24_prune_compress and
 the weight quantisation) is timed separately and reported under "load_path".
 
+--workload down: the down-projection (K=14336, N=4096) at the same M.
+--workload prefill: the M=8192, K=8192, N=28672 GEMM (bound: matrix cores).
+--workload layers: 32 layers x (QKV, O, gate+up, down) at M=256, 128 sequential
+sparse GEMMs per step (see run_layers).
+
 Inputs are seeded synthetic tensors (workloads/) resident in HBM before the
 timed region.  Each call reads a different one of R weight copies (> 2x the
 256 MB last-level cache), so weight bytes come from HBM.  Steps are captured
@@ -151,7 +156,8 @@ def main():
             "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16", Ms[0], K, N)
         bound = "mfma"
     else:
-        raise SystemExit("--workload layers: use the layer-sweep mode of this script (not yet built)")
+        print(json.dumps(run_layers(args, torch, np, sp, W, ev, dev)))
+        return
 
     # ---------------------------------------------------------------- load path
     w = w_cpu.to(dev)
@@ -353,6 +359,157 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out))
+
+
+def run_layers(args, torch, np, sp, W, ev, dev):
+    """Layer sweep: 32 layers x (QKV, O, gate+up, down) of a Llama-3-8B-sized block at 256
+    tokens, 128 sequential sparse GEMMs per step on weights pruned, compressed and (FP8)
+    quantised once at load.  Weights are drawn on the GPU from seeded generators (seed
+    5000 + 4*layer + projection, 0.02 * N(0, 1)); the two inputs X [256, 4096] ~ N(0, 1) and
+    [256, 14336] ~ SiLU(N(0, 1)) come from workloads/ and are quantised once.  The whole
+    sweep (4.4 GB of FP8 weights) exceeds the last-level cache, so no weight copies."""
+    fp8 = args.dtype == "fp8"
+    dt = sp.FP8 if fp8 else sp.BF16
+    M, L = W.LAYER_M, W.N_LAYERS
+    projs = W.LAYER_PROJS
+    xs, xq, sx = {}, {}, {}
+    for _, k, _ in projs:
+        if k not in xs:
+            xs[k] = W.layer_x(k).to(dev)
+            if fp8:
+                xq[k], sx[k] = sp.quant_fp8(xs[k])
+            else:
+                xq[k], sx[k] = xs[k], None
+    t0 = time.perf_counter()
+    wts = []
+    for layer in range(L):
+        row = []
+        for p, (name, k, n) in enumerate(projs):
+            g = torch.Generator(device=dev)
+            g.manual_seed(5000 + 4 * layer + p)
+            w = (torch.randn(n, k, generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            values, meta = sp.prune_compress(w)
+            del w
+            qv, sw = sp.quant_fp8(values) if fp8 else (values, None)
+            row.append((qv, meta, sw))
+            del values
+        wts.append(row)
+    torch.cuda.synchronize()
+    load_s = time.perf_counter() - t0
+    ys = [torch.empty(M, n, dtype=torch.bfloat16, device=dev) for _, _, n in projs]
+    wss = [torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, M, n, k)), dtype=torch.uint8,
+                       device=dev) for _, k, n in projs]
+    plans = [sp.plan(sp.OP_GEMM, dt, M, n, k) for _, k, n in projs]
+
+    def call(layer, p):
+        _, k, _ = projs[p]
+        qv, meta, sw = wts[layer][p]
+        sp.gemm(xq[k], qv, meta, x_scale=sx[k], w_scale=sw, out=ys[p], ws=wss[p])
+
+    def sweep():
+        for layer in range(L):
+            for p in range(len(projs)):
+                call(layer, p)
+
+    sweep()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sweep()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sweep()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    steps = max(1, min(args.steps, 50))
+    t = ev.time(lambda i: graph.replay(), steps) / steps
+    graph.replay()
+    torch.cuda.synchronize()
+    for p in range(len(projs)):
+        if not torch.equal(ys[p].view(torch.int16), eager[p].view(torch.int16)):
+            raise SystemExit("graph replay output differs from the eager run for %s" % projs[p][0])
+
+    per_proj, tot_b, tot_t = {}, 0, 0.0
+    for p, (name, k, n) in enumerate(projs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in range(L):
+                call(layer, p)
+        g.replay()
+        torch.cuda.synchronize()
+        tp = ev.time(lambda i: g.replay(), 5) / 5 / L
+        b = gemm_bytes(M, n, k, fp8)
+        tot_b += b * L
+        tot_t += tp * L
+        per_proj[name] = {"K": k, "N": n, "gemm_us": tp * 1e6, "GBs": b / tp / 1e9,
+                          "hbm_frac": b / tp / 1e9 / HBM_PEAK_GBS,
+                          "tflops_dense_equiv": 2 * M * n * k / tp / 1e12,
+                          "plan": {k2: v for k2, v in plans[p].items()
+                                   if k2 in ("kernel", "config", "tile_n", "tile_m", "waves", "split_k")}}
+        del g
+    sweep_bytes = sum(gemm_bytes(M, n, k, fp8) for _, k, n in projs) * L
+    achieved = tot_b / tot_t / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_layer_baseline(W, fp8, gemm_bytes(M, 4096, 4096, fp8))
+    return {
+        "metric": METRIC,
+        "value": sweep_bytes / t / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": t * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded; weights drawn on the GPU, inputs from workloads/)",
+        "config": {"workload": "layer sweep: %d layers x QKV/O/gate+up/down, M=%d tokens, 2:4 sparse %s"
+                               % (L, M, "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16"),
+                   "M": M, "layers": L, "projections": [list(pr) for pr in projs],
+                   "step": "128 sequential sparse GEMMs (X quantised once)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "%s (sparse %s), all 128 calls" % (
+                         "/".join(sorted({KERNEL_NAMES[pl["kernel"]] for pl in plans})),
+                         "fp8" if fp8 else "bf16")},
+        "cpu_baseline": cpu,
+        "per_projection": per_proj,
+        "sweep_GB": sweep_bytes / 1e9,
+        "sweep_tflops_dense_equiv": sum(2 * M * n * k for _, k, n in projs) * L / t / 1e12,
+        "load_path": {"generate_prune_compress_quantise_s": load_s},
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+
+def cpu_layer_baseline(W, fp8, call_bytes):
+    """The CPU oracle on one call of the sweep (layer 0's O projection, 256 x 4096 x 4096),
+    repeated for about 10 s."""
+    from oracle import sp24_ref as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wb = W.bf16_bits(W.layer_weight(0, 1))
+    xb = W.bf16_bits(W.layer_x(4096))
+    v, meta = O.prune_compress(wb)
+    if fp8:
+        vq, sw = O.quant_fp8(v)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if fp8:
+            xq, sx = O.quant_fp8(xb)
+            O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, 4096))
+        else:
+            O.gemm_ref(*O.sparse_operands_bf16(xb, v, meta, 4096))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 20:
+            break
+    return {"value": call_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%d call(s) of layer 0's O projection (256 x 4096 x 4096: quantise X, "
+                      "decompress W, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
 
 
 def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes):

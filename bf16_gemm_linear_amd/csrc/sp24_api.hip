@@ -70,7 +70,7 @@ struct Cfg {
 };
 
 struct StreamShape {
-  int rbw, kw, mb, u;
+  int rbw, rb, kw, mb, u, smax;
 };
 
 struct StreamChoice {
@@ -80,24 +80,27 @@ struct StreamChoice {
 
 StreamShape stream_shape(int id) {
   switch (id) {
-#define SP24_STREAM_SHAPE(ID, RBW, KW, MB, U, SMAX) \
-  case ID: return StreamShape{RBW, KW, MB, U};
+#define SP24_STREAM_SHAPE(ID, RBW, RB, KW, MB, U, SMAX) \
+  case ID: return StreamShape{RBW, RB, KW, MB, U, SMAX};
     SP24_STREAM_CONFIGS(SP24_STREAM_SHAPE)
 #undef SP24_STREAM_SHAPE
   }
-  return StreamShape{1, 1, 1, 1};
+  return StreamShape{1, 1, 1, 1, 1, 2};
 }
 
 // Plan of stream configuration `id` (0-based) for a shape, or false if the
-// configuration cannot run it (K must split into whole steps).  Each
+// configuration cannot run it (K must split into whole steps, and two LDS
+// buffers of the operand type must fit).  Each
 // workgroup takes one range of rows: the rows are shared equally over about
 // 256 workgroups per token block (a multiple of 4 rows, at least 16, at most
 // the configuration's row blocks), so every CU streams the same amount of W.
 // split_k 0 picks the split automatically: K is split over the grid only when
 // the row ranges alone leave more than half of the CUs idle.
-bool plan_stream(int id, int sk_req, int rows_req, int64_t m, int64_t n, int64_t k, sp24_plan* out) {
+bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64_t m, int64_t n,
+                 int64_t k, sp24_plan* out) {
   const StreamShape c = stream_shape(id);
-  const int64_t bn = 16 * c.rbw, bm = 16 * c.mb, ups = (int64_t)c.u * c.kw;
+  if (!stream_fits(dtype, sparse, c.rbw, c.rb, c.kw, c.mb, c.u, c.smax)) return false;
+  const int64_t bn = 16 * c.rbw * c.rb, bm = 16 * c.mb, ups = (int64_t)c.u * c.kw;
   const int64_t units = k / 128;
   if (units % ups != 0) return false;
   const int64_t gy = (m + bm - 1) / bm;
@@ -222,12 +225,13 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     return SP24_OK;
   }
   if (forced && id >= kStreamBase) {
-    if (!plan_stream(id - kStreamBase, sk, orows, m, n, k, out)) return SP24_ERR_SHAPE;
+    if (!plan_stream(id - kStreamBase, dtype, op == SP24_OP_GEMM, sk, orows, m, n, k, out))
+      return SP24_ERR_SHAPE;
     return SP24_OK;
   }
   if (!forced) {
     const StreamChoice d = stream_default(m, n, k);
-    if (plan_stream(d.id, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
+    if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
   }
   const Cfg c = skinny_cfg(id);
   const int tn = 16 * c.rb, tm = 16 * c.mb, nw = c.nw;

@@ -1,5 +1,5 @@
-// Direct global -> LDS loads and the vector-memory wait used by the kernels
-// that stage operands through an LDS ring (gfx950 only).
+// Helpers of the kernels that stage operands through an LDS ring (gfx950
+// only): direct global -> LDS loads, vector-memory waits, LDS swizzles.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,6 +24,32 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+
+// Wait until at most later * PER of this wave's loads are outstanding
+// (`later` is wave-uniform and at most MAXL).
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      wait_vmcnt<MAXL * PER>();
+      return;
+    }
+    wait_later<PER, MAXL - 1>(later);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Slot of 16-byte piece c of LDS row r in rows of P pieces: the 16 rows read
+// by one quarter-wave of a ds_read_b128 land on the 16 distinct 16-byte bank
+// groups (64 banks of 4 bytes).  XOR swizzles are their own inverse: slot s
+// of row r holds piece swz16<P>(r, s).
+template <int P>
+__device__ __forceinline__ int swz16(int r, int c) {
+  static_assert(P > 0 && (P & (P - 1)) == 0, "power of two");
+  if constexpr (P >= 16) return c ^ (r & 15);
+  else return c ^ ((r / (16 / P)) & (P - 1));
 }
 
 }  // namespace sp24

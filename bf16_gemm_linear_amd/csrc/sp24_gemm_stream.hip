@@ -11,10 +11,11 @@
 // ahead of the step being multiplied; the X rows of a step are then read from
 // LDS by every wave that needs them.
 //
-// Waves.  A workgroup has RBW x KW waves: wave (rg, kg) multiplies row block
-// rg (16 W rows) by MB token blocks (16 X rows each) over units
-// [kg*U, (kg+1)*U) of every step (a unit is 128 values of K; a step holds
-// U*KW units).  The KW partial tiles of a row block are summed through LDS in
+// Waves.  A workgroup has RBW x KW waves: wave (rg, kg) multiplies RB row
+// blocks (16 W rows each, rows [16*RB*rg, 16*RB*(rg+1))) by MB token blocks
+// (16 X rows each) over units [kg*U, (kg+1)*U) of every step (a unit is 128
+// values of K; a step holds U*KW units).  A wave reads each X fragment once
+// for its RB row blocks, so RB > 1 divides the LDS reads of X by RB.  The KW partial tiles of a row block are summed through LDS in
 // a fixed order at the end, and K slices of the grid (grid.z) through the
 // split-K workspace, so results are bitwise reproducible.
 //
@@ -37,16 +38,16 @@
 namespace sp24 {
 namespace {
 
-constexpr int kLdsBytes = 160 * 1024;
+constexpr int kLdsBytes = kStreamLdsBytes;
 
-template <int DT, bool SPARSE, int RBW, int KW, int MB, int U, int SMAX>
+template <int DT, bool SPARSE, int RBW, int RB, int KW, int MB, int U, int SMAX>
 struct StreamCfg {
-  static constexpr int DT_ = DT, RBW_ = RBW, KW_ = KW, MB_ = MB, U_ = U;
+  static constexpr int DT_ = DT, RBW_ = RBW, RB_ = RB, KW_ = KW, MB_ = MB, U_ = U;
   static constexpr bool SPARSE_ = SPARSE;
   static constexpr bool FP8 = DT == SP24_FP8_E4M3;
   static constexpr int ESZ = FP8 ? 1 : 2;
   static constexpr int NW = RBW * KW, NT = NW * 64;
-  static constexpr int BN = RBW * 16, BM = MB * 16;       // W rows, X rows per workgroup
+  static constexpr int BN = RBW * RB * 16, BM = MB * 16;  // W rows, X rows per workgroup
   static constexpr int UPS = U * KW;                      // units of 128 K per step
   static constexpr int XU = 128 * ESZ;                    // X bytes per row per unit
   static constexpr int WU = (SPARSE ? 64 : 128) * ESZ;    // W bytes per row per unit
@@ -56,31 +57,23 @@ struct StreamCfg {
   static constexpr int PXU = XU / 16, PWU = WU / 16;      // ... per unit
   static constexpr int W_OFF = 0, M_OFF = BN * WB, X_OFF = M_OFF + BN * MW * 4;
   static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
-  static constexpr int STAGES = SMAX < kLdsBytes / STAGE ? SMAX : kLdsBytes / STAGE;
+  static constexpr int STAGES = stream_stages(DT, SPARSE, RBW, RB, KW, MB, U, SMAX);
+  static constexpr bool FITS = stream_fits(DT, SPARSE, RBW, RB, KW, MB, U, SMAX);
   // load instructions per step: 1 KB (dwordx4) for values and X, 256 B (dword) for metadata
   static constexpr int W_TOT = BN * WB / 1024, M_TOT = BN * MW / 64, X_TOT = BM * XB / 1024;
   static constexpr int W_PER = (W_TOT + NW - 1) / NW, M_PER = (M_TOT + NW - 1) / NW,
                        X_PER = (X_TOT + NW - 1) / NW;
   // every wave issues at least this many loads per step
   static constexpr int MIN_PER_STEP = W_TOT / NW + M_TOT / NW + X_TOT / NW;
-  static constexpr int RED = KW > 1 ? KW * RBW * MB * 1024 : 0;  // epilogue LDS bytes
+  static constexpr int RED = KW > 1 ? KW * RBW * RB * MB * 1024 : 0;  // epilogue LDS bytes
   static constexpr int LDS = STAGES * STAGE > RED ? STAGES * STAGE : RED;
-  static_assert(STAGES >= 2, "two LDS buffers at least");
+  static_assert(STAGE == stream_stage_bytes(DT, SPARSE, RBW, RB, KW, MB, U), "one stage formula");
+  static_assert(!FITS || (STAGES >= 2 && LDS <= kLdsBytes), "LDS budget");
   static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MW,
                 "whole load instructions");
-  static_assert(MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(LDS <= kLdsBytes, "LDS budget");
+  static_assert(!FITS || MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// Slot of 16-byte piece c of LDS row r in a row of P pieces: the 16 rows read
-// by one instruction land on the 16 distinct 16-byte bank groups (64 banks).
-// XOR swizzles are their own inverse: slot s of row r holds piece swz(r, s).
-template <int P>
-__device__ __forceinline__ int swz16(int r, int c) {
-  static_assert((P & (P - 1)) == 0, "power of two");
-  if constexpr (P >= 16) return c ^ (r & 15);
-  else return c ^ ((r / (16 / P)) & (P - 1));
-}
 // Metadata words (MW per row): the 16 rows x 4 words of one read land on 64
 // distinct banks.
 template <int MW>
@@ -157,57 +150,46 @@ struct StreamLoader {
   }
 };
 
-// Wait until at most later * PER of this wave's loads are outstanding
-// (`later` is wave-uniform and at most MAXL).
-template <int PER, int MAXL>
-__device__ __forceinline__ void wait_later(int later) {
-  if constexpr (MAXL > 0) {
-    if (later >= MAXL) {
-      wait_vmcnt<MAXL * PER>();
-      return;
-    }
-    wait_later<PER, MAXL - 1>(later);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 __device__ __forceinline__ i32x4 lds16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
 
-// Units kg*U .. kg*U + U - 1 of one step for row block rg and MB token blocks.
-// All LDS reads of the step are issued before its matrix instructions.
+// Units kg*U .. kg*U + U - 1 of one step for the RB row blocks of row group
+// rg and MB token blocks.  All LDS reads of the step are issued before its
+// matrix instructions.
 template <class C>
-__device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::MB_], const uint8_t* __restrict__ buf,
+__device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
                                            int rg, int kg, int lane) {
-  constexpr int MB = C::MB_, U = C::U_;
+  constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
   constexpr bool FP8 = C::FP8, SPARSE = C::SPARSE_;
   const int q = lane >> 4, r = lane & 15;
-  const int wrow = 16 * rg + r;
-  const uint8_t* wr = buf + C::W_OFF + wrow * C::WB;
   // A: sparse fp8 1 piece, sparse bf16 2, dense fp8 2, dense bf16 4 per unit
   constexpr int AP = SPARSE ? (FP8 ? 1 : 2) : (FP8 ? 2 : 4);
   // B: sparse fp8 2 pieces, sparse bf16 4, dense fp8 2, dense bf16 4 per unit and token block
   constexpr int BP = FP8 ? 2 : 4;
-  i32x4 a[U][AP];
-  uint32_t ix[U];
+  i32x4 a[U][RB][AP];
+  uint32_t ix[U][RB];
   i32x4 b[U][MB][BP];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int v = kg * U + u;  // unit within the step
 #pragma unroll
-    for (int e = 0; e < AP; ++e) {
-      int c;
-      if constexpr (SPARSE && FP8) c = v * C::PWU + q;                 // K [32q, +32)
-      else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
-      else if constexpr (FP8) c = v * C::PWU + 2 * q + e;              // K [32q, +32)
-      else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
-      a[u][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
+    for (int rb = 0; rb < RB; ++rb) {
+      const int wrow = 16 * (RB * rg + rb) + r;
+      const uint8_t* wr = buf + C::W_OFF + wrow * C::WB;
+#pragma unroll
+      for (int e = 0; e < AP; ++e) {
+        int c;
+        if constexpr (SPARSE && FP8) c = v * C::PWU + q;                 // K [32q, +32)
+        else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
+        else if constexpr (FP8) c = v * C::PWU + 2 * q + e;              // K [32q, +32)
+        else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
+        a[u][rb][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
+      }
+      if constexpr (SPARSE)
+        ix[u][rb] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MW * 4 +
+                                                       4 * swzm<C::MW>(wrow, 4 * v + q));
     }
-    if constexpr (SPARSE)
-      ix[u] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MW * 4 +
-                                                 4 * swzm<C::MW>(wrow, 4 * v + q));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int xrow = 16 * mb + r;
@@ -230,26 +212,29 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::MB_], const uint8_t* 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if constexpr (SPARSE && FP8) {
-        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[u][0], cat8(b[u][mb][0], b[u][mb][1]),
-                                                                acc[mb], (int)ix[u], 0, 0);
-      } else if constexpr (SPARSE) {
-        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-            __builtin_bit_cast(bf16x8, a[u][0]),
-            __builtin_bit_cast(bf16x16, cat8(b[u][mb][0], b[u][mb][1])), acc[mb], (int)ix[u], 0, 0);
-        acc[mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-            __builtin_bit_cast(bf16x8, a[u][1]),
-            __builtin_bit_cast(bf16x16, cat8(b[u][mb][2], b[u][mb][3])), acc[mb], (int)ix[u], 0, 1);
-      } else if constexpr (FP8) {
-        acc[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            cat8(a[u][0], a[u][1]), cat8(b[u][mb][0], b[u][mb][1]), acc[mb], 0, 0, 0, 0, 0, 0);
-      } else {
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][e]),
-                                                            __builtin_bit_cast(bf16x8, b[u][mb][e]),
-                                                            acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x4& c = acc[rb][mb];
+        if constexpr (SPARSE && FP8) {
+          c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[u][rb][0], cat8(b[u][mb][0], b[u][mb][1]), c,
+                                                            (int)ix[u][rb], 0, 0);
+        } else if constexpr (SPARSE) {
+          c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+              __builtin_bit_cast(bf16x8, a[u][rb][0]),
+              __builtin_bit_cast(bf16x16, cat8(b[u][mb][0], b[u][mb][1])), c, (int)ix[u][rb], 0, 0);
+          c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+              __builtin_bit_cast(bf16x8, a[u][rb][1]),
+              __builtin_bit_cast(bf16x16, cat8(b[u][mb][2], b[u][mb][3])), c, (int)ix[u][rb], 0, 1);
+        } else if constexpr (FP8) {
+          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              cat8(a[u][rb][0], a[u][rb][1]), cat8(b[u][mb][0], b[u][mb][1]), c, 0, 0, 0, 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][rb][e]),
+                                                        __builtin_bit_cast(bf16x8, b[u][mb][e]), c, 0, 0, 0);
+        }
       }
     }
   }
@@ -260,7 +245,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice) {
-  constexpr int MB = C::MB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
+  constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -271,9 +256,11 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   const int u0 = blockIdx.z * units_per_slice;
   const int nks = units_per_slice / C::UPS;  // the host keeps units_per_slice a multiple of UPS
 
-  f32x4 acc[MB];
+  f32x4 acc[RB][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of STAGES buffers.  At the top of step ks a wave waits for its own
   // loads of step ks; the barrier then makes every wave's loads visible and
@@ -294,82 +281,96 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   }
 
   // Sum the KW partial tiles of each row block in wave order kg = 0, 1, ...
+  // Tile (rb, mb) of wave (rg, kg) sits at red[(((kg*RBW + rg)*RB + rb)*MB + mb)*256 ...].
   if constexpr (KW > 1) {
     __syncthreads();  // every wave is done reading the ring
     float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(((kg * RBW + rg) * MB + mb) * 4 + i) * 64 + lane] = acc[mb][i];
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[((((kg * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane] = acc[rb][mb][i];
     __syncthreads();
     if (kg != 0) return;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float s = red[((rg * MB + mb) * 4 + i) * 64 + lane];
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int g = 1; g < KW; ++g) s += red[(((g * RBW + rg) * MB + mb) * 4 + i) * 64 + lane];
-        acc[mb][i] = s;
-      }
+        for (int i = 0; i < 4; ++i) {
+          float s = red[(((rg * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
+#pragma unroll
+          for (int g = 1; g < KW; ++g) s += red[((((g * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
+          acc[rb][mb][i] = s;
+        }
   }
 
   float scale = 1.0f;
   if constexpr (C::FP8 && !PARTIAL) scale = x_scale[0] * w_scale[0];
   const int q = lane >> 4, c = lane & 15;
-  const int n = n0 + 16 * rg + 4 * q;  // accumulator registers 0..3: rows n .. n + 3
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + 16 * mb + c;
-    if (m >= M || n >= n_end) continue;
-    if constexpr (PARTIAL) {
-      float* pr = partial + ((size_t)blockIdx.z * M + m) * N;
-      if (n + 3 < n_end && (N & 3) == 0) {
-        *reinterpret_cast<f32x4*>(pr + n) = acc[mb];
+  for (int rb = 0; rb < RB; ++rb) {
+    const int n = n0 + 16 * (RB * rg + rb) + 4 * q;  // accumulator registers 0..3: rows n .. n + 3
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + 16 * mb + c;
+      if (m >= M || n >= n_end) continue;
+      const f32x4 v = acc[rb][mb];
+      if constexpr (PARTIAL) {
+        float* pr = partial + ((size_t)blockIdx.z * M + m) * N;
+        if (n + 3 < n_end && (N & 3) == 0) {
+          *reinterpret_cast<f32x4*>(pr + n) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_end) pr[n + e] = v[e];
+        }
       } else {
+        uint16_t* yr = y + (size_t)m * N;
+        const uint32_t lo = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2] * scale) | (f32_to_bf16_rne(v[3] * scale) << 16);
+        if (n + 3 < n_end && (N & 3) == 0) {
+          *reinterpret_cast<u32x2*>(yr + n) = u32x2{lo, hi};
+        } else {
+          const uint32_t h[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < n_end) pr[n + e] = acc[mb][e];
-      }
-    } else {
-      uint16_t* yr = y + (size_t)m * N;
-      const uint32_t lo = f32_to_bf16_rne(acc[mb][0] * scale) | (f32_to_bf16_rne(acc[mb][1] * scale) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc[mb][2] * scale) | (f32_to_bf16_rne(acc[mb][3] * scale) << 16);
-      if (n + 3 < n_end && (N & 3) == 0) {
-        *reinterpret_cast<u32x2*>(yr + n) = u32x2{lo, hi};
-      } else {
-        const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < n_end) yr[n + e] = (uint16_t)v[e];
+          for (int e = 0; e < 4; ++e)
+            if (n + e < n_end) yr[n + e] = (uint16_t)h[e];
+        }
       }
     }
   }
 }
 
-template <int DT, bool SPARSE, int RBW, int KW, int MB, int U, int SMAX>
+template <int DT, bool SPARSE, int RBW, int RB, int KW, int MB, int U, int SMAX>
 hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
-  using C = StreamCfg<DT, SPARSE, RBW, KW, MB, U, SMAX>;
-  const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(C::NT);
-  const int units_per_slice = a.k / 128 / p.split_k;
-  if (p.tile_n > C::BN || p.tile_m != C::BM || p.waves != C::NW || units_per_slice % C::UPS != 0)
-    return hipErrorInvalidConfiguration;
-  const uint8_t* x = static_cast<const uint8_t*>(a.x);
-  const uint8_t* w = static_cast<const uint8_t*>(a.w);
-  if (p.split_k > 1)
-    hipLaunchKernelGGL((gemm_stream_kernel<C, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
-                       a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
-  else
-    hipLaunchKernelGGL((gemm_stream_kernel<C, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
-                       a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
-  return hipGetLastError();
+  using C = StreamCfg<DT, SPARSE, RBW, RB, KW, MB, U, SMAX>;
+  if constexpr (!C::FITS) {
+    return hipErrorInvalidConfiguration;  // the planner never picks it for this operand type
+  } else {
+    const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(C::NT);
+    const int units_per_slice = a.k / 128 / p.split_k;
+    if (p.tile_n > C::BN || p.tile_m != C::BM || p.waves != C::NW || units_per_slice % C::UPS != 0)
+      return hipErrorInvalidConfiguration;
+    const uint8_t* x = static_cast<const uint8_t*>(a.x);
+    const uint8_t* w = static_cast<const uint8_t*>(a.w);
+    if (p.split_k > 1)
+      hipLaunchKernelGGL((gemm_stream_kernel<C, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+    else
+      hipLaunchKernelGGL((gemm_stream_kernel<C, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+    return hipGetLastError();
+  }
 }
 
 template <int DT, bool SPARSE>
 hipError_t launch_stream_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   switch (p.config - kStreamBase) {
-#define SP24_STREAM_CASE(ID, RBW, KW, MB, U, SMAX) \
-  case ID: return launch_stream_cfg<DT, SPARSE, RBW, KW, MB, U, SMAX>(a, p, s);
+#define SP24_STREAM_CASE(ID, RBW, RB, KW, MB, U, SMAX) \
+  case ID: return launch_stream_cfg<DT, SPARSE, RBW, RB, KW, MB, U, SMAX>(a, p, s);
     SP24_STREAM_CONFIGS(SP24_STREAM_CASE)
 #undef SP24_STREAM_CASE
     default: return hipErrorInvalidConfiguration;

@@ -46,29 +46,33 @@ constexpr int TI = BN / WGN / 32;   // 32-row instruction tiles per wave along n
 constexpr int TJ = BM / WGM / 32;   // 32-row instruction tiles per wave along m
 constexpr int GROUP_N = 8;          // tile columns per group in the tile order
 
+// K step and ring depth of the sparse FP8 kernel (the other three keep
+// one 128-byte X row segment per step and as many buffers as fit).
+constexpr int kKsFp8Sparse = 128;
+constexpr int kStagesFp8Sparse = 3;
+
 template <int DT, bool SPARSE>
 struct TiledLayout {
   static constexpr bool FP8 = DT == SP24_FP8_E4M3;
   static constexpr int ESZ = FP8 ? 1 : 2;
-  static constexpr int KS = FP8 ? 128 : 64;             // K values per step
-  static constexpr int WB = SPARSE ? 64 : 128;          // W bytes per row per step
-  static constexpr int MWORDS = SPARSE ? KS / 32 : 0;   // metadata words per row per step
-  static constexpr int XB = 128;                        // X bytes per row per step
+  static constexpr int KS = FP8 ? (SPARSE ? kKsFp8Sparse : 128) : 64;  // K values per step
+  static constexpr int WB = (SPARSE ? KS / 2 : KS) * ESZ;  // W bytes per row per step
+  static constexpr int MWORDS = SPARSE ? KS / 32 : 0;     // metadata words per row per step
+  static constexpr int XB = KS * ESZ;                      // X bytes per row per step
+  static constexpr int WP = WB / 16, XP = XB / 16;        // 16-byte pieces per row
   static constexpr int W_OFF = 0;
   static constexpr int M_OFF = W_OFF + BN * WB;
   static constexpr int X_OFF = M_OFF + BN * MWORDS * 4;
-  static constexpr int STAGE = X_OFF + BM * XB;         // bytes per LDS buffer
-  static constexpr int STAGES = SPARSE ? 3 : 2;         // LDS buffers in the ring
-  static constexpr int SUB = (SPARSE || FP8) ? 2 : 4;   // instructions along K per step
+  static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
+  static constexpr int STAGES = SPARSE ? (FP8 ? kStagesFp8Sparse : 3) : 2;  // LDS buffers
+  // 32x32 instructions along K per step: K 64 (sparse fp8, dense fp8), 32 (sparse bf16), 16 (dense bf16)
+  static constexpr int SUB = KS / (FP8 ? 64 : (SPARSE ? 32 : 16));
+  static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
 };
 
-// 16-byte column swizzles: piece c of row `row` sits at slot swz(row, c).
-__device__ __forceinline__ int swz_w(int row, int c, int pieces) {
-  return pieces == 4 ? (c ^ ((row >> 2) & 3)) : (c ^ ((row >> 1) & 7));
-}
-__device__ __forceinline__ int swz_x(int row, int c) { return c ^ ((row >> 1) & 7); }
-// fp8 metadata (4 words per row): word w of row r at position w ^ (2 * ((r >> 4) & 1)),
-// so the 64 lanes of a read (32 rows x words 2s, 2s+1) hit 64 distinct banks.
+// Metadata words of a row (MWORDS per row): with 4 words, word w of row r sits
+// at w ^ (2 * ((r >> 4) & 1)), so the 64 lanes of a read (32 rows x words 2s,
+// 2s+1) hit 64 distinct banks; with 2 words a read is already contiguous.
 __device__ __forceinline__ int swz_m(int row, int w, int words) {
   return words == 4 ? (w ^ (((row >> 4) & 1) * 2)) : w;
 }
@@ -76,7 +80,6 @@ __device__ __forceinline__ int swz_m(int row, int w, int words) {
 template <int DT, bool SPARSE>
 struct StageLoads {
   using L = TiledLayout<DT, SPARSE>;
-  static constexpr int WPR = L::WB / 16;                         // 16-byte pieces per W row
   static constexpr int W_INSTR = BN * L::WB / 1024 / NWAVES;     // per wave
   static constexpr int X_INSTR = BM * L::XB / 1024 / NWAVES;
   static constexpr int M_INSTR = SPARSE ? BN * L::MWORDS / 64 / NWAVES : 0;  // dword loads
@@ -106,9 +109,9 @@ struct Loader {
     const size_t wrow = SPARSE ? (size_t)(K / 2) * L::ESZ : (size_t)K * L::ESZ;
 #pragma unroll
     for (int j = 0; j < S::W_INSTR; ++j) {
-      const int p = (wave * S::W_INSTR + j) * 64 + lane, row = p / S::WPR;
+      const int p = (wave * S::W_INSTR + j) * 64 + lane, row = p / L::WP;
       const int n = min(n0 + row, N - 1);  // ragged n: clamp the load, the store is masked
-      wp[j] = w + (size_t)n * wrow + 16 * swz_w(row, p % S::WPR, S::WPR);
+      wp[j] = w + (size_t)n * wrow + 16 * swz16<L::WP>(row, p % L::WP);
     }
     if constexpr (SPARSE) {
 #pragma unroll
@@ -121,9 +124,9 @@ struct Loader {
     const size_t xrow = (size_t)K * L::ESZ;
 #pragma unroll
     for (int j = 0; j < S::X_INSTR; ++j) {
-      const int p = (wave * S::X_INSTR + j) * 64 + lane, row = p / 8;
+      const int p = (wave * S::X_INSTR + j) * 64 + lane, row = p / L::XP;
       const int m = min(m0 + row, M - 1);
-      xp[j] = x + (size_t)m * xrow + 16 * swz_x(row, p % 8);
+      xp[j] = x + (size_t)m * xrow + 16 * swz16<L::XP>(row, p % L::XP);
     }
   }
 
@@ -147,15 +150,29 @@ __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Scheduling groups: N times (A matrix instructions, then B vector-memory
+// instructions), so the loads of a later step issue between matrix
+// instructions instead of in one burst that stalls the wave.
+template <int N, int A, int B>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, B, 0);
+    interleave_groups<N - 1, A, B>();
+  }
+}
+
 // One K step from an LDS buffer: SUB substeps x TI x TJ instructions per wave.
 // Every operand of the step is read from LDS first and a scheduling barrier
 // keeps the compiler from interleaving (and serialising) reads and matrix
 // instructions, so the reads of later substeps overlap the first instructions.
-template <int DT, bool SPARSE>
+// With ISSUE, the loads of step `nxt` into `nbuf` are issued interleaved with
+// the matrix instructions.
+template <int DT, bool SPARSE, bool ISSUE>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[TI][TJ], const uint8_t* __restrict__ buf,
-                                         int wn, int wm, int lane) {
+                                         int wn, int wm, int lane, const Loader<DT, SPARSE>& ld,
+                                         uint8_t* nbuf, int nxt) {
   using L = TiledLayout<DT, SPARSE>;
-  constexpr int WPR = L::WB / 16;
   constexpr int SUB = L::SUB;
   const int q = lane >> 5, r = lane & 31;
   i32x4 a[SUB][TI][SPARSE ? 1 : 2];
@@ -171,17 +188,17 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[TI][TJ], const uint8_t* _
         // fp8: bytes [32s + 16q, +16) and word 2s + q; bf16: bytes [32q + 16s, +16),
         // word q (its 16-bit half s is selected by abid)
         const int c = DT == SP24_FP8_E4M3 ? 2 * s + q : 2 * q + s;
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz_w(row, c, WPR));
+        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, c));
         const int word = DT == SP24_FP8_E4M3 ? 2 * s + q : q;
         ix[s][i] = *reinterpret_cast<const uint32_t*>(buf + L::M_OFF + row * L::MWORDS * 4 +
                                                       4 * swz_m(row, word, L::MWORDS));
       } else if constexpr (DT == SP24_FP8_E4M3) {
         // dense fp8: 32 bytes [64s + 32q, +32)
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz_w(row, 4 * s + 2 * q, WPR));
-        a[s][i][1] = *reinterpret_cast<const i32x4*>(wr + 16 * swz_w(row, 4 * s + 2 * q + 1, WPR));
+        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q));
+        a[s][i][1] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q + 1));
       } else {
         // dense bf16: 16 bytes [32s + 16q, +16)
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz_w(row, 2 * s + q, WPR));
+        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 2 * s + q));
       }
     }
 #pragma unroll
@@ -193,17 +210,18 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[TI][TJ], const uint8_t* _
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int c = DT == SP24_FP8_E4M3 ? 4 * s + 2 * h + q : 4 * h + 2 * s + q;
-          b[s][j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz_x(row, c));
+          b[s][j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, c));
         }
       } else if constexpr (DT == SP24_FP8_E4M3) {
-        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz_x(row, 4 * s + 2 * q));
-        b[s][j][1] = *reinterpret_cast<const i32x4*>(xr + 16 * swz_x(row, 4 * s + 2 * q + 1));
+        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q));
+        b[s][j][1] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q + 1));
       } else {
-        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz_x(row, 2 * s + q));
+        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 2 * s + q));
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (ISSUE) ld.issue(nbuf, nxt);
 #pragma unroll
   for (int s = 0; s < SUB; ++s) {
 #pragma unroll
@@ -234,6 +252,11 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[TI][TJ], const uint8_t* _
         }
       }
     }
+  }
+  if constexpr (ISSUE) {
+    constexpr int NMMA = SUB * TI * TJ, NLD = StageLoads<DT, SPARSE>::TOTAL;
+    interleave_groups<NLD, NMMA / NLD, 1>();
+    if constexpr (NMMA % NLD != 0) __builtin_amdgcn_sched_group_barrier(0x008, NMMA % NLD, 0);
   }
 }
 
@@ -280,21 +303,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < nks) ld.issue(lds + p * L::STAGE, p);
-  for (int ks = 0; ks < nks; ++ks) {
+  // steps whose loop issues the loads of step ks + STAGES - 1, then the last ones
+  const int nissue = max(0, nks - (STAGES - 1));
+  for (int ks = 0; ks < nissue; ++ks) {
+    wait_vmcnt<(STAGES - 2) * PER_STEP>();  // loads of steps ks+1 .. ks+STAGES-2 may be in flight
+    __builtin_amdgcn_s_barrier();
+    const int nxt = ks + STAGES - 1;
+    mma_step<DT, SPARSE, true>(acc, lds + (ks % STAGES) * L::STAGE, wn, wm, lane, ld,
+                               lds + (nxt % STAGES) * L::STAGE, nxt);
+  }
+  for (int ks = nissue; ks < nks; ++ks) {
     // loads issued after those of step ks: steps ks+1 .. ks+STAGES-2 (when they exist)
-    const int later = min(nks - 1 - ks, STAGES - 2);
-    if (later >= 2) wait_vmcnt<2 * PER_STEP>();
-    else if (later == 1) wait_vmcnt<PER_STEP>();
-    else wait_vmcnt<0>();
+    wait_later<PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
     // A bare barrier: __syncthreads() adds a workgroup release fence, which
     // would wait for every outstanding LDS-DMA load (vmcnt(0)) and drain the
     // pipeline.  The explicit vmcnt wait above already covers step ks, and each
     // wave's LDS reads of the previous step completed before their results
     // fed its matrix instructions.
     __builtin_amdgcn_s_barrier();
-    const int nxt = ks + STAGES - 1;
-    if (nxt < nks) ld.issue(lds + (nxt % STAGES) * L::STAGE, nxt);
-    mma_step<DT, SPARSE>(acc, lds + (ks % STAGES) * L::STAGE, wn, wm, lane);
+    mma_step<DT, SPARSE, false>(acc, lds + (ks % STAGES) * L::STAGE, wn, wm, lane, ld, nullptr, 0);
   }
 
   float scale = 1.0f;

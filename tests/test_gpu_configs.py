@@ -14,15 +14,16 @@ import re
 import pytest
 
 import workloads as W
-from gpu_helpers import full_case
+from gpu_helpers import full_case, need_sp
 
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 _SRC = open(os.path.join(ROOT, "bf16_gemm_linear_amd", "csrc", "sp24_internal.hpp")).read()
-# stream: id -> (row-block waves, K waves, token blocks, units per wave per step, buffers)
+# stream: id -> (waves along n, row blocks per wave, waves along K, token blocks,
+#                units per wave per step, buffers)
 STREAM = {int(i): tuple(int(v) for v in t) for i, *t in
-          re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
+          re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
 # skinny: id -> (row blocks, token blocks, waves, batch)
 SKINNY = {int(i): tuple(int(v) for v in t) for i, *t in
           re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
@@ -30,6 +31,18 @@ VARIANTS = [(False, False), (True, False), (False, True), (True, True)]  # (fp8,
 
 
 def _run(tile, m, n, k, fp8, dense, what, seed):
+    sp = need_sp()
+    old = os.environ.get("SP24_TILE")
+    os.environ["SP24_TILE"] = tile
+    try:
+        sp.plan(sp.OP_DENSE_GEMM if dense else sp.OP_GEMM, sp.FP8 if fp8 else sp.BF16, m, n, k)
+    except sp.Sp24Error:
+        pytest.skip("configuration does not fit LDS for this operand type (the planner never picks it)")
+    finally:
+        if old is None:
+            os.environ.pop("SP24_TILE", None)
+        else:
+            os.environ["SP24_TILE"] = old
     x = W.randn_bf16((m, k), seed=seed)
     w = W.randn_bf16((n, k), seed=seed + 1, std=0.02)
     old = os.environ.get("SP24_TILE")
@@ -46,8 +59,8 @@ def _run(tile, m, n, k, fp8, dense, what, seed):
 @pytest.mark.parametrize("fp8,dense", VARIANTS)
 @pytest.mark.parametrize("cid", sorted(STREAM))
 def test_stream_config_full_rows_ring_wraps(cid, fp8, dense):
-    rbw, kw, mb, u, smax = STREAM[cid]
-    rows, ups = 16 * rbw, u * kw
+    rbw, rb, kw, mb, u, smax = STREAM[cid]
+    rows, ups = 16 * rbw * rb, u * kw
     # 3 row ranges (the last one 8 rows), 2 token blocks (the last one 5 rows), 9 steps
     m, n, k = 16 * mb + 5, 2 * rows + 8, 128 * ups * 9
     _run("%d,1,%d" % (100 + cid, rows), m, n, k, fp8, dense, "stream %d" % cid, seed=cid * 131)
@@ -56,7 +69,7 @@ def test_stream_config_full_rows_ring_wraps(cid, fp8, dense):
 @pytest.mark.parametrize("fp8,dense", VARIANTS)
 @pytest.mark.parametrize("cid", sorted(STREAM))
 def test_stream_config_partial_rows_split_k(cid, fp8, dense):
-    rbw, kw, mb, u, smax = STREAM[cid]
+    rbw, rb, kw, mb, u, smax = STREAM[cid]
     ups = u * kw
     # 12-row ranges (the last one 4 rows), 3 tokens, 2 K slices of 1 step each
     m, n, k = 3, 40, 128 * ups * 2
