@@ -70,7 +70,7 @@ struct Cfg {
 };
 
 struct StreamShape {
-  int rbw, rb, kw, mb, u, smax;
+  int rbw, rb, mw, kw, mb, u, smax;
 };
 
 struct StreamChoice {
@@ -80,12 +80,12 @@ struct StreamChoice {
 
 StreamShape stream_shape(int id) {
   switch (id) {
-#define SP24_STREAM_SHAPE(ID, RBW, RB, KW, MB, U, SMAX) \
-  case ID: return StreamShape{RBW, RB, KW, MB, U, SMAX};
+#define SP24_STREAM_SHAPE(ID, RBW, RB, MW, KW, MB, U, SMAX) \
+  case ID: return StreamShape{RBW, RB, MW, KW, MB, U, SMAX};
     SP24_STREAM_CONFIGS(SP24_STREAM_SHAPE)
 #undef SP24_STREAM_SHAPE
   }
-  return StreamShape{1, 1, 1, 1, 1, 2};
+  return StreamShape{1, 1, 1, 1, 1, 1, 2};
 }
 
 // Plan of stream configuration `id` (0-based) for a shape, or false if the
@@ -99,8 +99,8 @@ StreamShape stream_shape(int id) {
 bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64_t m, int64_t n,
                  int64_t k, sp24_plan* out) {
   const StreamShape c = stream_shape(id);
-  if (!stream_fits(dtype, sparse, c.rbw, c.rb, c.kw, c.mb, c.u, c.smax)) return false;
-  const int64_t bn = 16 * c.rbw * c.rb, bm = 16 * c.mb, ups = (int64_t)c.u * c.kw;
+  if (!stream_fits(dtype, sparse, c.rbw, c.rb, c.mw, c.kw, c.mb, c.u, c.smax)) return false;
+  const int64_t bn = 16 * c.rbw * c.rb, bm = 16 * c.mw * c.mb, ups = (int64_t)c.u * c.kw;
   const int64_t units = k / 128;
   if (units % ups != 0) return false;
   const int64_t gy = (m + bm - 1) / bm;
@@ -122,7 +122,7 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
   out->kernel = SP24_KERNEL_STREAM;
   out->tile_n = (int)rows;
   out->tile_m = (int)bm;
-  out->waves = c.rbw * c.kw;
+  out->waves = c.rbw * c.mw * c.kw;
   out->split_k = (int)sk;
   out->grid_x = (int)gx;
   out->grid_y = (int)gy;
@@ -144,6 +144,10 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 //    W's share when a CU has few rows, so few-row shapes take 32 tokens per
 //    workgroup (W read twice, the second time from cache), or, for long K, 64
 //    rows per workgroup with K split over 4 workgroups.
+//  * m <= 256: wide shapes (more than 64 rows per CU) keep all 256 tokens in
+//    one workgroup with 8 waves along m, so that W streams once; long-K
+//    few-row shapes take 64 rows per workgroup and split K; the rest take
+//    64-token blocks.
 StreamChoice stream_default(int64_t m, int64_t n, int64_t k) {
   const int64_t rows_cu = (n + 255) / 256;
   auto rows_for = [&](int64_t shares, int64_t lo, int64_t hi) {
@@ -165,6 +169,11 @@ StreamChoice stream_default(int64_t m, int64_t n, int64_t k) {
     if (rows_cu <= 32) return StreamChoice{13, 0};
     if (rows_cu <= 64) return StreamChoice{3, 0};
     return StreamChoice{12, 0};
+  }
+  if (m <= 256) {
+    // 256 tokens per workgroup (8 waves along m): W is streamed once
+    if (rows_cu > 64) return StreamChoice{22, 0};
+    if (rows_cu <= 16 && k >= 8192) return StreamChoice{24, 64};
   }
   const int64_t gy = (m + 63) / 64;
   const int64_t shares = gy >= 256 ? 1 : 256 / gy;
@@ -230,8 +239,13 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     return SP24_OK;
   }
   if (!forced) {
+    // the choice for this shape, else (it does not fit this operand type, or K
+    // does not split into its steps) the 64-token-block configurations
     const StreamChoice d = stream_default(m, n, k);
     if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
+    const int64_t gy = (m + 63) / 64, shares = gy >= 256 ? 1 : 256 / gy;
+    const int g = (n + shares - 1) / shares > 64 ? 12 : 3;
+    if (m > 64 && plan_stream(g, dtype, op == SP24_OP_GEMM, 0, 0, m, n, k, out)) return SP24_OK;
   }
   const Cfg c = skinny_cfg(id);
   const int tn = 16 * c.rb, tm = 16 * c.mb, nw = c.nw;

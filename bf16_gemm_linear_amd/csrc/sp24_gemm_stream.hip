@@ -11,13 +11,16 @@
 // ahead of the step being multiplied; the X rows of a step are then read from
 // LDS by every wave that needs them.
 //
-// Waves.  A workgroup has RBW x KW waves: wave (rg, kg) multiplies RB row
-// blocks (16 W rows each, rows [16*RB*rg, 16*RB*(rg+1))) by MB token blocks
-// (16 X rows each) over units [kg*U, (kg+1)*U) of every step (a unit is 128
-// values of K; a step holds U*KW units).  A wave reads each X fragment once
-// for its RB row blocks, so RB > 1 divides the LDS reads of X by RB.  The KW partial tiles of a row block are summed through LDS in
-// a fixed order at the end, and K slices of the grid (grid.z) through the
-// split-K workspace, so results are bitwise reproducible.
+// Waves.  A workgroup has RBW x MW x KW waves: wave (rg, mg, kg) multiplies
+// RB row blocks (16 W rows each, rows [16*RB*rg, 16*RB*(rg+1))) by MB token
+// blocks (16 X rows each, token blocks [MB*mg, MB*(mg+1))) over units
+// [kg*U, (kg+1)*U) of every step (a unit is 128 values of K; a step holds
+// U*KW units).  A wave reads each X fragment once for its RB row blocks and
+// each W fragment once for its MB token blocks; the MW waves along the tokens
+// let one workgroup cover a few hundred tokens, so that W is streamed once.
+// The KW partial tiles of a row block are summed through LDS in a fixed order
+// at the end, and K slices of the grid (grid.z) through the split-K
+// workspace, so results are bitwise reproducible.
 //
 // Instruction mapping (16 x 16 tiles; measured on gfx950 with one-hot
 // probes).  The compressed operand is A, so W is A and X is B and the
@@ -40,36 +43,36 @@ namespace {
 
 constexpr int kLdsBytes = kStreamLdsBytes;
 
-template <int DT, bool SPARSE, int RBW, int RB, int KW, int MB, int U, int SMAX>
+template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, int SMAX>
 struct StreamCfg {
-  static constexpr int DT_ = DT, RBW_ = RBW, RB_ = RB, KW_ = KW, MB_ = MB, U_ = U;
+  static constexpr int DT_ = DT, RBW_ = RBW, RB_ = RB, MW_ = MW, KW_ = KW, MB_ = MB, U_ = U;
   static constexpr bool SPARSE_ = SPARSE;
   static constexpr bool FP8 = DT == SP24_FP8_E4M3;
   static constexpr int ESZ = FP8 ? 1 : 2;
-  static constexpr int NW = RBW * KW, NT = NW * 64;
-  static constexpr int BN = RBW * RB * 16, BM = MB * 16;  // W rows, X rows per workgroup
+  static constexpr int NW = RBW * MW * KW, NT = NW * 64;
+  static constexpr int BN = RBW * RB * 16, BM = MW * MB * 16;  // W rows, X rows per workgroup
   static constexpr int UPS = U * KW;                      // units of 128 K per step
   static constexpr int XU = 128 * ESZ;                    // X bytes per row per unit
   static constexpr int WU = (SPARSE ? 64 : 128) * ESZ;    // W bytes per row per unit
   static constexpr int MU = SPARSE ? 4 : 0;               // metadata words per row per unit
-  static constexpr int XB = UPS * XU, WB = UPS * WU, MW = UPS * MU;  // per row per step
+  static constexpr int XB = UPS * XU, WB = UPS * WU, MWD = UPS * MU;  // per row per step
   static constexpr int PX = XB / 16, PW = WB / 16;        // 16-byte pieces per row per step
   static constexpr int PXU = XU / 16, PWU = WU / 16;      // ... per unit
-  static constexpr int W_OFF = 0, M_OFF = BN * WB, X_OFF = M_OFF + BN * MW * 4;
+  static constexpr int W_OFF = 0, M_OFF = BN * WB, X_OFF = M_OFF + BN * MWD * 4;
   static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
-  static constexpr int STAGES = stream_stages(DT, SPARSE, RBW, RB, KW, MB, U, SMAX);
-  static constexpr bool FITS = stream_fits(DT, SPARSE, RBW, RB, KW, MB, U, SMAX);
+  static constexpr int STAGES = stream_stages(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX);
+  static constexpr bool FITS = stream_fits(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX);
   // load instructions per step: 1 KB (dwordx4) for values and X, 256 B (dword) for metadata
-  static constexpr int W_TOT = BN * WB / 1024, M_TOT = BN * MW / 64, X_TOT = BM * XB / 1024;
+  static constexpr int W_TOT = BN * WB / 1024, M_TOT = BN * MWD / 64, X_TOT = BM * XB / 1024;
   static constexpr int W_PER = (W_TOT + NW - 1) / NW, M_PER = (M_TOT + NW - 1) / NW,
                        X_PER = (X_TOT + NW - 1) / NW;
   // every wave issues at least this many loads per step
   static constexpr int MIN_PER_STEP = W_TOT / NW + M_TOT / NW + X_TOT / NW;
-  static constexpr int RED = KW > 1 ? KW * RBW * RB * MB * 1024 : 0;  // epilogue LDS bytes
+  static constexpr int RED = KW > 1 ? KW * RBW * MW * RB * MB * 1024 : 0;  // epilogue LDS bytes
   static constexpr int LDS = STAGES * STAGE > RED ? STAGES * STAGE : RED;
-  static_assert(STAGE == stream_stage_bytes(DT, SPARSE, RBW, RB, KW, MB, U), "one stage formula");
+  static_assert(STAGE == stream_stage_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U), "one stage formula");
   static_assert(!FITS || (STAGES >= 2 && LDS <= kLdsBytes), "LDS budget");
-  static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MW,
+  static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MWD,
                 "whole load instructions");
   static_assert(!FITS || MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
 };
@@ -112,8 +115,8 @@ struct StreamLoader {
     if constexpr (C::SPARSE_) {
 #pragma unroll
       for (int j = 0; j < C::M_PER; ++j) {
-        const int p = (j * C::NW + wave) * 64 + lane, row = p / C::MW;
-        const int sw = swzm<C::MW>(row, p % C::MW);
+        const int p = (j * C::NW + wave) * 64 + lane, row = p / C::MWD;
+        const int sw = swzm<C::MWD>(row, p % C::MWD);
         const int n = min(n0 + row, n_last);
         mp[j] = meta + (size_t)n * (K / 32) + (size_t)(u0 + sw / 4) * 4 + (sw % 4);
       }
@@ -139,7 +142,7 @@ struct StreamLoader {
     for (int j = 0; j < C::M_PER; ++j) {
       const int g = j * C::NW + wave;
       if (C::M_TOT % C::NW == 0 || g < C::M_TOT)
-        dma4(mp[j] + (size_t)ks * C::MW, buf + C::M_OFF + g * 256);
+        dma4(mp[j] + (size_t)ks * C::MWD, buf + C::M_OFF + g * 256);
     }
 #pragma unroll
     for (int j = 0; j < C::X_PER; ++j) {
@@ -155,11 +158,11 @@ __device__ __forceinline__ i32x4 lds16(const uint8_t* p) {
 }
 
 // Units kg*U .. kg*U + U - 1 of one step for the RB row blocks of row group
-// rg and MB token blocks.  All LDS reads of the step are issued before its
-// matrix instructions.
+// rg and the MB token blocks of token group mg.  All LDS reads of the step
+// are issued before its matrix instructions.
 template <class C>
 __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
-                                           int rg, int kg, int lane) {
+                                           int rg, int mg, int kg, int lane) {
   constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
   constexpr bool FP8 = C::FP8, SPARSE = C::SPARSE_;
   const int q = lane >> 4, r = lane & 15;
@@ -187,12 +190,12 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
         a[u][rb][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
       }
       if constexpr (SPARSE)
-        ix[u][rb] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MW * 4 +
-                                                       4 * swzm<C::MW>(wrow, 4 * v + q));
+        ix[u][rb] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MWD * 4 +
+                                                       4 * swzm<C::MWD>(wrow, 4 * v + q));
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int xrow = 16 * mb + r;
+      const int xrow = 16 * (MB * mg + mb) + r;
       const uint8_t* xr = buf + C::X_OFF + xrow * C::XB;
 #pragma unroll
       for (int e = 0; e < BP; ++e) {
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
-  const int rg = wave % RBW, kg = wave / RBW;
+  const int rg = wave % RBW, mg = (wave / RBW) % C::MW_, kg = wave / (RBW * C::MW_);
   const int n0 = blockIdx.x * rows_per_wg, m0 = blockIdx.y * C::BM;
   const int n_end = min(N, n0 + rows_per_wg);
   const int u0 = blockIdx.z * units_per_slice;
@@ -277,11 +280,12 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     __builtin_amdgcn_s_barrier();
     const int nxt = ks + STAGES - 1;
     if (nxt < nks) ld.issue(lds + (nxt % STAGES) * C::STAGE, nxt);
-    stream_mma<C>(acc, lds + (ks % STAGES) * C::STAGE, rg, kg, lane);
+    stream_mma<C>(acc, lds + (ks % STAGES) * C::STAGE, rg, mg, kg, lane);
   }
 
   // Sum the KW partial tiles of each row block in wave order kg = 0, 1, ...
-  // Tile (rb, mb) of wave (rg, kg) sits at red[(((kg*RBW + rg)*RB + rb)*MB + mb)*256 ...].
+  // Tile (rb, mb) of wave (rg, mg, kg) sits at
+  // red[((((kg*MW + mg)*RBW + rg)*RB + rb)*MB + mb)*256 ...].
   if constexpr (KW > 1) {
     __syncthreads();  // every wave is done reading the ring
     float* red = reinterpret_cast<float*>(lds);
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          red[((((kg * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane] = acc[rb][mb][i];
+          red[(((((kg * C::MW_ + mg) * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane] = acc[rb][mb][i];
     __syncthreads();
     if (kg != 0) return;
 #pragma unroll
@@ -300,9 +304,10 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = red[(((rg * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
+          float s = red[((((mg * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
 #pragma unroll
-          for (int g = 1; g < KW; ++g) s += red[((((g * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
+          for (int g = 1; g < KW; ++g)
+            s += red[(((((g * C::MW_ + mg) * RBW + rg) * RB + rb) * MB + mb) * 4 + i) * 64 + lane];
           acc[rb][mb][i] = s;
         }
   }
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const int n = n0 + 16 * (RB * rg + rb) + 4 * q;  // accumulator registers 0..3: rows n .. n + 3
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + 16 * mb + c;
+      const int m = m0 + 16 * (MB * mg + mb) + c;
       if (m >= M || n >= n_end) continue;
       const f32x4 v = acc[rb][mb];
       if constexpr (PARTIAL) {
@@ -344,9 +349,9 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   }
 }
 
-template <int DT, bool SPARSE, int RBW, int RB, int KW, int MB, int U, int SMAX>
+template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, int SMAX>
 hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
-  using C = StreamCfg<DT, SPARSE, RBW, RB, KW, MB, U, SMAX>;
+  using C = StreamCfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX>;
   if constexpr (!C::FITS) {
     return hipErrorInvalidConfiguration;  // the planner never picks it for this operand type
   } else {
@@ -369,8 +374,8 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
 template <int DT, bool SPARSE>
 hipError_t launch_stream_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   switch (p.config - kStreamBase) {
-#define SP24_STREAM_CASE(ID, RBW, RB, KW, MB, U, SMAX) \
-  case ID: return launch_stream_cfg<DT, SPARSE, RBW, RB, KW, MB, U, SMAX>(a, p, s);
+#define SP24_STREAM_CASE(ID, RBW, RB, MW, KW, MB, U, SMAX) \
+  case ID: return launch_stream_cfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX>(a, p, s);
     SP24_STREAM_CONFIGS(SP24_STREAM_CASE)
 #undef SP24_STREAM_CASE
     default: return hipErrorInvalidConfiguration;

@@ -58,50 +58,59 @@ constexpr int kSkinnyConfigs = 18;
 constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
 
 // Small-m LDS-ring kernel configurations (config id = kStreamBase + id):
-// X(id, waves along n, row blocks of 16 per wave, waves along K, token blocks
-//   of 16, 128-K units per wave per step, LDS buffers at most).  An entry runs
-// an operand type only where two LDS buffers fit (stream_fits); the planner
-// never picks it otherwise.
-#define SP24_STREAM_CONFIGS(X)  \
-  X(0, 4, 1, 1, 1, 2, 6)        \
-  X(1, 4, 1, 2, 1, 1, 6)        \
-  X(2, 4, 1, 1, 4, 2, 4)        \
-  X(3, 4, 1, 2, 4, 1, 4)        \
-  X(4, 1, 1, 4, 1, 1, 6)        \
-  X(5, 1, 1, 8, 1, 1, 4)        \
-  X(6, 1, 1, 4, 4, 1, 3)        \
-  X(7, 2, 1, 2, 1, 1, 6)        \
-  X(8, 2, 1, 4, 2, 1, 3)        \
-  X(9, 8, 1, 1, 1, 2, 4)        \
-  X(10, 4, 1, 1, 2, 2, 4)       \
-  X(11, 2, 1, 2, 4, 1, 4)       \
-  X(12, 8, 1, 1, 4, 1, 3)       \
-  X(13, 4, 1, 2, 2, 1, 4)       \
-  X(14, 1, 1, 4, 2, 1, 4)       \
-  X(15, 2, 1, 4, 1, 1, 4)       \
-  X(16, 4, 1, 2, 1, 1, 10)      \
-  X(17, 2, 1, 4, 1, 1, 8)       \
-  X(18, 4, 1, 4, 1, 1, 6)       \
-  X(19, 1, 1, 8, 1, 1, 8)       \
-  X(20, 2, 2, 4, 4, 1, 3)
-constexpr int kStreamConfigs = 21;
+// X(id, waves along n, row blocks of 16 per wave, waves along m, waves along
+//   K, token blocks of 16 per wave, 128-K units per wave per step, LDS
+//   buffers at most).  An entry runs an operand type only where two LDS
+// buffers fit (stream_fits); the planner never picks it otherwise.
+#define SP24_STREAM_CONFIGS(X)       \
+  X(0, 4, 1, 1, 1, 1, 2, 6)          \
+  X(1, 4, 1, 1, 2, 1, 1, 6)          \
+  X(2, 4, 1, 1, 1, 4, 2, 4)          \
+  X(3, 4, 1, 1, 2, 4, 1, 4)          \
+  X(4, 1, 1, 1, 4, 1, 1, 6)          \
+  X(5, 1, 1, 1, 8, 1, 1, 4)          \
+  X(6, 1, 1, 1, 4, 4, 1, 3)          \
+  X(7, 2, 1, 1, 2, 1, 1, 6)          \
+  X(8, 2, 1, 1, 4, 2, 1, 3)          \
+  X(9, 8, 1, 1, 1, 1, 2, 4)          \
+  X(10, 4, 1, 1, 1, 2, 2, 4)         \
+  X(11, 2, 1, 1, 2, 4, 1, 4)         \
+  X(12, 8, 1, 1, 1, 4, 1, 3)         \
+  X(13, 4, 1, 1, 2, 2, 1, 4)         \
+  X(14, 1, 1, 1, 4, 2, 1, 4)         \
+  X(15, 2, 1, 1, 4, 1, 1, 4)         \
+  X(16, 4, 1, 1, 2, 1, 1, 10)        \
+  X(17, 2, 1, 1, 4, 1, 1, 8)         \
+  X(18, 4, 1, 1, 4, 1, 1, 6)         \
+  X(19, 1, 1, 1, 8, 1, 1, 8)         \
+  X(20, 2, 2, 1, 4, 4, 1, 3)         \
+  X(21, 1, 8, 4, 1, 4, 1, 3)         \
+  X(22, 1, 8, 8, 1, 2, 1, 3)         \
+  X(23, 1, 4, 4, 1, 4, 1, 3)         \
+  X(24, 1, 4, 8, 1, 2, 1, 3)         \
+  X(25, 2, 4, 4, 1, 2, 1, 3)         \
+  X(26, 1, 2, 8, 1, 2, 1, 4)         \
+  X(27, 1, 4, 4, 2, 4, 1, 2)
+constexpr int kStreamConfigs = 28;
 constexpr int kStreamBase = 100;
 constexpr int kStreamLdsBytes = 160 * 1024;
 
 // Bytes of one LDS buffer of a stream configuration: W values and metadata of
-// 16 * rbw * rb rows plus 16 * mb X rows, for u * kw units of 128 K.
-constexpr int stream_stage_bytes(int dtype, bool sparse, int rbw, int rb, int kw, int mb, int u) {
+// 16 * rbw * rb rows plus 16 * mw * mb X rows, for u * kw units of 128 K.
+constexpr int stream_stage_bytes(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u) {
   const int esz = dtype == SP24_FP8_E4M3 ? 1 : 2;
   const int ups = u * kw;
-  const int wb = ups * (sparse ? 64 : 128) * esz, mw = sparse ? ups * 4 : 0, xb = ups * 128 * esz;
-  return 16 * rbw * rb * (wb + 4 * mw) + 16 * mb * xb;
+  const int wb = ups * (sparse ? 64 : 128) * esz, mwords = sparse ? ups * 4 : 0, xb = ups * 128 * esz;
+  return 16 * rbw * rb * (wb + 4 * mwords) + 16 * mw * mb * xb;
 }
-constexpr int stream_stages(int dtype, bool sparse, int rbw, int rb, int kw, int mb, int u, int smax) {
-  const int fit = kStreamLdsBytes / stream_stage_bytes(dtype, sparse, rbw, rb, kw, mb, u);
+constexpr int stream_stages(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
+                            int smax) {
+  const int fit = kStreamLdsBytes / stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u);
   return smax < fit ? smax : fit;
 }
-constexpr bool stream_fits(int dtype, bool sparse, int rbw, int rb, int kw, int mb, int u, int smax) {
-  return stream_stages(dtype, sparse, rbw, rb, kw, mb, u, smax) >= 2;
+constexpr bool stream_fits(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
+                           int smax) {
+  return stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) >= 2;
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);

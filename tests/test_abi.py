@@ -131,7 +131,7 @@ def test_plan_table_shapes():
     table = {int(i): (16 * int(rb), 16 * int(mb), int(nw), int(b)) for i, rb, mb, nw, b in
              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
     stream = {100 + int(i): tuple(int(v) for v in t) for i, *t in
-              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
     assert len(table) >= 8 and len(stream) >= 8
     shapes = [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (1, 4096, 14336),
               (64, 4096, 14336), (8, 256, 256), (256, 6144, 4096), (256, 4096, 14336),
@@ -145,8 +145,8 @@ def test_plan_table_shapes():
                     assert pl["grid_x"] == -(-n // 256) * -(-m // 256)
                     continue
                 if pl["kernel"] == 2:   # LDS ring: one range of rows per workgroup
-                    rbw, rb, kw, mb, u, smax = stream[pl["config"]]
-                    assert (pl["tile_m"], pl["waves"], pl["batch"]) == (16 * mb, rbw * kw, u)
+                    rbw, rb, mw, kw, mb, u, smax = stream[pl["config"]]
+                    assert (pl["tile_m"], pl["waves"], pl["batch"]) == (16 * mw * mb, rbw * mw * kw, u)
                     assert 0 < pl["tile_n"] <= 16 * rbw * rb
                     assert pl["tile_n"] % 4 == 0
                     assert (k // 128) % (pl["split_k"] * u * kw) == 0
@@ -187,32 +187,44 @@ def test_plan_stream_rows_cover_every_cu_equally():
         assert (gx * gz) % 256 == 0
 
 
-def _stream_stage_bytes(dtype, sparse, rbw, rb, kw, mb, u):
+def _stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u):
     esz = 1 if dtype == sp.FP8 else 2
     ups = u * kw
-    wb, mw, xb = ups * (64 if sparse else 128) * esz, (ups * 4 if sparse else 0), ups * 128 * esz
-    return 16 * rbw * rb * (wb + 4 * mw) + 16 * mb * xb
+    wb, mwords, xb = ups * (64 if sparse else 128) * esz, (ups * 4 if sparse else 0), ups * 128 * esz
+    return 16 * rbw * rb * (wb + 4 * mwords) + 16 * mw * mb * xb
 
 
 def test_plan_rejects_stream_configs_that_do_not_fit_lds(monkeypatch):
     # every forced stream configuration plans iff two LDS buffers of its operand type fit
     src = open(os.path.join(ROOT, "bf16_gemm_linear_amd", "csrc", "sp24_internal.hpp")).read()
     stream = {int(i): tuple(int(v) for v in t) for i, *t in
-              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+              re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
     seen = set()
-    for cid, (rbw, rb, kw, mb, u, smax) in stream.items():
+    for cid, (rbw, rb, mw, kw, mb, u, smax) in stream.items():
         k = 128 * u * kw * 4
         monkeypatch.setenv("SP24_TILE", "%d,1" % (100 + cid))
         for dt in (sp.BF16, sp.FP8):
             for op, sparse in ((sp.OP_GEMM, True), (sp.OP_DENSE_GEMM, False)):
-                fits = min(smax, 160 * 1024 // _stream_stage_bytes(dt, sparse, rbw, rb, kw, mb, u)) >= 2
+                fits = min(smax, 160 * 1024 // _stream_stage_bytes(dt, sparse, rbw, rb, mw, kw, mb, u)) >= 2
                 seen.add(fits)
                 if fits:
-                    assert sp.plan(op, dt, 16 * mb, 16 * rbw * rb * 3, k)["config"] == 100 + cid
+                    assert sp.plan(op, dt, 16 * mw * mb, 16 * rbw * rb * 3, k)["config"] == 100 + cid
                 else:
                     with pytest.raises(sp.Sp24Error):
-                        sp.plan(op, dt, 16 * mb, 16 * rbw * rb * 3, k)
+                        sp.plan(op, dt, 16 * mw * mb, 16 * rbw * rb * 3, k)
     assert seen == {True, False}
+
+
+def test_plan_prefers_the_lds_ring_kernels():
+    # every operand type of the decode and layer-sweep shapes plans an LDS-ring kernel (stream
+    # or tiled); the skinny kernel is only the fallback for K that no stream step divides
+    shapes = [(1, 14336, 4096), (16, 14336, 4096), (64, 14336, 4096), (1, 4096, 14336),
+              (64, 4096, 14336), (256, 6144, 4096), (256, 4096, 4096), (256, 28672, 4096),
+              (256, 4096, 14336), (200, 28672, 4096), (129, 14336, 4096)]
+    for dt in (sp.BF16, sp.FP8):
+        for op in (sp.OP_GEMM, sp.OP_DENSE_GEMM):
+            for m, n, k in shapes:
+                assert sp.plan(op, dt, m, n, k)["kernel"] in (1, 2), (dt, op, m, n, k)
 
 
 def test_plan_falls_back_to_skinny_kernel_for_odd_k():

@@ -20,10 +20,10 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 _SRC = open(os.path.join(ROOT, "bf16_gemm_linear_amd", "csrc", "sp24_internal.hpp")).read()
-# stream: id -> (waves along n, row blocks per wave, waves along K, token blocks,
-#                units per wave per step, buffers)
+# stream: id -> (waves along n, row blocks per wave, waves along m, waves along K,
+#                token blocks per wave, units per wave per step, buffers)
 STREAM = {int(i): tuple(int(v) for v in t) for i, *t in
-          re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
+          re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
 # skinny: id -> (row blocks, token blocks, waves, batch)
 SKINNY = {int(i): tuple(int(v) for v in t) for i, *t in
           re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", _SRC)}
@@ -59,17 +59,17 @@ def _run(tile, m, n, k, fp8, dense, what, seed):
 @pytest.mark.parametrize("fp8,dense", VARIANTS)
 @pytest.mark.parametrize("cid", sorted(STREAM))
 def test_stream_config_full_rows_ring_wraps(cid, fp8, dense):
-    rbw, rb, kw, mb, u, smax = STREAM[cid]
+    rbw, rb, mw, kw, mb, u, smax = STREAM[cid]
     rows, ups = 16 * rbw * rb, u * kw
-    # 3 row ranges (the last one 8 rows), 2 token blocks (the last one 5 rows), 9 steps
-    m, n, k = 16 * mb + 5, 2 * rows + 8, 128 * ups * 9
+    # 3 row ranges (the last one 8 rows), 2 token groups (the last one 5 rows), 9 steps
+    m, n, k = 16 * mw * mb + 5, 2 * rows + 8, 128 * ups * 9
     _run("%d,1,%d" % (100 + cid, rows), m, n, k, fp8, dense, "stream %d" % cid, seed=cid * 131)
 
 
 @pytest.mark.parametrize("fp8,dense", VARIANTS)
 @pytest.mark.parametrize("cid", sorted(STREAM))
 def test_stream_config_partial_rows_split_k(cid, fp8, dense):
-    rbw, rb, kw, mb, u, smax = STREAM[cid]
+    rbw, rb, mw, kw, mb, u, smax = STREAM[cid]
     ups = u * kw
     # 12-row ranges (the last one 4 rows), 3 tokens, 2 K slices of 1 step each
     m, n, k = 3, 40, 128 * ups * 2
