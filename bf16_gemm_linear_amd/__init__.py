@@ -34,7 +34,7 @@ lib_path = os.path.join(_HERE, "libsp24.so")
 
 if not os.path.exists(lib_path):
     raise ImportError(
-        "libsp24.so is not built (expected at %s); run `python -m bf16_gemm_linear_amd.build`" % lib_path)
+        "libsp24.so is not built (expected at %s); run `python bf16_gemm_linear_amd/build.py`" % lib_path)
 
 lib = ctypes.CDLL(lib_path)
 
@@ -53,6 +53,7 @@ class Plan(ctypes.Structure):
 _SIGS = {
     "sp24_prune_compress": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_decompress": [_int, _vp, _vp, _i64, _i64, _vp, _vp],
+    "sp24_check_meta": [_vp, _i64, _i64, _vp, _vp],
     "sp24_quant_fp8": [_vp, _i64, _vp, _vp, _int, _vp, _sz, _vp],
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -67,7 +68,11 @@ _SIGS = {
     "sp24_probe_read_blocks": [],
 }
 for _name, _args in _SIGS.items():
-    _f = getattr(lib, _name)
+    try:
+        _f = getattr(lib, _name)
+    except AttributeError as _e:
+        raise ImportError("%s lacks %s: it was built from older sources; rebuild it with "
+                          "`python bf16_gemm_linear_amd/build.py`" % (lib_path, _name)) from _e
     _f.argtypes = _args
     _f.restype = _int
 lib.sp24_workspace_size.restype = _sz
@@ -166,6 +171,18 @@ def decompress(values: torch.Tensor, meta: torch.Tensor, k: int, out: torch.Tens
     _check("sp24_decompress",
            lib.sp24_decompress(dt, _ptr(values), _ptr(meta), n, k, _ptr(out), _stream(values.device)))
     return out
+
+
+def check_meta(meta: torch.Tensor, k: int, bad: torch.Tensor | None = None) -> torch.Tensor:
+    """Count the metadata nibbles that are not a valid kept pair; returns a uint32[1] device
+    tensor (`bad`, if given, is added to; otherwise a zeroed one is made)."""
+    _need(meta, "meta", torch.int32, 2)
+    if bad is None:
+        bad = torch.zeros(1, dtype=torch.int32, device=meta.device)
+    _need(bad, "bad", torch.int32, None, meta.device)
+    _check("sp24_check_meta",
+           lib.sp24_check_meta(_ptr(meta), meta.shape[0], k, _ptr(bad), _stream(meta.device)))
+    return bad
 
 
 def quant_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Tensor | None = None,

@@ -1,6 +1,9 @@
 """Build libsp24.so (HIP, gfx950 only) in-tree.
 
-    python -m bf16_gemm_linear_amd.build          # or: python bf16_gemm_linear_amd/build.py
+    python bf16_gemm_linear_amd/build.py
+
+(run as a script: importing the package first would load the library being
+replaced, and fail if it predates a symbol the binding declares).
 
 Every source in csrc/ is compiled with hipcc for gfx950 and linked into
 bf16_gemm_linear_amd/libsp24.so.  No fast-math: float32 division and square

@@ -338,6 +338,15 @@ int sp24_decompress(int dtype, const void* values, const uint32_t* meta, int64_t
   return finish(launch_decompress(dtype, values, meta, n, k, w_out, s), s);
 }
 
+int sp24_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad_dev, void* stream) {
+  if (!meta || !bad_dev) return SP24_ERR_NULL;
+  if (n < 1 || k < 32 || k % 32 != 0 || n > kMaxDim || k > kMaxDim) return SP24_ERR_SHAPE;
+  if (!aligned16(meta) || ((uintptr_t)bad_dev & 3u)) return SP24_ERR_ALIGN;
+  if (overlaps(bad_dev, 4, meta, (size_t)n * (k / 32) * 4)) return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_check_meta(meta, n, k, bad_dev, s), s);
+}
+
 int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
                    void* ws, size_t ws_bytes, void* stream) {
   if (mode != SP24_SCALE_DYNAMIC && mode != SP24_SCALE_STATIC) return SP24_ERR_MODE;

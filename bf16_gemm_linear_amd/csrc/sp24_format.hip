@@ -122,6 +122,25 @@ int grid_for(int64_t items, int per_block) {
   return (int)g;
 }
 
+// Counts the nibbles that are not a valid kept pair (i0 < i1: 4, 8, 9, 12, 13, 14)
+// and adds the count to *bad with one atomic per wave.
+__global__ __launch_bounds__(256) void check_meta_kernel(const uint32_t* __restrict__ meta,
+                                                         int64_t nwords, uint32_t* __restrict__ bad) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t cnt = 0;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
+    const uint32_t word = meta[t];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t nib = (word >> (4 * g)) & 0xFu;
+      cnt += (nib & 3u) >= (nib >> 2) ? 1u : 0u;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += (uint32_t)__shfl_xor((int)cnt, off, 64);
+  if ((threadIdx.x & 63) == 0 && cnt != 0) atomicAdd(bad, cnt);
+}
+
 }  // namespace
 
 hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16_t* values,
@@ -130,6 +149,13 @@ hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16
   hipLaunchKernelGGL(prune_compress_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, s,
                      reinterpret_cast<const u32x4*>(w), nwords, reinterpret_cast<u32x4*>(values),
                      meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad,
+                             hipStream_t s) {
+  const int64_t nwords = n * (k / 32);
+  hipLaunchKernelGGL(check_meta_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, s, meta, nwords, bad);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@ hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16
                                  uint32_t* meta, hipStream_t s);
 hipError_t launch_decompress(int dtype, const void* values, const uint32_t* meta, int64_t n,
                              int64_t k, void* out, hipStream_t s);
+hipError_t launch_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad,
+                             hipStream_t s);
 
 // sp24_quant.hip
 size_t quant_workspace_bytes(int64_t count);

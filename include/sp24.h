@@ -118,6 +118,16 @@ int sp24_prune_compress(const void* w_bf16, int64_t n, int64_t k, void* values_b
 int sp24_decompress(int dtype, const void* values, const uint32_t* meta, int64_t n, int64_t k,
                     void* w_out, void* stream);
 
+/* Count the metadata nibbles of a compressed weight that are not a valid kept
+ * pair (i0 < i1, i.e. one of 4, 8, 9, 12, 13, 14): a check for compressed
+ * weights that did not come from sp24_prune_compress (sp24_gemm and
+ * sp24_decompress use nibbles as given).
+ *   meta    in : [n, k/32] uint32
+ *   bad_dev out: one uint32 on the device; the count is ADDED to it (the
+ *                caller zeroes it first), so several tensors can share one.
+ * Requires n >= 1, k >= 32, k % 32 == 0; bad_dev 4-byte aligned. */
+int sp24_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad_dev, void* stream);
+
 /* Quantise count bf16 values to E4M3 codes with one per-tensor scale.
  *   mode SP24_SCALE_DYNAMIC: amax = max|x| over the tensor (exact), then
  *        *scale_dev = fp32(amax / 448) (1.0 if amax == 0), written by the

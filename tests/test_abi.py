@@ -93,6 +93,17 @@ def test_dense_gemm_validation():
     assert f(1, 1, 1, 128, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ENULL
 
 
+def test_check_meta_validation():
+    f = lib.sp24_check_meta
+    assert f(None, 4, 64, p(A), None) == ENULL
+    assert f(p(A), 4, 64, None, None) == ENULL
+    assert f(p(A), 0, 64, p(A + 0x10000), None) == ESHAPE
+    assert f(p(A), 4, 48, p(A + 0x10000), None) == ESHAPE
+    assert f(p(A + 4), 4, 64, p(A + 0x10000), None) == EALIGN
+    assert f(p(A), 4, 64, p(A + 0x10002), None) == EALIGN
+    assert f(p(A), 4, 64, p(A + 4), None) == EALIAS
+
+
 def test_prune_and_decompress_validation():
     f = lib.sp24_prune_compress
     assert f(None, 4, 64, p(A), p(A + 0x1000), None) == ENULL

@@ -96,3 +96,26 @@ def test_decompress_random_codes_all_nibbles():
                       torch.from_numpy(meta.view(np.int32)).to(DEV), k)
     torch.cuda.synchronize()
     assert np.array_equal(codes(d), O.decompress(vals, meta, k))
+
+
+def test_check_meta_counts_invalid_nibbles():
+    sp = need_sp()
+    announce("check_meta")
+    w = W.randn_bf16((96, 1024), seed=77, std=0.02)
+    _, meta = sp.prune_compress(w.to(DEV))
+    assert int(sp.check_meta(meta, 1024).cpu()[0]) == 0          # every written nibble is valid
+    m = u32(meta).copy()
+    rng = np.random.default_rng(78)
+    invalid = np.array([0, 1, 2, 3, 5, 6, 7, 10, 11, 15], dtype=np.uint32)
+    cells = rng.choice(m.size * 8, size=500, replace=False)         # (word, nibble) cells
+    for c in cells:
+        word, g = divmod(int(c), 8)
+        r, col = divmod(word, m.shape[1])
+        m[r, col] = (m[r, col] & ~np.uint32(0xF << (4 * g))) | (rng.choice(invalid) << np.uint32(4 * g))
+    nib = (m[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
+    expected = int(((nib & 3) >= (nib >> 2)).sum())                # i0 >= i1: not a kept pair
+    assert expected == 500
+    bad = sp.check_meta(torch.from_numpy(m.view(np.int32)).to(DEV), 1024)
+    assert int(bad.cpu()[0]) == expected
+    # the count is added to the given counter
+    assert int(sp.check_meta(torch.from_numpy(m.view(np.int32)).to(DEV), 1024, bad).cpu()[0]) == 2 * expected
