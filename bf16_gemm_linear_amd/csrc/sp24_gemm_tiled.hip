@@ -32,6 +32,8 @@
 // measured slower: its loads gather 32-byte pieces.)  Workgroups are mapped to
 // tiles XCD by XCD and, inside an XCD, in groups of 8 tile columns, so that
 // workgroups resident at the same time share W and X tiles in their XCD's L2.
+#include <type_traits>
+
 #include "sp24_common.hpp"
 #include "sp24_dma.hpp"
 #include "sp24_internal.hpp"
@@ -67,7 +69,9 @@ struct TiledLayout {
   static constexpr int STAGES = SPARSE ? (FP8 ? kStagesFp8Sparse : 3) : 2;  // LDS buffers
   // 32x32 instructions along K per step: K 64 (sparse fp8, dense fp8), 32 (sparse bf16), 16 (dense bf16)
   static constexpr int SUB = KS / (FP8 ? 64 : (SPARSE ? 32 : 16));
-  static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
+  static constexpr int YS = BN * 2 + 16;  // bytes per row of the output tile staged in LDS
+  static constexpr int LDS_BYTES = STAGES * STAGE > BM * YS ? STAGES * STAGE : BM * YS;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
 // Metadata words of a row (MWORDS per row): with 4 words, word w of row r sits
@@ -130,6 +134,20 @@ struct Loader {
     }
   }
 
+  // Load J of this wave's share of K step ks (W pieces, then metadata words, then X pieces).
+  template <int J>
+  __device__ __forceinline__ void issue_one(uint8_t* buf, int ks) const {
+    if constexpr (J < S::W_INSTR) {
+      dma16(wp[J] + (size_t)ks * L::WB, buf + L::W_OFF + (wave * S::W_INSTR + J) * 1024);
+    } else if constexpr (J < S::W_INSTR + S::M_INSTR) {
+      constexpr int j = J - S::W_INSTR;
+      dma4(mp[j] + (size_t)ks * L::MWORDS, buf + L::M_OFF + (wave * S::M_INSTR + j) * 256);
+    } else {
+      constexpr int j = J - S::W_INSTR - S::M_INSTR;
+      dma16(xp[j] + (size_t)ks * L::XB, buf + L::X_OFF + (wave * S::X_INSTR + j) * 1024);
+    }
+  }
+
   // Issue every load of K step ks into the LDS buffer `buf`.
   __device__ __forceinline__ void issue(uint8_t* buf, int ks) const {
 #pragma unroll
@@ -150,113 +168,144 @@ __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
   return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Scheduling groups: N times (A matrix instructions, then B vector-memory
-// instructions), so the loads of a later step issue between matrix
-// instructions instead of in one burst that stalls the wave.
-template <int N, int A, int B>
-__device__ __forceinline__ void interleave_groups() {
-  if constexpr (N > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, B, 0);
-    interleave_groups<N - 1, A, B>();
+// Operands of one substep (one instruction along K) for a wave's TI x TJ
+// instruction tiles.
+template <int DT, bool SPARSE>
+struct Frag {
+  i32x4 a[TI][SPARSE ? 1 : 2];
+  uint32_t ix[TI];
+  i32x4 b[TJ][2];
+};
+
+// Reads of one substep, numbered: A operands (one per instruction row i),
+// then X runs (two per instruction column j), then metadata words (one per i).
+template <bool SPARSE>
+constexpr int n_pieces() {
+  return TI + 2 * TJ + (SPARSE ? TI : 0);
+}
+
+// Read piece P of substep s from an LDS buffer into f.
+template <int DT, bool SPARSE, int P>
+__device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const uint8_t* __restrict__ buf, int s, int wn,
+                                           int wm, int lane) {
+  using L = TiledLayout<DT, SPARSE>;
+  const int q = lane >> 5, r = lane & 31;
+  if constexpr (P < TI) {
+    constexpr int i = P;
+    const int row = wn * (BN / WGN) + 32 * i + r;
+    const uint8_t* wr = buf + L::W_OFF + row * L::WB;
+    if constexpr (SPARSE) {
+      // fp8: bytes [32s + 16q, +16); bf16: bytes [32q + 16s, +16)
+      const int c = DT == SP24_FP8_E4M3 ? 2 * s + q : 2 * q + s;
+      f.a[i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, c));
+    } else if constexpr (DT == SP24_FP8_E4M3) {
+      // dense fp8: 32 bytes [64s + 32q, +32)
+      f.a[i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q));
+      f.a[i][1] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q + 1));
+    } else {
+      // dense bf16: 16 bytes [32s + 16q, +16)
+      f.a[i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 2 * s + q));
+    }
+  } else if constexpr (P < TI + 2 * TJ) {
+    constexpr int j = (P - TI) / 2, h = (P - TI) % 2;
+    const int row = wm * (BM / WGM) + 32 * j + r;
+    const uint8_t* xr = buf + L::X_OFF + row * L::XB;
+    if constexpr (SPARSE) {
+      // run h of lane group q: fp8 bytes 64s + 32h + 16q; bf16 bytes 64h + 32s + 16q
+      const int c = DT == SP24_FP8_E4M3 ? 4 * s + 2 * h + q : 4 * h + 2 * s + q;
+      f.b[j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, c));
+    } else if constexpr (DT == SP24_FP8_E4M3) {
+      f.b[j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q + h));
+    } else if constexpr (h == 0) {
+      f.b[j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 2 * s + q));
+    }
+  } else {
+    // index bits: fp8 word 2s + q; bf16 word q (its 16-bit half s is selected by abid)
+    constexpr int i = P - TI - 2 * TJ;
+    const int row = wn * (BN / WGN) + 32 * i + r;
+    const int word = DT == SP24_FP8_E4M3 ? 2 * s + q : q;
+    f.ix[i] = *reinterpret_cast<const uint32_t*>(buf + L::M_OFF + row * L::MWORDS * 4 +
+                                                 4 * swz_m(row, word, L::MWORDS));
   }
 }
 
-// One K step from an LDS buffer: SUB substeps x TI x TJ instructions per wave.
-// Every operand of the step is read from LDS first and a scheduling barrier
-// keeps the compiler from interleaving (and serialising) reads and matrix
-// instructions, so the reads of later substeps overlap the first instructions.
-// With ISSUE, the loads of step `nxt` into `nbuf` are issued interleaved with
-// the matrix instructions.
-template <int DT, bool SPARSE, bool ISSUE>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[TI][TJ], const uint8_t* __restrict__ buf,
-                                         int wn, int wm, int lane, const Loader<DT, SPARSE>& ld,
-                                         uint8_t* nbuf, int nxt) {
+template <int DT, bool SPARSE, int P0, int P1>
+__device__ __forceinline__ void read_pieces(Frag<DT, SPARSE>& f, const uint8_t* __restrict__ buf, int s, int wn,
+                                            int wm, int lane) {
+  if constexpr (P0 < P1) {
+    read_piece<DT, SPARSE, P0>(f, buf, s, wn, wm, lane);
+    read_pieces<DT, SPARSE, P0 + 1, P1>(f, buf, s, wn, wm, lane);
+  }
+}
+
+template <int DT, bool SPARSE, int J0, int J1>
+__device__ __forceinline__ void issue_loads(const Loader<DT, SPARSE>& ld, uint8_t* buf, int ks) {
+  if constexpr (J0 < J1) {
+    ld.template issue_one<J0>(buf, ks);
+    issue_loads<DT, SPARSE, J0 + 1, J1>(ld, buf, ks);
+  }
+}
+
+// Matrix instruction (I, J) of substep S.
+template <int DT, bool SPARSE, int S, int I, int J>
+__device__ __forceinline__ void mma_one(f32x16 (&acc)[TI][TJ], const Frag<DT, SPARSE>& f) {
+  if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
+    acc[I][J] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(f.a[I][0], cat8(f.b[J][0], f.b[J][1]), acc[I][J],
+                                                             (int)f.ix[I], 0, 0);
+  } else if constexpr (SPARSE) {
+    acc[I][J] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+        __builtin_bit_cast(bf16x8, f.a[I][0]), __builtin_bit_cast(bf16x16, cat8(f.b[J][0], f.b[J][1])),
+        acc[I][J], (int)f.ix[I], 0, S & 1);
+  } else if constexpr (DT == SP24_FP8_E4M3) {
+    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(f.a[I][0], f.a[I][1]),
+                                                                cat8(f.b[J][0], f.b[J][1]), acc[I][J], 0, 0,
+                                                                0, 0, 0, 0);
+  } else {
+    acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[I][0]),
+                                                        __builtin_bit_cast(bf16x8, f.b[J][0]), acc[I][J], 0,
+                                                        0, 0);
+  }
+}
+
+// One substep's matrix instructions from `cur`, each followed by its share of
+// the reads of the next substep (into `nxt`, substep `rs` of `rbuf`) and, with
+// ISSUE, of the global->LDS loads of step `fill_ks` into `fill`.  The order is
+// fixed (scheduling barriers), so every wave starts its matrix instructions
+// at once and no wave issues a long burst of LDS reads that would stall its
+// own matrix instructions behind a full LDS queue.
+template <int DT, bool SPARSE, int S, int T, bool ISSUE>
+__device__ __forceinline__ void phase(f32x16 (&acc)[TI][TJ], const Frag<DT, SPARSE>& cur, Frag<DT, SPARSE>& nxt,
+                                      const uint8_t* __restrict__ rbuf, int rs, int wn, int wm, int lane,
+                                      const Loader<DT, SPARSE>& ld, uint8_t* fill, int fill_ks) {
+  constexpr int NMMA = TI * TJ, NP = n_pieces<SPARSE>();
+  constexpr int NV = ISSUE ? StageLoads<DT, SPARSE>::TOTAL : 0;
+  // the reads go out with the first RS instructions, so the last ones cover
+  // their latency before the wait at the end of the phase
+  constexpr int RS = NMMA > 4 ? NMMA - 3 : NMMA;
+  if constexpr (T < NMMA) {
+    mma_one<DT, SPARSE, S, T / TJ, T % TJ>(acc, cur);
+    issue_loads<DT, SPARSE, T * NV / NMMA, (T + 1) * NV / NMMA>(ld, fill, fill_ks);
+    if constexpr (T < RS) read_pieces<DT, SPARSE, T * NP / RS, (T + 1) * NP / RS>(nxt, rbuf, rs, wn, wm, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    phase<DT, SPARSE, S, T + 1, ISSUE>(acc, cur, nxt, rbuf, rs, wn, wm, lane, ld, fill, fill_ks);
+  }
+}
+
+// Substeps S .. SUB-2 of a K step: substep S + 1 is read while substep S is
+// multiplied.
+template <int DT, bool SPARSE, int S>
+__device__ __forceinline__ void inner_substeps(f32x16 (&acc)[TI][TJ], Frag<DT, SPARSE> (&f)[2],
+                                               const uint8_t* __restrict__ cur, int wn, int wm, int lane,
+                                               const Loader<DT, SPARSE>& ld) {
   using L = TiledLayout<DT, SPARSE>;
-  constexpr int SUB = L::SUB;
-  const int q = lane >> 5, r = lane & 31;
-  i32x4 a[SUB][TI][SPARSE ? 1 : 2];
-  uint32_t ix[SUB][TI];
-  i32x4 b[SUB][TJ][2];
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int row = wn * (BN / WGN) + 32 * i + r;
-      const uint8_t* wr = buf + L::W_OFF + row * L::WB;
-      if constexpr (SPARSE) {
-        // fp8: bytes [32s + 16q, +16) and word 2s + q; bf16: bytes [32q + 16s, +16),
-        // word q (its 16-bit half s is selected by abid)
-        const int c = DT == SP24_FP8_E4M3 ? 2 * s + q : 2 * q + s;
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, c));
-        const int word = DT == SP24_FP8_E4M3 ? 2 * s + q : q;
-        ix[s][i] = *reinterpret_cast<const uint32_t*>(buf + L::M_OFF + row * L::MWORDS * 4 +
-                                                      4 * swz_m(row, word, L::MWORDS));
-      } else if constexpr (DT == SP24_FP8_E4M3) {
-        // dense fp8: 32 bytes [64s + 32q, +32)
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q));
-        a[s][i][1] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q + 1));
-      } else {
-        // dense bf16: 16 bytes [32s + 16q, +16)
-        a[s][i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 2 * s + q));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int row = wm * (BM / WGM) + 32 * j + r;
-      const uint8_t* xr = buf + L::X_OFF + row * L::XB;
-      if constexpr (SPARSE) {
-        // run h of lane group q: fp8 bytes 64s + 32h + 16q; bf16 bytes 64h + 32s + 16q
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = DT == SP24_FP8_E4M3 ? 4 * s + 2 * h + q : 4 * h + 2 * s + q;
-          b[s][j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, c));
-        }
-      } else if constexpr (DT == SP24_FP8_E4M3) {
-        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q));
-        b[s][j][1] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q + 1));
-      } else {
-        b[s][j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 2 * s + q));
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (ISSUE) ld.issue(nbuf, nxt);
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(
-              a[s][i][0], cat8(b[s][j][0], b[s][j][1]), acc[i][j], (int)ix[s][i], 0, 0);
-        } else if constexpr (SPARSE) {
-          if (s == 0)
-            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                __builtin_bit_cast(bf16x8, a[s][i][0]),
-                __builtin_bit_cast(bf16x16, cat8(b[s][j][0], b[s][j][1])), acc[i][j], (int)ix[s][i], 0,
-                0);
-          else
-            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                __builtin_bit_cast(bf16x8, a[s][i][0]),
-                __builtin_bit_cast(bf16x16, cat8(b[s][j][0], b[s][j][1])), acc[i][j], (int)ix[s][i], 0,
-                1);
-        } else if constexpr (DT == SP24_FP8_E4M3) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              cat8(a[s][i][0], a[s][i][1]), cat8(b[s][j][0], b[s][j][1]), acc[i][j], 0, 0, 0, 0, 0, 0);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a[s][i][0]), __builtin_bit_cast(bf16x8, b[s][j][0]), acc[i][j],
-              0, 0, 0);
-        }
-      }
-    }
-  }
-  if constexpr (ISSUE) {
-    constexpr int NMMA = SUB * TI * TJ, NLD = StageLoads<DT, SPARSE>::TOTAL;
-    interleave_groups<NLD, NMMA / NLD, 1>();
-    if constexpr (NMMA % NLD != 0) __builtin_amdgcn_sched_group_barrier(0x008, NMMA % NLD, 0);
+  if constexpr (S + 1 < L::SUB) {
+    // The reads of substep S (issued a phase earlier) are done; waiting here,
+    // before the next reads go out, lets the matrix instructions start
+    // without waiting for those.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    phase<DT, SPARSE, S, 0, false>(acc, f[S & 1], f[(S + 1) & 1], cur, S + 1, wn, wm, lane, ld, nullptr, 0);
+    inner_substeps<DT, SPARSE, S + 1>(acc, f, cur, wn, wm, lane, ld);
   }
 }
 
@@ -266,7 +315,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     int M, int N, int K) {
   using L = TiledLayout<DT, SPARSE>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::STAGES * L::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS destinations stay in SGPRs
@@ -291,66 +340,110 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // STAGES LDS buffers in a ring.  At the top of step ks a wave waits for its
-  // own loads of step ks, the barrier makes every wave's loads visible (and
-  // guarantees every wave is done reading buffer (ks - 1) % STAGES), and then
-  // the loads of step ks + STAGES - 1 go into that buffer while step ks is
-  // multiplied.
-  constexpr int STAGES = L::STAGES;
+  // STAGES LDS buffers in a ring, K step ks in buffer ks % STAGES, and two
+  // register sets of operands, so LDS reads, global->LDS loads and matrix
+  // instructions overlap.  Within step ks, substep s + 1 is read while
+  // substep s is multiplied.  Before the last substep's instructions each
+  // wave waits for its own loads of step ks + 1 and for its LDS reads of step
+  // ks; the barrier after that makes every wave's loads of step ks + 1 visible
+  // and guarantees that no wave still reads buffer ks % STAGES, which then
+  // receives the loads of step ks + STAGES while the last substep's
+  // instructions run and substep 0 of step ks + 1 is read.
+  //
+  // The barrier is a bare s_barrier: __syncthreads() adds a workgroup release
+  // fence, which would wait for every outstanding LDS-DMA load (vmcnt(0)) and
+  // drain the ring; the explicit counter waits provide the ordering.
+  constexpr int STAGES = L::STAGES, SUB = L::SUB;
   constexpr int PER_STEP = StageLoads<DT, SPARSE>::TOTAL;
   const int nks = K / L::KS;
   const Loader<DT, SPARSE> ld(w, meta, x, n0, m0, N, M, K, wave, lane);
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
+  for (int p = 0; p < STAGES; ++p)
     if (p < nks) ld.issue(lds + p * L::STAGE, p);
-  // steps whose loop issues the loads of step ks + STAGES - 1, then the last ones
-  const int nissue = max(0, nks - (STAGES - 1));
-  for (int ks = 0; ks < nissue; ++ks) {
-    wait_vmcnt<(STAGES - 2) * PER_STEP>();  // loads of steps ks+1 .. ks+STAGES-2 may be in flight
-    __builtin_amdgcn_s_barrier();
-    const int nxt = ks + STAGES - 1;
-    mma_step<DT, SPARSE, true>(acc, lds + (ks % STAGES) * L::STAGE, wn, wm, lane, ld,
-                               lds + (nxt % STAGES) * L::STAGE, nxt);
-  }
-  for (int ks = nissue; ks < nks; ++ks) {
-    // loads issued after those of step ks: steps ks+1 .. ks+STAGES-2 (when they exist)
-    wait_later<PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
-    // A bare barrier: __syncthreads() adds a workgroup release fence, which
-    // would wait for every outstanding LDS-DMA load (vmcnt(0)) and drain the
-    // pipeline.  The explicit vmcnt wait above already covers step ks, and each
-    // wave's LDS reads of the previous step completed before their results
-    // fed its matrix instructions.
-    __builtin_amdgcn_s_barrier();
-    mma_step<DT, SPARSE, false>(acc, lds + (ks % STAGES) * L::STAGE, wn, wm, lane, ld, nullptr, 0);
-  }
+  wait_later<PER_STEP, STAGES - 1>(min(nks - 1, STAGES - 1));  // step 0 has landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  Frag<DT, SPARSE> f[2];
+  read_pieces<DT, SPARSE, 0, n_pieces<SPARSE>()>(f[0], lds, 0, wn, wm, lane);
 
+  // One K step.  ISSUE: step ks + STAGES exists and is loaded here.
+  auto step = [&](int ks, auto issue_tag) {
+    constexpr bool ISSUE = decltype(issue_tag)::value;
+    const uint8_t* cur = lds + (ks % STAGES) * L::STAGE;
+    inner_substeps<DT, SPARSE, 0>(acc, f, cur, wn, wm, lane, ld);
+    // loads issued after those of step ks + 1: steps ks+2 .. ks+STAGES-1 (when they exist)
+    if constexpr (ISSUE) {
+      wait_vmcnt<(STAGES - 2) * PER_STEP>();
+    } else {
+      wait_later<PER_STEP, STAGES - 2>(max(0, min(nks - 2 - ks, STAGES - 2)));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step ks are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // The last substep, the reads of substep 0 of step ks + 1 (after the last
+    // step: a harmless read of a valid buffer) and the loads of step ks + STAGES.
+    phase<DT, SPARSE, SUB - 1, 0, ISSUE>(acc, f[(SUB - 1) & 1], f[0], lds + ((ks + 1) % STAGES) * L::STAGE, 0,
+                                         wn, wm, lane, ld, lds + (ks % STAGES) * L::STAGE, ks + STAGES);
+  };
+  const int nissue = max(0, nks - STAGES);
+  for (int ks = 0; ks < nissue; ++ks) step(ks, std::true_type{});
+  for (int ks = nissue; ks < nks; ++ks) step(ks, std::false_type{});
+
+  // Epilogue through LDS.  Each accumulator register holds one output of a
+  // 32-row column strip, so direct stores would send 8-byte pieces of 32
+  // different rows per instruction; instead the tile is staged in LDS (the
+  // ring is free: the last step waited for every load, and the barrier below
+  // waits for every wave's last reads) and written back as whole rows, 16
+  // bytes per lane.  Rows of the staged tile are padded by 16 bytes so the
+  // 8-byte writes of a 32-row strip spread over the banks.
+  constexpr int YS = L::YS;
+  static_assert(BM * YS <= L::LDS_BYTES, "staged output tile fits");
   float scale = 1.0f;
   if constexpr (DT == SP24_FP8_E4M3) scale = x_scale[0] * w_scale[0];
-  const int q = lane >> 5, c = lane & 31;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's last (discarded) reads are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  {
+    const int q = lane >> 5, c = lane & 31;
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int m = m0 + wm * (BM / WGM) + 32 * j + c;
-    if (m >= M) continue;
-    uint16_t* yr = y + (size_t)m * N;
+    for (int j = 0; j < TJ; ++j) {
+      const int ml = wm * (BM / WGM) + 32 * j + c;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+      for (int i = 0; i < TI; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // accumulator registers 4g..4g+3 hold rows n .. n+3 of this column
-        const int n = n0 + wn * (BN / WGN) + 32 * i + 8 * g + 4 * q;
-        const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * g + 0] * scale) |
-                            (f32_to_bf16_rne(acc[i][j][4 * g + 1] * scale) << 16);
-        const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * g + 2] * scale) |
-                            (f32_to_bf16_rne(acc[i][j][4 * g + 3] * scale) << 16);
-        if (n + 3 < N && (N & 3) == 0) {
-          *reinterpret_cast<u32x2*>(yr + n) = u32x2{lo, hi};
-        } else {
-          const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yr[n + e] = (uint16_t)v[e];
+        for (int g = 0; g < 4; ++g) {
+          // accumulator registers 4g..4g+3 hold columns nl .. nl+3 of row ml
+          const int nl = wn * (BN / WGN) + 32 * i + 8 * g + 4 * q;
+          const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * g + 0] * scale) |
+                              (f32_to_bf16_rne(acc[i][j][4 * g + 1] * scale) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * g + 2] * scale) |
+                              (f32_to_bf16_rne(acc[i][j][4 * g + 3] * scale) << 16);
+          *reinterpret_cast<u32x2*>(lds + ml * YS + nl * 2) = u32x2{lo, hi};
         }
       }
+    }
+  }
+  __syncthreads();
+  // 32 lanes per row, 8 columns (16 bytes) per lane, two rows per wave per pass
+  constexpr int LPR = BN / 8;           // lanes per row
+  constexpr int RPP = 64 / LPR;         // rows per wave per pass
+  const int nl = 8 * (lane % LPR);
+  const int n = n0 + nl;
+  const bool vec = (N & 7) == 0 && n + 7 < N;
+#pragma unroll 4
+  for (int r0 = wave * RPP; r0 < BM; r0 += NWAVES * RPP) {
+    const int ml = r0 + lane / LPR;
+    const int m = m0 + ml;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + ml * YS + nl * 2);
+    if (m >= M) continue;
+    uint16_t* yr = y + (size_t)m * N;
+    if (vec) {
+      *reinterpret_cast<u32x4*>(yr + n) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) yr[n + e] = (uint16_t)(v[e / 2] >> (16 * (e & 1)));
     }
   }
 }

@@ -33,7 +33,9 @@ def test_tiny_workload_fp8():
 SHAPES = [(1, 16, 128), (3, 17, 256), (16, 64, 384), (17, 100, 640), (33, 48, 1152),
           (64, 256, 2048), (65, 40, 512), (100, 33, 1408), (8, 32, 16384), (129, 80, 896),
           # LDS-tiled kernel: ragged tiles in m and n, several K steps
-          (1000, 8200, 640), (2048, 8192, 1024), (777, 32784, 256)]
+          (1000, 8200, 640), (2048, 8192, 1024), (777, 32784, 256),
+          # ... and n not a multiple of 8 (the epilogue's per-element tail)
+          (600, 32771, 384), (1111, 8198, 256)]
 
 
 @pytest.mark.parametrize("fp8", [False, True])
