@@ -163,7 +163,7 @@ def main():
     w = w_cpu.to(dev)
     xs = {m: xs_cpu[m].to(dev) for m in Ms}
     values = torch.empty(N, K // 2, dtype=torch.bfloat16, device=dev)
-    meta = torch.empty(N, K // 32, dtype=torch.int32, device=dev)
+    meta = torch.empty(N * (K // 32), dtype=torch.int32, device=dev)
     t_prune = ev.time(lambda i: sp.prune_compress(w, values, meta), 5) / 5
     qv, sw = (sp.quant_fp8(values) if fp8 else (values, None))
     if fp8:

@@ -143,17 +143,28 @@ def _workspace(nbytes, device, ws=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _meta_size(meta: torch.Tensor, n: int, k: int):
+    if meta.numel() != max(n * (k // 32), 1):
+        raise ValueError("metadata has %d words, expected n * k/32 = %d" % (meta.numel(), n * (k // 32)))
+
+
 def prune_compress(w: torch.Tensor, values: torch.Tensor | None = None,
                    meta: torch.Tensor | None = None):
-    """2:4-prune a bf16 weight [n, k] along k and compress it -> (values [n, k/2], meta [n, k/32] int32)."""
+    """2:4-prune a bf16 weight [n, k] along k and compress it -> (values [n, k/2], meta).
+
+    `meta` is an int32 tensor of n * k/32 words in the library's storage order:
+    the k/32 words of a row are cut into blocks of 4 (128 values of k), and
+    block b holds every row's words of that block, row after row.
+    """
     _need(w, "w", torch.bfloat16, 2)
     n, k = w.shape
     if values is None:
         values = torch.empty(n, k // 2, dtype=torch.bfloat16, device=w.device)
     if meta is None:
-        meta = torch.empty(n, max(k // 32, 1), dtype=torch.int32, device=w.device)
+        meta = torch.empty(max(n * (k // 32), 1), dtype=torch.int32, device=w.device)
     _need(values, "values", torch.bfloat16, 2, w.device)
-    _need(meta, "meta", torch.int32, 2, w.device)
+    _need(meta, "meta", torch.int32, 1, w.device)
+    _meta_size(meta, n, k)
     _check("sp24_prune_compress",
            lib.sp24_prune_compress(_ptr(w), n, k, _ptr(values), _ptr(meta), _stream(w.device)))
     return values, meta
@@ -162,8 +173,9 @@ def prune_compress(w: torch.Tensor, values: torch.Tensor | None = None,
 def decompress(values: torch.Tensor, meta: torch.Tensor, k: int, out: torch.Tensor | None = None):
     """Dense pruned W [n, k] from (values, meta); bf16 values give bf16, E4M3 codes give uint8 codes."""
     _need(values, "values", (torch.bfloat16,) + _CODE_T, 2)
-    _need(meta, "meta", torch.int32, 2, values.device)
+    _need(meta, "meta", torch.int32, 1, values.device)
     n = values.shape[0]
+    _meta_size(meta, n, k)
     dt = BF16 if values.dtype == torch.bfloat16 else FP8
     if out is None:
         out = torch.empty(n, k, dtype=torch.bfloat16 if dt == BF16 else torch.uint8, device=values.device)
@@ -176,12 +188,15 @@ def decompress(values: torch.Tensor, meta: torch.Tensor, k: int, out: torch.Tens
 def check_meta(meta: torch.Tensor, k: int, bad: torch.Tensor | None = None) -> torch.Tensor:
     """Count the metadata nibbles that are not a valid kept pair; returns a uint32[1] device
     tensor (`bad`, if given, is added to; otherwise a zeroed one is made)."""
-    _need(meta, "meta", torch.int32, 2)
+    _need(meta, "meta", torch.int32, 1)
+    words = max(k // 32, 1)
+    if meta.numel() % words:
+        raise ValueError("metadata of %d words does not hold whole rows of k=%d" % (meta.numel(), k))
     if bad is None:
         bad = torch.zeros(1, dtype=torch.int32, device=meta.device)
     _need(bad, "bad", torch.int32, None, meta.device)
     _check("sp24_check_meta",
-           lib.sp24_check_meta(_ptr(meta), meta.shape[0], k, _ptr(bad), _stream(meta.device)))
+           lib.sp24_check_meta(_ptr(meta), meta.numel() // words, k, _ptr(bad), _stream(meta.device)))
     return bad
 
 
@@ -222,9 +237,10 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
     _need(w, "w", torch.bfloat16 if dt == BF16 else _CODE_T, 2, x.device)
     n = w.shape[0]
     if sparse:
-        _need(meta, "meta", torch.int32, 2, x.device)
-        if w.shape[1] * 2 != k or meta.shape != (n, k // 32):
+        _need(meta, "meta", torch.int32, 1, x.device)
+        if w.shape[1] * 2 != k:
             raise ValueError("compressed weight shapes do not match k=%d" % k)
+        _meta_size(meta, n, k)
     elif w.shape[1] != k:
         raise ValueError("w has %d columns, x has %d" % (w.shape[1], k))
     if dt == FP8:

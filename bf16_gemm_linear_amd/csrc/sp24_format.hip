@@ -3,9 +3,10 @@
 // Pruning keeps the two largest-magnitude values of every 4 contiguous values
 // along K ("Deploying 2:4 Sparsity with FP8 on Hopper", pipeline step 4 and
 // Practical Example 1); ties go to the lower index.  The work is one pass over
-// W: thread t owns the 32 values of metadata word t (8 groups), which are
-// contiguous in the row-major [n, k] weight (k % 32 == 0), so the whole kernel
-// is a linear stream: 64 bytes in, 32 bytes of values + 4 bytes of metadata out.
+// W: thread t owns the 32 values of row-major word t (8 groups), which are
+// contiguous in the row-major [n, k] weight (k % 32 == 0), so the kernel reads
+// and writes the values as a linear stream (64 bytes in, 32 bytes out) and
+// writes the metadata word at its place in the K-blocked storage order.
 #include "sp24_common.hpp"
 #include "sp24_internal.hpp"
 
@@ -28,9 +29,10 @@ __device__ __forceinline__ void keep_pair(const uint32_t a[4], int& i0, int& i1)
 }
 
 __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __restrict__ w,
-                                                             int64_t nwords,
+                                                             int64_t n, int64_t words,
                                                              u32x4* __restrict__ values,
                                                              uint32_t* __restrict__ meta) {
+  const int64_t nwords = n * words;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
     u32x4 in[4];
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __rest
     }
     values[t * 2 + 0] = u32x4{out[0], out[1], out[2], out[3]};
     values[t * 2 + 1] = u32x4{out[4], out[5], out[6], out[7]};
-    meta[t] = word;
+    const int64_t r = t / words;
+    meta[meta_index(r, t - r * words, n, words)] = word;
   }
 }
 
@@ -66,10 +69,13 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __rest
 template <int ESZ>
 __global__ __launch_bounds__(256) void decompress_kernel(const uint8_t* __restrict__ values,
                                                          const uint32_t* __restrict__ meta,
-                                                         int64_t nwords, uint8_t* __restrict__ out) {
+                                                         int64_t n, int64_t words,
+                                                         uint8_t* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nwords = n * words;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
-    const uint32_t word = meta[t];
+    const int64_t r = t / words;
+    const uint32_t word = meta[meta_index(r, t - r * words, n, words)];
     if constexpr (ESZ == 2) {
       const u32x4* vp = reinterpret_cast<const u32x4*>(values + t * 32);
       u32x4 va = vp[0], vb = vp[1];
@@ -147,7 +153,7 @@ hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16
                                  uint32_t* meta, hipStream_t s) {
   const int64_t nwords = n * (k / 32);
   hipLaunchKernelGGL(prune_compress_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4*>(w), nwords, reinterpret_cast<u32x4*>(values),
+                     reinterpret_cast<const u32x4*>(w), n, k / 32, reinterpret_cast<u32x4*>(values),
                      meta);
   return hipGetLastError();
 }
@@ -164,11 +170,11 @@ hipError_t launch_decompress(int dtype, const void* values, const uint32_t* meta
   const int64_t nwords = n * (k / 32);
   if (dtype == SP24_BF16)
     hipLaunchKernelGGL(decompress_kernel<2>, dim3(grid_for(nwords, 256)), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(values), meta, nwords,
+                       static_cast<const uint8_t*>(values), meta, n, k / 32,
                        static_cast<uint8_t*>(out));
   else
     hipLaunchKernelGGL(decompress_kernel<1>, dim3(grid_for(nwords, 256)), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(values), meta, nwords,
+                       static_cast<const uint8_t*>(values), meta, n, k / 32,
                        static_cast<uint8_t*>(out));
   return hipGetLastError();
 }

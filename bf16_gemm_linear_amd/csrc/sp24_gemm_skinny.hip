@@ -96,7 +96,10 @@ __device__ __forceinline__ void load_chunk(Chunk<DT, SPARSE, T, RB, MB>& r,
     row = row < N ? row : N - 1;  // ragged n: clamp the load, the store is masked
     const uint8_t* wp;
     if constexpr (SPARSE) {
-      const uint32_t* mp = meta + (size_t)row * (K / 32) + kq / 32;
+      // T consecutive words from word kq / 32; T = 4 and T = 2 stay inside one
+      // 128-K block (kb is a multiple of 128), T = 1 and 3 take word by word
+      const int w0 = kq / 32;
+      const uint32_t* mp = meta + (size_t)(w0 >> 2) * N * 4 + (size_t)row * 4 + (w0 & 3);
       if constexpr (T == 4) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(mp);
         r.mt[rb][0] = v[0]; r.mt[rb][1] = v[1]; r.mt[rb][2] = v[2]; r.mt[rb][3] = v[3];
@@ -105,7 +108,8 @@ __device__ __forceinline__ void load_chunk(Chunk<DT, SPARSE, T, RB, MB>& r,
         r.mt[rb][0] = v[0]; r.mt[rb][1] = v[1];
       } else {
 #pragma unroll
-        for (int j = 0; j < T; ++j) r.mt[rb][j] = mp[j];
+        for (int j = 0; j < T; ++j)
+          r.mt[rb][j] = meta[(size_t)((w0 + j) >> 2) * N * 4 + (size_t)row * 4 + ((w0 + j) & 3)];
       }
       wp = w + ((size_t)row * (K / 2) + kq / 2) * ESZ;
     } else {

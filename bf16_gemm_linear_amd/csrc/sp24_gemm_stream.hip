@@ -98,12 +98,13 @@ struct StreamLoader {
   const uint32_t* mp[C::M_PER > 0 ? C::M_PER : 1];
   const uint8_t* xp[C::X_PER];
   int wave;
+  size_t mstep;  // metadata words of UPS 128-K blocks of all N rows
 
   __device__ __forceinline__ StreamLoader(const uint8_t* __restrict__ w,
                                           const uint32_t* __restrict__ meta,
                                           const uint8_t* __restrict__ x, int n0, int n_last,
-                                          int m0, int M, int K, int u0, int wave_, int lane)
-      : wave(wave_) {
+                                          int m0, int M, int N, int K, int u0, int wave_, int lane)
+      : wave(wave_), mstep((size_t)C::UPS * N * 4) {
     const size_t wrow = (size_t)(K / 128) * C::WU;
 #pragma unroll
     for (int j = 0; j < C::W_PER; ++j) {
@@ -118,7 +119,8 @@ struct StreamLoader {
         const int p = (j * C::NW + wave) * 64 + lane, row = p / C::MWD;
         const int sw = swzm<C::MWD>(row, p % C::MWD);
         const int n = min(n0 + row, n_last);
-        mp[j] = meta + (size_t)n * (K / 32) + (size_t)(u0 + sw / 4) * 4 + (sw % 4);
+        // unit u is metadata block u: every row's 4 words, row after row
+        mp[j] = meta + (size_t)(u0 + sw / 4) * N * 4 + (size_t)n * 4 + (sw % 4);
       }
     }
     const size_t xrow = (size_t)K * C::ESZ;
@@ -142,7 +144,7 @@ struct StreamLoader {
     for (int j = 0; j < C::M_PER; ++j) {
       const int g = j * C::NW + wave;
       if (C::M_TOT % C::NW == 0 || g < C::M_TOT)
-        dma4(mp[j] + (size_t)ks * C::MWD, buf + C::M_OFF + g * 256);
+        dma4(mp[j] + (size_t)ks * mstep, buf + C::M_OFF + g * 256);
     }
 #pragma unroll
     for (int j = 0; j < C::X_PER; ++j) {
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   // which receives the loads of step ks + STAGES - 1 while step ks is
   // multiplied.  A bare s_barrier: __syncthreads() adds a release fence that
   // waits for every outstanding LDS-DMA load and would drain the ring.
-  const StreamLoader<C> ld(w, meta, x, n0, n_end - 1, m0, M, K, u0, wave, lane);
+  const StreamLoader<C> ld(w, meta, x, n0, n_end - 1, m0, M, N, K, u0, wave, lane);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < nks) ld.issue(lds + p * C::STAGE, p);

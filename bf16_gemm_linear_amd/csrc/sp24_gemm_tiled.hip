@@ -105,11 +105,12 @@ struct Loader {
   const uint32_t* mp[S::M_INSTR > 0 ? S::M_INSTR : 1];
   const uint8_t* xp[S::X_INSTR];
   int wave;  // wave-uniform (scalar)
+  size_t mblock;  // metadata words per 128-K block of all N rows
 
   __device__ __forceinline__ Loader(const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
                                     const uint8_t* __restrict__ x, int n0, int m0, int N, int M,
                                     int K, int wave_, int lane)
-      : wave(wave_) {
+      : wave(wave_), mblock((size_t)N * 4) {
     const size_t wrow = SPARSE ? (size_t)(K / 2) * L::ESZ : (size_t)K * L::ESZ;
 #pragma unroll
     for (int j = 0; j < S::W_INSTR; ++j) {
@@ -122,7 +123,7 @@ struct Loader {
       for (int j = 0; j < S::M_INSTR; ++j) {
         const int p = (wave * S::M_INSTR + j) * 64 + lane, row = p / L::MWORDS;
         const int n = min(n0 + row, N - 1);
-        mp[j] = meta + (size_t)n * (K / 32) + swz_m(row, p % L::MWORDS, L::MWORDS);
+        mp[j] = meta + (size_t)n * 4 + swz_m(row, p % L::MWORDS, L::MWORDS);
       }
     }
     const size_t xrow = (size_t)K * L::ESZ;
@@ -134,6 +135,13 @@ struct Loader {
     }
   }
 
+  // Metadata of K step ks: its MWORDS words of every row sit at word (ks * MWORDS) % 4
+  // of each row's 16 bytes in block (ks * MWORDS) / 4 (K % 128 == 0: whole blocks).
+  __device__ __forceinline__ size_t meta_step(int ks) const {
+    const int w0 = ks * L::MWORDS;
+    return (size_t)(w0 >> 2) * mblock + (w0 & 3);
+  }
+
   // Load J of this wave's share of K step ks (W pieces, then metadata words, then X pieces).
   template <int J>
   __device__ __forceinline__ void issue_one(uint8_t* buf, int ks) const {
@@ -141,7 +149,7 @@ struct Loader {
       dma16(wp[J] + (size_t)ks * L::WB, buf + L::W_OFF + (wave * S::W_INSTR + J) * 1024);
     } else if constexpr (J < S::W_INSTR + S::M_INSTR) {
       constexpr int j = J - S::W_INSTR;
-      dma4(mp[j] + (size_t)ks * L::MWORDS, buf + L::M_OFF + (wave * S::M_INSTR + j) * 256);
+      dma4(mp[j] + meta_step(ks), buf + L::M_OFF + (wave * S::M_INSTR + j) * 256);
     } else {
       constexpr int j = J - S::W_INSTR - S::M_INSTR;
       dma16(xp[j] + (size_t)ks * L::XB, buf + L::X_OFF + (wave * S::X_INSTR + j) * 1024);
@@ -156,7 +164,7 @@ struct Loader {
     if constexpr (SPARSE) {
 #pragma unroll
       for (int j = 0; j < S::M_INSTR; ++j)
-        dma4(mp[j] + (size_t)ks * L::MWORDS, buf + L::M_OFF + (wave * S::M_INSTR + j) * 256);
+        dma4(mp[j] + meta_step(ks), buf + L::M_OFF + (wave * S::M_INSTR + j) * 256);
     }
 #pragma unroll
     for (int j = 0; j < S::X_INSTR; ++j)

@@ -9,6 +9,18 @@
 
 namespace sp24 {
 
+// Storage index of metadata word w (K values [32w, 32w + 32)) of row r, for a
+// weight of n rows with `words` = k / 32 words per row.  The words of a row
+// are cut into blocks of 4 (128 values of K); block b holds every row's words
+// of that block, row after row, and a last, narrower block does the same.  A
+// K step of a row range is then one contiguous piece of the metadata, so the
+// GEMM kernels load it in whole cache lines.
+__host__ __device__ inline int64_t meta_index(int64_t r, int64_t w, int64_t n, int64_t words) {
+  const int64_t b = w >> 2;
+  const int64_t width = words - 4 * b < 4 ? words - 4 * b : 4;
+  return 4 * n * b + r * width + (w & 3);
+}
+
 // sp24_format.hip
 hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16_t* values,
                                  uint32_t* meta, hipStream_t s);

@@ -167,6 +167,43 @@ def prune_compress(w_bits: np.ndarray):
     return compress(np.asarray(w_bits, dtype=np.uint16), prune_mask(w_bits))
 
 
+# Storage order of the metadata words.  The words of a row are cut into blocks
+# of 4 (128 values of K); block b holds, row after row, every row's words of
+# that block, and a last block of fewer than 4 words (K not a multiple of 128)
+# does the same with its narrower rows.  The pages leave the layout of the
+# compressed form to the implementation (the SlideSparse page has weights
+# converted once, offline, into the hardware's format).
+META_BLOCK_WORDS = 4
+
+
+def meta_word_index(n: int, k: int, rows=None):
+    """Storage index of word w of row r, as an ``[N, K/32]`` array (or for ``rows`` only)."""
+    words = k // 32
+    r = (np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
+    w = np.arange(words, dtype=np.int64)[None, :]
+    b = w // META_BLOCK_WORDS
+    width = np.minimum(META_BLOCK_WORDS, words - META_BLOCK_WORDS * b)
+    return META_BLOCK_WORDS * n * b + r * width + (w - META_BLOCK_WORDS * b)
+
+
+def store_meta(meta: np.ndarray) -> np.ndarray:
+    """Metadata ``[N, K/32]`` in storage order (a flat array of N*K/32 words)."""
+    meta = np.asarray(meta, dtype=np.uint32)
+    n, words = meta.shape
+    out = np.zeros(n * words, dtype=np.uint32)
+    out[meta_word_index(n, 32 * words)] = meta
+    return out
+
+
+def load_meta(stored: np.ndarray, n: int, k: int, rows=None) -> np.ndarray:
+    """Inverse of :func:`store_meta`: the ``[N, K/32]`` words of a stored array
+    (or the words of ``rows`` only)."""
+    stored = np.asarray(stored, dtype=np.uint32).reshape(-1)
+    if stored.size != n * (k // 32):
+        raise ValueError("stored metadata has %d words, expected %d" % (stored.size, n * (k // 32)))
+    return stored[meta_word_index(n, k, rows)]
+
+
 # ----------------------------------------------------------------------------
 # FP8 E4M3 (OCP "E4M3FN": bias 7, no infinities, max finite 448)
 # ----------------------------------------------------------------------------

@@ -136,7 +136,7 @@ def full_case(x_cpu, w_cpu, fp8, what, dense=False):
     torch.cuda.synchronize()
     ow = OracleWeight(W.bf16_bits(w_cpu), fp8)
     oxq, oxs = oracle_x(W.bf16_bits(x_cpu), fp8)
-    assert np.array_equal(u32(gw.meta), ow.meta)
+    assert np.array_equal(u32(gw.meta), O.store_meta(ow.meta))
     if fp8:
         assert f32_bits(f32(gw.scale)) == f32_bits(ow.scale)
         assert f32_bits(f32(xs)) == f32_bits(oxs)

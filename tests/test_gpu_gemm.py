@@ -113,7 +113,7 @@ def _sampled_case(x_cpu, w_cpu, fp8, what, n_rows=512, n_tokens=None, seed=0):
     else:
         oxq, oxs = xb[toks], None
         assert np.array_equal(bits(gw.values)[rows], ow.values)
-    assert np.array_equal(u32(gw.meta)[rows], ow.meta)
+    assert np.array_equal(O.load_meta(u32(gw.meta), n, gw.k, rows), ow.meta)
     ref, mag = oracle_ref(oxq, oxs, ow)
     yb = bits(y)[np.ix_(toks, rows)]
     assert_within_tolerance(yb, ref, mag, what)

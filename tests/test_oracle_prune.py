@@ -176,3 +176,30 @@ def test_brute_force_on_workload_rows():
         for g in range(64):
             a = mags[r, 4 * g:4 * g + 4].tolist()
             assert tuple(np.nonzero(mask[r, 4 * g:4 * g + 4])[0].tolist()) == _brute_keep(a)
+
+
+def test_meta_storage_order_hand_examples():
+    # meta[r, w] = 16 r + w; blocks of 4 words, rows one after another per block
+    m = (16 * np.arange(2)[:, None] + np.arange(5)[None, :]).astype(np.uint32)   # K = 160
+    assert O.store_meta(m).tolist() == [0, 1, 2, 3, 16, 17, 18, 19, 4, 20]
+    m = (16 * np.arange(3)[:, None] + np.arange(8)[None, :]).astype(np.uint32)   # K = 256
+    assert O.store_meta(m).tolist() == [0, 1, 2, 3, 16, 17, 18, 19, 32, 33, 34, 35,
+                                        4, 5, 6, 7, 20, 21, 22, 23, 36, 37, 38, 39]
+    m = (16 * np.arange(2)[:, None] + np.arange(3)[None, :]).astype(np.uint32)   # K = 96: one short block
+    assert O.store_meta(m).tolist() == [0, 1, 2, 16, 17, 18]
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (1, 4096), (5, 96), (7, 160), (33, 1024), (4, 1120)])
+def test_meta_storage_order_is_a_permutation(n, k):
+    idx = O.meta_word_index(n, k)
+    assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(n * (k // 32)))
+    m = np.random.default_rng(n * k).integers(0, 2**32, size=(n, k // 32), dtype=np.uint64).astype(np.uint32)
+    s = O.store_meta(m)
+    assert np.array_equal(O.load_meta(s, n, k), m)
+    if n == 1 or k <= 128:
+        assert np.array_equal(s, m.reshape(-1))   # one row, or one block: row order
+    if k % 128 == 0:
+        # block b of row r is the 16 bytes at (b * n + r) * 4 words
+        b = np.arange(k // 128)
+        for r in (0, n - 1):
+            assert np.array_equal(s.reshape(k // 128, n, 4)[b, r].reshape(-1), m[r])
