@@ -27,9 +27,15 @@
  *   - Compressed weight of W [n, k]:
  *       values [n, k/2]: the two kept values of group g (columns 4g..4g+3) at
  *                        columns 2g and 2g+1, in ascending position order;
- *       meta   [n, k/32] uint32: group g's nibble (i0 | i1 << 2), i0 < i1 the
- *                        kept positions inside the group, at bits 4*(g % 8) of
- *                        word g / 8.
+ *       meta   n * k/32 uint32 words: word w of row r holds, at bits
+ *                        4*(g % 8), the nibble (i0 | i1 << 2) of group
+ *                        g = 8w + (g % 8), i0 < i1 the kept positions inside the
+ *                        group.  Storage order: the k/32 words of a row are cut
+ *                        into blocks of 4 (128 values of k); block b holds every
+ *                        row's words of that block, row after row (a last block
+ *                        of fewer than 4 words likewise), so word w of row r sits
+ *                        at 4*n*(w/4) + r*min(4, k/32 - 4*(w/4)) + w%4.  A K step
+ *                        of a row range is then contiguous.
  *     The kept pair of a group: the two largest |w|, magnitudes compared
  *     exactly, ties to the lower index, +0 == -0.  Inputs must be finite.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
@@ -104,7 +110,7 @@ typedef struct sp24_plan {
 /* Prune W [n, k] (bf16) to 2:4 along k and compress it.
  *   w_bf16      in : [n, k] bf16
  *   values_bf16 out: [n, k/2] bf16
- *   meta        out: [n, k/32] uint32
+ *   meta        out: n * k/32 uint32 words (storage order above)
  * Requires n >= 1, k >= 32, k % 32 == 0.  Dropped values are not stored. */
 int sp24_prune_compress(const void* w_bf16, int64_t n, int64_t k, void* values_bf16,
                         uint32_t* meta, void* stream);
@@ -122,7 +128,7 @@ int sp24_decompress(int dtype, const void* values, const uint32_t* meta, int64_t
  * pair (i0 < i1, i.e. one of 4, 8, 9, 12, 13, 14): a check for compressed
  * weights that did not come from sp24_prune_compress (sp24_gemm and
  * sp24_decompress use nibbles as given).
- *   meta    in : [n, k/32] uint32
+ *   meta    in : n * k/32 uint32 words (storage order above)
  *   bad_dev out: one uint32 on the device; the count is ADDED to it (the
  *                caller zeroes it first), so several tensors can share one.
  * Requires n >= 1, k >= 32, k % 32 == 0; bad_dev 4-byte aligned. */
@@ -144,7 +150,7 @@ int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* sca
  *   dtype SP24_BF16    : x is bf16 [m, k], w_values bf16 [n, k/2]; scales ignored (may be NULL).
  *   dtype SP24_FP8_E4M3: x is E4M3 [m, k] with *x_scale_dev, w_values E4M3 [n, k/2]
  *                        with *w_scale_dev; y = bf16_rne(acc * fp32(sx * sw)).
- *   w_meta [n, k/32]; y_bf16 [m, n].
+ *   w_meta n * k/32 words (storage order above); y_bf16 [m, n].
  * Requires m >= 1, n >= 1, k >= 128, k % 128 == 0.  The sum over k is formed in
  * a fixed order for a given (m, n, k): results are bitwise reproducible.
  * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM, dtype, m, n, k)
