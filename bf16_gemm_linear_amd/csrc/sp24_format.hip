@@ -3,10 +3,9 @@
 // Pruning keeps the two largest-magnitude values of every 4 contiguous values
 // along K ("Deploying 2:4 Sparsity with FP8 on Hopper", pipeline step 4 and
 // Practical Example 1); ties go to the lower index.  The work is one pass over
-// W: thread t owns the 32 values of row-major word t (8 groups), which are
-// contiguous in the row-major [n, k] weight (k % 32 == 0), so the kernel reads
-// and writes the values as a linear stream (64 bytes in, 32 bytes out) and
-// writes the metadata word at its place in the K-blocked storage order.
+// W: the row-major [n, k] weight (k % 32 == 0) is read and the kept values
+// written as linear streams, and each metadata word goes to its place in the
+// K-blocked storage order.
 #include "sp24_common.hpp"
 #include "sp24_internal.hpp"
 
@@ -28,25 +27,28 @@ __device__ __forceinline__ void keep_pair(const uint32_t a[4], int& i0, int& i1)
   i1 = p < q ? q : p;
 }
 
+// Thread t owns 16 bytes of W (8 values, 2 groups) and writes 8 bytes of
+// kept values and one byte of nibbles; the four threads of a metadata word
+// (consecutive lanes) combine their bytes with shuffles and the first writes
+// the word.  Every load and value store of a wave is one contiguous 1 KB or
+// 512 B piece.  nchunks = n * k / 8 is a multiple of 4, so the four threads
+// of a word are always in the same wave and all active together.
 __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __restrict__ w,
                                                              int64_t n, int64_t words,
-                                                             u32x4* __restrict__ values,
+                                                             u32x2* __restrict__ values,
                                                              uint32_t* __restrict__ meta) {
-  const int64_t nwords = n * words;
+  const int64_t nchunks = n * words * 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nwords; t += stride) {
-    u32x4 in[4];
+  // the stride is a multiple of 256, so every thread keeps its place in its word
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nchunks; t += stride) {
+    const u32x4 in = w[t];
+    uint32_t out[2];
+    uint32_t nibs = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) in[j] = *(w + t * 4 + j);
-    uint32_t out[8];
-    uint32_t word = 0;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      // group g = 4 halves = 2 dwords: in[g/2][(g%2)*2 + 0..1]
-      uint32_t d0 = in[g >> 1][(g & 1) * 2 + 0];
-      uint32_t d1 = in[g >> 1][(g & 1) * 2 + 1];
-      uint32_t h[4] = {d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16};
-      uint32_t a[4] = {h[0] & 0x7FFFu, h[1] & 0x7FFFu, h[2] & 0x7FFFu, h[3] & 0x7FFFu};
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t d0 = in[2 * g], d1 = in[2 * g + 1];
+      const uint32_t h[4] = {d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16};
+      const uint32_t a[4] = {h[0] & 0x7FFFu, h[1] & 0x7FFFu, h[2] & 0x7FFFu, h[3] & 0x7FFFu};
       int i0, i1;
       keep_pair(a, i0, i1);
       uint32_t v0 = h[0], v1 = h[0];
@@ -56,12 +58,18 @@ __global__ __launch_bounds__(256) void prune_compress_kernel(const u32x4* __rest
         if (i == i1) v1 = h[i];
       }
       out[g] = v0 | (v1 << 16);
-      word |= (uint32_t)(i0 | (i1 << 2)) << (4 * g);
+      nibs |= (uint32_t)(i0 | (i1 << 2)) << (4 * g);
     }
-    values[t * 2 + 0] = u32x4{out[0], out[1], out[2], out[3]};
-    values[t * 2 + 1] = u32x4{out[4], out[5], out[6], out[7]};
-    const int64_t r = t / words;
-    meta[meta_index(r, t - r * words, n, words)] = word;
+    values[t] = u32x2{out[0], out[1]};
+    // chunk c of a word holds groups 2c, 2c+1: its byte goes to bits 8c..8c+7
+    const int c = (int)(t & 3);
+    uint32_t word = nibs << (8 * c);
+    word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+    word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+    if (c == 0) {
+      const int64_t wi = t >> 2, r = wi / words;
+      meta[meta_index(r, wi - r * words, n, words)] = word;
+    }
   }
 }
 
@@ -152,8 +160,8 @@ __global__ __launch_bounds__(256) void check_meta_kernel(const uint32_t* __restr
 hipError_t launch_prune_compress(const uint16_t* w, int64_t n, int64_t k, uint16_t* values,
                                  uint32_t* meta, hipStream_t s) {
   const int64_t nwords = n * (k / 32);
-  hipLaunchKernelGGL(prune_compress_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4*>(w), n, k / 32, reinterpret_cast<u32x4*>(values),
+  hipLaunchKernelGGL(prune_compress_kernel, dim3(grid_for(nwords * 4, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(w), n, k / 32, reinterpret_cast<u32x2*>(values),
                      meta);
   return hipGetLastError();
 }
