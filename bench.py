@@ -164,10 +164,12 @@ def main():
     xs = {m: xs_cpu[m].to(dev) for m in Ms}
     values = torch.empty(N, K // 2, dtype=torch.bfloat16, device=dev)
     meta = torch.empty(N * (K // 32), dtype=torch.int32, device=dev)
+    sp.prune_compress(w, values, meta)  # first launch loads the code object: not timed
     t_prune = ev.time(lambda i: sp.prune_compress(w, values, meta), 5) / 5
     qv, sw = (sp.quant_fp8(values) if fp8 else (values, None))
     if fp8:
         qbuf = torch.empty_like(qv)
+        sp.quant_fp8(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC)
         t_wq = ev.time(lambda i: sp.quant_fp8(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC), 5) / 5
     else:
         t_wq = 0.0
