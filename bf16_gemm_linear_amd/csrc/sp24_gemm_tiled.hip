@@ -74,11 +74,21 @@ struct TiledLayout {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Metadata words of a row (MWORDS per row): with 4 words, word w of row r sits
-// at w ^ (2 * ((r >> 4) & 1)), so the 64 lanes of a read (32 rows x words 2s,
-// 2s+1) hit 64 distinct banks; with 2 words a read is already contiguous.
-__device__ __forceinline__ int swz_m(int row, int w, int words) {
-  return words == 4 ? (w ^ (((row >> 4) & 1) * 2)) : w;
+// Metadata of a row in an LDS buffer.  With 4 words per step (fp8), the
+// words that lane group q needs for its two substeps (word q for substep 0,
+// word q + 2 for substep 1) are adjacent: slot 2 * (q ^ ((r >> 4) & 1)) + s
+// of row r holds word 2s + q, so one 8-byte read per row gives both, and the
+// 32 rows of a half-wave read hit 64 distinct banks.  With 2 words per step
+// (bf16) lane group q needs word q for both substeps, in slot q.
+// meta_slot_word: the word of the step held by slot `slot` of row r.
+template <int MWORDS>
+__device__ __forceinline__ int meta_slot_word(int r, int slot) {
+  if constexpr (MWORDS == 4) {
+    const int q = (slot >> 1) ^ ((r >> 4) & 1), sub = slot & 1;
+    return 2 * sub + q;
+  } else {
+    return slot;
+  }
 }
 
 template <int DT, bool SPARSE>
@@ -123,7 +133,7 @@ struct Loader {
       for (int j = 0; j < S::M_INSTR; ++j) {
         const int p = (wave * S::M_INSTR + j) * 64 + lane, row = p / L::MWORDS;
         const int n = min(n0 + row, N - 1);
-        mp[j] = meta + (size_t)n * 4 + swz_m(row, p % L::MWORDS, L::MWORDS);
+        mp[j] = meta + (size_t)n * 4 + meta_slot_word<L::MWORDS>(row, p % L::MWORDS);
       }
     }
     const size_t xrow = (size_t)K * L::ESZ;
@@ -181,7 +191,8 @@ __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
 template <int DT, bool SPARSE>
 struct Frag {
   i32x4 a[TI][SPARSE ? 1 : 2];
-  uint32_t ix[TI];
+  uint32_t ix[TI];   // index bits of this substep
+  uint32_t ixn[TI];  // index bits of the next substep of the same step (read together)
   i32x4 b[TJ][2];
 };
 
@@ -194,8 +205,8 @@ constexpr int n_pieces() {
 
 // Read piece P of substep s from an LDS buffer into f.
 template <int DT, bool SPARSE, int P>
-__device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const uint8_t* __restrict__ buf, int s, int wn,
-                                           int wm, int lane) {
+__device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const Frag<DT, SPARSE>& prev,
+                                           const uint8_t* __restrict__ buf, int s, int wn, int wm, int lane) {
   using L = TiledLayout<DT, SPARSE>;
   const int q = lane >> 5, r = lane & 31;
   if constexpr (P < TI) {
@@ -228,21 +239,33 @@ __device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const uint8_t* _
       f.b[j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 2 * s + q));
     }
   } else {
-    // index bits: fp8 word 2s + q; bf16 word q (its 16-bit half s is selected by abid)
+    // index bits: fp8 word 2s + q; bf16 word q (its 16-bit half s is selected by
+    // abid).  Substep 0 reads both substeps' words; substep 1 takes them over.
+    static_assert(L::SUB == 2, "two substeps per step in the sparse kernels");
     constexpr int i = P - TI - 2 * TJ;
-    const int row = wn * (BN / WGN) + 32 * i + r;
-    const int word = DT == SP24_FP8_E4M3 ? 2 * s + q : q;
-    f.ix[i] = *reinterpret_cast<const uint32_t*>(buf + L::M_OFF + row * L::MWORDS * 4 +
-                                                 4 * swz_m(row, word, L::MWORDS));
+    if (s == 0) {
+      const int row = wn * (BN / WGN) + 32 * i + r;
+      if constexpr (DT == SP24_FP8_E4M3) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(buf + L::M_OFF + row * 16 +
+                                                        8 * (q ^ ((row >> 4) & 1)));
+        f.ix[i] = v[0];
+        f.ixn[i] = v[1];
+      } else {
+        f.ix[i] = *reinterpret_cast<const uint32_t*>(buf + L::M_OFF + row * 8 + 4 * q);
+        f.ixn[i] = f.ix[i];
+      }
+    } else {
+      f.ix[i] = prev.ixn[i];
+    }
   }
 }
 
 template <int DT, bool SPARSE, int P0, int P1>
-__device__ __forceinline__ void read_pieces(Frag<DT, SPARSE>& f, const uint8_t* __restrict__ buf, int s, int wn,
-                                            int wm, int lane) {
+__device__ __forceinline__ void read_pieces(Frag<DT, SPARSE>& f, const Frag<DT, SPARSE>& prev,
+                                            const uint8_t* __restrict__ buf, int s, int wn, int wm, int lane) {
   if constexpr (P0 < P1) {
-    read_piece<DT, SPARSE, P0>(f, buf, s, wn, wm, lane);
-    read_pieces<DT, SPARSE, P0 + 1, P1>(f, buf, s, wn, wm, lane);
+    read_piece<DT, SPARSE, P0>(f, prev, buf, s, wn, wm, lane);
+    read_pieces<DT, SPARSE, P0 + 1, P1>(f, prev, buf, s, wn, wm, lane);
   }
 }
 
@@ -293,7 +316,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[TI][TJ], const Frag<DT, SPAR
   if constexpr (T < NMMA) {
     mma_one<DT, SPARSE, S, T / TJ, T % TJ>(acc, cur);
     issue_loads<DT, SPARSE, T * NV / NMMA, (T + 1) * NV / NMMA>(ld, fill, fill_ks);
-    if constexpr (T < RS) read_pieces<DT, SPARSE, T * NP / RS, (T + 1) * NP / RS>(nxt, rbuf, rs, wn, wm, lane);
+    if constexpr (T < RS) read_pieces<DT, SPARSE, T * NP / RS, (T + 1) * NP / RS>(nxt, cur, rbuf, rs, wn, wm, lane);
     __builtin_amdgcn_sched_barrier(0);
     phase<DT, SPARSE, S, T + 1, ISSUE>(acc, cur, nxt, rbuf, rs, wn, wm, lane, ld, fill, fill_ks);
   }
@@ -372,7 +395,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   Frag<DT, SPARSE> f[2];
-  read_pieces<DT, SPARSE, 0, n_pieces<SPARSE>()>(f[0], lds, 0, wn, wm, lane);
+  read_pieces<DT, SPARSE, 0, n_pieces<SPARSE>()>(f[0], f[1], lds, 0, wn, wm, lane);
 
   // One K step.  ISSUE: step ks + STAGES exists and is loaded here.
   auto step = [&](int ks, auto issue_tag) {
