@@ -199,6 +199,9 @@ def main():
             b["qws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         nb = sp.workspace_size(sp.OP_GEMM, dt, m, N, K)
         b["gws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        if fp8:  # quantise + GEMM in one call (X quantised inside the kernel at M = 1)
+            nb = sp.workspace_size(sp.OP_GEMM_QX, dt, m, N, K)
+            b["qxws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         b["plan"] = sp.plan(sp.OP_GEMM, dt, m, N, K)
         bufs[m] = b
 
@@ -215,10 +218,17 @@ def main():
         else:
             sp.gemm(xs[m], wq_copies[r], meta_copies[r], out=b["y"], ws=b["gws"])
 
+    def call_step(m, r):
+        """One step's work for M tokens: quantise X (FP8) and the sparse GEMM."""
+        b = bufs[m]
+        if fp8:
+            sp.gemm_qx(xs[m], wq_copies[r], meta_copies[r], sw, x_scale=b["sx"], out=b["y"], ws=b["qxws"])
+        else:
+            call_gemm(m, r)
+
     def step(r):
         for j, m in enumerate(Ms):
-            call_quant(m)
-            call_gemm(m, (r * len(Ms) + j) % R)
+            call_step(m, (r * len(Ms) + j) % R)
 
     # eager reference of every M's output for one rotation index
     step(0)
@@ -351,7 +361,7 @@ def main():
         "dtype": "fp8_e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded, workloads/)",
         "config": {"workload": desc, "M": Ms, "K": K, "N": N, "weight_copies": R,
-                   "step": "per M: quantise X + sparse GEMM" if fp8 else "per M: sparse GEMM"},
+                   "step": "per M: sp24_gemm_qx (quantise X + sparse GEMM; one launch at M=1)" if fp8 else "per M: sparse GEMM"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_m": {str(m): per_m[m] for m in Ms},

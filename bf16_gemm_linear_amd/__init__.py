@@ -19,15 +19,15 @@ import os
 import torch
 
 __all__ = [
-    "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM",
-    "Sp24Error", "lib", "lib_path", "version",
+    "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
+    "Sp24Error", "lib", "lib_path", "version", "gemm_qx",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
     "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
 ]
 
 BF16, FP8 = 0, 1
 SCALE_DYNAMIC, SCALE_STATIC = 0, 1
-OP_GEMM, OP_QUANT, OP_DENSE_GEMM = 0, 1, 2
+OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsp24.so")
@@ -57,6 +57,7 @@ _SIGS = {
     "sp24_quant_fp8": [_vp, _i64, _vp, _vp, _int, _vp, _sz, _vp],
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
     "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
     "sp24_status_string": [_int],
@@ -272,6 +273,34 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
 def gemm(x, values, meta, x_scale=None, w_scale=None, out=None, ws=None):
     """Y = X . W^T with W compressed 2:4 (values, meta); bf16 output [m, n]."""
     return _gemm(True, x, values, meta, x_scale, w_scale, out, ws)
+
+
+def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):
+    """Y = quant_fp8(X) . W^T for a bf16 X [m, k] and E4M3 compressed weights, in one call
+    (sp24_gemm_qx): returns (y [m, n] bf16, x_scale fp32[1]), bit-identical to
+    quant_fp8 followed by gemm."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    _need(values, "values", _CODE_T, 2, x.device)
+    n = values.shape[0]
+    if values.shape[1] * 2 != k:
+        raise ValueError("compressed weight shapes do not match k=%d" % k)
+    _need(meta, "meta", torch.int32, 1, x.device)
+    _meta_size(meta, n, k)
+    _need(w_scale, "w_scale", torch.float32, None, x.device)
+    if x_scale is None:
+        x_scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(x_scale, "x_scale", torch.float32, None, x.device)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    nbytes = workspace_size(OP_GEMM_QX, FP8, m, n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_gemm_qx", lib.sp24_gemm_qx(m, n, k, _ptr(x), _ptr(x_scale), _ptr(values), _ptr(meta),
+                                            _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
+    return out, x_scale
 
 
 def dense_gemm(x, w, x_scale=None, w_scale=None, out=None, ws=None):

@@ -272,6 +272,63 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   return SP24_OK;
 }
 
+namespace {
+
+// X quantised inside the GEMM (sp24_gemm_qx): every workgroup of the sparse FP8
+// stream kernel reads all of X for the per-tensor scale, so X must be small
+// (M * K <= kQxMaxValues, 128 KB of bf16), and the codes of its tokens over its
+// K slice must fit the kStreamQxBytes region after the ring.
+constexpr int64_t kQxMaxValues = 65536;
+
+bool qx_fused(const sp24_plan& p, int64_t m, int64_t k) {
+  if (p.kernel != SP24_KERNEL_STREAM || m * k > kQxMaxValues) return false;
+  int64_t room = -1;
+  int ups = 0, bm = 0;
+  switch (p.config - kStreamBase) {
+#define SP24_QX_ROOM(ID, RBW, RB, MW, KW, MB, U, SMAX)                                     \
+  case ID:                                                                           \
+    ups = (U) * (KW);                                                                \
+    bm = 16 * (MW) * (MB);                                                           \
+    if (stream_fits(SP24_FP8_E4M3, true, RBW, RB, MW, KW, MB, U, SMAX) &&               \
+        stream_ring_bytes(SP24_FP8_E4M3, true, RBW, RB, MW, KW, MB, U, SMAX, true) +     \
+                kStreamQxBytes + 64 <= kStreamLdsBytes)                                   \
+      room = kStreamQxBytes;                                                          \
+    break;
+    SP24_STREAM_CONFIGS(SP24_QX_ROOM)
+#undef SP24_QX_ROOM
+    default: return false;
+  }
+  const int64_t rows = m < bm ? m : bm;
+  return room >= 0 && rows * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
+}
+
+// Workspace of sp24_gemm_qx: the GEMM's own, then (when X is not quantised
+// inside the kernel) the E4M3 codes of X and the quantiser's workspace.
+struct QxWorkspace {
+  size_t gemm, codes, quant, total;
+  bool fused;
+};
+
+QxWorkspace qx_workspace(const sp24_plan& p, int64_t m, int64_t k) {
+  QxWorkspace w;
+  w.gemm = (p.workspace_bytes + 15) / 16 * 16;
+  w.fused = qx_fused(p, m, k);
+  w.codes = w.fused ? 0 : ((size_t)(m * k) + 15) / 16 * 16;
+  w.quant = w.fused ? 0 : quant_workspace_bytes(m * k);
+  w.total = w.gemm + w.codes + w.quant;
+  return w;
+}
+
+hipError_t launch_plan(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+  hipError_t e = p.kernel == SP24_KERNEL_TILED    ? launch_gemm_tiled(a, p, s)
+                 : p.kernel == SP24_KERNEL_STREAM ? launch_gemm_stream(a, p, s)
+                                                  : launch_gemm_skinny(a, p, s);
+  if (e == hipSuccess && p.split_k > 1) e = launch_splitk_reduce(a, p.split_k, s);
+  return e;
+}
+
+}  // namespace
+
 }  // namespace sp24
 
 using namespace sp24;
@@ -307,6 +364,10 @@ size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k) {
     return quant_workspace_bytes(m * k);
   }
   sp24_plan p;
+  if (op == SP24_OP_GEMM_QX) {
+    if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &p) != SP24_OK) return 0;
+    return qx_workspace(p, m, k).total;
+  }
   if (plan_gemm(op, dtype, m, n, k, &p) != SP24_OK) return 0;
   return p.workspace_bytes;
 }
@@ -412,11 +473,7 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   a.y = static_cast<uint16_t*>(y);
   a.partial = p.split_k > 1 ? static_cast<float*>(ws) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p.kernel == SP24_KERNEL_TILED    ? launch_gemm_tiled(a, p, s)
-                 : p.kernel == SP24_KERNEL_STREAM ? launch_gemm_stream(a, p, s)
-                                                  : launch_gemm_skinny(a, p, s);
-  if (e == hipSuccess && p.split_k > 1) e = launch_splitk_reduce(a, p.split_k, s);
-  return finish(e, s);
+  return finish(launch_plan(a, p, s), s);
 }
 
 int sp24_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const float* x_scale_dev,
@@ -431,6 +488,61 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                     void* y_bf16, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common(false, dtype, m, n, k, x, x_scale_dev, w_dense, nullptr, w_scale_dev, y_bf16, ws,
                      ws_bytes, stream);
+}
+
+int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
+                 const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (!x_bf16 || !x_scale_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
+  sp24_plan p;
+  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  if (st != SP24_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
+    return SP24_ERR_ALIGN;
+  if (((uintptr_t)x_scale_dev & 3u) || ((uintptr_t)w_scale_dev & 3u)) return SP24_ERR_ALIGN;
+  const QxWorkspace wsp = qx_workspace(p, m, k);
+  if (wsp.total > 0) {
+    if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  }
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 2, wb = (size_t)n * (k / 2);
+  const size_t mb = (size_t)n * (k / 32) * 4;
+  const void* in[4] = {x_bf16, w_values, w_meta, w_scale_dev};
+  const size_t inb[4] = {xb, wb, mb, 4};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(y_bf16, yb, in[i], inb[i]) || overlaps(x_scale_dev, 4, in[i], inb[i]) ||
+        (wsp.total > 0 && overlaps(ws, wsp.total, in[i], inb[i])))
+      return SP24_ERR_ALIAS;
+  if (overlaps(y_bf16, yb, x_scale_dev, 4) ||
+      (wsp.total > 0 && (overlaps(ws, wsp.total, y_bf16, yb) || overlaps(ws, wsp.total, x_scale_dev, 4))))
+    return SP24_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  GemmArgs a;
+  a.dtype = SP24_FP8_E4M3;
+  a.sparse = true;
+  a.m = (int)m;
+  a.n = (int)n;
+  a.k = (int)k;
+  a.x_scale = x_scale_dev;
+  a.w = w_values;
+  a.meta = w_meta;
+  a.w_scale = w_scale_dev;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  a.partial = p.split_k > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  if (wsp.fused) {
+    a.x = nullptr;
+    a.x_bf16 = static_cast<const uint16_t*>(x_bf16);
+    a.x_scale_out = x_scale_dev;
+    return finish(launch_plan(a, p, s), s);
+  }
+  uint8_t* codes = wsb + wsp.gemm;
+  hipError_t e = launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), m * k, codes, x_scale_dev,
+                                  SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
+  a.x = codes;
+  if (e == hipSuccess) e = launch_plan(a, p, s);
+  return finish(e, s);
 }
 
 }  // extern "C"

@@ -36,6 +36,7 @@
 // bytes to slot i, so the swizzle is applied on the global side.
 #include "sp24_common.hpp"
 #include "sp24_dma.hpp"
+#include "sp24_fp8.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -75,6 +76,12 @@ struct StreamCfg {
   static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MWD,
                 "whole load instructions");
   static_assert(!FITS || MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(LDS == stream_ring_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, false), "one LDS formula");
+  // X quantised by the kernel (QX): ring buffers without X rows, the X rows of
+  // the workgroup's tokens and K slice after RING_QX
+  static constexpr int STAGE_QX = X_OFF;
+  static constexpr int RING_QX = stream_ring_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, true);
+  static constexpr int MIN_PER_STEP_QX = W_TOT / NW + M_TOT / NW;
 };
 
 // Metadata words (MW per row): the 16 rows x 4 words of one read land on 64
@@ -92,7 +99,7 @@ __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
 // Per-lane sources of this wave's loads.  Load g of a stream (g = j*NW +
 // wave) fills slots [64g, 64g + 64) of the stream's LDS region; step ks adds
 // ks * UPS units to every source.
-template <class C>
+template <class C, bool QX>
 struct StreamLoader {
   const uint8_t* wp[C::W_PER];
   const uint32_t* mp[C::M_PER > 0 ? C::M_PER : 1];
@@ -125,7 +132,7 @@ struct StreamLoader {
     }
     const size_t xrow = (size_t)K * C::ESZ;
 #pragma unroll
-    for (int j = 0; j < C::X_PER; ++j) {
+    for (int j = 0; j < (QX ? 0 : C::X_PER); ++j) {
       const int p = (j * C::NW + wave) * 64 + lane, row = p / C::PX;
       const int sp = swz16<C::PX>(row, p % C::PX);
       const int m = min(m0 + row, M - 1);  // rows past M: clamp the load, never stored
@@ -147,7 +154,7 @@ struct StreamLoader {
         dma4(mp[j] + (size_t)ks * mstep, buf + C::M_OFF + g * 256);
     }
 #pragma unroll
-    for (int j = 0; j < C::X_PER; ++j) {
+    for (int j = 0; j < (QX ? 0 : C::X_PER); ++j) {
       const int g = j * C::NW + wave;
       if (C::X_TOT % C::NW == 0 || g < C::X_TOT)
         dma16(xp[j] + (size_t)ks * C::XB, buf + C::X_OFF + g * 1024);
@@ -162,8 +169,11 @@ __device__ __forceinline__ i32x4 lds16(const uint8_t* p) {
 // Units kg*U .. kg*U + U - 1 of one step for the RB row blocks of row group
 // rg and the MB token blocks of token group mg.  All LDS reads of the step
 // are issued before its matrix instructions.
+// X rows of the step: row r at xs + min(r, xlast) * xstride (a ring buffer:
+// xs = buf + X_OFF, xstride = XB; resident X: the step's part of each row).
 template <class C>
 __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
+                                           const uint8_t* __restrict__ xs, int xstride, int xlast,
                                            int rg, int mg, int kg, int lane) {
   constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
   constexpr bool FP8 = C::FP8, SPARSE = C::SPARSE_;
@@ -197,8 +207,8 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int xrow = 16 * (MB * mg + mb) + r;
-      const uint8_t* xr = buf + C::X_OFF + xrow * C::XB;
+      const int xrow = min(16 * (MB * mg + mb) + r, xlast);
+      const uint8_t* xr = xs + xrow * xstride;
 #pragma unroll
       for (int e = 0; e < BP; ++e) {
         int c;
@@ -245,13 +255,26 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
   }
 }
 
-template <class C, bool PARTIAL>
+// QX: X is bf16 (xh) and quantised here with the per-tensor scale of the whole
+// of X, exactly as the quantiser does it (same key, scale and cast); block
+// (0, 0, 0) stores the scale to sx_out.
+template <class C, bool PARTIAL, bool QX>
 __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-    float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice) {
+    float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice,
+    const uint16_t* __restrict__ xh, float* __restrict__ sx_out) {
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+  constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
+  // QX: the X codes sit in an array of their own, so the compiler can tell its
+  // reads from the LDS-DMA writes into the ring (it would otherwise wait for
+  // every load in flight before each step's reads); and the two take at least
+  // the LDS of the same configuration without QX, so that as many workgroups
+  // share a CU (the host sizes the grid for that occupancy).
+  constexpr int LDS_QX = C::RING_QX + kStreamQxBytes > C::LDS ? C::LDS - kStreamQxBytes : C::RING_QX;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[QX ? LDS_QX : C::LDS];
+  __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
+  __shared__ uint32_t wave_max[QX ? C::NW : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -273,16 +296,92 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   // which receives the loads of step ks + STAGES - 1 while step ks is
   // multiplied.  A bare s_barrier: __syncthreads() adds a release fence that
   // waits for every outstanding LDS-DMA load and would drain the ring.
-  const StreamLoader<C> ld(w, meta, x, n0, n_end - 1, m0, M, N, K, u0, wave, lane);
+  const StreamLoader<C, QX> ld(w, meta, x, n0, n_end - 1, m0, M, N, K, u0, wave, lane);
+
+  // QX: take the scale from all of X and cast this workgroup's tokens over its
+  // K slice into LDS (an array of kStreamQxBytes), piece p of a step's part of
+  // row r in slot swz16(r, p) as a ring buffer would hold it.
+  float sx = 1.0f;
+  uint8_t* const xres = xcodes;
+  const int mrows = min(C::BM, M - m0);
+  const int xrs = (int)stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB);
+  if constexpr (QX) {
+    const int tid = threadIdx.x;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xh);
+    const int64_t nvec = (int64_t)M * K / 8;  // 8-value vectors of X (K % 8 == 0: none spans two rows)
+    const int kslice = units_per_slice * 128;
+    // small X (every decode token at once): each thread keeps its vectors in
+    // registers from the maximum to the cast, one pass over global memory
+    constexpr int RV = 4;
+    const bool in_regs = nvec <= (int64_t)RV * C::NT;
+    u32x4 xr[RV];
+    uint32_t mk = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const int64_t i = tid + (int64_t)r * C::NT;
+        xr[r] = i < nvec ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+        mk = max(mk, key_max8(xr[r]));
+      }
+    } else {
+      int64_t i = tid;
+      for (; i + 3 * C::NT < nvec; i += 4 * C::NT) {  // four loads in flight
+        const u32x4 a = xv[i], b = xv[i + C::NT], c = xv[i + 2 * C::NT], d = xv[i + 3 * C::NT];
+        mk = max(mk, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+      }
+      for (; i < nvec; i += C::NT) mk = max(mk, key_max8(xv[i]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
+    if (lane == 0) wave_max[wave] = mk;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < C::NW; ++g) mk = max(mk, wave_max[g]);
+    sx = scale_from_key(mk);
+    if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *sx_out = sx;
+    // codes of value kk (relative to the K slice) of token row rr
+    auto put = [&](int rr, int kk, u32x2 c8) {
+      const int st = kk / C::XB, within = kk - st * C::XB;
+      *reinterpret_cast<u32x2*>(xres + rr * xrs + st * C::XB + 16 * swz16<C::PX>(rr, within / 16) +
+                                (within & 15)) = c8;
+    };
+    const int k0 = u0 * 128;
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const int64_t i = tid + (int64_t)r * C::NT;
+        if (i >= nvec) continue;
+        const int row = (int)(8 * i / K), kk = (int)(8 * i - (int64_t)row * K) - k0;
+        if (row >= m0 && row < m0 + mrows && kk >= 0 && kk < kslice) put(row - m0, kk, cast8(xr[r], sx));
+      }
+    } else {
+      const int vpr = kslice / 8;  // 8-value vectors per row of the slice
+      const uint16_t* xs0 = xh + (size_t)m0 * K + k0;
+      for (int v = tid; v < mrows * vpr; v += C::NT) {
+        const int rr = v / vpr, kk = (v - rr * vpr) * 8;
+        put(rr, kk, cast8(*reinterpret_cast<const u32x4*>(xs0 + (size_t)rr * K + kk), sx));
+      }
+    }
+    __syncthreads();  // the codes are in LDS for every wave (no loads are in flight yet)
+  }
+
+  // The ring's first loads go out after the QX prologue: ordinary LDS writes
+  // issued while LDS-DMA loads are in flight make the compiler wait for every
+  // load in flight before each later LDS read.
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nks) ld.issue(lds + p * C::STAGE, p);
+    if (p < nks) ld.issue(lds + p * STAGE, p);
   for (int ks = 0; ks < nks; ++ks) {
-    wait_later<C::MIN_PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
+    wait_later<QX ? C::MIN_PER_STEP_QX : C::MIN_PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // LDS reads stay after the barrier
     const int nxt = ks + STAGES - 1;
-    if (nxt < nks) ld.issue(lds + (nxt % STAGES) * C::STAGE, nxt);
-    stream_mma<C>(acc, lds + (ks % STAGES) * C::STAGE, rg, mg, kg, lane);
+    if (nxt < nks) ld.issue(lds + (nxt % STAGES) * STAGE, nxt);
+    const uint8_t* buf = lds + (ks % STAGES) * STAGE;
+    if constexpr (QX)
+      stream_mma<C>(acc, buf, xres + ks * C::XB, xrs, mrows - 1, rg, mg, kg, lane);
+    else
+      stream_mma<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
   }
 
   // Sum the KW partial tiles of each row block in wave order kg = 0, 1, ...
@@ -315,7 +414,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   }
 
   float scale = 1.0f;
-  if constexpr (C::FP8 && !PARTIAL) scale = x_scale[0] * w_scale[0];
+  if constexpr (C::FP8 && !PARTIAL) scale = (QX ? sx : x_scale[0]) * w_scale[0];
   const int q = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -363,12 +462,33 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
       return hipErrorInvalidConfiguration;
     const uint8_t* x = static_cast<const uint8_t*>(a.x);
     const uint8_t* w = static_cast<const uint8_t*>(a.w);
+    if (a.x_bf16 != nullptr) {
+      if constexpr (DT == SP24_FP8_E4M3 && SPARSE && C::RING_QX + kStreamQxBytes + 64 <= kLdsBytes) {
+        // the X rows of a workgroup must fit the region after the ring
+        const int64_t rows = a.m < C::BM ? a.m : C::BM;
+        if (rows * stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB) > kStreamQxBytes)
+          return hipErrorInvalidConfiguration;
+        if (p.split_k > 1)
+          hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                             a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
+                             a.x_scale_out);
+        else
+          hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                             a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
+                             a.x_scale_out);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidConfiguration;
+      }
+    }
     if (p.split_k > 1)
-      hipLaunchKernelGGL((gemm_stream_kernel<C, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
-                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+      hipLaunchKernelGGL((gemm_stream_kernel<C, true, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
+                         (const uint16_t*)nullptr, (float*)nullptr);
     else
-      hipLaunchKernelGGL((gemm_stream_kernel<C, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
-                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice);
+      hipLaunchKernelGGL((gemm_stream_kernel<C, false, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+                         a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
+                         (const uint16_t*)nullptr, (float*)nullptr);
     return hipGetLastError();
   }
 }

@@ -46,6 +46,11 @@ struct GemmArgs {
   const float* w_scale;
   uint16_t* y;
   float* partial;       // split-K partial sums [split_k][m][n], or nullptr
+  // X quantised inside the GEMM (sparse FP8 stream kernel only): x_bf16 is X,
+  // and the kernel writes the per-tensor scale to x_scale_out, which x_scale
+  // then points to for the split-K reduction
+  const uint16_t* x_bf16 = nullptr;
+  float* x_scale_out = nullptr;
 };
 // Small-m kernel configurations: X(id, row blocks of 16, token blocks of 16,
 // waves per workgroup, chunks of loads issued per batch).
@@ -108,6 +113,10 @@ constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
 constexpr int kStreamConfigs = 28;
 constexpr int kStreamBase = 100;
 constexpr int kStreamLdsBytes = 160 * 1024;
+// A stream kernel that quantises X itself holds its tokens' X codes in a
+// region of kStreamQxBytes after its ring (M * K-slice bytes must fit: M = 1
+// decode), small enough to keep the configuration's occupancy.
+constexpr int kStreamQxBytes = 16384;
 
 // Bytes of one LDS buffer of a stream configuration: W values and metadata of
 // 16 * rbw * rb rows plus 16 * mw * mb X rows, for u * kw units of 128 K.
@@ -125,6 +134,25 @@ constexpr int stream_stages(int dtype, bool sparse, int rbw, int rb, int mw, int
 constexpr bool stream_fits(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
                            int smax) {
   return stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) >= 2;
+}
+// LDS bytes of a stream configuration below anything else: its ring or the
+// reduction of the KW partial tiles, whichever is larger.  With qx (X
+// quantised by the kernel itself and held in LDS) the ring buffers hold W and
+// metadata only; the X rows live after these bytes.
+constexpr int stream_ring_bytes(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
+                                int smax, bool qx) {
+  const int esz = dtype == SP24_FP8_E4M3 ? 1 : 2;
+  const int stage = stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u) -
+                    (qx ? 16 * mw * mb * u * kw * 128 * esz : 0);
+  const int ring = stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) * stage;
+  const int red = kw > 1 ? kw * rbw * mw * rb * mb * 1024 : 0;
+  return ring > red ? ring : red;
+}
+// Row stride of the X rows a quantising stream kernel holds in LDS: its K
+// slice, plus 128 bytes when that keeps 128-byte steps (one unit per step) on
+// alternating bank halves as in a ring buffer.
+constexpr int64_t stream_qx_row_bytes(int64_t k_slice, int step_bytes) {
+  return k_slice + ((step_bytes == 128 && (k_slice / 128) % 2 == 0) ? 128 : 0);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);

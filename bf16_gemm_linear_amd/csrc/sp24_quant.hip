@@ -17,6 +17,7 @@
 //                   workgroup (a few KB from L2), stores the scale from
 //                   workgroup 0 and casts.  No atomics, no memset, no host sync.
 #include "sp24_common.hpp"
+#include "sp24_fp8.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -46,30 +47,6 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sh) {
   for (int i = 0; i < NT / kWave; ++i) r = max(r, sh[i]);
   __syncthreads();
   return r;
-}
-
-__device__ __forceinline__ uint32_t key_max8(u32x4 d) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m = max(m, d[j] & 0x7FFFu);
-    m = max(m, (d[j] >> 16) & 0x7FFFu);
-  }
-  return m;
-}
-
-__device__ __forceinline__ float scale_from_key(uint32_t key) {
-  // amax is the bf16 value with bits `key`; the division is IEEE float32.
-  return key == 0 ? 1.0f : bf16_to_f32(key) / 448.0f;
-}
-
-// 8 bf16 -> 8 E4M3 codes
-__device__ __forceinline__ u32x2 cast8(u32x4 d, float s) {
-  uint32_t b[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    b[j] = f32x2_to_e4m3(bf16_to_f32(d[j] & 0xFFFFu) / s, bf16_to_f32(d[j] >> 16) / s);
-  return u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
 }
 
 __device__ __forceinline__ uint8_t cast1(uint32_t h, float s) {

@@ -83,7 +83,8 @@ typedef enum sp24_scale_mode {
 typedef enum sp24_op {
   SP24_OP_GEMM = 0,       /* sp24_gemm */
   SP24_OP_QUANT = 1,      /* sp24_quant_fp8 */
-  SP24_OP_DENSE_GEMM = 2  /* sp24_dense_gemm */
+  SP24_OP_DENSE_GEMM = 2, /* sp24_dense_gemm */
+  SP24_OP_GEMM_QX = 3     /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
 } sp24_op;
 
 typedef enum sp24_kernel {
@@ -166,6 +167,27 @@ int sp24_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const f
 int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                     const float* x_scale_dev, const void* w_dense, const float* w_scale_dev,
                     void* y_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/* Y = X . W^T for a bf16 X with FP8 weights: exactly sp24_quant_fp8(x_bf16,
+ * m*k, codes, x_scale_dev, SP24_SCALE_DYNAMIC) followed by sp24_gemm(
+ * SP24_FP8_E4M3, ..., codes, x_scale_dev, ...), bit for bit in y and in
+ * *x_scale_dev, in one call.  The per-tensor scale follows the cookbook's
+ * dynamic FP8 scaling ("Deploying 2:4 Sparsity with FP8 on Hopper", pipeline
+ * step 3); the quantisation happens inside the GEMM kernel when X is small
+ * (m*k <= 65536 values and the plan's small-m kernel has room for its tokens'
+ * codes in LDS: decode shapes), which saves the quantiser's launch and the
+ * round trip of the codes through memory; otherwise the two steps run as two
+ * launches with the codes in the workspace.
+ *   x_bf16      in : [m, k] bf16
+ *   x_scale_dev out: fp32, the scale amax(|x|)/448 (1 when x is all zero)
+ *   w_values    in : [n, k/2] E4M3 codes; w_meta as for sp24_gemm;
+ *   w_scale_dev in : fp32;  y_bf16 out: [m, n]
+ * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM_QX, SP24_FP8_E4M3, m,
+ * n, k).  Same shape limits, alignment (x_scale_dev and w_scale_dev: 4 bytes)
+ * and errors as sp24_gemm; x_scale_dev may alias no other argument. */
+int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
+                 const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by an op at a shape (0 if none; also 0 for invalid
  * arguments, which the op itself then rejects). */

@@ -262,3 +262,41 @@ def test_probe_validation():
     assert lib.sp24_probe_copy(p(A), p(A + 4096), 65, None) == ESHAPE
     assert lib.sp24_probe_read(p(A), 0, p(A + 4096), None) == ESHAPE
     assert lib.sp24_probe_read_blocks() > 0
+
+
+def gemm_qx(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
+            wsc=A + 0x400000, y=A + 0x500000, ws=A + 0x600000, wsb=1 << 20):
+    return lib.sp24_gemm_qx(m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), p(ws), wsb, None)
+
+
+def test_gemm_qx_validation():
+    for kw in ("x", "xs", "w", "meta", "wsc", "y"):
+        assert gemm_qx(**{kw: None}) == ENULL, kw
+    assert gemm_qx(m=0) == ESHAPE
+    assert gemm_qx(k=96) == ESHAPE
+    assert gemm_qx(x=A + 8) == EALIGN
+    assert gemm_qx(meta=A + 0x300004) == EALIGN
+    assert gemm_qx(xs=A + 0x100002) == EALIGN
+    # the scale output may alias no input and not the output
+    assert gemm_qx(xs=A + 0x100) == EALIAS               # inside x (8 x 256 bf16 = 4 KB)
+    assert gemm_qx(xs=A + 0x400000) == EALIAS            # the weight scale
+    assert gemm_qx(y=A + 0x200000) == EALIAS             # output over the weights
+    assert gemm_qx(ws=A + 0x500100) == EALIAS            # workspace over the output
+
+
+def test_gemm_qx_workspace_rule():
+    ws_qx = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM_QX, sp.FP8, m, n, k)
+    ws_g = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)
+    # one decode token (its codes fit the kernel's 16 KB): only the GEMM's own workspace
+    for m, n, k in ((1, 14336, 4096), (1, 4096, 14336), (1, 1024, 16384)):
+        assert ws_qx(m, n, k) == (ws_g(m, n, k) + 15) // 16 * 16, (m, n, k)
+    # larger X: the codes (m*k bytes) and the quantiser's workspace as well
+    for m, n, k in ((16, 14336, 4096), (64, 14336, 4096), (16, 4096, 14336), (8192, 28672, 8192)):
+        need = lib.sp24_workspace_size(sp.OP_QUANT, sp.BF16, m, 1, k)
+        assert ws_qx(m, n, k) == (ws_g(m, n, k) + 15) // 16 * 16 + (m * k + 15) // 16 * 16 + need, (m, n, k)
+    assert ws_qx(1, 256, 96) == 0                         # invalid shape
+    assert lib.sp24_workspace_size(sp.OP_GEMM_QX, sp.BF16, 1, 256, 256) == 0  # FP8 only
+    # a workspace too small is rejected before any launch
+    m, n, k = 64, 14336, 4096
+    assert gemm_qx(m=m, n=n, k=k, x=A, xs=A + (1 << 24), w=A + (2 << 24), meta=A + (4 << 26),
+                   wsc=A + (6 << 26), y=A + (7 << 26), ws=A + (8 << 26), wsb=ws_qx(m, n, k) - 16) == EWS
