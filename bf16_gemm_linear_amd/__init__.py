@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
-    "Sp24Error", "lib", "lib_path", "version", "gemm_qx",
+    "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
     "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
 ]
@@ -58,6 +58,8 @@ _SIGS = {
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "sp24_gemm_rows": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
     "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
     "sp24_status_string": [_int],
@@ -273,6 +275,53 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
 def gemm(x, values, meta, x_scale=None, w_scale=None, out=None, ws=None):
     """Y = X . W^T with W compressed 2:4 (values, meta); bf16 output [m, n]."""
     return _gemm(True, x, values, meta, x_scale, w_scale, out, ws)
+
+
+def quant_fp8_rows(x: torch.Tensor, out: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Per-token E4M3 quantisation of a bf16 X [m, k] (k % 8 == 0) -> (codes uint8 [m, k],
+    scales fp32 [m]): row r is quantised with its own dynamic scale amax_r / 448."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty(m, k, dtype=torch.uint8, device=x.device)
+    _need(out, "out", _CODE_T, 2, x.device)
+    if tuple(out.shape) != (m, k):
+        raise ValueError("out must be [%d, %d]" % (m, k))
+    if scales is None:
+        scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(scales, "scales", torch.float32, 1, x.device)
+    if scales.numel() != m:
+        raise ValueError("scales must hold %d values" % m)
+    _check("sp24_quant_fp8_rows", lib.sp24_quant_fp8_rows(_ptr(x), m, k, _ptr(out), _ptr(scales),
+                                                          _stream(x.device)))
+    return out, scales
+
+
+def gemm_rows(x, values, meta, x_scales, w_scale, out=None, ws=None):
+    """Y = X . W^T for E4M3 X [m, k] with one scale per row (x_scales fp32 [m], from
+    quant_fp8_rows) and E4M3 compressed weights; bf16 output [m, n]."""
+    _need(x, "x", _CODE_T, 2)
+    m, k = x.shape
+    _need(values, "values", _CODE_T, 2, x.device)
+    n = values.shape[0]
+    if values.shape[1] * 2 != k:
+        raise ValueError("compressed weight shapes do not match k=%d" % k)
+    _need(meta, "meta", torch.int32, 1, x.device)
+    _meta_size(meta, n, k)
+    _need(x_scales, "x_scales", torch.float32, 1, x.device)
+    if x_scales.numel() != m:
+        raise ValueError("x_scales must hold %d values" % m)
+    _need(w_scale, "w_scale", torch.float32, None, x.device)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    nbytes = workspace_size(OP_GEMM, FP8, m, n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_gemm_rows", lib.sp24_gemm_rows(m, n, k, _ptr(x), _ptr(x_scales), _ptr(values), _ptr(meta),
+                                                _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
+    return out
 
 
 def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):

@@ -431,7 +431,8 @@ int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* sca
 
 static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                        const float* x_scale, const void* w, const uint32_t* meta,
-                       const float* w_scale, void* y, void* ws, size_t ws_bytes, void* stream) {
+                       const float* w_scale, void* y, void* ws, size_t ws_bytes, void* stream,
+                       int xs_step = 0) {
   if (dtype != SP24_BF16 && dtype != SP24_FP8_E4M3) return SP24_ERR_DTYPE;
   if (!x || !w || !y || (sparse && !meta)) return SP24_ERR_NULL;
   if (dtype == SP24_FP8_E4M3 && (!x_scale || !w_scale)) return SP24_ERR_NULL;
@@ -452,7 +453,8 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   const size_t mb = sparse ? (size_t)n * (k / 32) * 4 : 0;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || (sparse && overlaps(y, yb, meta, mb)))
     return SP24_ERR_ALIAS;
-  if (dtype == SP24_FP8_E4M3 && (overlaps(y, yb, x_scale, 4) || overlaps(y, yb, w_scale, 4)))
+  const size_t xsb = xs_step ? (size_t)m * 4 : 4;  // bytes of X scales: one per tensor or per row
+  if (dtype == SP24_FP8_E4M3 && (overlaps(y, yb, x_scale, xsb) || overlaps(y, yb, w_scale, 4)))
     return SP24_ERR_ALIAS;
   if (p.workspace_bytes > 0 &&
       (overlaps(ws, p.workspace_bytes, y, yb) || overlaps(ws, p.workspace_bytes, x, xb) ||
@@ -472,6 +474,7 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   a.w_scale = w_scale;
   a.y = static_cast<uint16_t*>(y);
   a.partial = p.split_k > 1 ? static_cast<float*>(ws) : nullptr;
+  a.x_scale_step = xs_step;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return finish(launch_plan(a, p, s), s);
 }
@@ -488,6 +491,27 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                     void* y_bf16, void* ws, size_t ws_bytes, void* stream) {
   return gemm_common(false, dtype, m, n, k, x, x_scale_dev, w_dense, nullptr, w_scale_dev, y_bf16, ws,
                      ws_bytes, stream);
+}
+
+int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
+                        void* stream) {
+  if (!x_bf16 || !q_out || !scales_dev) return SP24_ERR_NULL;
+  if (m < 1 || k < 8 || k % 8 != 0 || m > kMaxDim || k > kMaxDim || m * k > ((int64_t)1 << 40))
+    return SP24_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(q_out) || ((uintptr_t)scales_dev & 3u)) return SP24_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * 2, qb = (size_t)m * k, sb = (size_t)m * 4;
+  if (overlaps(q_out, qb, x_bf16, xb) || overlaps(scales_dev, sb, x_bf16, xb) ||
+      overlaps(scales_dev, sb, q_out, qb))
+    return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_quant_fp8_rows(static_cast<const uint16_t*>(x_bf16), m, k, q_out, scales_dev, s), s);
+}
+
+int sp24_gemm_rows(int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
+                   const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return gemm_common(true, SP24_FP8_E4M3, m, n, k, x, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16,
+                     ws, ws_bytes, stream, 1);
 }
 
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ meta, const float* __restrict__ x_scale,
     const float* __restrict__ w_scale, uint16_t* __restrict__ y, float* __restrict__ partial,
-    int M, int N, int K) {
+    int M, int N, int K, int xs_step) {
   constexpr int TILE = RB * MB * 256;  // floats per wave tile
   __shared__ float red[NW * TILE];
 
@@ -238,10 +238,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
       for (int i = 0; i < 4; ++i) red[wave * TILE + ((rb * MB + mb) * 4 + i) * 64 + lane] = acc[rb][mb][i];
   __syncthreads();
 
-  float scale = 1.0f;
-  if constexpr (DT == SP24_FP8_E4M3) {
-    if (!PARTIAL) scale = x_scale[0] * w_scale[0];
-  }
   // Output o = ((rb*MB + mb)*16 + mi)*16 + nj: consecutive threads take
   // consecutive n of one token row; waves are summed in a fixed order.
   for (int o = threadIdx.x; o < TILE; o += NW * 64) {
@@ -256,7 +252,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
       if constexpr (PARTIAL)
         partial[((size_t)blockIdx.z * M + m) * N + n] = s;
       else
+      {
+        // FP8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
+        const float scale = DT == SP24_FP8_E4M3 ? x_scale[(size_t)m * xs_step] * w_scale[0] : 1.0f;
         y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s * scale);
+      }
     }
   }
 }
@@ -268,10 +268,10 @@ hipError_t launch_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   const uint8_t* w = static_cast<const uint8_t*>(a.w);
   if (p.split_k > 1)
     hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, true>), grid, block, 0, s,
-                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step);
   else
     hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, false>), grid, block, 0, s,
-                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k);
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step);
   return hipGetLastError();
 }
 

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice,
-    const uint16_t* __restrict__ xh, float* __restrict__ sx_out) {
+    const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step) {
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
   // QX: the X codes sit in an array of their own, so the compiler can tell its
@@ -413,8 +413,6 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         }
   }
 
-  float scale = 1.0f;
-  if constexpr (C::FP8 && !PARTIAL) scale = (QX ? sx : x_scale[0]) * w_scale[0];
   const int q = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -435,6 +433,9 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         }
       } else {
         uint16_t* yr = y + (size_t)m * N;
+        // FP8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
+        float scale = 1.0f;
+        if constexpr (C::FP8) scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
         const uint32_t lo = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
         const uint32_t hi = f32_to_bf16_rne(v[2] * scale) | (f32_to_bf16_rne(v[3] * scale) << 16);
         if (n + 3 < n_end && (N & 3) == 0) {
@@ -471,11 +472,11 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
         if (p.split_k > 1)
           hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out);
+                             a.x_scale_out, 0);
         else
           hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out);
+                             a.x_scale_out, 0);
         return hipGetLastError();
       } else {
         return hipErrorInvalidConfiguration;
@@ -484,11 +485,11 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
     if (p.split_k > 1)
       hipLaunchKernelGGL((gemm_stream_kernel<C, true, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step);
     else
       hipLaunchKernelGGL((gemm_stream_kernel<C, false, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step);
     return hipGetLastError();
   }
 }

@@ -344,7 +344,7 @@ template <int DT, bool SPARSE>
 __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-    int M, int N, int K) {
+    int M, int N, int K, int xs_step) {
   using L = TiledLayout<DT, SPARSE>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::LDS_BYTES];
 
@@ -430,8 +430,6 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
   // 8-byte writes of a 32-row strip spread over the banks.
   constexpr int YS = L::YS;
   static_assert(BM * YS <= L::LDS_BYTES, "staged output tile fits");
-  float scale = 1.0f;
-  if constexpr (DT == SP24_FP8_E4M3) scale = x_scale[0] * w_scale[0];
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's last (discarded) reads are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -440,6 +438,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int ml = wm * (BM / WGM) + 32 * j + c;
+      // FP8: fp32(sx * sw) with the scale of X row m0 + ml (one per tensor: xs_step = 0;
+      // rows past M are staged but never stored)
+      float scale = 1.0f;
+      if constexpr (DT == SP24_FP8_E4M3) scale = x_scale[(size_t)min(m0 + ml, M - 1) * xs_step] * w_scale[0];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -483,7 +485,7 @@ template <int DT, bool SPARSE>
 hipError_t launch_tiled_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE>), dim3(p.grid_x), dim3(NT), 0, s,
                      static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta,
-                     a.x_scale, a.w_scale, a.y, a.m, a.n, a.k);
+                     a.x_scale, a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step);
   return hipGetLastError();
 }
 

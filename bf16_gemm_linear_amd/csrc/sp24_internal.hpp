@@ -31,6 +31,8 @@ hipError_t launch_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_
 
 // sp24_quant.hip
 size_t quant_workspace_bytes(int64_t count);
+hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
+                                 hipStream_t s);
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
                             void* ws, hipStream_t s);
 
@@ -51,6 +53,8 @@ struct GemmArgs {
   // then points to for the split-K reduction
   const uint16_t* x_bf16 = nullptr;
   float* x_scale_out = nullptr;
+  // FP8: the scale of X row m is x_scale[m * x_scale_step] (0: one per tensor, 1: one per row)
+  int x_scale_step = 0;
 };
 // Small-m kernel configurations: X(id, row blocks of 16, token blocks of 16,
 // waves per workgroup, chunks of loads issued per batch).

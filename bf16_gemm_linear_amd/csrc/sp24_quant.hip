@@ -129,6 +129,47 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
   if (blockIdx.x == gridDim.x - 1 && tail < count) q[tail] = cast1(x[tail], s);
 }
 
+// Per-row (per-token) scales: workgroup b quantises rows b, b + gridDim.x, ...
+// of X [m, k] (k % 8 == 0), each with s_r = fp32(amax_r / 448) (1 for a zero
+// row).  A row of up to kRowRegVecs * kThreads vectors stays in registers from
+// the maximum to the cast (k <= 8192: one pass over global memory).
+constexpr int kRowRegVecs = 4;
+
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
+                                                              int64_t k, uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
+  __shared__ uint32_t sh[kThreads / kWave];
+  const int64_t nvec = k / 8;
+  const bool in_regs = nvec <= (int64_t)kRowRegVecs * kThreads;
+  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x + r * k);
+    u32x2* qv = reinterpret_cast<u32x2*>(q + r * k);
+    u32x4 v[kRowRegVecs];
+    uint32_t mk = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kRowRegVecs; ++j) {
+        const int64_t i = threadIdx.x + (int64_t)j * kThreads;
+        v[j] = i < nvec ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+        mk = max(mk, key_max8(v[j]));
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
+    }
+    const float s = scale_from_key(block_max<kThreads>(mk, sh));
+    if (threadIdx.x == 0) scales[r] = s;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kRowRegVecs; ++j) {
+        const int64_t i = threadIdx.x + (int64_t)j * kThreads;
+        if (i < nvec) qv[i] = cast8(v[j], s);
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) qv[i] = cast8(xv[i], s);
+    }
+  }
+}
+
 int n_partials(int64_t count) {
   int64_t g = (count / 8 + kThreads * 4 - 1) / (kThreads * 4);  // >= 4 vectors per thread
   if (g > kMaxPartials) g = kMaxPartials;
@@ -141,6 +182,13 @@ int n_partials(int64_t count) {
 size_t quant_workspace_bytes(int64_t count) {
   if (count <= kFusedMax) return 0;
   return (size_t)n_partials(count) * sizeof(uint32_t);
+}
+
+hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
+                                 hipStream_t s) {
+  const int64_t blocks = m < 65536 ? m : 65536;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((int)blocks), dim3(kThreads), 0, s, x, m, k, q, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,

@@ -168,6 +168,26 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                     const float* x_scale_dev, const void* w_dense, const float* w_scale_dev,
                     void* y_bf16, void* ws, size_t ws_bytes, void* stream);
 
+/* Per-token (per-row) E4M3 quantisation of X [m, k] (bf16): row r gets its own
+ * dynamic scale scales_dev[r] = fp32(amax(|x[r, :]|) / 448) (1 for an all-zero
+ * row) and its codes exactly as sp24_quant_fp8 would quantise that row alone.
+ * The per-token quantisation of the SlideSparse page ("SlideSparse: Fast and
+ * Flexible (2N-2):2N Structured Sparsity", activation lifting); finer scales
+ * keep an outlier token from coarsening every other token's codes.
+ *   x_bf16 in : [m, k] bf16, k % 8 == 0;  q_out out: [m, k] E4M3 codes;
+ *   scales_dev out: [m] fp32.  No workspace, no host synchronisation. */
+int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
+                        void* stream);
+
+/* Y = X . W^T as sp24_gemm with dtype SP24_FP8_E4M3, except that X carries one
+ * scale per row: y[r, :] = bf16_rne(acc[r, :] * fp32(x_scales_dev[r] * sw)).
+ *   x E4M3 [m, k] (from sp24_quant_fp8_rows); x_scales_dev [m] fp32; the rest,
+ *   the workspace (sp24_workspace_size(SP24_OP_GEMM, SP24_FP8_E4M3, ...)) and
+ *   the errors as for sp24_gemm. */
+int sp24_gemm_rows(int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
+                   const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                   void* ws, size_t ws_bytes, void* stream);
+
 /* Y = X . W^T for a bf16 X with FP8 weights: exactly sp24_quant_fp8(x_bf16,
  * m*k, codes, x_scale_dev, SP24_SCALE_DYNAMIC) followed by sp24_gemm(
  * SP24_FP8_E4M3, ..., codes, x_scale_dev, ...), bit for bit in y and in

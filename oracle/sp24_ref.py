@@ -294,6 +294,29 @@ def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
     return np.float64(np.float32(scale)) * e4m3_decode(codes)
 
 
+def quant_fp8_rows(x_bits: np.ndarray):
+    """Quantise each row (token) of X ``[M, K]`` with its own dynamic scale.
+
+    The per-token quantisation the SlideSparse page ("SlideSparse: Fast and
+    Flexible (2N-2):2N Structured Sparsity", activation lifting) fuses its
+    activation step into, and the finer scales the page "La Densite Dynamique et
+    les Noyaux Non Structures ..." recommends for outlier-heavy layers: row m is
+    quantised exactly as :func:`quant_fp8` would quantise that row alone.
+    Returns (codes ``[M, K]``, scales ``[M]`` float32).
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[0], dtype=np.float32)
+    for m in range(x.shape[0]):
+        codes[m], scales[m] = quant_fp8(x[m])
+    return codes, scales
+
+
+def dequant_fp8_rows(codes: np.ndarray, scales) -> np.ndarray:
+    """float64 values ``scales[m] * decode(code)`` of row-scaled E4M3 codes."""
+    return np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None] * e4m3_decode(codes)
+
+
 # ----------------------------------------------------------------------------
 # Reference product Y = X . W^T (float64) and its magnitude sum
 # ----------------------------------------------------------------------------
@@ -319,6 +342,11 @@ def sparse_operands_bf16(x_bits, values, meta, k):
 def sparse_operands_fp8(xq, x_scale, wq_values, meta, w_scale, k):
     """Dense float64 operands of the FP8 path: both dequantised, W decompressed."""
     return dequant_fp8(xq, x_scale), dequant_fp8(decompress(wq_values, meta, k), w_scale)
+
+
+def sparse_operands_fp8_rows(xq, x_scales, wq_values, meta, w_scale, k):
+    """Dense float64 operands of the FP8 path with one scale per X row."""
+    return dequant_fp8_rows(xq, x_scales), dequant_fp8(decompress(wq_values, meta, k), w_scale)
 
 
 def within_tolerance(y, ref, mag, rel=8e-3, absmag=1e-4):

@@ -300,3 +300,24 @@ def test_gemm_qx_workspace_rule():
     m, n, k = 64, 14336, 4096
     assert gemm_qx(m=m, n=n, k=k, x=A, xs=A + (1 << 24), w=A + (2 << 24), meta=A + (4 << 26),
                    wsc=A + (6 << 26), y=A + (7 << 26), ws=A + (8 << 26), wsb=ws_qx(m, n, k) - 16) == EWS
+
+
+def test_quant_rows_validation():
+    f = lambda x=A, m=4, k=256, q=A + 0x100000, s=A + 0x200000: lib.sp24_quant_fp8_rows(
+        p(x), m, k, p(q), p(s), None)
+    assert f(x=None) == ENULL and f(q=None) == ENULL and f(s=None) == ENULL
+    assert f(m=0) == ESHAPE and f(k=0) == ESHAPE and f(k=12) == ESHAPE
+    assert f(x=A + 8) == EALIGN and f(q=A + 0x100008) == EALIGN and f(s=A + 0x200002) == EALIGN
+    assert f(q=A + 0x400) == EALIAS                       # codes over X (4 x 256 bf16 = 2 KB)
+    assert f(s=A + 0x10) == EALIAS                        # scales over X
+    assert f(s=A + 0x100010) == EALIAS                    # scales over the codes
+
+
+def test_gemm_rows_validation():
+    g = lambda m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000, wsc=A + 0x400000, \
+        y=A + 0x500000: lib.sp24_gemm_rows(m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), None, 0, None)
+    assert g(xs=None) == ENULL and g(wsc=None) == ENULL and g(meta=None) == ENULL
+    assert g(k=96) == ESHAPE
+    assert g(xs=A + 0x100002) == EALIGN
+    # the output may not overlap any of the m row scales (m * 4 bytes)
+    assert g(xs=A + 0x500000 - 16, m=8) == EALIAS

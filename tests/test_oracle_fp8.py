@@ -143,3 +143,65 @@ def test_scale_after_pruning_equals_before():
     bits = W.bf16_bits(w)
     v, meta = O.prune_compress(bits)
     assert O.fp8_scale(v) == O.fp8_scale(bits)
+
+
+# ---------------------------------------------------------------- per-row (per-token) scales
+
+def _bits(a):
+    return W.bf16_bits(torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16))
+
+
+def test_rows_single_value_maps_to_448():
+    # row m holds one nonzero value v_m; its scale is |v_m| / 448 and v_m becomes +-448 (0x7E / 0xFE)
+    x = np.zeros((3, 64), dtype=np.float32)
+    x[0, 5], x[1, 63], x[2, 0] = 3.5, -0.0078125, 1000.0
+    codes, s = O.quant_fp8_rows(_bits(x))
+    assert s.shape == (3,) and s.dtype == np.float32
+    assert s.tolist() == [np.float32(3.5) / np.float32(448), np.float32(0.0078125) / np.float32(448),
+                          np.float32(1000) / np.float32(448)]
+    assert codes[0, 5] == 0x7E and codes[1, 63] == 0xFE and codes[2, 0] == 0x7E
+    mask = np.zeros_like(codes, dtype=bool)
+    mask[0, 5] = mask[1, 63] = mask[2, 0] = True
+    assert np.all(codes[~mask] == 0)
+
+
+def test_rows_are_independent_of_each_other(rng):
+    # an outlier row must not change the other rows' codes or scales (a per-tensor or
+    # per-column scale would); each row matches torch's cast of that row over its own amax
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    x[2] *= 1000.0
+    bits = _bits(x)
+    codes, s = O.quant_fp8_rows(bits)
+    xf = O.bf16_to_f32(bits)
+    for m in range(4):
+        amax = max(abs(float(v)) for v in xf[m])
+        assert s[m] == np.float32(np.float32(amax) / np.float32(448.0))
+        assert np.array_equal(codes[m], _torch_cast(xf[m] / s[m]))
+    # rows 0, 1, 3 are unchanged without the outlier row
+    keep = [0, 1, 3]
+    c2, s2 = O.quant_fp8_rows(bits[keep])
+    assert np.array_equal(c2, codes[keep]) and np.array_equal(s2, s[keep])
+
+
+def test_rows_power_of_two_scaling_changes_only_the_scale(rng):
+    x = rng.standard_normal((1, 512)).astype(np.float32)
+    rows = np.concatenate([x, x * 2.0 ** 7, x * 2.0 ** -5])   # exact in bf16
+    codes, s = O.quant_fp8_rows(_bits(rows))
+    assert np.array_equal(codes[0], codes[1]) and np.array_equal(codes[0], codes[2])
+    assert s[1] == s[0] * np.float32(2.0 ** 7) and s[2] == s[0] * np.float32(2.0 ** -5)
+
+
+def test_rows_reduce_to_per_tensor_for_one_row_and_zero_rows(rng):
+    x = _bits(rng.standard_normal((1, 300)).astype(np.float32))
+    c1, s1 = O.quant_fp8_rows(x)
+    c0, s0 = O.quant_fp8(x)
+    assert np.array_equal(c1, c0) and s1[0] == s0
+    z = np.zeros((2, 64), dtype=np.uint16)
+    cz, sz = O.quant_fp8_rows(z)
+    assert np.all(sz == 1.0) and np.all(cz == 0)
+
+
+def test_dequant_rows_by_hand():
+    codes = np.array([[0x38, 0xB8, 0x00], [0x40, 0x7E, 0x01]], dtype=np.uint8)   # 1, -1, 0 ; 2, 448, 2^-9
+    out = O.dequant_fp8_rows(codes, np.array([2.0, 0.5], dtype=np.float32))
+    assert out.tolist() == [[2.0, -2.0, 0.0], [1.0, 224.0, 2.0 ** -10]]
