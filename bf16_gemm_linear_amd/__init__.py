@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
+    "slide_prune_pack", "slide_quant_fp8_rows",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
     "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
 ]
@@ -59,6 +60,8 @@ _SIGS = {
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "sp24_slide_prune_pack": [_vp, _i64, _i64, _int, _vp, _vp],
+    "sp24_slide_quant_fp8_rows": [_vp, _i64, _i64, _int, _vp, _vp, _vp],
     "sp24_gemm_rows": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
     "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
@@ -294,6 +297,38 @@ def quant_fp8_rows(x: torch.Tensor, out: torch.Tensor | None = None, scales: tor
         raise ValueError("scales must hold %d values" % m)
     _check("sp24_quant_fp8_rows", lib.sp24_quant_fp8_rows(_ptr(x), m, k, _ptr(out), _ptr(scales),
                                                           _stream(x.device)))
+    return out, scales
+
+
+def slide_prune_pack(w: torch.Tensor, n_pat: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
+    """SlideSparse load step: prune a bf16 W [n, k] to (2N-2):2N along k and expand it into
+    the 2:4 weight W' [n, k (2N-2)/N] (bf16) of N-1 overlapping windows per block of 2N."""
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    kp = k // (2 * n_pat) * 4 * (n_pat - 1)
+    if out is None:
+        out = torch.empty(n, max(kp, 1), dtype=torch.bfloat16, device=w.device)
+    _need(out, "out", torch.bfloat16, 2, w.device)
+    _check("sp24_slide_prune_pack", lib.sp24_slide_prune_pack(_ptr(w), n, k, n_pat, _ptr(out),
+                                                              _stream(w.device)))
+    return out
+
+
+def slide_quant_fp8_rows(x: torch.Tensor, n_pat: int = 4, out: torch.Tensor | None = None,
+                         scales: torch.Tensor | None = None):
+    """SlideSparse per-call step: lift a bf16 X [m, k] to the windows of W' and quantise it per
+    token -> (codes uint8 [m, k (2N-2)/N], scales fp32 [m])."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    kp = k // (2 * n_pat) * 4 * (n_pat - 1)
+    if out is None:
+        out = torch.empty(m, max(kp, 1), dtype=torch.uint8, device=x.device)
+    _need(out, "out", _CODE_T, 2, x.device)
+    if scales is None:
+        scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(scales, "scales", torch.float32, 1, x.device)
+    _check("sp24_slide_quant_fp8_rows", lib.sp24_slide_quant_fp8_rows(_ptr(x), m, k, n_pat, _ptr(out),
+                                                                      _ptr(scales), _stream(x.device)))
     return out, scales
 
 

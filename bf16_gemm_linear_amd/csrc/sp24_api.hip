@@ -507,6 +507,38 @@ int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out
   return finish(launch_quant_fp8_rows(static_cast<const uint16_t*>(x_bf16), m, k, q_out, scales_dev, s), s);
 }
 
+int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, void* w_out_bf16,
+                          void* stream) {
+  if (!w_bf16 || !w_out_bf16) return SP24_ERR_NULL;
+  if (n_pat < 3 || n_pat > 8) return SP24_ERR_MODE;
+  if (n < 1 || k < 2 * n_pat || k % (2 * n_pat) != 0 || n > kMaxDim || k > kMaxDim) return SP24_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(w_out_bf16)) return SP24_ERR_ALIGN;
+  const int64_t kp = k / (2 * n_pat) * 4 * (n_pat - 1);
+  if (overlaps(w_bf16, (size_t)n * k * 2, w_out_bf16, (size_t)n * kp * 2)) return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_slide_prune_pack(static_cast<const uint16_t*>(w_bf16), n, k, n_pat,
+                                        static_cast<uint16_t*>(w_out_bf16), s),
+                s);
+}
+
+int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
+                              float* scales_dev, void* stream) {
+  if (!x_bf16 || !q_out || !scales_dev) return SP24_ERR_NULL;
+  if (n_pat < 3 || n_pat > 8) return SP24_ERR_MODE;
+  if (m < 1 || k < 8 || k % 8 != 0 || k % (2 * n_pat) != 0 || m > kMaxDim || k > kMaxDim ||
+      m * k > ((int64_t)1 << 40))
+    return SP24_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(q_out) || ((uintptr_t)scales_dev & 3u)) return SP24_ERR_ALIGN;
+  const int64_t kp = k / (2 * n_pat) * 4 * (n_pat - 1);
+  const size_t xb = (size_t)m * k * 2, qb = (size_t)m * kp, sb = (size_t)m * 4;
+  if (overlaps(q_out, qb, x_bf16, xb) || overlaps(scales_dev, sb, x_bf16, xb) ||
+      overlaps(scales_dev, sb, q_out, qb))
+    return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_slide_quant_rows(static_cast<const uint16_t*>(x_bf16), m, k, n_pat, q_out, scales_dev, s),
+                s);
+}
+
 int sp24_gemm_rows(int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
                    const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                    void* ws, size_t ws_bytes, void* stream) {

@@ -179,6 +179,30 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
 int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
                         void* stream);
 
+/* SlideSparse ("SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity",
+ * technical summary, section 2): a (2N-2):2N weight on the 2:4 path.
+ *
+ * sp24_slide_prune_pack: prune W [n, k] (bf16) to (2N-2):2N along k (the 2N-2
+ * largest magnitudes of every block of 2N, ties to the lower index) and write
+ * the expanded weight W' [n, k'] (bf16), k' = k (2N-2)/N: block b becomes N-1
+ * groups of 4, group j holding the values of window j (block positions 2j ..
+ * 2j+3) that it owns, zeros elsewhere.  Window j owns the nonzero values at
+ * positions 2j, 2j+1, then fills up to two from positions 2j+2, 2j+3 (the last
+ * window owns whatever remains).  W' is 2:4 along k', so sp24_prune_compress
+ * of W' keeps every value; multiply it with X' from sp24_slide_quant_fp8_rows.
+ *   n_pat = N in [3, 8] (6:8 is N = 4); k % (2N) == 0.  Errors: SP24_ERR_MODE
+ *   for N, the usual ones otherwise. */
+int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, void* w_out_bf16,
+                          void* stream);
+
+/* Activation lifting fused into per-token quantisation: X [m, k] (bf16) ->
+ * E4M3 codes of X' [m, k'] with X'[r, b*4(N-1) + 4j + p] = X[r, b*2N + 2j + p],
+ * and scales_dev[r] = fp32(amax(|x[r, :]|) / 448) as sp24_quant_fp8_rows (the
+ * lifted row has the same maximum), so X' . W'^T = X . W^T.
+ *   k % 8 == 0 and k % (2N) == 0; q_out [m, k']; scales_dev [m]. */
+int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
+                              float* scales_dev, void* stream);
+
 /* Y = X . W^T as sp24_gemm with dtype SP24_FP8_E4M3, except that X carries one
  * scale per row: y[r, :] = bf16_rne(acc[r, :] * fp32(x_scales_dev[r] * sw)).
  *   x E4M3 [m, k] (from sp24_quant_fp8_rows); x_scales_dev [m] fp32; the rest,

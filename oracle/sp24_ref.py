@@ -353,3 +353,86 @@ def within_tolerance(y, ref, mag, rel=8e-3, absmag=1e-4):
     """Elementwise test ``|y - ref| <= rel*|ref| + absmag*mag`` (y: the BF16 output as float)."""
     y = np.asarray(y, dtype=np.float64)
     return np.abs(y - ref) <= rel * np.abs(ref) + absmag * mag
+
+
+# ----------------------------------------------------------------------------
+# SlideSparse: (2N-2):2N weights on 2:4 hardware ("SlideSparse: Fast and
+# Flexible (2N-2):2N Structured Sparsity", technical summary, section 2)
+# ----------------------------------------------------------------------------
+
+
+def slide_prune_mask(w_bits: np.ndarray, n_pat: int) -> np.ndarray:
+    """Keep the 2N-2 largest |w| of every block of 2N along K (ties to the lower
+    index, exact bf16 magnitudes, as for 2:4): the (2N-2):2N pattern."""
+    w = np.asarray(w_bits, dtype=np.uint16)
+    rows, k = w.shape
+    blk = 2 * n_pat
+    if k % blk:
+        raise ValueError("K must be a multiple of 2N")
+    a = (w & np.uint16(0x7FFF)).astype(np.int64).reshape(rows, k // blk, blk)
+    # rank of each value: how many beat it (larger, or equal at a lower index)
+    rank = np.zeros(a.shape, dtype=np.int64)
+    for i in range(blk):
+        for j in range(blk):
+            if i == j:
+                continue
+            beats = (a[..., j] > a[..., i]) | ((a[..., j] == a[..., i]) & (j < i))
+            rank[..., i] += beats
+    return (rank < blk - 2).reshape(rows, k)
+
+
+def slide_windows(nonzero: np.ndarray, n_pat: int):
+    """Assign the nonzero positions of one block of 2N to the N-1 windows of 4
+    at stride 2 (window j covers block positions 2j .. 2j+3), at most 2 per
+    window.  Window j first takes what no later window can (positions 2j,
+    2j+1), then fills up from positions 2j+2, 2j+3 in ascending order; what it
+    cannot hold spills into the next window.  Returns the window of every
+    position (-1 for zeros); raises if the block does not fit."""
+    nz = [bool(v) for v in nonzero]
+    if len(nz) != 2 * n_pat:
+        raise ValueError("a block holds 2N values")
+    owner = [-1] * (2 * n_pat)
+    for j in range(n_pat - 1):
+        must = [p for p in (2 * j, 2 * j + 1) if nz[p] and owner[p] < 0]
+        last = j == n_pat - 2
+        may = [p for p in (2 * j + 2, 2 * j + 3) if nz[p] and owner[p] < 0]
+        if last:
+            must += may
+            may = []
+        if len(must) > 2:
+            raise ValueError("block has more than 2N-2 nonzeros that fit: %s" % nonzero)
+        take = must + may[: 2 - len(must)]
+        for p in take:
+            owner[p] = j
+    return owner
+
+
+def slide_pack(w: np.ndarray, n_pat: int) -> np.ndarray:
+    """The expanded weight W' [rows, K * (2N-2)/N] of a (2N-2):2N weight: block b
+    of 2N values becomes N-1 groups of 4, group j holding the values its window
+    owns at window positions 0..3 and zero elsewhere (any element type; zero
+    bits are the zero value)."""
+    w = np.asarray(w)
+    rows, k = w.shape
+    blk, grp = 2 * n_pat, 4 * (n_pat - 1)
+    out = np.zeros((rows, k // blk * grp), dtype=w.dtype)
+    zero = np.zeros((), dtype=w.dtype)
+    for r in range(rows):
+        for b in range(k // blk):
+            block = w[r, b * blk:(b + 1) * blk]
+            owner = slide_windows(block != zero, n_pat)
+            for p, j in enumerate(owner):
+                if j >= 0:
+                    out[r, b * grp + 4 * j + (p - 2 * j)] = block[p]
+    return out
+
+
+def slide_lift(x: np.ndarray, n_pat: int) -> np.ndarray:
+    """Activation lifting: X' [M, K * (2N-2)/N] with X'[m, b*4(N-1) + 4j + p] =
+    X[m, b*2N + 2j + p], so that X' W'^T = X W^T (any element type)."""
+    x = np.asarray(x)
+    rows, k = x.shape
+    blk, grp = 2 * n_pat, 4 * (n_pat - 1)
+    idx = np.array([b * blk + 2 * j + p for b in range(k // blk) for j in range(n_pat - 1) for p in range(4)])
+    assert idx.size == k // blk * grp
+    return x[:, idx]

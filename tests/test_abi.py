@@ -321,3 +321,19 @@ def test_gemm_rows_validation():
     assert g(xs=A + 0x100002) == EALIGN
     # the output may not overlap any of the m row scales (m * 4 bytes)
     assert g(xs=A + 0x500000 - 16, m=8) == EALIAS
+
+
+def test_slide_validation():
+    pk = lambda w=A, n=4, k=64, np_=4, out=A + 0x100000: lib.sp24_slide_prune_pack(p(w), n, k, np_, p(out), None)
+    assert pk(w=None) == ENULL and pk(out=None) == ENULL
+    assert pk(np_=2) == EMODE and pk(np_=9) == EMODE
+    assert pk(k=60) == ESHAPE and pk(n=0) == ESHAPE
+    assert pk(w=A + 4) == EALIGN
+    assert pk(out=A + 0x100) == EALIAS
+    qz = lambda x=A, m=2, k=64, np_=4, q=A + 0x100000, s=A + 0x200000: lib.sp24_slide_quant_fp8_rows(
+        p(x), m, k, np_, p(q), p(s), None)
+    assert qz(x=None) == ENULL and qz(s=None) == ENULL
+    assert qz(np_=1) == EMODE
+    assert qz(k=60) == ESHAPE and qz(k=36, np_=3) == ESHAPE     # 36 % 8 != 0
+    assert qz(q=A + 8) == EALIGN
+    assert qz(s=A + 0x10) == EALIAS

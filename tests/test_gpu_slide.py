@@ -1,0 +1,74 @@
+"""GPU parity of the SlideSparse path ("SlideSparse: Fast and Flexible
+(2N-2):2N Structured Sparsity"): the packed weight and the lifted codes are
+bit-exact with the oracle, and the 2:4 GEMM over K' gives the (2N-2):2N
+product over K within the GEMM tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import DEV, announce, assert_within_tolerance, bits, codes, f32, f32_bits, need_sp, u32
+from oracle import sp24_ref as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_pack(wb, n_pat):
+    return O.slide_pack(O.apply_mask(wb, O.slide_prune_mask(wb, n_pat)), n_pat)
+
+
+@pytest.mark.parametrize("n,k,n_pat", [(5, 64, 4), (33, 4096, 4), (7, 96, 3), (9, 160, 5), (4, 256, 8)])
+def test_prune_pack_bit_exact(n, k, n_pat):
+    sp = need_sp()
+    rng = np.random.default_rng(n * k + n_pat)
+    alphabet = np.array([0.0, -0.0, 1.0, -1.0, 2.0, -2.0, 3.0], dtype=np.float32)
+    for what, w in (("normal", W.randn_bf16((n, k), seed=n + k, std=0.02)),
+                    ("ties", torch.from_numpy(rng.choice(alphabet, size=(n, k))).to(torch.bfloat16))):
+        announce("slide_prune_pack", what, n, k, n_pat)
+        wp = sp.slide_prune_pack(w.to(DEV), n_pat)
+        torch.cuda.synchronize()
+        ref = _oracle_pack(W.bf16_bits(w), n_pat)
+        got = bits(wp)
+        assert np.array_equal(got, ref), "%s: %d values differ" % (what, int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("m,k,n_pat", [(1, 4096, 4), (16, 14336, 4), (5, 96, 3), (3, 160, 5)])
+def test_lift_quant_bit_exact(m, k, n_pat):
+    sp = need_sp()
+    x = W.randn_bf16((m, k), seed=m + k).float()
+    if m > 2:
+        x[1] *= 300.0
+    x = x.to(torch.bfloat16)
+    announce("slide_quant_fp8_rows", m, k, n_pat)
+    q, s = sp.slide_quant_fp8_rows(x.to(DEV), n_pat)
+    torch.cuda.synchronize()
+    oq, os_ = O.quant_fp8_rows(W.bf16_bits(x))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(codes(q), O.slide_lift(oq, n_pat))
+
+
+# (m, n, k): stream without and with split-K, tiled
+@pytest.mark.parametrize("m,n,k", [(1, 14336, 4096), (16, 1024, 4096), (64, 2048, 2048), (512, 16384, 1024)])
+def test_slide_gemm_matches_the_6_of_8_product(m, n, k):
+    sp = need_sp()
+    n_pat = 4
+    w = W.randn_bf16((n, k), seed=n + k, std=0.02)
+    x = W.randn_bf16((m, k), seed=m + k + 1)
+    kp = k * (2 * n_pat - 2) // n_pat
+    announce("slide gemm", m, n, k, "K'", kp, "kernel", sp.plan(sp.OP_GEMM, sp.FP8, m, n, kp)["kernel"])
+    wp = sp.slide_prune_pack(w.to(DEV), n_pat)
+    values, meta = sp.prune_compress(wp)
+    qv, sw = sp.quant_fp8(values)
+    xq, sx = sp.slide_quant_fp8_rows(x.to(DEV), n_pat)
+    y = sp.gemm_rows(xq, qv, meta, sx, sw)
+    torch.cuda.synchronize()
+    # the weight: 6:8 pruned, per-tensor scale (W' holds exactly its nonzero values)
+    wb = W.bf16_bits(w)
+    w68 = O.apply_mask(wb, O.slide_prune_mask(wb, n_pat))
+    wq, osw = O.quant_fp8(w68)
+    assert f32_bits(f32(sw)) == f32_bits(osw)
+    ov, om = O.prune_compress(O.slide_pack(w68, n_pat))
+    assert np.array_equal(u32(meta), O.store_meta(om))      # the 2:4 prune kept every value
+    oxq, oxs = O.quant_fp8_rows(W.bf16_bits(x))
+    ref, mag = O.gemm_ref(O.dequant_fp8_rows(oxq, oxs), O.dequant_fp8(wq, osw))
+    assert_within_tolerance(bits(y), ref, mag, "slide %dx%dx%d" % (m, n, k))
