@@ -31,6 +31,10 @@ A Production Cookbook"):
   the scale is ``s = fp32(amax / 448)`` (``s = 1`` when amax is 0) and a value is
   quantised as ``e4m3_rne(clamp(fp32(v / s), -448, 448))``.
 
+* INT8 W8A8: the cookbook's table "Precision and sparsity recipes" and its
+  step 6 "INT8 alternative"; symmetric per-tensor scale ``fp32(amax / 127)``
+  and codes ``clamp(round_half_even(fp32(v / s)), -127, 127)`` are a reading.
+
 Representation: bfloat16 tensors are passed as ``numpy.uint16`` bit patterns,
 FP8-E4M3 tensors as ``numpy.uint8`` codes, metadata as ``numpy.uint32`` words.
 
@@ -292,6 +296,46 @@ def quant_fp8(v_bits: np.ndarray, scale=None):
 def dequant_fp8(codes: np.ndarray, scale) -> np.ndarray:
     """float64 values ``scale * decode(code)`` represented by E4M3 codes."""
     return np.float64(np.float32(scale)) * e4m3_decode(codes)
+
+
+# ----------------------------------------------------------------------------
+# INT8 W8A8 (symmetric, per tensor): the cookbook's table "Precision and
+# sparsity recipes" lists INT8 W8A8 beside 2:4 + FP8, its pipeline step 6 "INT8
+# alternative" re-quantises after pruning, and the SlideSparse page reports INT8
+# results.  No page fixes the INT8 rounding; the reading taken is the FP8 recipe
+# with the format's range: s = fp32(amax / 127) (1 for an all-zero tensor),
+# q = clamp(round_half_even(fp32(v / s)), -127, 127) (never -128).
+# ----------------------------------------------------------------------------
+
+INT8_MAX = 127.0
+
+
+def int8_scale(v_bits: np.ndarray) -> np.float32:
+    """Per-tensor INT8 scale ``fp32(amax / 127)``, or 1 when the tensor is all zero."""
+    amax = np.float32(np.max(np.abs(bf16_to_f32(v_bits)))) if np.size(v_bits) else np.float32(0)
+    if amax == 0:
+        return np.float32(1.0)
+    return np.float32(amax) / np.float32(INT8_MAX)
+
+
+def quant_int8(v_bits: np.ndarray, scale=None):
+    """INT8 codes of bfloat16 values: ``clamp(rne(fp32(v / s)), -127, 127)``, dynamic
+    (``scale=None``) or static scale.  Returns (codes int8, scale)."""
+    s = int8_scale(v_bits) if scale is None else np.float32(scale)
+    t = bf16_to_f32(v_bits) / s
+    assert t.dtype == np.float32
+    r = np.rint(t)                               # IEEE round to nearest, ties to even
+    return np.clip(r, -INT8_MAX, INT8_MAX).astype(np.int8), s
+
+
+def dequant_int8(codes: np.ndarray, scale) -> np.ndarray:
+    """float64 values ``scale * code`` of INT8 codes."""
+    return np.float64(np.float32(scale)) * np.asarray(codes, dtype=np.int8).astype(np.float64)
+
+
+def sparse_operands_int8(xq, x_scale, wq_values, meta, w_scale, k):
+    """Dense float64 operands of the INT8 path: both dequantised, W decompressed."""
+    return dequant_int8(xq, x_scale), dequant_int8(decompress(wq_values, meta, k), w_scale)
 
 
 def quant_fp8_rows(x_bits: np.ndarray):
