@@ -338,6 +338,24 @@ def sparse_operands_int8(xq, x_scale, wq_values, meta, w_scale, k):
     return dequant_int8(xq, x_scale), dequant_int8(decompress(wq_values, meta, k), w_scale)
 
 
+def quant_int8_rows(x_bits: np.ndarray):
+    """Per-token INT8: row m quantised on its own, ``quant_int8(x[m])``.
+    Returns (codes int8 [M, K], scales float32 [M])."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(x.shape[0], dtype=np.float32)
+    for m in range(x.shape[0]):
+        codes[m], scales[m] = quant_int8(x[m])
+    return codes, scales
+
+
+def sparse_operands_int8_rows(xq, x_scales, wq_values, meta, w_scale, k):
+    """Dense float64 operands of the INT8 path with one scale per X row."""
+    xs = np.asarray(x_scales, dtype=np.float32).astype(np.float64)[:, None]
+    return xs * np.asarray(xq, dtype=np.int8).astype(np.float64), dequant_int8(decompress(wq_values, meta, k),
+                                                                                 w_scale)
+
+
 def quant_fp8_rows(x_bits: np.ndarray):
     """Quantise each row (token) of X ``[M, K]`` with its own dynamic scale.
 

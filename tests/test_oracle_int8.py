@@ -46,3 +46,36 @@ def test_random_matches_torch_round(rng):
     assert np.abs(q).max() == 127
     # dequantised values within half a step of the input
     assert np.all(np.abs(O.dequant_int8(q, s) - O.bf16_to_f64(x)) <= 0.5 * s + 1e-12)
+
+
+def test_rows_are_independent_and_one_row_is_per_tensor(rng):
+    x = rng.standard_normal((4, 96)).astype(np.float32)
+    x[1] *= 300.0                                    # an outlier row does not touch the others
+    x[3] = 0.0                                       # a zero row gets scale 1 and zero codes
+    xb = _bits(x)
+    q, s = O.quant_int8_rows(xb)
+    for m in range(4):
+        qm, sm = O.quant_int8(xb[m])
+        assert s[m] == sm and np.array_equal(q[m], qm)
+    assert s[3] == 1.0 and not q[3].any()
+    assert np.abs(q[[0, 1, 2]]).max(axis=1).tolist() == [127, 127, 127]
+
+
+def test_int8_product_is_the_integer_product(rng):
+    """The dequantised product equals sx * sw * (integer dot product), up to float64
+    rounding of the dequantised terms (each (sx qx)(sw qw) needs up to 64 bits)."""
+    k = 256
+    x = _bits(rng.standard_normal((3, k)).astype(np.float32))
+    w = _bits(rng.standard_normal((5, k)).astype(np.float32))
+    vals, meta = O.prune_compress(w)
+    wq, sw = O.quant_int8(vals)
+    xq, sx = O.quant_int8(x)
+    xh, wh = O.sparse_operands_int8(xq, sx, wq, meta, sw, k)
+    ref, mag = O.gemm_ref(xh, wh)
+    wd = O.decompress(wq, meta, k).astype(np.int64)
+    exact = xq.astype(np.int64) @ wd.T                       # integer arithmetic
+    want = np.float64(sx) * np.float64(sw) * exact.astype(np.float64)
+    assert np.all(np.abs(ref - want) <= 1e-13 * mag)
+    assert np.abs(exact).max() > 1000                        # a real sum, not a trivial one
+    # the decompressed INT8 weight holds the kept codes at their positions and zeros elsewhere
+    assert (np.count_nonzero(wd.reshape(5, -1, 4), axis=2) <= 2).all()
