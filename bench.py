@@ -13,6 +13,9 @@ the weight quantisation) is timed separately and reported under "load_path".
 --workload prefill: the M=8192, K=8192, N=28672 GEMM (bound: matrix cores).
 --workload layers: 32 layers x (QKV, O, gate+up, down) at M=256, 128 sequential
 sparse GEMMs per step (see run_layers).
+--dtype int8: up, down or prefill with symmetric per-tensor INT8 codes (the
+cookbook's INT8 W8A8 recipe): a step is sp24_quant_int8 of X and the INT8
+sparse GEMM (exact int32 sums); the roofline peak is the dense INT8 MFMA rate.
 
 Inputs are seeded synthetic tensors (workloads/) resident in HBM before the
 timed region.  Each call reads a different one of R weight copies (> 2x the
@@ -37,7 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse GEMM TFLOP/s + GB/s and % of roofline vs dense MFMA, decode & prefill"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA; equal to SMFMAC's rate of nonzero MACs
+FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (and INT8: 5.0 POP/s); SMFMAC's rate of nonzero MACs
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="up", choices=["up", "down", "prefill", "layers", "slide"])
-    ap.add_argument("--dtype", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--dtype", default="fp8", choices=["fp8", "int8", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=0,
@@ -134,8 +137,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    fp8 = args.dtype == "fp8"
-    dt = sp.FP8 if fp8 else sp.BF16
+    kind = args.dtype
+    fp8 = kind != "bf16"  # one-byte codes with per-tensor scales: E4M3 or INT8
+    dt = {"fp8": sp.FP8, "int8": sp.INT8, "bf16": sp.BF16}[kind]
+    quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
+    code_t = torch.int8 if kind == "int8" else torch.uint8
+    label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
+    if kind == "int8" and args.workload in ("slide", "layers"):
+        print("--dtype int8 is measured on the up, down and prefill workloads", file=sys.stderr)
+        sys.exit(2)
     ev = Events(torch)
 
     # ---------------------------------------------------------------- workload
@@ -145,15 +155,14 @@ def main():
         w_cpu = W.up_weight() if args.workload == "up" else W.down_weight()
         xs_cpu = {m: (W.up_x(m) if args.workload == "up" else W.down_x(m)) for m in Ms}
         desc = ("decode FFN %s-projection, 2:4 sparse %s, M=%s tokens, K=%d, N=%d"
-                % (args.workload, "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16",
+                % (args.workload, label,
                    "/".join(map(str, Ms)), K, N))
         bound = "hbm"
     elif args.workload == "prefill":
         K, N, Ms = W.PREFILL["K"], W.PREFILL["N"], [W.PREFILL["M"]]
         w_cpu = W.prefill_weight()
         xs_cpu = {Ms[0]: W.prefill_x()}
-        desc = "prefill GEMM, 2:4 sparse %s, M=%d, K=%d, N=%d" % (
-            "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16", Ms[0], K, N)
+        desc = "prefill GEMM, 2:4 sparse %s, M=%d, K=%d, N=%d" % (label, Ms[0], K, N)
         bound = "mfma"
     elif args.workload == "slide":
         print(json.dumps(run_slide(args, torch, np, sp, W, ev, dev)))
@@ -169,11 +178,11 @@ def main():
     meta = torch.empty(N * (K // 32), dtype=torch.int32, device=dev)
     sp.prune_compress(w, values, meta)  # first launch loads the code object: not timed
     t_prune = ev.time(lambda i: sp.prune_compress(w, values, meta), 5) / 5
-    qv, sw = (sp.quant_fp8(values) if fp8 else (values, None))
+    qv, sw = (quant(values) if fp8 else (values, None))
     if fp8:
         qbuf = torch.empty_like(qv)
-        sp.quant_fp8(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC)
-        t_wq = ev.time(lambda i: sp.quant_fp8(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC), 5) / 5
+        quant(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC)
+        t_wq = ev.time(lambda i: quant(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC), 5) / 5
     else:
         t_wq = 0.0
     torch.cuda.synchronize()
@@ -196,13 +205,13 @@ def main():
     for m in Ms:
         b = {"y": torch.empty(m, N, dtype=torch.bfloat16, device=dev)}
         if fp8:
-            b["xq"] = torch.empty(m, K, dtype=torch.uint8, device=dev)
+            b["xq"] = torch.empty(m, K, dtype=code_t, device=dev)
             b["sx"] = torch.empty(1, dtype=torch.float32, device=dev)
             nb = sp.workspace_size(sp.OP_QUANT, sp.BF16, m * K, 1, 1)
             b["qws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         nb = sp.workspace_size(sp.OP_GEMM, dt, m, N, K)
         b["gws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
-        if fp8:  # quantise + GEMM in one call (X quantised inside the kernel at M = 1)
+        if kind == "fp8":  # quantise + GEMM in one call (X quantised inside the kernel at M = 1)
             nb = sp.workspace_size(sp.OP_GEMM_QX, dt, m, N, K)
             b["qxws"] = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         b["plan"] = sp.plan(sp.OP_GEMM, dt, m, N, K)
@@ -211,7 +220,7 @@ def main():
     def call_quant(m):
         b = bufs[m]
         if fp8:
-            sp.quant_fp8(xs[m], scale=b["sx"], out=b["xq"], ws=b["qws"], mode=sp.SCALE_DYNAMIC)
+            quant(xs[m], scale=b["sx"], out=b["xq"], ws=b["qws"], mode=sp.SCALE_DYNAMIC)
 
     def call_gemm(m, r):
         b = bufs[m]
@@ -222,11 +231,12 @@ def main():
             sp.gemm(xs[m], wq_copies[r], meta_copies[r], out=b["y"], ws=b["gws"])
 
     def call_step(m, r):
-        """One step's work for M tokens: quantise X (FP8) and the sparse GEMM."""
+        """One step's work for M tokens: quantise X (FP8, INT8) and the sparse GEMM."""
         b = bufs[m]
-        if fp8:
+        if kind == "fp8":
             sp.gemm_qx(xs[m], wq_copies[r], meta_copies[r], sw, x_scale=b["sx"], out=b["y"], ws=b["qxws"])
         else:
+            call_quant(m)
             call_gemm(m, r)
 
     def step(r):
@@ -336,35 +346,38 @@ def main():
         achieved = tot_b / tot_t / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": counted_traffic(args.workload, "hbm") if fp8 else None,
+                    "traffic": counted_traffic(args.workload, "hbm") if kind == "fp8" else None,
                     "kernel": "%s (sparse %s), mean over M=%s"
                               % ("/".join(sorted({KERNEL_NAMES[bufs[m]["plan"]["kernel"]] for m in Ms})),
-                                 "fp8" if fp8 else "bf16", "/".join(map(str, Ms)))}
+                                 kind, "/".join(map(str, Ms)))}
     else:
         m = Ms[0]
         eff = per_m[m]["tflops_effective"]
         peak = FP8_DENSE_PEAK_TFLOPS if fp8 else BF16_DENSE_PEAK_TFLOPS
-        roofline = {"bound": "mfma", "achieved": eff, "peak": peak, "unit": "TFLOP/s",
+        roofline = {"bound": "mfma", "achieved": eff, "peak": peak,
+                    "unit": "TOP/s" if kind == "int8" else "TFLOP/s",
                     "frac": eff / peak,
-                    "traffic": counted_traffic(args.workload, "mfma") if fp8 else None,
+                    "traffic": counted_traffic(args.workload, "mfma") if kind == "fp8" else None,
                     "kernel": "sparse GEMM, nonzero MACs x2 per second vs the dense %s MFMA peak"
-                              % ("FP8" if fp8 else "BF16")}
+                              % kind.upper()}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline and bound == "hbm":
-        cpu = cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes)
+        cpu = cpu_baseline(w_cpu, xs_cpu, Ms, N, K, kind, step_bytes)
 
     out = {
         "metric": METRIC,
         "value": value_gbs if bound == "hbm" else step_flops / 2 / (ms_per_step / 1e3) / 1e12,
-        "unit": "GB/s" if bound == "hbm" else "TFLOP/s (nonzero MACs x2)",
+        "unit": "GB/s" if bound == "hbm" else ("TOP/s" if kind == "int8" else "TFLOP/s") + " (nonzero MACs x2)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "dtype": {"fp8": "fp8_e4m3", "int8": "int8", "bf16": "bf16"}[kind],
         "data": "synthetic (seeded, workloads/)",
         "config": {"workload": desc, "M": Ms, "K": K, "N": N, "weight_copies": R,
-                   "step": "per M: sp24_gemm_qx (quantise X + sparse GEMM; one launch at M=1)" if fp8 else "per M: sparse GEMM"},
+                   "step": {"fp8": "per M: sp24_gemm_qx (quantise X + sparse GEMM; one launch at M=1)",
+                            "int8": "per M: sp24_quant_int8 + sparse INT8 GEMM",
+                            "bf16": "per M: sparse GEMM"}[kind]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_m": {str(m): per_m[m] for m in Ms},
@@ -626,7 +639,7 @@ def cpu_layer_baseline(W, fp8, call_bytes):
                       "decompress W, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
 
 
-def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes):
+def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, kind, step_bytes):
     """The CPU oracle's per-call path on the same inputs: quantise X and the float64
     product over the decompressed weight, one full step (all M) per repetition."""
     import numpy as np
@@ -640,15 +653,20 @@ def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, fp8, step_bytes):
         threads = 1
     wb = W.bf16_bits(w_cpu)
     v, meta = O.prune_compress(wb)            # load path, not timed
-    if fp8:
+    if kind == "fp8":
         vq, sw = O.quant_fp8(v)
+    elif kind == "int8":
+        vq, sw = O.quant_int8(v)
     xb = {m: W.bf16_bits(xs_cpu[m]) for m in Ms}
     reps, t0 = 0, time.perf_counter()
     while True:
         for m in Ms:
-            if fp8:
+            if kind == "fp8":
                 xq, sx = O.quant_fp8(xb[m])
                 ref, mag = O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, K))
+            elif kind == "int8":
+                xq, sx = O.quant_int8(xb[m])
+                ref, mag = O.gemm_ref(*O.sparse_operands_int8(xq, sx, vq, meta, sw, K))
             else:
                 ref, mag = O.gemm_ref(*O.sparse_operands_bf16(xb[m], v, meta, K))
         reps += 1

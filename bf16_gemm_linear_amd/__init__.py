@@ -10,6 +10,9 @@ there is no fallback.
     values, meta = prune_compress(w)                    # w: [n, k] bf16 on the GPU
     xq, sx = quant_fp8(x)                               # per-tensor dynamic scale
     y = gemm(xq, values_q, meta, x_scale=sx, w_scale=sw)
+
+The operand type follows the tensors: bfloat16, E4M3 codes (torch.uint8 or
+torch.float8_e4m3fn) or INT8 codes (torch.int8, from quant_int8).
 """
 from __future__ import annotations
 
@@ -19,14 +22,15 @@ import os
 import torch
 
 __all__ = [
-    "BF16", "FP8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
+    "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
     "slide_prune_pack", "slide_quant_fp8_rows",
+    "quant_int8", "quant_int8_rows",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
     "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
 ]
 
-BF16, FP8 = 0, 1
+BF16, FP8, INT8 = 0, 1, 2
 SCALE_DYNAMIC, SCALE_STATIC = 0, 1
 OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX = 0, 1, 2, 3
 
@@ -56,13 +60,15 @@ _SIGS = {
     "sp24_decompress": [_int, _vp, _vp, _i64, _i64, _vp, _vp],
     "sp24_check_meta": [_vp, _i64, _i64, _vp, _vp],
     "sp24_quant_fp8": [_vp, _i64, _vp, _vp, _int, _vp, _sz, _vp],
+    "sp24_quant_int8": [_vp, _i64, _vp, _vp, _int, _vp, _sz, _vp],
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "sp24_quant_int8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_slide_prune_pack": [_vp, _i64, _i64, _int, _vp, _vp],
     "sp24_slide_quant_fp8_rows": [_vp, _i64, _i64, _int, _vp, _vp, _vp],
-    "sp24_gemm_rows": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_gemm_rows": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
     "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
     "sp24_status_string": [_int],
@@ -125,10 +131,17 @@ def _need(t, name, dtype=None, ndim=None, device=None):
 
 _FP8_T = torch.float8_e4m3fn
 _CODE_T = (torch.uint8, torch.float8_e4m3fn)
+_ANY_T = (torch.bfloat16, torch.int8) + _CODE_T
 
 
 def _dtype_of(t):
-    return BF16 if t.dtype == torch.bfloat16 else FP8
+    """Library dtype of an operand tensor: bf16, int8 codes, else E4M3 codes."""
+    return BF16 if t.dtype == torch.bfloat16 else INT8 if t.dtype == torch.int8 else FP8
+
+
+def _tensor_types(dt):
+    """torch dtypes accepted for operands of library dtype `dt`."""
+    return torch.bfloat16 if dt == BF16 else torch.int8 if dt == INT8 else _CODE_T
 
 
 def workspace_size(op: int, dtype: int, m: int, n: int, k: int) -> int:
@@ -177,15 +190,17 @@ def prune_compress(w: torch.Tensor, values: torch.Tensor | None = None,
 
 
 def decompress(values: torch.Tensor, meta: torch.Tensor, k: int, out: torch.Tensor | None = None):
-    """Dense pruned W [n, k] from (values, meta); bf16 values give bf16, E4M3 codes give uint8 codes."""
-    _need(values, "values", (torch.bfloat16,) + _CODE_T, 2)
+    """Dense pruned W [n, k] from (values, meta); bf16 values give bf16, E4M3 codes give uint8
+    codes, INT8 codes give int8 codes."""
+    _need(values, "values", _ANY_T, 2)
     _need(meta, "meta", torch.int32, 1, values.device)
     n = values.shape[0]
     _meta_size(meta, n, k)
-    dt = BF16 if values.dtype == torch.bfloat16 else FP8
+    dt = _dtype_of(values)
     if out is None:
-        out = torch.empty(n, k, dtype=torch.bfloat16 if dt == BF16 else torch.uint8, device=values.device)
-    _need(out, "out", torch.bfloat16 if dt == BF16 else _CODE_T, 2, values.device)
+        t = torch.bfloat16 if dt == BF16 else torch.int8 if dt == INT8 else torch.uint8
+        out = torch.empty(n, k, dtype=t, device=values.device)
+    _need(out, "out", _tensor_types(dt), 2, values.device)
     _check("sp24_decompress",
            lib.sp24_decompress(dt, _ptr(values), _ptr(meta), n, k, _ptr(out), _stream(values.device)))
     return out
@@ -236,11 +251,37 @@ def quant_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Ten
     return out, scale
 
 
+def quant_int8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, mode: int | None = None):
+    """Per-tensor symmetric INT8 quantisation of a bf16 tensor -> (codes int8, scale fp32[1]):
+    s = amax/127 (dynamic) or the given device scalar (static), q = clamp(rne(x/s), -127, 127)."""
+    _need(x, "x", torch.bfloat16)
+    count = x.numel()
+    if mode is None:
+        mode = SCALE_DYNAMIC if scale is None else SCALE_STATIC
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _need(out, "out", torch.int8, None, x.device)
+    if out.numel() != count:
+        raise ValueError("out has the wrong size")
+    if scale is None:
+        if mode == SCALE_STATIC:
+            raise ValueError("static mode needs a scale")
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(scale, "scale", torch.float32, None, x.device)
+    nbytes = workspace_size(OP_QUANT, BF16, count, 1, 1) if mode == SCALE_DYNAMIC else 0
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_quant_int8",
+           lib.sp24_quant_int8(_ptr(x), count, _ptr(out), _ptr(scale), mode, _ptr(ws), nbytes,
+                               _stream(x.device)))
+    return out, scale
+
+
 def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
-    _need(x, "x", (torch.bfloat16,) + _CODE_T, 2)
-    dt = BF16 if x.dtype == torch.bfloat16 else FP8
+    _need(x, "x", _ANY_T, 2)
+    dt = _dtype_of(x)
     m, k = x.shape
-    _need(w, "w", torch.bfloat16 if dt == BF16 else _CODE_T, 2, x.device)
+    _need(w, "w", _tensor_types(dt), 2, x.device)
     n = w.shape[0]
     if sparse:
         _need(meta, "meta", torch.int32, 1, x.device)
@@ -249,9 +290,9 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
         _meta_size(meta, n, k)
     elif w.shape[1] != k:
         raise ValueError("w has %d columns, x has %d" % (w.shape[1], k))
-    if dt == FP8:
+    if dt != BF16:
         if x_scale is None or w_scale is None:
-            raise ValueError("FP8 operands need x_scale and w_scale")
+            raise ValueError("FP8 and INT8 operands need x_scale and w_scale")
         _need(x_scale, "x_scale", torch.float32, None, x.device)
         _need(w_scale, "w_scale", torch.float32, None, x.device)
     if out is None:
@@ -262,8 +303,8 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
     op = OP_GEMM if sparse else OP_DENSE_GEMM
     nbytes = workspace_size(op, dt, m, n, k)
     ws = _workspace(nbytes, x.device, ws)
-    xs = _ptr(x_scale) if dt == FP8 else None
-    wsc = _ptr(w_scale) if dt == FP8 else None
+    xs = _ptr(x_scale) if dt != BF16 else None
+    wsc = _ptr(w_scale) if dt != BF16 else None
     if sparse:
         st = lib.sp24_gemm(dt, m, n, k, _ptr(x), xs, _ptr(w), _ptr(meta), wsc, _ptr(out), _ptr(ws),
                            nbytes, _stream(x.device))
@@ -300,6 +341,26 @@ def quant_fp8_rows(x: torch.Tensor, out: torch.Tensor | None = None, scales: tor
     return out, scales
 
 
+def quant_int8_rows(x: torch.Tensor, out: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Per-token INT8 quantisation of a bf16 X [m, k] (k % 8 == 0) -> (codes int8 [m, k],
+    scales fp32 [m]): row r is quantised with its own dynamic scale amax_r / 127."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty(m, k, dtype=torch.int8, device=x.device)
+    _need(out, "out", torch.int8, 2, x.device)
+    if tuple(out.shape) != (m, k):
+        raise ValueError("out must be [%d, %d]" % (m, k))
+    if scales is None:
+        scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(scales, "scales", torch.float32, 1, x.device)
+    if scales.numel() != m:
+        raise ValueError("scales must hold %d values" % m)
+    _check("sp24_quant_int8_rows", lib.sp24_quant_int8_rows(_ptr(x), m, k, _ptr(out), _ptr(scales),
+                                                            _stream(x.device)))
+    return out, scales
+
+
 def slide_prune_pack(w: torch.Tensor, n_pat: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
     """SlideSparse load step: prune a bf16 W [n, k] to (2N-2):2N along k and expand it into
     the 2:4 weight W' [n, k (2N-2)/N] (bf16) of N-1 overlapping windows per block of 2N."""
@@ -333,11 +394,13 @@ def slide_quant_fp8_rows(x: torch.Tensor, n_pat: int = 4, out: torch.Tensor | No
 
 
 def gemm_rows(x, values, meta, x_scales, w_scale, out=None, ws=None):
-    """Y = X . W^T for E4M3 X [m, k] with one scale per row (x_scales fp32 [m], from
-    quant_fp8_rows) and E4M3 compressed weights; bf16 output [m, n]."""
-    _need(x, "x", _CODE_T, 2)
+    """Y = X . W^T for E4M3 or INT8 X [m, k] with one scale per row (x_scales fp32 [m], from
+    quant_fp8_rows / quant_int8_rows) and compressed weights of the same code type; bf16
+    output [m, n]."""
+    _need(x, "x", (torch.int8,) + _CODE_T, 2)
+    dt = _dtype_of(x)
     m, k = x.shape
-    _need(values, "values", _CODE_T, 2, x.device)
+    _need(values, "values", _tensor_types(dt), 2, x.device)
     n = values.shape[0]
     if values.shape[1] * 2 != k:
         raise ValueError("compressed weight shapes do not match k=%d" % k)
@@ -352,9 +415,9 @@ def gemm_rows(x, values, meta, x_scales, w_scale, out=None, ws=None):
     _need(out, "out", torch.bfloat16, 2, x.device)
     if out.shape != (m, n):
         raise ValueError("out must be [%d, %d]" % (m, n))
-    nbytes = workspace_size(OP_GEMM, FP8, m, n, k)
+    nbytes = workspace_size(OP_GEMM, dt, m, n, k)
     ws = _workspace(nbytes, x.device, ws)
-    _check("sp24_gemm_rows", lib.sp24_gemm_rows(m, n, k, _ptr(x), _ptr(x_scales), _ptr(values), _ptr(meta),
+    _check("sp24_gemm_rows", lib.sp24_gemm_rows(dt, m, n, k, _ptr(x), _ptr(x_scales), _ptr(values), _ptr(meta),
                                                 _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
     return out
 

@@ -20,6 +20,12 @@ namespace sp24 {
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// INT8 sums stay exact in int32: at most k products of magnitude <= 127 * 127
+// per output (k/2 kept pairs for the sparse kernels), 16129 * 131072 < 2^31.
+constexpr int64_t kMaxKInt8 = 131072;
+
+bool known_dtype(int dtype) { return dtype == SP24_BF16 || dtype == SP24_FP8_E4M3 || dtype == SP24_INT8; }
+bool scaled_dtype(int dtype) { return dtype == SP24_FP8_E4M3 || dtype == SP24_INT8; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -196,9 +202,10 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   if (out == nullptr) return SP24_ERR_NULL;
   memset(out, 0, sizeof(*out));
   if (op != SP24_OP_GEMM && op != SP24_OP_DENSE_GEMM) return SP24_ERR_MODE;
-  if (dtype != SP24_BF16 && dtype != SP24_FP8_E4M3) return SP24_ERR_DTYPE;
+  if (!known_dtype(dtype)) return SP24_ERR_DTYPE;
   if (m < 1 || n < 1 || k < 128 || k % 128 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim)
     return SP24_ERR_SHAPE;
+  if (dtype == SP24_INT8 && k > kMaxKInt8) return SP24_ERR_SHAPE;
 
   // Large m with enough 256 x 256 tiles to fill the chip: LDS-tiled kernel.
   const int64_t tiles = ((n + 255) / 256) * ((m + 255) / 256);
@@ -389,7 +396,7 @@ int sp24_prune_compress(const void* w_bf16, int64_t n, int64_t k, void* values_b
 
 int sp24_decompress(int dtype, const void* values, const uint32_t* meta, int64_t n, int64_t k,
                     void* w_out, void* stream) {
-  if (dtype != SP24_BF16 && dtype != SP24_FP8_E4M3) return SP24_ERR_DTYPE;
+  if (!known_dtype(dtype)) return SP24_ERR_DTYPE;
   if (!values || !meta || !w_out) return SP24_ERR_NULL;
   if (n < 1 || k < 32 || k % 32 != 0 || n > kMaxDim || k > kMaxDim) return SP24_ERR_SHAPE;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(w_out)) return SP24_ERR_ALIGN;
@@ -408,8 +415,8 @@ int sp24_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad_de
   return finish(launch_check_meta(meta, n, k, bad_dev, s), s);
 }
 
-int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
-                   void* ws, size_t ws_bytes, void* stream) {
+static int quant_common(int dtype, const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev,
+                        int mode, void* ws, size_t ws_bytes, void* stream) {
   if (mode != SP24_SCALE_DYNAMIC && mode != SP24_SCALE_STATIC) return SP24_ERR_MODE;
   if (!x_bf16 || !q_out || !scale_dev) return SP24_ERR_NULL;
   if (count < 1 || count > ((int64_t)1 << 40)) return SP24_ERR_SHAPE;
@@ -424,24 +431,35 @@ int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* sca
                     overlaps(ws, need, scale_dev, 4))))
     return SP24_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return finish(launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), count, q_out, scale_dev, mode,
-                                 need > 0 ? ws : nullptr, s),
+  return finish(launch_quant(dtype, static_cast<const uint16_t*>(x_bf16), count, q_out, scale_dev, mode,
+                             need > 0 ? ws : nullptr, s),
                 s);
+}
+
+int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return quant_common(SP24_FP8_E4M3, x_bf16, count, q_out, scale_dev, mode, ws, ws_bytes, stream);
+}
+
+int sp24_quant_int8(const void* x_bf16, int64_t count, int8_t* q_out, float* scale_dev, int mode,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return quant_common(SP24_INT8, x_bf16, count, reinterpret_cast<uint8_t*>(q_out), scale_dev, mode, ws,
+                      ws_bytes, stream);
 }
 
 static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                        const float* x_scale, const void* w, const uint32_t* meta,
                        const float* w_scale, void* y, void* ws, size_t ws_bytes, void* stream,
                        int xs_step = 0) {
-  if (dtype != SP24_BF16 && dtype != SP24_FP8_E4M3) return SP24_ERR_DTYPE;
+  if (!known_dtype(dtype)) return SP24_ERR_DTYPE;
   if (!x || !w || !y || (sparse && !meta)) return SP24_ERR_NULL;
-  if (dtype == SP24_FP8_E4M3 && (!x_scale || !w_scale)) return SP24_ERR_NULL;
+  if (scaled_dtype(dtype) && (!x_scale || !w_scale)) return SP24_ERR_NULL;
   sp24_plan p;
   int st = plan_gemm(sparse ? SP24_OP_GEMM : SP24_OP_DENSE_GEMM, dtype, m, n, k, &p);
   if (st != SP24_OK) return st;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (sparse && !aligned16(meta)))
     return SP24_ERR_ALIGN;
-  if (dtype == SP24_FP8_E4M3 && (((uintptr_t)x_scale & 3u) || ((uintptr_t)w_scale & 3u)))
+  if (scaled_dtype(dtype) && (((uintptr_t)x_scale & 3u) || ((uintptr_t)w_scale & 3u)))
     return SP24_ERR_ALIGN;
   if (p.workspace_bytes > 0) {
     if (ws == nullptr || ws_bytes < p.workspace_bytes) return SP24_ERR_WORKSPACE;
@@ -454,7 +472,7 @@ static int gemm_common(bool sparse, int dtype, int64_t m, int64_t n, int64_t k, 
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || (sparse && overlaps(y, yb, meta, mb)))
     return SP24_ERR_ALIAS;
   const size_t xsb = xs_step ? (size_t)m * 4 : 4;  // bytes of X scales: one per tensor or per row
-  if (dtype == SP24_FP8_E4M3 && (overlaps(y, yb, x_scale, xsb) || overlaps(y, yb, w_scale, 4)))
+  if (scaled_dtype(dtype) && (overlaps(y, yb, x_scale, xsb) || overlaps(y, yb, w_scale, 4)))
     return SP24_ERR_ALIAS;
   if (p.workspace_bytes > 0 &&
       (overlaps(ws, p.workspace_bytes, y, yb) || overlaps(ws, p.workspace_bytes, x, xb) ||
@@ -493,8 +511,8 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                      ws_bytes, stream);
 }
 
-int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
-                        void* stream) {
+static int quant_rows_common(int dtype, const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out,
+                             float* scales_dev, void* stream) {
   if (!x_bf16 || !q_out || !scales_dev) return SP24_ERR_NULL;
   if (m < 1 || k < 8 || k % 8 != 0 || m > kMaxDim || k > kMaxDim || m * k > ((int64_t)1 << 40))
     return SP24_ERR_SHAPE;
@@ -504,7 +522,17 @@ int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out
       overlaps(scales_dev, sb, q_out, qb))
     return SP24_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return finish(launch_quant_fp8_rows(static_cast<const uint16_t*>(x_bf16), m, k, q_out, scales_dev, s), s);
+  return finish(launch_quant_rows(dtype, static_cast<const uint16_t*>(x_bf16), m, k, q_out, scales_dev, s), s);
+}
+
+int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
+                        void* stream) {
+  return quant_rows_common(SP24_FP8_E4M3, x_bf16, m, k, q_out, scales_dev, stream);
+}
+
+int sp24_quant_int8_rows(const void* x_bf16, int64_t m, int64_t k, int8_t* q_out, float* scales_dev,
+                         void* stream) {
+  return quant_rows_common(SP24_INT8, x_bf16, m, k, reinterpret_cast<uint8_t*>(q_out), scales_dev, stream);
 }
 
 int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, void* w_out_bf16,
@@ -539,10 +567,11 @@ int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pa
                 s);
 }
 
-int sp24_gemm_rows(int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
+int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
                    const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                    void* ws, size_t ws_bytes, void* stream) {
-  return gemm_common(true, SP24_FP8_E4M3, m, n, k, x, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16,
+  if (!scaled_dtype(dtype)) return SP24_ERR_DTYPE;
+  return gemm_common(true, dtype, m, n, k, x, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16,
                      ws, ws_bytes, stream, 1);
 }
 
@@ -594,8 +623,8 @@ int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_s
     return finish(launch_plan(a, p, s), s);
   }
   uint8_t* codes = wsb + wsp.gemm;
-  hipError_t e = launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), m * k, codes, x_scale_dev,
-                                  SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
+  hipError_t e = launch_quant(SP24_FP8_E4M3, static_cast<const uint16_t*>(x_bf16), m * k, codes,
+                              x_scale_dev, SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
   a.x = codes;
   if (e == hipSuccess) e = launch_plan(a, p, s);
   return finish(e, s);

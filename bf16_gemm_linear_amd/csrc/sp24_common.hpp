@@ -8,6 +8,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -28,6 +29,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+
+// INT8 products accumulate exactly in int32; the accumulators live in float
+// registers as bit patterns and become fp32 values once, after the K loop.
+__device__ __forceinline__ float i32_bits_to_f32(float v) { return (float)__builtin_bit_cast(int, v); }
 
 // Two floats -> two E4M3 codes (low byte = a), after a clamp to the format's
 // range; the hardware conversion rounds to nearest even and does not saturate

@@ -26,6 +26,10 @@
 // order, so results are bitwise reproducible.
 //
 // The dense baseline (W uncompressed, dense MFMA) shares the structure.
+//
+// INT8 takes the integer forms of the E4M3 instructions, with the same operand
+// layouts; products are summed exactly in int32 and converted to fp32 once,
+// after the K loop, before the wave reduction.
 #include "sp24_common.hpp"
 #include "sp24_internal.hpp"
 
@@ -51,7 +55,7 @@ __device__ __forceinline__ bf16x16 as_bf16x16(i32x4 a, i32x4 b) {
 template <int DT, bool SPARSE, int T>
 __device__ __forceinline__ int x_piece(int kb, int q, int u, int v) {
   if constexpr (SPARSE) {
-    if constexpr (DT == SP24_FP8_E4M3) {
+    if constexpr (DT != SP24_BF16) {  // one-byte codes (E4M3 or INT8)
       return kb + 32 * T * ((q >> 1) + 2 * v) + 32 * u + 16 * (q & 1);
     } else {
       const int h = v >> 1, half = v & 1;  // instruction h of the unit, B half
@@ -156,6 +160,16 @@ __device__ __forceinline__ void mma_chunk(f32x4 (&acc)[RB][MB], const Chunk<DT, 
           acc[rb][mb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
               as_bf16x8(r.wv[rb][2 * u + 1]), as_bf16x16(r.xv[mb][4 * u + 2], r.xv[mb][4 * u + 3]),
               acc[rb][mb], (int)r.mt[rb][u], 0, 1);
+        } else if constexpr (SPARSE && DT == SP24_INT8) {
+          acc[rb][mb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_smfmac_i32_16x16x128_i8(
+              r.wv[rb][u], cat(r.xv[mb][2 * u], r.xv[mb][2 * u + 1]),
+              __builtin_bit_cast(i32x4, acc[rb][mb]), (int)r.mt[rb][u], 0, 0));
+        } else if constexpr (!SPARSE && DT == SP24_INT8) {
+          // dense INT8: two instructions of K=64, 16 bytes per lane group each
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[rb][mb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                r.wv[rb][2 * u + h], r.xv[mb][2 * u + h], __builtin_bit_cast(i32x4, acc[rb][mb]), 0, 0, 0));
         } else if constexpr (!SPARSE && DT == SP24_FP8_E4M3) {
           acc[rb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               cat(r.wv[rb][2 * u], r.wv[rb][2 * u + 1]), cat(r.xv[mb][2 * u], r.xv[mb][2 * u + 1]),
@@ -229,6 +243,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
       one_chunk<DT, SPARSE, 3, RB, MB>(acc, w, meta, x, n0, m0, kb, lane, N, M, K);
   }
 
+  if constexpr (DT == SP24_INT8)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][mb][i] = i32_bits_to_f32(acc[rb][mb][i]);
+
   // wave tiles -> LDS, element (rb, mb, i, lane) at ((rb*MB + mb)*4 + i)*64 + lane
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -253,8 +275,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
         partial[((size_t)blockIdx.z * M + m) * N + n] = s;
       else
       {
-        // FP8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
-        const float scale = DT == SP24_FP8_E4M3 ? x_scale[(size_t)m * xs_step] * w_scale[0] : 1.0f;
+        // FP8, INT8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
+        const float scale = DT != SP24_BF16 ? x_scale[(size_t)m * xs_step] * w_scale[0] : 1.0f;
         y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s * scale);
       }
     }
@@ -291,6 +313,8 @@ hipError_t launch_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   if (a.dtype == SP24_FP8_E4M3)
     return a.sparse ? launch_dt<SP24_FP8_E4M3, true>(a, p, s) : launch_dt<SP24_FP8_E4M3, false>(a, p, s);
+  if (a.dtype == SP24_INT8)
+    return a.sparse ? launch_dt<SP24_INT8, true>(a, p, s) : launch_dt<SP24_INT8, false>(a, p, s);
   return a.sparse ? launch_dt<SP24_BF16, true>(a, p, s) : launch_dt<SP24_BF16, false>(a, p, s);
 }
 

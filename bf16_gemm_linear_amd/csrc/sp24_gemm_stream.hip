@@ -30,6 +30,8 @@
 // the sparse B operand holds two runs of K (the measured split-half layout),
 // which for fp8 are the unit's bytes [64h + 16q, +16), h = 0, 1.  The bf16
 // and dense variants use the same unit with their own instruction shapes.
+// INT8 takes the integer forms of the fp8 instructions with the same operand
+// layouts; its int32 accumulators become fp32 once, after the K loop.
 //
 // LDS rows are XOR-swizzled in 16-byte pieces so that the 16 rows read by one
 // instruction fall on distinct bank groups; the LDS-DMA load writes lane i's
@@ -48,8 +50,9 @@ template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, i
 struct StreamCfg {
   static constexpr int DT_ = DT, RBW_ = RBW, RB_ = RB, MW_ = MW, KW_ = KW, MB_ = MB, U_ = U;
   static constexpr bool SPARSE_ = SPARSE;
-  static constexpr bool FP8 = DT == SP24_FP8_E4M3;
-  static constexpr int ESZ = FP8 ? 1 : 2;
+  static constexpr bool B8 = DT != SP24_BF16;  // one-byte codes (E4M3 or INT8)
+  static constexpr bool I8 = DT == SP24_INT8;
+  static constexpr int ESZ = B8 ? 1 : 2;
   static constexpr int NW = RBW * MW * KW, NT = NW * 64;
   static constexpr int BN = RBW * RB * 16, BM = MW * MB * 16;  // W rows, X rows per workgroup
   static constexpr int UPS = U * KW;                      // units of 128 K per step
@@ -176,12 +179,12 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
                                            const uint8_t* __restrict__ xs, int xstride, int xlast,
                                            int rg, int mg, int kg, int lane) {
   constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
-  constexpr bool FP8 = C::FP8, SPARSE = C::SPARSE_;
+  constexpr bool B8 = C::B8, I8 = C::I8, SPARSE = C::SPARSE_;
   const int q = lane >> 4, r = lane & 15;
   // A: sparse fp8 1 piece, sparse bf16 2, dense fp8 2, dense bf16 4 per unit
-  constexpr int AP = SPARSE ? (FP8 ? 1 : 2) : (FP8 ? 2 : 4);
+  constexpr int AP = SPARSE ? (B8 ? 1 : 2) : (B8 ? 2 : 4);
   // B: sparse fp8 2 pieces, sparse bf16 4, dense fp8 2, dense bf16 4 per unit and token block
-  constexpr int BP = FP8 ? 2 : 4;
+  constexpr int BP = B8 ? 2 : 4;
   i32x4 a[U][RB][AP];
   uint32_t ix[U][RB];
   i32x4 b[U][MB][BP];
@@ -195,9 +198,9 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
 #pragma unroll
       for (int e = 0; e < AP; ++e) {
         int c;
-        if constexpr (SPARSE && FP8) c = v * C::PWU + q;                 // K [32q, +32)
+        if constexpr (SPARSE && B8) c = v * C::PWU + q;                  // K [32q, +32)
         else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
-        else if constexpr (FP8) c = v * C::PWU + 2 * q + e;              // K [32q, +32)
+        else if constexpr (B8) c = v * C::PWU + 2 * q + e;               // K [32q, +32)
         else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
         a[u][rb][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
       }
@@ -212,12 +215,12 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
 #pragma unroll
       for (int e = 0; e < BP; ++e) {
         int c;
-        if constexpr (SPARSE && FP8) c = v * C::PXU + 4 * e + q;  // run e: bytes [64e + 16q, +16)
+        if constexpr (SPARSE && B8) c = v * C::PXU + 4 * e + q;  // run e: bytes [64e + 16q, +16)
         else if constexpr (SPARSE) {
           // instruction h = e >> 1, run hb = e & 1: K 64hb + 32(q>>1) + 16h + 8(q&1)
           const int h = e >> 1, hb = e & 1;
           c = v * C::PXU + 8 * hb + 4 * (q >> 1) + 2 * h + (q & 1);
-        } else if constexpr (FP8) c = v * C::PXU + 2 * q + e;
+        } else if constexpr (B8) c = v * C::PXU + 2 * q + e;
         else c = v * C::PXU + 4 * e + q;
         b[u][mb][e] = lds16(xr + 16 * swz16<C::PX>(xrow, c));
       }
@@ -231,7 +234,11 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         f32x4& c = acc[rb][mb];
-        if constexpr (SPARSE && FP8) {
+        if constexpr (SPARSE && I8) {
+          c = __builtin_bit_cast(f32x4, __builtin_amdgcn_smfmac_i32_16x16x128_i8(
+                                            a[u][rb][0], cat8(b[u][mb][0], b[u][mb][1]),
+                                            __builtin_bit_cast(i32x4, c), (int)ix[u][rb], 0, 0));
+        } else if constexpr (SPARSE && B8) {
           c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[u][rb][0], cat8(b[u][mb][0], b[u][mb][1]), c,
                                                             (int)ix[u][rb], 0, 0);
         } else if constexpr (SPARSE) {
@@ -241,7 +248,13 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
           c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
               __builtin_bit_cast(bf16x8, a[u][rb][1]),
               __builtin_bit_cast(bf16x16, cat8(b[u][mb][2], b[u][mb][3])), c, (int)ix[u][rb], 0, 1);
-        } else if constexpr (FP8) {
+        } else if constexpr (I8) {
+          // dense INT8: two instructions of K=64 over the lane group's 32 bytes
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            c = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                              a[u][rb][e], b[u][mb][e], __builtin_bit_cast(i32x4, c), 0, 0, 0));
+        } else if constexpr (B8) {
           c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               cat8(a[u][rb][0], a[u][rb][1]), cat8(b[u][mb][0], b[u][mb][1]), c, 0, 0, 0, 0, 0, 0);
         } else {
@@ -384,6 +397,14 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       stream_mma<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
   }
 
+  if constexpr (C::I8)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][mb][i] = i32_bits_to_f32(acc[rb][mb][i]);
+
   // Sum the KW partial tiles of each row block in wave order kg = 0, 1, ...
   // Tile (rb, mb) of wave (rg, mg, kg) sits at
   // red[((((kg*MW + mg)*RBW + rg)*RB + rb)*MB + mb)*256 ...].
@@ -433,9 +454,9 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         }
       } else {
         uint16_t* yr = y + (size_t)m * N;
-        // FP8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
+        // FP8, INT8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
         float scale = 1.0f;
-        if constexpr (C::FP8) scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
+        if constexpr (C::B8) scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
         const uint32_t lo = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
         const uint32_t hi = f32_to_bf16_rne(v[2] * scale) | (f32_to_bf16_rne(v[3] * scale) << 16);
         if (n + 3 < n_end && (N & 3) == 0) {
@@ -511,6 +532,8 @@ hipError_t launch_gemm_stream(const GemmArgs& a, const sp24_plan& p, hipStream_t
   if (a.dtype == SP24_FP8_E4M3)
     return a.sparse ? launch_stream_dt<SP24_FP8_E4M3, true>(a, p, s)
                     : launch_stream_dt<SP24_FP8_E4M3, false>(a, p, s);
+  if (a.dtype == SP24_INT8)
+    return a.sparse ? launch_stream_dt<SP24_INT8, true>(a, p, s) : launch_stream_dt<SP24_INT8, false>(a, p, s);
   return a.sparse ? launch_stream_dt<SP24_BF16, true>(a, p, s) : launch_stream_dt<SP24_BF16, false>(a, p, s);
 }
 

@@ -21,7 +21,10 @@
 // instruction K [h*Kt/2 + q*Kt/4, ...).  Instruction K is mapped to the
 // step's K so that every operand of a lane is one 16-byte piece of its row
 // and the index bits of a lane are one metadata word (fp8) or one 16-bit half
-// of one, selected by abid (bf16).
+// of one, selected by abid (bf16).  INT8 takes the integer forms of the fp8
+// instructions (v_smfmac_i32_32x32x64_i8; dense: two v_mfma_i32_32x32x32_i8)
+// with the fp8 operand layouts; its int32 accumulators become fp32 before the
+// epilogue.
 //
 // LDS rows are XOR-swizzled in 16-byte units (and metadata words within a
 // row) so that the operand reads of a wave spread over the banks; the LDS-DMA
@@ -48,16 +51,16 @@ constexpr int TI = BN / WGN / 32;   // 32-row instruction tiles per wave along n
 constexpr int TJ = BM / WGM / 32;   // 32-row instruction tiles per wave along m
 constexpr int GROUP_N = 8;          // tile columns per group in the tile order
 
-// K step and ring depth of the sparse FP8 kernel (the other three keep
+// K step and ring depth of the sparse one-byte kernels (the others keep
 // one 128-byte X row segment per step and as many buffers as fit).
 constexpr int kKsFp8Sparse = 128;
 constexpr int kStagesFp8Sparse = 3;
 
 template <int DT, bool SPARSE>
 struct TiledLayout {
-  static constexpr bool FP8 = DT == SP24_FP8_E4M3;
-  static constexpr int ESZ = FP8 ? 1 : 2;
-  static constexpr int KS = FP8 ? (SPARSE ? kKsFp8Sparse : 128) : 64;  // K values per step
+  static constexpr bool B8 = DT != SP24_BF16;  // one-byte codes (E4M3 or INT8)
+  static constexpr int ESZ = B8 ? 1 : 2;
+  static constexpr int KS = B8 ? (SPARSE ? kKsFp8Sparse : 128) : 64;  // K values per step
   static constexpr int WB = (SPARSE ? KS / 2 : KS) * ESZ;  // W bytes per row per step
   static constexpr int MWORDS = SPARSE ? KS / 32 : 0;     // metadata words per row per step
   static constexpr int XB = KS * ESZ;                      // X bytes per row per step
@@ -66,9 +69,9 @@ struct TiledLayout {
   static constexpr int M_OFF = W_OFF + BN * WB;
   static constexpr int X_OFF = M_OFF + BN * MWORDS * 4;
   static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
-  static constexpr int STAGES = SPARSE ? (FP8 ? kStagesFp8Sparse : 3) : 2;  // LDS buffers
+  static constexpr int STAGES = SPARSE ? (B8 ? kStagesFp8Sparse : 3) : 2;  // LDS buffers
   // 32x32 instructions along K per step: K 64 (sparse fp8, dense fp8), 32 (sparse bf16), 16 (dense bf16)
-  static constexpr int SUB = KS / (FP8 ? 64 : (SPARSE ? 32 : 16));
+  static constexpr int SUB = KS / (B8 ? 64 : (SPARSE ? 32 : 16));
   static constexpr int YS = BN * 2 + 16;  // bytes per row of the output tile staged in LDS
   static constexpr int LDS_BYTES = STAGES * STAGE > BM * YS ? STAGES * STAGE : BM * YS;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -215,10 +218,10 @@ __device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const Frag<DT, S
     const uint8_t* wr = buf + L::W_OFF + row * L::WB;
     if constexpr (SPARSE) {
       // fp8: bytes [32s + 16q, +16); bf16: bytes [32q + 16s, +16)
-      const int c = DT == SP24_FP8_E4M3 ? 2 * s + q : 2 * q + s;
+      const int c = DT != SP24_BF16 ? 2 * s + q : 2 * q + s;
       f.a[i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, c));
-    } else if constexpr (DT == SP24_FP8_E4M3) {
-      // dense fp8: 32 bytes [64s + 32q, +32)
+    } else if constexpr (DT != SP24_BF16) {
+      // dense fp8, int8: 32 bytes [64s + 32q, +32)
       f.a[i][0] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q));
       f.a[i][1] = *reinterpret_cast<const i32x4*>(wr + 16 * swz16<L::WP>(row, 4 * s + 2 * q + 1));
     } else {
@@ -231,9 +234,9 @@ __device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const Frag<DT, S
     const uint8_t* xr = buf + L::X_OFF + row * L::XB;
     if constexpr (SPARSE) {
       // run h of lane group q: fp8 bytes 64s + 32h + 16q; bf16 bytes 64h + 32s + 16q
-      const int c = DT == SP24_FP8_E4M3 ? 4 * s + 2 * h + q : 4 * h + 2 * s + q;
+      const int c = DT != SP24_BF16 ? 4 * s + 2 * h + q : 4 * h + 2 * s + q;
       f.b[j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, c));
-    } else if constexpr (DT == SP24_FP8_E4M3) {
+    } else if constexpr (DT != SP24_BF16) {
       f.b[j][h] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 4 * s + 2 * q + h));
     } else if constexpr (h == 0) {
       f.b[j][0] = *reinterpret_cast<const i32x4*>(xr + 16 * swz16<L::XP>(row, 2 * s + q));
@@ -245,7 +248,7 @@ __device__ __forceinline__ void read_piece(Frag<DT, SPARSE>& f, const Frag<DT, S
     constexpr int i = P - TI - 2 * TJ;
     if (s == 0) {
       const int row = wn * (BN / WGN) + 32 * i + r;
-      if constexpr (DT == SP24_FP8_E4M3) {
+      if constexpr (DT != SP24_BF16) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(buf + L::M_OFF + row * 16 +
                                                         8 * (q ^ ((row >> 4) & 1)));
         f.ix[i] = v[0];
@@ -280,13 +283,23 @@ __device__ __forceinline__ void issue_loads(const Loader<DT, SPARSE>& ld, uint8_
 // Matrix instruction (I, J) of substep S.
 template <int DT, bool SPARSE, int S, int I, int J>
 __device__ __forceinline__ void mma_one(f32x16 (&acc)[TI][TJ], const Frag<DT, SPARSE>& f) {
-  if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
+  if constexpr (SPARSE && DT == SP24_INT8) {
+    acc[I][J] = __builtin_bit_cast(f32x16, __builtin_amdgcn_smfmac_i32_32x32x64_i8(
+                                               f.a[I][0], cat8(f.b[J][0], f.b[J][1]),
+                                               __builtin_bit_cast(i32x16, acc[I][J]), (int)f.ix[I], 0, 0));
+  } else if constexpr (SPARSE && DT == SP24_FP8_E4M3) {
     acc[I][J] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(f.a[I][0], cat8(f.b[J][0], f.b[J][1]), acc[I][J],
                                                              (int)f.ix[I], 0, 0);
   } else if constexpr (SPARSE) {
     acc[I][J] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
         __builtin_bit_cast(bf16x8, f.a[I][0]), __builtin_bit_cast(bf16x16, cat8(f.b[J][0], f.b[J][1])),
         acc[I][J], (int)f.ix[I], 0, S & 1);
+  } else if constexpr (DT == SP24_INT8) {
+    // dense INT8: two instructions of K=32 over the lane group's 32 bytes
+    acc[I][J] = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                               f.a[I][0], f.b[J][0], __builtin_bit_cast(i32x16, acc[I][J]), 0, 0, 0));
+    acc[I][J] = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                               f.a[I][1], f.b[J][1], __builtin_bit_cast(i32x16, acc[I][J]), 0, 0, 0));
   } else if constexpr (DT == SP24_FP8_E4M3) {
     acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(f.a[I][0], f.a[I][1]),
                                                                 cat8(f.b[J][0], f.b[J][1]), acc[I][J], 0, 0,
@@ -430,6 +443,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
   // 8-byte writes of a 32-row strip spread over the banks.
   constexpr int YS = L::YS;
   static_assert(BM * YS <= L::LDS_BYTES, "staged output tile fits");
+  if constexpr (DT == SP24_INT8)
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = i32_bits_to_f32(acc[i][j][e]);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's last (discarded) reads are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -438,10 +458,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int ml = wm * (BM / WGM) + 32 * j + c;
-      // FP8: fp32(sx * sw) with the scale of X row m0 + ml (one per tensor: xs_step = 0;
+      // FP8, INT8: fp32(sx * sw) with the scale of X row m0 + ml (one per tensor: xs_step = 0;
       // rows past M are staged but never stored)
       float scale = 1.0f;
-      if constexpr (DT == SP24_FP8_E4M3) scale = x_scale[(size_t)min(m0 + ml, M - 1) * xs_step] * w_scale[0];
+      if constexpr (DT != SP24_BF16) scale = x_scale[(size_t)min(m0 + ml, M - 1) * xs_step] * w_scale[0];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -495,6 +515,8 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t 
   if (a.dtype == SP24_FP8_E4M3)
     return a.sparse ? launch_tiled_dt<SP24_FP8_E4M3, true>(a, p, s)
                     : launch_tiled_dt<SP24_FP8_E4M3, false>(a, p, s);
+  if (a.dtype == SP24_INT8)
+    return a.sparse ? launch_tiled_dt<SP24_INT8, true>(a, p, s) : launch_tiled_dt<SP24_INT8, false>(a, p, s);
   return a.sparse ? launch_tiled_dt<SP24_BF16, true>(a, p, s) : launch_tiled_dt<SP24_BF16, false>(a, p, s);
 }
 

@@ -35,10 +35,11 @@ hipError_t launch_slide_prune_pack(const uint16_t* w, int64_t n, int64_t k, int 
                                    hipStream_t s);
 hipError_t launch_slide_quant_rows(const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q, float* scales,
                                    hipStream_t s);
-hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
-                                 hipStream_t s);
-hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
-                            void* ws, hipStream_t s);
+// dtype SP24_FP8_E4M3 or SP24_INT8
+hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
+                             hipStream_t s);
+hipError_t launch_quant(int dtype, const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
+                        void* ws, hipStream_t s);
 
 // sp24_gemm_skinny.hip / sp24_gemm_stream.hip / sp24_gemm_tiled.hip / sp24_reduce.hip
 struct GemmArgs {
@@ -129,7 +130,7 @@ constexpr int kStreamQxBytes = 16384;
 // Bytes of one LDS buffer of a stream configuration: W values and metadata of
 // 16 * rbw * rb rows plus 16 * mw * mb X rows, for u * kw units of 128 K.
 constexpr int stream_stage_bytes(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u) {
-  const int esz = dtype == SP24_FP8_E4M3 ? 1 : 2;
+  const int esz = dtype == SP24_BF16 ? 2 : 1;
   const int ups = u * kw;
   const int wb = ups * (sparse ? 64 : 128) * esz, mwords = sparse ? ups * 4 : 0, xb = ups * 128 * esz;
   return 16 * rbw * rb * (wb + 4 * mwords) + 16 * mw * mb * xb;
@@ -149,7 +150,7 @@ constexpr bool stream_fits(int dtype, bool sparse, int rbw, int rb, int mw, int 
 // metadata only; the X rows live after these bytes.
 constexpr int stream_ring_bytes(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
                                 int smax, bool qx) {
-  const int esz = dtype == SP24_FP8_E4M3 ? 1 : 2;
+  const int esz = dtype == SP24_BF16 ? 2 : 1;
   const int stage = stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u) -
                     (qx ? 16 * mw * mb * u * kw * 128 * esz : 0);
   const int ring = stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) * stage;

@@ -5,6 +5,8 @@
 // lanes, registers and sparse index bits to matrix coordinates with one-hot
 // inputs.  Every access is at a fixed per-lane stride inside buffers whose
 // size the caller derives from n_exp.
+#include <type_traits>
+
 #include "../../include/sp24_probe.h"
 #include "sp24_common.hpp"
 #include "sp24_internal.hpp"
@@ -25,7 +27,25 @@ __global__ __launch_bounds__(64) void layout_kernel(const uint8_t* __restrict__ 
   const int ix = (int)idx[slot];
   const i32x8 bb{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   float* out = c + slot * 16;
-  if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_FP8 || V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0 ||
+  if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_I8 || V == SP24_PROBE_MFMA_16x16x64_I8) {
+    i32x4 acc{0, 0, 0, 0};
+    if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_I8)
+      acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a0, bb, acc, ix, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = (float)acc[i];
+  } else if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_I8 || V == SP24_PROBE_MFMA_32x32x32_I8) {
+    i32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0;
+    if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_I8)
+      acc = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a0, bb, acc, ix, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = (float)acc[i];
+  } else if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_FP8 || V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID0 ||
                 V == SP24_PROBE_SMFMAC_16x16x64_BF16_ABID1 || V == SP24_PROBE_MFMA_16x16x128_FP8 ||
                 V == SP24_PROBE_MFMA_16x16x32_BF16) {
     f32x4 acc{0.f, 0.f, 0.f, 0.f};
@@ -70,7 +90,35 @@ __global__ void rate_kernel(int iters, float* __restrict__ out) {
   i32x8 b = {lane, 1, 2, 3, 4, 5, 6, lane};
   const int ix = 0x88888888 ^ lane;  // any valid-looking index pattern
   float r = 0.f;
-  if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8 || V == SP24_PROBE_SMFMAC_32x32x32_BF16_ABID0) {
+  if constexpr (V >= SP24_PROBE_SMFMAC_16x16x128_I8) {
+    constexpr bool WIDE = V == SP24_PROBE_SMFMAC_32x32x64_I8 || V == SP24_PROBE_MFMA_32x32x32_I8;
+    using Acc = typename std::conditional<WIDE, i32x16, i32x4>::type;
+    Acc c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+      if constexpr (V == SP24_PROBE_SMFMAC_16x16x128_I8) {
+        c0 = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c3, ix, 0, 0);
+      } else if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_I8) {
+        c0 = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c0, ix, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c1, ix, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c2, ix, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c3, ix, 0, 0);
+      } else if constexpr (V == SP24_PROBE_MFMA_16x16x64_I8) {
+        c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, a + 1, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, a + 1, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, a + 1, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, a + 1, c3, 0, 0, 0);
+      } else {
+        c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a + 1, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a + 1, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a + 1, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a + 1, c3, 0, 0, 0);
+      }
+    }
+    for (int i = 0; i < (WIDE ? 16 : 4); ++i) r += (float)(c0[i] + c1[i] + c2[i] + c3[i]);
+  } else if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8 || V == SP24_PROBE_SMFMAC_32x32x32_BF16_ABID0) {
     f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
     for (int it = 0; it < iters; ++it) {
       if constexpr (V == SP24_PROBE_SMFMAC_32x32x64_FP8) {
@@ -168,6 +216,7 @@ int sp24_probe_mfma_layout(int variant, const void* a, const void* b, const uint
   case V: hipLaunchKernelGGL(layout_kernel<V>, dim3(n_exp), dim3(64), 0, s, pa, pb, idx, c); break;
     SP24_LAYOUT_CASE(0) SP24_LAYOUT_CASE(1) SP24_LAYOUT_CASE(2) SP24_LAYOUT_CASE(3)
     SP24_LAYOUT_CASE(4) SP24_LAYOUT_CASE(5) SP24_LAYOUT_CASE(6) SP24_LAYOUT_CASE(7)
+    SP24_LAYOUT_CASE(8) SP24_LAYOUT_CASE(9) SP24_LAYOUT_CASE(10) SP24_LAYOUT_CASE(11)
 #undef SP24_LAYOUT_CASE
   }
   return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
@@ -188,6 +237,10 @@ int sp24_probe_mfma_rate(int variant, int iters, int blocks, int waves, float* o
     case 4: hipLaunchKernelGGL(rate_kernel<4>, g, blk, 0, s, iters, out); break;
     case 6: hipLaunchKernelGGL(rate_kernel<6>, g, blk, 0, s, iters, out); break;
     case 7: hipLaunchKernelGGL(rate_kernel<7>, g, blk, 0, s, iters, out); break;
+    case 8: hipLaunchKernelGGL(rate_kernel<8>, g, blk, 0, s, iters, out); break;
+    case 9: hipLaunchKernelGGL(rate_kernel<9>, g, blk, 0, s, iters, out); break;
+    case 10: hipLaunchKernelGGL(rate_kernel<10>, g, blk, 0, s, iters, out); break;
+    case 11: hipLaunchKernelGGL(rate_kernel<11>, g, blk, 0, s, iters, out); break;
   }
   return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;
 }

@@ -1,9 +1,12 @@
-// Per-tensor FP8-E4M3 quantisation of bf16 tensors.
+// Per-tensor FP8-E4M3 and INT8 quantisation of bf16 tensors.
 //
 // One scale per tensor from the tensor's own maximum magnitude, chosen so no
 // value overflows, with a clip at the format maximum ("Deploying 2:4 Sparsity
 // with FP8 on Hopper", pipeline step 3, step 6 and "Troubleshooting quick
-// hits").  s = fp32(amax / 448) (1 when amax is 0); q = e4m3_rne(clamp(x / s)).
+// hits").  E4M3: s = fp32(amax / 448) (1 when amax is 0), q = e4m3_rne(clamp(x / s)).
+// INT8 (the page's W8A8 recipe, symmetric): s = fp32(amax / 127) (1 when amax
+// is 0), q = clamp(rne(x / s), -127, 127).  The kernels are templates on the
+// code type; the reduction is shared.
 //
 // amax is order-independent and exact: it is taken on the integer keys
 // (bits & 0x7FFF), which order finite bf16 magnitudes exactly.
@@ -49,10 +52,6 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sh) {
   return r;
 }
 
-__device__ __forceinline__ uint8_t cast1(uint32_t h, float s) {
-  return (uint8_t)(f32x2_to_e4m3(bf16_to_f32(h) / s, 0.0f) & 0xFFu);
-}
-
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t* __restrict__ x,
                                                                 int64_t count,
                                                                 uint32_t* __restrict__ partial) {
@@ -68,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t* 
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
+template <int DT>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t count,
                                                         uint8_t* __restrict__ q,
                                                         float* __restrict__ scale,
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
     uint32_t m = 0;
     for (int i = threadIdx.x; i < npartial; i += kThreads) m = max(m, partial[i]);
     m = block_max<kThreads>(m, sh);
-    s = scale_from_key(m);
+    s = qscale<DT>(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
   } else {
     s = *scale;
@@ -89,12 +89,13 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
-  for (int64_t i = t0; i < nvec; i += stride) qv[i] = cast8(*(xv + i), s);
-  for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = cast1(x[i], s);
+  for (int64_t i = t0; i < nvec; i += stride) qv[i] = qcast8<DT>(*(xv + i), s);
+  for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = qcast1<DT>(x[i], s);
 }
 
 // Small tensors in one launch: workgroup b takes amax over the whole tensor,
 // then casts values [b * kFusedSlice, (b + 1) * kFusedSlice).
+template <int DT>
 __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16_t* __restrict__ x,
                                                                     int64_t count,
                                                                     uint8_t* __restrict__ q,
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
     const int tail = nvec * 8 + threadIdx.x;
     if (tail < count) m = max(m, (uint32_t)(x[tail] & 0x7FFFu));
     m = block_max<kFusedThreads>(m, sh);
-    s = scale_from_key(m);
+    s = qscale<DT>(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
   } else {
     s = *scale;
@@ -124,9 +125,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
   const int v0 = blockIdx.x * (kFusedSlice / 8);
   const int v1 = min(nvec, v0 + kFusedSlice / 8);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
-  for (int i = v0 + threadIdx.x; i < v1; i += kFusedThreads) qv[i] = cast8(xv[i], s);
+  for (int i = v0 + threadIdx.x; i < v1; i += kFusedThreads) qv[i] = qcast8<DT>(xv[i], s);
   const int tail = nvec * 8 + threadIdx.x;  // the last workgroup casts the 0..7 trailing values
-  if (blockIdx.x == gridDim.x - 1 && tail < count) q[tail] = cast1(x[tail], s);
+  if (blockIdx.x == gridDim.x - 1 && tail < count) q[tail] = qcast1<DT>(x[tail], s);
 }
 
 // Per-row (per-token) scales: workgroup b quantises rows b, b + gridDim.x, ...
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
 // the maximum to the cast (k <= 8192: one pass over global memory).
 constexpr int kRowRegVecs = 4;
 
+template <int DT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                               int64_t k, uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
@@ -156,16 +158,16 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __
     } else {
       for (int64_t i = threadIdx.x; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
     }
-    const float s = scale_from_key(block_max<kThreads>(mk, sh));
+    const float s = qscale<DT>(block_max<kThreads>(mk, sh));
     if (threadIdx.x == 0) scales[r] = s;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kRowRegVecs; ++j) {
         const int64_t i = threadIdx.x + (int64_t)j * kThreads;
-        if (i < nvec) qv[i] = cast8(v[j], s);
+        if (i < nvec) qv[i] = qcast8<DT>(v[j], s);
       }
     } else {
-      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) qv[i] = cast8(xv[i], s);
+      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) qv[i] = qcast8<DT>(xv[i], s);
     }
   }
 }
@@ -184,19 +186,23 @@ size_t quant_workspace_bytes(int64_t count) {
   return (size_t)n_partials(count) * sizeof(uint32_t);
 }
 
-hipError_t launch_quant_fp8_rows(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
-                                 hipStream_t s) {
+namespace {
+
+template <int DT>
+hipError_t launch_quant_rows_dt(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
+                                hipStream_t s) {
   const int64_t blocks = m < 65536 ? m : 65536;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((int)blocks), dim3(kThreads), 0, s, x, m, k, q, scales);
+  hipLaunchKernelGGL(quant_rows_kernel<DT>, dim3((int)blocks), dim3(kThreads), 0, s, x, m, k, q, scales);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
-                            void* ws, hipStream_t s) {
+template <int DT>
+hipError_t launch_quant_dt(const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode, void* ws,
+                           hipStream_t s) {
   const bool dynamic = mode == SP24_SCALE_DYNAMIC;
   if (count <= kFusedMax) {
     const int blocks = (int)((count + kFusedSlice - 1) / kFusedSlice);
-    hipLaunchKernelGGL(fused_quant_kernel, dim3(blocks), dim3(kFusedThreads), 0, s, x, count, q, scale,
+    hipLaunchKernelGGL(fused_quant_kernel<DT>, dim3(blocks), dim3(kFusedThreads), 0, s, x, count, q, scale,
                        dynamic ? 1 : 0);
     return hipGetLastError();
   }
@@ -204,7 +210,7 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float*
   if (cast_blocks > 256 * 8) cast_blocks = 256 * 8;
   if (cast_blocks < 1) cast_blocks = 1;
   if (!dynamic) {
-    hipLaunchKernelGGL(cast_kernel, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q,
+    hipLaunchKernelGGL(cast_kernel<DT>, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q,
                        scale, (const uint32_t*)nullptr, 0);
     return hipGetLastError();
   }
@@ -213,9 +219,23 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t count, uint8_t* q, float*
   hipLaunchKernelGGL(amax_partial_kernel, dim3(np), dim3(kThreads), 0, s, x, count, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cast_kernel, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q, scale,
+  hipLaunchKernelGGL(cast_kernel<DT>, dim3((int)cast_blocks), dim3(kThreads), 0, s, x, count, q, scale,
                      (const uint32_t*)partial, np);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
+                             hipStream_t s) {
+  return dtype == SP24_INT8 ? launch_quant_rows_dt<SP24_INT8>(x, m, k, q, scales, s)
+                            : launch_quant_rows_dt<SP24_FP8_E4M3>(x, m, k, q, scales, s);
+}
+
+hipError_t launch_quant(int dtype, const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
+                        void* ws, hipStream_t s) {
+  return dtype == SP24_INT8 ? launch_quant_dt<SP24_INT8>(x, count, q, scale, mode, ws, s)
+                            : launch_quant_dt<SP24_FP8_E4M3>(x, count, q, scale, mode, ws, s);
 }
 
 }  // namespace sp24

@@ -1,5 +1,5 @@
 // Split-K reduction: y[m, n] = bf16_rne((sum over slices z in order of
-// partial[z, m, n]) * scale), scale = fp32(sx * sw) for FP8 (sx per tensor or
+// partial[z, m, n]) * scale), scale = fp32(sx * sw) for FP8 and INT8 (sx per tensor or
 // per X row).  The fixed slice order makes the result bitwise
 // reproducible.
 #include "sp24_common.hpp"
@@ -13,7 +13,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             const float* __restrict__ x_scale,
                                                             const float* __restrict__ w_scale, int xs_step,
                                                             uint16_t* __restrict__ y) {
-  // FP8: fp32(sx * sw), sx the scale of X row i / n (one per tensor: xs_step = 0)
+  // FP8, INT8: fp32(sx * sw), sx the scale of X row i / n (one per tensor: xs_step = 0)
   const float s0 = x_scale != nullptr ? x_scale[0] * w_scale[0] : 1.0f;
   auto scale_of = [&](int64_t i) { return xs_step == 0 ? s0 : x_scale[i / n] * w_scale[0]; };
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -39,9 +39,10 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s) {
   int64_t blocks = (mn / 4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
-  const bool fp8 = a.dtype == SP24_FP8_E4M3;
+  const bool scaled = a.dtype != SP24_BF16;  // E4M3 and INT8 carry scales
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((int)blocks), dim3(256), 0, s, a.partial, split_k, mn,
-                     (int64_t)a.n, fp8 ? a.x_scale : nullptr, fp8 ? a.w_scale : nullptr, a.x_scale_step, a.y);
+                     (int64_t)a.n, scaled ? a.x_scale : nullptr, scaled ? a.w_scale : nullptr, a.x_scale_step,
+                     a.y);
   return hipGetLastError();
 }
 

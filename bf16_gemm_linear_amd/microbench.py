@@ -34,6 +34,10 @@ VARIANTS = {
     4: ("smfmac_f32_32x32x32_bf16", 2 * 32 * 32 * 32, 32),
     6: ("mfma_f32_16x16x128_f8f6f4(fp8)", 2 * 16 * 16 * 128, 32),
     7: ("mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32, 16),
+    8: ("smfmac_i32_16x16x128_i8", 2 * 16 * 16 * 128, 16),
+    9: ("smfmac_i32_32x32x64_i8", 2 * 32 * 32 * 64, 32),
+    10: ("mfma_i32_16x16x64_i8", 2 * 16 * 16 * 64, 16),
+    11: ("mfma_i32_32x32x32_i8", 2 * 32 * 32 * 32, 32),
 }
 
 

@@ -1,7 +1,7 @@
 /*
  * sp24.h -- C ABI of libsp24: 2:4 structured-sparse GEMM Y = X . W^T for
- * gfx950 (AMD Instinct MI355X), BF16 or FP8-E4M3 operands, fp32 accumulation,
- * BF16 output.
+ * gfx950 (AMD Instinct MI355X), BF16, FP8-E4M3 or INT8 operands, fp32
+ * accumulation (exact int32 sums for INT8), BF16 output.
  *
  * Operation sources ("the cookbook" = the page "Deploying 2:4 Sparsity with
  * FP8 on Hopper: A Production Cookbook"):
@@ -14,6 +14,10 @@
  *     the hardware's compressed layout; this library defines that layout below.
  *   - Per-tensor dynamic FP8 scaling with a clip at the format maximum: the
  *     cookbook, pipeline steps 3 and 6 and "Troubleshooting quick hits".
+ *   - INT8 W8A8 beside 2:4 + FP8: the cookbook's table "Precision and sparsity
+ *     recipes" and pipeline step 6 "INT8 alternative"; its symmetric scale
+ *     amax/127 and round-half-even codes in [-127, 127] are this library's
+ *     reading (no page fixes them).
  *   - The sparse product on the linear/FFN projections: the cookbook, pipeline
  *     step 2 and its "What to prune" table.
  *
@@ -23,7 +27,8 @@
  *     mutable global state; calls are reentrant.
  *   - W is [n, k] (the nn.Linear weight layout), X is [m, k], Y is [m, n].
  *   - bf16 buffers hold IEEE bfloat16 bit patterns; FP8 buffers hold OCP
- *     E4M3FN byte codes (bias 7, max 448, NaN = 0x7F/0xFF, no infinities).
+ *     E4M3FN byte codes (bias 7, max 448, NaN = 0x7F/0xFF, no infinities);
+ *     INT8 buffers hold two's-complement bytes (the quantisers write -127..127).
  *   - Compressed weight of W [n, k]:
  *       values [n, k/2]: the two kept values of group g (columns 4g..4g+3) at
  *                        columns 2g and 2g+1, in ascending position order;
@@ -71,18 +76,19 @@ typedef enum sp24_status {
 } sp24_status;
 
 typedef enum sp24_dtype {
-  SP24_BF16 = 0,     /* bfloat16 operands, no scales */
-  SP24_FP8_E4M3 = 1  /* OCP E4M3FN codes with one fp32 scale per tensor */
+  SP24_BF16 = 0,      /* bfloat16 operands, no scales */
+  SP24_FP8_E4M3 = 1,  /* OCP E4M3FN codes with one fp32 scale per tensor */
+  SP24_INT8 = 2       /* int8 codes with one fp32 scale per tensor; int32 sums */
 } sp24_dtype;
 
 typedef enum sp24_scale_mode {
-  SP24_SCALE_DYNAMIC = 0, /* compute s = amax/448 on the device and store it */
+  SP24_SCALE_DYNAMIC = 0, /* compute s = amax/448 (INT8: amax/127) on the device and store it */
   SP24_SCALE_STATIC = 1   /* use the scale already stored at scale_dev */
 } sp24_scale_mode;
 
 typedef enum sp24_op {
   SP24_OP_GEMM = 0,       /* sp24_gemm */
-  SP24_OP_QUANT = 1,      /* sp24_quant_fp8 */
+  SP24_OP_QUANT = 1,      /* sp24_quant_fp8, sp24_quant_int8 */
   SP24_OP_DENSE_GEMM = 2, /* sp24_dense_gemm */
   SP24_OP_GEMM_QX = 3     /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
 } sp24_op;
@@ -118,7 +124,7 @@ int sp24_prune_compress(const void* w_bf16, int64_t n, int64_t k, void* values_b
 
 /* Rebuild the dense pruned W [n, k] from (values, meta): kept values at their
  * positions, all-zero bit patterns (+0) elsewhere.
- *   dtype  SP24_BF16 (values and w_out are bf16) or SP24_FP8_E4M3 (byte codes)
+ *   dtype  SP24_BF16 (values and w_out are bf16), SP24_FP8_E4M3 or SP24_INT8 (byte codes)
  * Requires n >= 1, k >= 32, k % 32 == 0.  Nibbles are used as given: a nibble
  * with i0 == i1 (never written by sp24_prune_compress) writes both values to
  * one position, the second last; every write stays inside the row. */
@@ -147,10 +153,27 @@ int sp24_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad_de
 int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Quantise count bf16 values to INT8 codes with one per-tensor symmetric scale
+ * (the cookbook's INT8 W8A8 recipe, table "Precision and sparsity recipes").
+ * As sp24_quant_fp8 with the INT8 range:
+ *   mode SP24_SCALE_DYNAMIC: *scale_dev = fp32(amax / 127) (1.0 if amax == 0).
+ *   Each value: q = clamp(round_half_even(fp32(x / s)), -127, 127) with an IEEE
+ *   float32 division (-128 is never written).  Inputs must be finite.
+ *   Workspace, limits and errors as sp24_quant_fp8 (op SP24_OP_QUANT). */
+int sp24_quant_int8(const void* x_bf16, int64_t count, int8_t* q_out, float* scale_dev, int mode,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* Y = X . W^T with W in compressed 2:4 form; fp32 accumulation; bf16 output.
  *   dtype SP24_BF16    : x is bf16 [m, k], w_values bf16 [n, k/2]; scales ignored (may be NULL).
  *   dtype SP24_FP8_E4M3: x is E4M3 [m, k] with *x_scale_dev, w_values E4M3 [n, k/2]
  *                        with *w_scale_dev; y = bf16_rne(acc * fp32(sx * sw)).
+ *   dtype SP24_INT8    : x int8 [m, k] with *x_scale_dev, w_values int8 [n, k/2] with
+ *                        *w_scale_dev; the products are summed exactly in int32 (per
+ *                        K slice when K is split), converted to fp32, then scaled as
+ *                        FP8.  Also requires k <= 131072: a sum then stays below
+ *                        2^31 in magnitude (at most k/2 products of at most
+ *                        128 * 128 for any codes; the dense baseline's k products
+ *                        of codes within [-127, 127], as the quantisers write).
  *   w_meta n * k/32 words (storage order above); y_bf16 [m, n].
  * Requires m >= 1, n >= 1, k >= 128, k % 128 == 0.  The sum over k is formed in
  * a fixed order for a given (m, n, k): results are bitwise reproducible.
@@ -162,7 +185,7 @@ int sp24_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const f
               void* ws, size_t ws_bytes, void* stream);
 
 /* Dense baseline for comparison: Y = X . W^T with an uncompressed W [n, k]
- * (bf16 or E4M3 codes) on dense MFMA; same scales, epilogue and limits as
+ * (bf16, E4M3 or INT8 codes) on dense MFMA; same scales, epilogue and limits as
  * sp24_gemm. */
 int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
                     const float* x_scale_dev, const void* w_dense, const float* w_scale_dev,
@@ -178,6 +201,12 @@ int sp24_dense_gemm(int dtype, int64_t m, int64_t n, int64_t k, const void* x,
  *   scales_dev out: [m] fp32.  No workspace, no host synchronisation. */
 int sp24_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, uint8_t* q_out, float* scales_dev,
                         void* stream);
+
+/* Per-token INT8 quantisation: as sp24_quant_fp8_rows with the INT8 codes and
+ * scale of sp24_quant_int8 (scales_dev[r] = fp32(amax_r / 127), 1 for a zero
+ * row); row r is quantised exactly as sp24_quant_int8 would quantise it alone. */
+int sp24_quant_int8_rows(const void* x_bf16, int64_t m, int64_t k, int8_t* q_out, float* scales_dev,
+                         void* stream);
 
 /* SlideSparse ("SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity",
  * technical summary, section 2): a (2N-2):2N weight on the 2:4 path.
@@ -203,12 +232,13 @@ int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, v
 int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
                               float* scales_dev, void* stream);
 
-/* Y = X . W^T as sp24_gemm with dtype SP24_FP8_E4M3, except that X carries one
- * scale per row: y[r, :] = bf16_rne(acc[r, :] * fp32(x_scales_dev[r] * sw)).
- *   x E4M3 [m, k] (from sp24_quant_fp8_rows); x_scales_dev [m] fp32; the rest,
- *   the workspace (sp24_workspace_size(SP24_OP_GEMM, SP24_FP8_E4M3, ...)) and
- *   the errors as for sp24_gemm. */
-int sp24_gemm_rows(int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
+/* Y = X . W^T as sp24_gemm with dtype SP24_FP8_E4M3 or SP24_INT8, except that
+ * X carries one scale per row: y[r, :] = bf16_rne(acc[r, :] * fp32(x_scales_dev[r] * sw)).
+ *   x [m, k] codes (from sp24_quant_fp8_rows / sp24_quant_int8_rows);
+ *   x_scales_dev [m] fp32; the rest, the workspace (sp24_workspace_size(
+ *   SP24_OP_GEMM, dtype, ...)) and the errors as for sp24_gemm; SP24_BF16 is
+ *   SP24_ERR_DTYPE. */
+int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,
                    const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                    void* ws, size_t ws_bytes, void* stream);
 

@@ -28,18 +28,22 @@ typedef enum sp24_probe_variant {
   SP24_PROBE_SMFMAC_32x32x32_BF16_ABID1 = 5,
   SP24_PROBE_MFMA_16x16x128_FP8 = 6,    /* dense v_mfma_f32_16x16x128_f8f6f4 (fp8 x fp8) */
   SP24_PROBE_MFMA_16x16x32_BF16 = 7,    /* dense v_mfma_f32_16x16x32_bf16 */
-  SP24_PROBE_N_VARIANTS = 8
+  SP24_PROBE_SMFMAC_16x16x128_I8 = 8,   /* v_smfmac_i32_16x16x128_i8 */
+  SP24_PROBE_SMFMAC_32x32x64_I8 = 9,    /* v_smfmac_i32_32x32x64_i8 */
+  SP24_PROBE_MFMA_16x16x64_I8 = 10,     /* dense v_mfma_i32_16x16x64_i8 */
+  SP24_PROBE_MFMA_32x32x32_I8 = 11,     /* dense v_mfma_i32_32x32x32_i8 */
+  SP24_PROBE_N_VARIANTS = 12
 } sp24_probe_variant;
 
 /* Run one instruction per experiment, accumulator starting at 0.
  * Experiment e uses one wave (64 lanes).  Per lane, with fixed strides:
  *   a   : 32 bytes at a   + (e*64 + lane)*32  (the A operand; 16 bytes used by
- *         sparse variants and by the dense bf16 variant, 32 by dense fp8)
+ *         sparse variants and by the dense bf16 and int8 variants, 32 by dense fp8)
  *   b   : 32 bytes at b   + (e*64 + lane)*32  (the B operand; 16 bytes used
- *         by the dense bf16 variant)
+ *         by the dense bf16 and int8 variants)
  *   idx : 4 bytes  at idx + (e*64 + lane)     (sparse index register)
  *   c   : 16 floats at c + (e*64 + lane)*16   (accumulator registers; 4 used
- *         by the 16x16 variants)
+ *         by the 16x16 variants; int8 variants' int32 results converted to float)
  * n_exp >= 1.  Returns SP24_ERR_MODE for an unknown variant. */
 int sp24_probe_mfma_layout(int variant, const void* a, const void* b, const uint32_t* idx,
                            float* c, int n_exp, void* stream);

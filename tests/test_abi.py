@@ -112,15 +112,16 @@ def test_prune_and_decompress_validation():
     assert f(p(A), 4, 64, p(A + 0x10008), p(A + 0x20000), None) == EALIGN
     assert f(p(A), 4, 64, p(A + 256), p(A + 0x20000), None) == EALIAS
     d = lib.sp24_decompress
-    assert d(2, p(A), p(A + 0x1000), 4, 64, p(A + 0x2000), None) == EDTYPE
+    assert d(3, p(A), p(A + 0x1000), 4, 64, p(A + 0x2000), None) == EDTYPE
     assert d(0, p(A), None, 4, 64, p(A + 0x2000), None) == ENULL
     assert d(1, p(A), p(A + 0x1000), 4, 16, p(A + 0x2000), None) == ESHAPE
     assert d(1, p(A), p(A + 0x1000), 4, 64, p(A + 0x2004), None) == EALIGN
     assert d(0, p(A), p(A + 0x1000), 4, 64, p(A + 64), None) == EALIAS
 
 
-def test_quant_validation():
-    f = lib.sp24_quant_fp8
+@pytest.mark.parametrize("name", ["sp24_quant_fp8", "sp24_quant_int8"])
+def test_quant_validation(name):
+    f = getattr(lib, name)
     big = 1 << 20
     need = lib.sp24_workspace_size(1, 0, big, 1, 1)
     assert need > 0
@@ -302,8 +303,9 @@ def test_gemm_qx_workspace_rule():
                    wsc=A + (6 << 26), y=A + (7 << 26), ws=A + (8 << 26), wsb=ws_qx(m, n, k) - 16) == EWS
 
 
-def test_quant_rows_validation():
-    f = lambda x=A, m=4, k=256, q=A + 0x100000, s=A + 0x200000: lib.sp24_quant_fp8_rows(
+@pytest.mark.parametrize("name", ["sp24_quant_fp8_rows", "sp24_quant_int8_rows"])
+def test_quant_rows_validation(name):
+    f = lambda x=A, m=4, k=256, q=A + 0x100000, s=A + 0x200000: getattr(lib, name)(
         p(x), m, k, p(q), p(s), None)
     assert f(x=None) == ENULL and f(q=None) == ENULL and f(s=None) == ENULL
     assert f(m=0) == ESHAPE and f(k=0) == ESHAPE and f(k=12) == ESHAPE
@@ -313,9 +315,12 @@ def test_quant_rows_validation():
     assert f(s=A + 0x100010) == EALIAS                    # scales over the codes
 
 
-def test_gemm_rows_validation():
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_gemm_rows_validation(dtype):
     g = lambda m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000, wsc=A + 0x400000, \
-        y=A + 0x500000: lib.sp24_gemm_rows(m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), None, 0, None)
+        y=A + 0x500000, dt=dtype: lib.sp24_gemm_rows(dt, m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y),
+                                                     None, 0, None)
+    assert g(dt=0) == EDTYPE and g(dt=3) == EDTYPE          # codes with scales only
     assert g(xs=None) == ENULL and g(wsc=None) == ENULL and g(meta=None) == ENULL
     assert g(k=96) == ESHAPE
     assert g(xs=A + 0x100002) == EALIGN
@@ -337,3 +342,24 @@ def test_slide_validation():
     assert qz(k=60) == ESHAPE and qz(k=36, np_=3) == ESHAPE     # 36 % 8 != 0
     assert qz(q=A + 8) == EALIGN
     assert qz(s=A + 0x10) == EALIAS
+
+
+def test_int8_validation_and_plan():
+    # INT8 carries scales like FP8 and has the same plans (one-byte codes)
+    assert gemm(dtype=2, xs=None) == ENULL
+    assert gemm(dtype=2, wsc=None) == ENULL
+    assert gemm(dtype=2, xs=A + 0x100002) == EALIGN
+    assert gemm(dtype=2, y=A + 0x400000 - 64, m=1, n=64) == EALIAS
+    # exact int32 sums: k is limited to 131072
+    assert gemm(dtype=2, k=131072 + 128, x=A, y=A + (1 << 36)) == ESHAPE
+    pl = sp.Plan()
+    assert lib.sp24_plan_gemm(sp.OP_GEMM, sp.INT8, 8, 256, 131072 + 128, ctypes.byref(pl)) == ESHAPE
+    assert lib.sp24_plan_gemm(sp.OP_GEMM, sp.INT8, 8, 256, 131072, ctypes.byref(pl)) == OK
+    assert lib.sp24_plan_gemm(sp.OP_GEMM, sp.FP8, 8, 256, 131072 + 128, ctypes.byref(pl)) == OK
+    for m, n, k in ((1, 14336, 4096), (16, 4096, 14336), (64, 28672, 8192), (8192, 28672, 8192), (600, 32771, 384)):
+        for op in (sp.OP_GEMM, sp.OP_DENSE_GEMM):
+            assert sp.plan(op, sp.INT8, m, n, k) == sp.plan(op, sp.FP8, m, n, k), (op, m, n, k)
+            assert lib.sp24_workspace_size(op, 2, m, n, k) == lib.sp24_workspace_size(op, 1, m, n, k)
+    f = lib.sp24_dense_gemm
+    assert f(2, 1, 1, 128, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ENULL
+    assert lib.sp24_workspace_size(sp.OP_GEMM_QX, 2, 1, 256, 256) == 0   # FP8 only

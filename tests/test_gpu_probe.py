@@ -1,8 +1,9 @@
 """On-device checks of the matrix-instruction operand layouts the GEMM kernels rely on.
 
 Model of the sparse instructions (SMFMAC) on gfx950, measured with one-hot
-probes: an instruction covers Kt values of K (fp8: 16x16x128 and 32x32x64;
-bf16: 16x16x64 and 32x32x32), with R rows (16 or 32) and G = 64/R lane groups.
+probes: an instruction covers Kt values of K (fp8 and int8: 16x16x128 and
+32x32x64; bf16: 16x16x64 and 32x32x32), with R rows (16 or 32) and G = 64/R
+lane groups; the int8 forms share the fp8 operand layouts.
   * A (compressed): lane l holds row l % R and, for lane group q = l // R, the
     contiguous instruction-K slice [q*Kt/G, (q+1)*Kt/G); its compressed value j
     belongs to group j // 2 of the slice and the 2-bit position within the
@@ -33,7 +34,7 @@ def _bf16_bits(v):
 
 def _c_coords(variant, lane, reg):
     """(row, col) of accumulator register `reg` of `lane`."""
-    if variant in (3, 4, 5):  # 32x32
+    if variant in (3, 4, 5, 9, 11):  # 32x32
         return 8 * (reg // 4) + 4 * (lane // 32) + reg % 4, lane % 32
     return 4 * (lane // 16) + reg, lane % 16
 
@@ -57,12 +58,13 @@ def _rand_idx(rng, n_exp):
     return (nib[sel] << (4 * np.arange(8, dtype=np.uint32))).sum(-1).astype(np.uint32)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 8, 9])
 def test_sparse_layout(variant):
     rng = np.random.default_rng(100 + variant)
     n_exp = 8
-    fp8 = variant in (0, 3)
-    rows = 32 if variant in (3, 4, 5) else 16
+    fp8 = variant in (0, 3, 8, 9)   # one-byte operands (E4M3 or int8)
+    i8 = variant in (8, 9)
+    rows = 32 if variant in (3, 4, 5, 9) else 16
     n_a = 16 if fp8 else 8         # compressed values per lane
     n_b = 32 if fp8 else 16        # B values per lane
     abid = 1 if variant in (2, 5) else 0
@@ -71,7 +73,10 @@ def test_sparse_layout(variant):
     idx = _rand_idx(rng, n_exp)
     a_bytes = np.zeros((n_exp, 64, 32), dtype=np.uint8)
     b_bytes = np.zeros((n_exp, 64, 32), dtype=np.uint8)
-    if fp8:
+    if i8:
+        a_bytes[..., :16] = av.astype(np.int8).view(np.uint8)
+        b_bytes[...] = bv.astype(np.int8).view(np.uint8)
+    elif fp8:
         a_bytes[..., :16] = np.vectorize(E4M3_SMALL.get)(av).astype(np.uint8)
         b_bytes[...] = np.vectorize(E4M3_SMALL.get)(bv).astype(np.uint8)
     else:
@@ -104,17 +109,22 @@ def test_sparse_layout(variant):
                 assert got[e, l, r] == want[i, col], (variant, e, l, r)
 
 
-@pytest.mark.parametrize("variant", [6, 7])
+@pytest.mark.parametrize("variant", [6, 7, 10, 11])
 def test_dense_layout_consistency(variant):
     rng = np.random.default_rng(200 + variant)
     n_exp = 4
     fp8 = variant == 6
-    n = 32 if fp8 else 8
+    i8 = variant in (10, 11)
+    rows = 32 if variant == 11 else 16
+    n = 32 if fp8 else 16 if i8 else 8
     av = rng.integers(-3, 4, size=(n_exp, 64, n))
     bv = rng.integers(-3, 4, size=(n_exp, 64, n))
     a_bytes = np.zeros((n_exp, 64, 32), dtype=np.uint8)
     b_bytes = np.zeros((n_exp, 64, 32), dtype=np.uint8)
-    if fp8:
+    if i8:
+        a_bytes[..., :16] = av.astype(np.int8).view(np.uint8)
+        b_bytes[..., :16] = bv.astype(np.int8).view(np.uint8)
+    elif fp8:
         a_bytes[...] = np.vectorize(E4M3_SMALL.get)(av).astype(np.uint8)
         b_bytes[...] = np.vectorize(E4M3_SMALL.get)(bv).astype(np.uint8)
     else:
@@ -123,10 +133,10 @@ def test_dense_layout_consistency(variant):
     idx = np.zeros((n_exp, 64), dtype=np.uint32)
     got = _run(variant, a_bytes, b_bytes, idx, n_exp)
     for e in range(n_exp):
-        want = np.zeros((16, 16))
-        for q in range(4):
-            want += av[e, 16 * q:16 * q + 16] @ bv[e, 16 * q:16 * q + 16].T
+        want = np.zeros((rows, rows))
+        for q in range(64 // rows):
+            want += av[e, rows * q:rows * q + rows] @ bv[e, rows * q:rows * q + rows].T
         for l in range(64):
-            for r in range(4):
+            for r in range(16 if rows == 32 else 4):
                 i, col = _c_coords(variant, l, r)
                 assert got[e, l, r] == want[i, col], (variant, e, l, r)
