@@ -13,6 +13,8 @@ the weight quantisation) is timed separately and reported under "load_path".
 --workload prefill: the M=8192, K=8192, N=28672 GEMM (bound: matrix cores).
 --workload layers: 32 layers x (QKV, O, gate+up, down) at M=256, 128 sequential
 sparse GEMMs per step (see run_layers).
+--workload palette: lossless BF16 exponent-palette weights (no sparsity) against the
+dense BF16 GEMM at decode sizes (see run_palette).
 --dtype int8: up, down or prefill with symmetric per-tensor INT8 codes (the
 cookbook's INT8 W8A8 recipe): a step is sp24_quant_int8 of X and the INT8
 sparse GEMM (exact int32 sums); the roofline peak is the dense INT8 MFMA rate.
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="up", choices=["up", "down", "prefill", "layers", "slide"])
+    ap.add_argument("--workload", default="up", choices=["up", "down", "prefill", "layers", "slide", "palette"])
     ap.add_argument("--dtype", default="fp8", choices=["fp8", "int8", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -143,7 +145,7 @@ def main():
     quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
     code_t = torch.int8 if kind == "int8" else torch.uint8
     label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
-    if kind == "int8" and args.workload in ("slide", "layers"):
+    if kind == "int8" and args.workload in ("slide", "layers", "palette"):
         print("--dtype int8 is measured on the up, down and prefill workloads", file=sys.stderr)
         sys.exit(2)
     ev = Events(torch)
@@ -166,6 +168,9 @@ def main():
         bound = "mfma"
     elif args.workload == "slide":
         print(json.dumps(run_slide(args, torch, np, sp, W, ev, dev)))
+        return
+    elif args.workload == "palette":
+        print(json.dumps(run_palette(args, torch, np, sp, W, ev, dev)))
         return
     else:
         print(json.dumps(run_layers(args, torch, np, sp, W, ev, dev)))
@@ -486,6 +491,76 @@ def run_slide(args, torch, np, sp, W, ev, dev):
             "config": {"workload": "SlideSparse 6:8 (N=4): decode up-projection M=1/16/64 (K=4096, N=14336) and "
                                    "prefill 8192x28672x8192; per-token X scales, per-tensor W scale"},
             "per_shape": out}
+
+
+def run_palette(args, torch, np, sp, W, ev, dev):
+    """Lossless BF16 exponent-palette weights against the dense BF16 GEMM of the same weight,
+    M = 1/4/16: the decode up- and down-projections (weights from workloads/), and the
+    up-projection weight with every magnitude raised to at least 0.02 * 2^-11 (sign kept),
+    which leaves 15 exponents, so that every row fits the palette (the page's premise that
+    the 16 most common exponents cover nearly all weights, here for every row).  A call
+    reads one of R copies of the encoded weight, past the last-level cache."""
+    def narrow(w):
+        f = w.float()
+        sign = torch.where(f >= 0, 1.0, -1.0)
+        return (sign * f.abs().clamp(min=0.02 * 2.0 ** -11)).to(torch.bfloat16)
+    cases = [("up", W.up_weight(), W.up_x), ("down", W.down_weight(), W.down_x),
+             ("up, every row in the palette", narrow(W.up_weight()), W.up_x)]
+    out = {}
+    for name, w_cpu, xfn in cases:
+        torch.cuda.empty_cache()
+        w = w_cpu.to(dev)
+        n, k = w.shape
+        pw = sp.palette_encode(w)
+        torch.cuda.synchronize()
+        t_enc = ev.time(lambda i: sp.palette_encode(w), 3) / 3   # includes its one host read of the counts
+        R = max(2, min(16, int(np.ceil(2.2 * LLC_BYTES / pw.nbytes))))
+        pws = [pw] + [sp.PaletteWeight(pw.n, pw.k, pw.palette.clone(), pw.pal_rows.clone(), pw.sm.clone(),
+                                       pw.ix.clone(), pw.verb_rows.clone(), pw.verb.clone()) for _ in range(R - 1)]
+        wds = [w] + [w.clone() for _ in range(R - 1)]
+        res = {"rows_in_palette": pw.n_pal, "rows_verbatim": pw.n_verb, "encoded_bytes": pw.nbytes,
+               "bf16_bytes": n * k * 2, "byte_ratio": pw.nbytes / (n * k * 2), "encode_ms": t_enc * 1e3,
+               "weight_copies": R}
+        for m in (1, 4, 16):
+            x = xfn(m).to(dev)
+            y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            dws = torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, sp.BF16, m, n, k)), dtype=torch.uint8,
+                              device=dev)
+            times = {}
+            for key, fn in (("palette", lambda i: sp.palette_gemm(x, pws[i % R], out=y)),
+                            ("dense_bf16", lambda i: sp.dense_gemm(x, wds[i % R], out=y, ws=dws))):
+                nrep = R * 8
+                fn(0)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for i in range(nrep):
+                        fn(i)
+                graph.replay()
+                torch.cuda.synchronize()
+                times[key] = ev.time(lambda i: graph.replay(), 3) / 3 / nrep
+                del graph
+            pb = pw.nbytes + m * k * 2 + m * n * 2
+            db = n * k * 2 + m * k * 2 + m * n * 2
+            res["M=%d" % m] = {"palette_us": times["palette"] * 1e6, "dense_bf16_us": times["dense_bf16"] * 1e6,
+                               "speedup_vs_dense": times["dense_bf16"] / times["palette"],
+                               "palette_GBs": pb / times["palette"] / 1e9,
+                               "dense_GBs": db / times["dense_bf16"] / 1e9}
+        out[name] = res
+        del pws, wds, pw, w
+    up1 = out["up"]["M=1"]
+    return {"metric": "lossless BF16 exponent-palette GEMM at decode: GB/s of encoded weight, and speedup over "
+                      "the dense BF16 GEMM",
+            "value": up1["palette_GBs"], "unit": "GB/s (up-projection, M=1)",
+            "n_gpus": 1, "steps": None, "warmup": None, "ms_per_step": up1["palette_us"] / 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded, workloads/)",
+            "config": {"workload": "exponent-palette weights (16-entry palette, verbatim rows), decode "
+                                   "up-projection K=4096 N=14336 and down-projection K=14336 N=4096, M=1/4/16"},
+            "roofline": {"bound": "hbm", "achieved": up1["palette_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": up1["palette_GBs"] / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "pal_gemm_kernel, up-projection M=1"},
+            "per_weight": out}
 
 
 def run_layers(args, torch, np, sp, W, ev, dev):

@@ -25,14 +25,15 @@ __all__ = [
     "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
     "slide_prune_pack", "slide_quant_fp8_rows",
-    "quant_int8", "quant_int8_rows",
+    "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
+    "palette_encode", "palette_decode", "palette_gemm",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
     "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
 ]
 
 BF16, FP8, INT8 = 0, 1, 2
 SCALE_DYNAMIC, SCALE_STATIC = 0, 1
-OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX = 0, 1, 2, 3
+OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX, OP_PALETTE_ANALYZE, OP_PALETTE_GEMM = 0, 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsp24.so")
@@ -44,6 +45,12 @@ if not os.path.exists(lib_path):
 lib = ctypes.CDLL(lib_path)
 
 _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+
+class _PaletteStruct(ctypes.Structure):
+    """sp24_palette_weight (include/sp24.h)."""
+    _fields_ = [("palette", _vp), ("n_pal", _i64), ("sm", _vp), ("ix", _vp), ("pal_rows", _vp),
+                ("n_verb", _i64), ("verb", _vp), ("verb_rows", _vp)]
 
 
 class Plan(ctypes.Structure):
@@ -70,6 +77,10 @@ _SIGS = {
     "sp24_slide_quant_fp8_rows": [_vp, _i64, _i64, _int, _vp, _vp, _vp],
     "sp24_gemm_rows": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
+    "sp24_palette_analyze": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_palette_pack": [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
+    "sp24_palette_decode": [ctypes.POINTER(_PaletteStruct), _i64, _i64, _vp, _vp],
+    "sp24_palette_gemm": [_i64, _i64, _i64, _vp, ctypes.POINTER(_PaletteStruct), _vp, _vp, _sz, _vp],
     "sp24_plan_gemm": [_int, _int, _i64, _i64, _i64, ctypes.POINTER(Plan)],
     "sp24_status_string": [_int],
     "sp24_version": [],
@@ -448,6 +459,97 @@ def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):
     _check("sp24_gemm_qx", lib.sp24_gemm_qx(m, n, k, _ptr(x), _ptr(x_scale), _ptr(values), _ptr(meta),
                                             _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
     return out, x_scale
+
+
+class PaletteWeight:
+    """A BF16 weight [n, k] in lossless exponent-palette form: a 16-entry exponent palette,
+    sign+mantissa bytes and 4-bit indices for the rows whose exponents are all in the
+    palette, and the other rows verbatim (see sp24_palette_weight in include/sp24.h)."""
+
+    def __init__(self, n, k, palette, pal_rows, sm, ix, verb_rows, verb):
+        self.n, self.k = n, k
+        self.palette, self.pal_rows, self.sm, self.ix = palette, pal_rows, sm, ix
+        self.verb_rows, self.verb = verb_rows, verb
+
+    @property
+    def n_pal(self) -> int:
+        return self.pal_rows.numel()
+
+    @property
+    def n_verb(self) -> int:
+        return self.verb_rows.numel()
+
+    @property
+    def nbytes(self) -> int:
+        """Bytes of the encoded weight (palette, row lists, bytes, indices, verbatim rows)."""
+        return sum(t.numel() * t.element_size() for t in
+                   (self.palette, self.pal_rows, self.sm, self.ix, self.verb_rows, self.verb))
+
+    def struct(self) -> _PaletteStruct:
+        p = lambda t: t.data_ptr() if t.numel() else None
+        return _PaletteStruct(self.palette.data_ptr(), self.n_pal, p(self.sm), p(self.ix), p(self.pal_rows),
+                              self.n_verb, p(self.verb), p(self.verb_rows))
+
+
+def palette_encode(w: torch.Tensor, ws: torch.Tensor | None = None) -> PaletteWeight:
+    """Encode a bf16 weight [n, k] (k % 128 == 0): sp24_palette_analyze, one host read of the
+    two row counts, then sp24_palette_pack into tensors of the exact (16-row padded) sizes,
+    zero-filled so that the padding is defined."""
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    dev = w.device
+    pal = torch.empty(16, dtype=torch.uint8, device=dev)
+    slot = torch.empty(n, dtype=torch.int32, device=dev)
+    counts = torch.empty(2, dtype=torch.int32, device=dev)
+    nbytes = workspace_size(OP_PALETTE_ANALYZE, BF16, 0, n, k)
+    if nbytes == 0:
+        raise ValueError("palette weights need n >= 1 and k % 128 == 0 (got %d x %d)" % (n, k))
+    ws = _workspace(nbytes, dev, ws)
+    _check("sp24_palette_analyze", lib.sp24_palette_analyze(_ptr(w), n, k, _ptr(pal), _ptr(slot), _ptr(counts),
+                                                            _ptr(ws), nbytes, _stream(dev)))
+    n_pal, n_verb = (int(v) for v in counts.cpu().tolist())
+    pad = lambda r: (r + 15) // 16 * 16
+    sm = torch.zeros(pad(n_pal) * k, dtype=torch.uint8, device=dev)
+    ix = torch.zeros(pad(n_pal) * k // 8, dtype=torch.int32, device=dev)
+    pal_rows = torch.empty(n_pal, dtype=torch.int32, device=dev)
+    verb = torch.zeros(pad(n_verb) * k, dtype=torch.bfloat16, device=dev)
+    verb_rows = torch.empty(n_verb, dtype=torch.int32, device=dev)
+    p = lambda t: _ptr(t) if t.numel() else None
+    _check("sp24_palette_pack", lib.sp24_palette_pack(_ptr(w), n, k, _ptr(pal), _ptr(slot), n_pal, n_verb, p(sm),
+                                                      p(ix), p(pal_rows), p(verb), p(verb_rows), _stream(dev)))
+    return PaletteWeight(n, k, pal, pal_rows, sm, ix, verb_rows, verb)
+
+
+def palette_decode(pw: PaletteWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The bf16 weight [n, k] back from its palette form, bit for bit."""
+    dev = pw.palette.device
+    if out is None:
+        out = torch.empty(pw.n, pw.k, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2, dev)
+    st = pw.struct()
+    _check("sp24_palette_decode", lib.sp24_palette_decode(ctypes.byref(st), pw.n, pw.k, _ptr(out), _stream(dev)))
+    return out
+
+
+def palette_gemm(x: torch.Tensor, pw: PaletteWeight, out: torch.Tensor | None = None,
+                 ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X . W^T for a bf16 X [m, k] and a palette-form W; bf16 output [m, n].  m <= 16
+    rebuilds BF16 in registers; larger m rebuilds W in the workspace and runs the dense GEMM."""
+    _need(x, "x", torch.bfloat16, 2, pw.palette.device)
+    m, k = x.shape
+    if k != pw.k:
+        raise ValueError("x has %d columns, the weight %d" % (k, pw.k))
+    if out is None:
+        out = torch.empty(m, pw.n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if tuple(out.shape) != (m, pw.n):
+        raise ValueError("out must be [%d, %d]" % (m, pw.n))
+    nbytes = workspace_size(OP_PALETTE_GEMM, BF16, m, pw.n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    st = pw.struct()
+    _check("sp24_palette_gemm", lib.sp24_palette_gemm(m, pw.n, k, _ptr(x), ctypes.byref(st), _ptr(out), _ptr(ws),
+                                                      nbytes, _stream(x.device)))
+    return out
 
 
 def dense_gemm(x, w, x_scale=None, w_scale=None, out=None, ws=None):

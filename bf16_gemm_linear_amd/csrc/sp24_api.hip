@@ -334,6 +334,71 @@ hipError_t launch_plan(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   return e;
 }
 
+// Workspace of sp24_palette_gemm: none for m <= kPaletteMaxM; otherwise the
+// rebuilt W (bf16) and the dense GEMM's own workspace after it.
+struct PaletteWs {
+  size_t weight, gemm, total;
+  bool ok;
+  sp24_plan plan;
+};
+
+PaletteWs palette_gemm_ws(int64_t m, int64_t n, int64_t k) {
+  PaletteWs w{0, 0, 0, false, {}};
+  if (m < 1 || n < 1 || k < 128 || k % 128 != 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return w;
+  w.ok = true;
+  if (m <= kPaletteMaxM) return w;
+  if (plan_gemm(SP24_OP_DENSE_GEMM, SP24_BF16, m, n, k, &w.plan) != SP24_OK) {
+    w.ok = false;
+    return w;
+  }
+  w.weight = ((size_t)n * (size_t)k * 2 + 255) / 256 * 256;
+  w.gemm = w.plan.workspace_bytes;
+  w.total = w.weight + w.gemm;
+  return w;
+}
+
+// Checks of an encoded palette weight of n rows: SP24_OK or the error.
+int check_palette(const sp24_palette_weight* pw, int64_t n) {
+  if (pw == nullptr || pw->palette == nullptr) return SP24_ERR_NULL;
+  if (pw->n_pal < 0 || pw->n_verb < 0 || pw->n_pal + pw->n_verb != n) return SP24_ERR_SHAPE;
+  if (pw->n_pal > 0 && (!pw->sm || !pw->ix || !pw->pal_rows)) return SP24_ERR_NULL;
+  if (pw->n_verb > 0 && (!pw->verb || !pw->verb_rows)) return SP24_ERR_NULL;
+  if (!aligned16(pw->palette)) return SP24_ERR_ALIGN;
+  if (pw->n_pal > 0 && (!aligned16(pw->sm) || !aligned16(pw->ix) || ((uintptr_t)pw->pal_rows & 3u)))
+    return SP24_ERR_ALIGN;
+  if (pw->n_verb > 0 && (!aligned16(pw->verb) || ((uintptr_t)pw->verb_rows & 3u))) return SP24_ERR_ALIGN;
+  return SP24_OK;
+}
+
+// Does an output of `bytes` at `out` overlap any array of the encoded weight?
+// Rows of each kind are stored in blocks of 16 (the last one padded).
+size_t pad16(int64_t rows) { return (size_t)((rows + 15) / 16 * 16); }
+
+bool overlaps_palette(const void* out, size_t bytes, const sp24_palette_weight* pw, int64_t k) {
+  if (overlaps(out, bytes, pw->palette, 16)) return true;
+  if (pw->n_pal > 0 &&
+      (overlaps(out, bytes, pw->sm, pad16(pw->n_pal) * k) || overlaps(out, bytes, pw->ix, pad16(pw->n_pal) * k / 2) ||
+       overlaps(out, bytes, pw->pal_rows, (size_t)pw->n_pal * 4)))
+    return true;
+  if (pw->n_verb > 0 && (overlaps(out, bytes, pw->verb, pad16(pw->n_verb) * k * 2) ||
+                         overlaps(out, bytes, pw->verb_rows, (size_t)pw->n_verb * 4)))
+    return true;
+  return false;
+}
+
+PaletteArgs palette_args(const sp24_palette_weight* pw) {
+  PaletteArgs a;
+  a.palette = pw->palette;
+  a.n_pal = pw->n_pal;
+  a.sm = pw->sm;
+  a.ix = pw->ix;
+  a.pal_rows = pw->pal_rows;
+  a.n_verb = pw->n_verb;
+  a.verb = static_cast<const uint16_t*>(pw->verb);
+  a.verb_rows = pw->verb_rows;
+  return a;
+}
+
 }  // namespace
 
 }  // namespace sp24
@@ -370,6 +435,11 @@ size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k) {
     if (m < 1 || k < 1) return 0;
     return quant_workspace_bytes(m * k);
   }
+  if (op == SP24_OP_PALETTE_ANALYZE) {
+    if (n < 1 || k < 128 || k % 128 != 0 || n > kMaxDim || k > kMaxDim) return 0;
+    return palette_analyze_ws_bytes(n);
+  }
+  if (op == SP24_OP_PALETTE_GEMM) return palette_gemm_ws(m, n, k).total;
   sp24_plan p;
   if (op == SP24_OP_GEMM_QX) {
     if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &p) != SP24_OK) return 0;
@@ -627,6 +697,117 @@ int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_s
                               x_scale_dev, SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
   a.x = codes;
   if (e == hipSuccess) e = launch_plan(a, p, s);
+  return finish(e, s);
+}
+
+int sp24_palette_analyze(const void* w_bf16, int64_t n, int64_t k, uint8_t* palette_dev, int32_t* row_slot_dev,
+                         int32_t* counts_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!w_bf16 || !palette_dev || !row_slot_dev || !counts_dev) return SP24_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n > kMaxDim || k > kMaxDim || n > INT_MAX) return SP24_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(palette_dev) || ((uintptr_t)row_slot_dev & 3u) || ((uintptr_t)counts_dev & 3u))
+    return SP24_ERR_ALIGN;
+  const size_t need = palette_analyze_ws_bytes(n);
+  if (ws == nullptr || ws_bytes < need) return SP24_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  const size_t wb = (size_t)n * k * 2, sb = (size_t)n * 4;
+  const void* outs[4] = {palette_dev, row_slot_dev, counts_dev, ws};
+  const size_t outb[4] = {16, sb, 8, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(outs[i], outb[i], w_bf16, wb)) return SP24_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outb[i], outs[j], outb[j])) return SP24_ERR_ALIAS;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_palette_analyze(static_cast<const uint16_t*>(w_bf16), n, k, palette_dev, row_slot_dev,
+                                       counts_dev, ws, s),
+                s);
+}
+
+int sp24_palette_pack(const void* w_bf16, int64_t n, int64_t k, const uint8_t* palette_dev,
+                      const int32_t* row_slot_dev, int64_t n_pal, int64_t n_verb, uint8_t* sm_out,
+                      uint32_t* ix_out, int32_t* pal_rows_out, void* verb_out, int32_t* verb_rows_out,
+                      void* stream) {
+  if (!w_bf16 || !palette_dev || !row_slot_dev) return SP24_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n > kMaxDim || k > kMaxDim || n > INT_MAX) return SP24_ERR_SHAPE;
+  if (n_pal < 0 || n_verb < 0 || n_pal + n_verb != n) return SP24_ERR_SHAPE;
+  if (n_pal > 0 && (!sm_out || !ix_out || !pal_rows_out)) return SP24_ERR_NULL;
+  if (n_verb > 0 && (!verb_out || !verb_rows_out)) return SP24_ERR_NULL;
+  if (!aligned16(w_bf16) || !aligned16(palette_dev) || ((uintptr_t)row_slot_dev & 3u)) return SP24_ERR_ALIGN;
+  if (n_pal > 0 && (!aligned16(sm_out) || !aligned16(ix_out) || ((uintptr_t)pal_rows_out & 3u)))
+    return SP24_ERR_ALIGN;
+  if (n_verb > 0 && (!aligned16(verb_out) || ((uintptr_t)verb_rows_out & 3u))) return SP24_ERR_ALIGN;
+  const void* ins[3] = {w_bf16, palette_dev, row_slot_dev};
+  const size_t inb[3] = {(size_t)n * k * 2, 16, (size_t)n * 4};
+  const void* outs[5] = {sm_out, ix_out, pal_rows_out, verb_out, verb_rows_out};
+  const size_t outb[5] = {pad16(n_pal) * k, pad16(n_pal) * k / 2, (size_t)n_pal * 4, pad16(n_verb) * k * 2,
+                          (size_t)n_verb * 4};
+  for (int i = 0; i < 5; ++i) {
+    if (outb[i] == 0) continue;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], outb[i], ins[j], inb[j])) return SP24_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (outb[j] != 0 && overlaps(outs[i], outb[i], outs[j], outb[j])) return SP24_ERR_ALIAS;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_palette_pack(static_cast<const uint16_t*>(w_bf16), n, k, palette_dev, row_slot_dev, n_pal,
+                                    n_verb, sm_out, ix_out, pal_rows_out, static_cast<uint16_t*>(verb_out),
+                                    verb_rows_out, s),
+                s);
+}
+
+int sp24_palette_decode(const sp24_palette_weight* pw, int64_t n, int64_t k, void* w_out_bf16, void* stream) {
+  if (!w_out_bf16) return SP24_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n > kMaxDim || k > kMaxDim || n > INT_MAX) return SP24_ERR_SHAPE;
+  const int st = check_palette(pw, n);
+  if (st != SP24_OK) return st;
+  if (!aligned16(w_out_bf16)) return SP24_ERR_ALIGN;
+  if (overlaps_palette(w_out_bf16, (size_t)n * k * 2, pw, k)) return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_palette_decode(palette_args(pw), n, k, static_cast<uint16_t*>(w_out_bf16), s), s);
+}
+
+int sp24_palette_gemm(int64_t m, int64_t n, int64_t k, const void* x_bf16, const sp24_palette_weight* pw,
+                      void* y_bf16, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_bf16 || !y_bf16) return SP24_ERR_NULL;
+  const PaletteWs wsp = palette_gemm_ws(m, n, k);
+  if (!wsp.ok || n > INT_MAX) return SP24_ERR_SHAPE;
+  const int st = check_palette(pw, n);
+  if (st != SP24_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(y_bf16)) return SP24_ERR_ALIGN;
+  if (wsp.total > 0) {
+    if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  }
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 2;
+  if (overlaps(y_bf16, yb, x_bf16, xb) || overlaps_palette(y_bf16, yb, pw, k)) return SP24_ERR_ALIAS;
+  if (wsp.total > 0 && (overlaps(ws, wsp.total, x_bf16, xb) || overlaps(ws, wsp.total, y_bf16, yb) ||
+                        overlaps_palette(ws, wsp.total, pw, k)))
+    return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PaletteArgs pa = palette_args(pw);
+  if (m <= kPaletteMaxM)
+    return finish(launch_palette_gemm_small(static_cast<const uint16_t*>(x_bf16), pa, static_cast<uint16_t*>(y_bf16),
+                                            (int)m, (int)n, (int)k, s),
+                  s);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  uint16_t* wd = reinterpret_cast<uint16_t*>(wsb);
+  hipError_t e = launch_palette_decode(pa, n, k, wd, s);
+  if (e == hipSuccess) {
+    GemmArgs a;
+    a.dtype = SP24_BF16;
+    a.sparse = false;
+    a.m = (int)m;
+    a.n = (int)n;
+    a.k = (int)k;
+    a.x = x_bf16;
+    a.x_scale = nullptr;
+    a.w = wd;
+    a.meta = nullptr;
+    a.w_scale = nullptr;
+    a.y = static_cast<uint16_t*>(y_bf16);
+    a.partial = wsp.plan.split_k > 1 ? reinterpret_cast<float*>(wsb + wsp.weight) : nullptr;
+    e = launch_plan(a, wsp.plan, s);
+  }
   return finish(e, s);
 }
 

@@ -41,6 +41,31 @@ hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k,
 hipError_t launch_quant(int dtype, const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
                         void* ws, hipStream_t s);
 
+// sp24_palette.hip: the encoded exponent-palette weight (device pointers)
+struct PaletteArgs {
+  const uint8_t* palette;   // 16 exponents
+  int64_t n_pal;            // rows in palette form
+  const uint8_t* sm;        // [n_pal, k] sign+mantissa bytes
+  const uint32_t* ix;       // [n_pal, k/8] index words
+  const int32_t* pal_rows;  // [n_pal] row numbers
+  int64_t n_verb;           // rows stored verbatim
+  const uint16_t* verb;     // [n_verb, k] bf16
+  const int32_t* verb_rows; // [n_verb] row numbers
+};
+constexpr int kPaletteWaves = 4;   // waves per workgroup of the small-m palette GEMM
+constexpr int kPaletteRb1MaxM = 4; // up to this m one 16-row block per workgroup ...
+constexpr int kPaletteRbWide = 2;  // ... above it this many blocks share a wave's X
+constexpr int kPaletteMaxM = 16;   // largest m of the kernel that rebuilds BF16 in registers
+size_t palette_analyze_ws_bytes(int64_t n);
+hipError_t launch_palette_analyze(const uint16_t* w, int64_t n, int64_t k, uint8_t* palette, int32_t* slot,
+                                  int32_t* counts, void* ws, hipStream_t s);
+hipError_t launch_palette_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* palette, const int32_t* slot,
+                               int64_t n_pal, int64_t n_verb, uint8_t* sm, uint32_t* ix, int32_t* pal_rows,
+                               uint16_t* verb, int32_t* verb_rows, hipStream_t s);
+hipError_t launch_palette_decode(const PaletteArgs& p, int64_t n, int64_t k, uint16_t* w, hipStream_t s);
+hipError_t launch_palette_gemm_small(const uint16_t* x, const PaletteArgs& p, uint16_t* y, int m, int n, int k,
+                                     hipStream_t s);
+
 // sp24_gemm_skinny.hip / sp24_gemm_stream.hip / sp24_gemm_tiled.hip / sp24_reduce.hip
 struct GemmArgs {
   int dtype;

@@ -20,6 +20,10 @@
  *     reading (no page fixes them).
  *   - The sparse product on the linear/FFN projections: the cookbook, pipeline
  *     step 2 and its "What to prune" table.
+ *   - Lossless BF16 exponent-palette weights (sp24_palette_*): the page "Unweight:
+ *     Compresion Lossless de Pesos de LLM para Inferencia en GPU H100",
+ *     architecture (16-entry exponent palette, verbatim rows) and execution
+ *     pipelines ("direct palette" and "full decode").
  *
  * Conventions shared by every entry point
  *   - All tensors are dense, contiguous, row-major device buffers owned by the
@@ -90,7 +94,9 @@ typedef enum sp24_op {
   SP24_OP_GEMM = 0,       /* sp24_gemm */
   SP24_OP_QUANT = 1,      /* sp24_quant_fp8, sp24_quant_int8 */
   SP24_OP_DENSE_GEMM = 2, /* sp24_dense_gemm */
-  SP24_OP_GEMM_QX = 3     /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
+  SP24_OP_GEMM_QX = 3,    /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
+  SP24_OP_PALETTE_ANALYZE = 4, /* sp24_palette_analyze (n = rows, k; m and dtype ignored) */
+  SP24_OP_PALETTE_GEMM = 5     /* sp24_palette_gemm (dtype ignored) */
 } sp24_op;
 
 typedef enum sp24_kernel {
@@ -262,6 +268,69 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
                  const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Lossless BF16 exponent-palette weights (no sparsity).  The 8 exponent bits of
+ * BF16 weights are highly redundant; sign and mantissa stay as one byte.  One
+ * palette per tensor holds its 16 most common exponents (by count, ties to the
+ * smaller exponent; unused entries 0xFF).  A row whose exponents are all in the
+ * palette is stored as sign+mantissa bytes sm [k] (sign << 7 | mantissa) and
+ * 4-bit palette indices ix [k/8] words (element 8g + t, t < 4, at bits
+ * [8t, 8t+4) of word g; element 8g + 4 + t at bits [8t+4, 8t+8)); every other
+ * row is stored verbatim (bf16).  Both kinds are compact, in ascending row
+ * order, with their row numbers.  Encoding is exact: sp24_palette_decode gives
+ * back W bit for bit.  Inputs must be finite; k % 128 == 0.
+ *   Storage order of sm, ix and verb: the rows of each kind in blocks of 16
+ *   (row count padded to a multiple of 16; padding is read, never stored), K in
+ *   chunks of 512 (the last chunk T*128 values, T = 1..3, when k % 512 != 0).
+ *   Inside a (block, chunk) tile the 16-byte pieces are ordered [piece j][lane
+ *   group q][row r16]: lane group q holds K [32Tq, 32T(q+1)) of the chunk and
+ *   piece j its j-th 16 bytes, so one 64-lane load reads 1 KB of consecutive
+ *   memory.  Sizes: sm pad16(n_pal)*k bytes, ix pad16(n_pal)*k/8 words, verb
+ *   pad16(n_verb)*k bf16.
+ * ------------------------------------------------------------------------- */
+typedef struct sp24_palette_weight {
+  const uint8_t* palette;   /* device, 16 bytes, 16-byte aligned */
+  int64_t n_pal;            /* rows in palette form */
+  const uint8_t* sm;        /* device, pad16(n_pal)*k bytes (16-byte aligned; NULL if n_pal == 0) */
+  const uint32_t* ix;       /* device, pad16(n_pal)*k/8 words (16-byte aligned; NULL if n_pal == 0) */
+  const int32_t* pal_rows;  /* device [n_pal] row numbers, ascending (4-byte aligned) */
+  int64_t n_verb;           /* rows stored verbatim; n_pal + n_verb == n */
+  const void* verb;         /* device, pad16(n_verb)*k bf16 (16-byte aligned; NULL if n_verb == 0) */
+  const int32_t* verb_rows; /* device [n_verb] row numbers, ascending (4-byte aligned) */
+} sp24_palette_weight;
+
+/* Encoding, first call: the palette and every row's slot.
+ *   w_bf16       in : [n, k] bf16, k % 128 == 0
+ *   palette_dev  out: 16 bytes (16-byte aligned)
+ *   row_slot_dev out: [n] int32: slot p >= 0 of a paletted row, -(v + 1) of a verbatim row
+ *   counts_dev   out: int32[2] = {n_pal, n_verb}, read by the caller to size the outputs
+ *   ws/ws_bytes: sp24_workspace_size(SP24_OP_PALETTE_ANALYZE, 0, 0, n, k). */
+int sp24_palette_analyze(const void* w_bf16, int64_t n, int64_t k, uint8_t* palette_dev, int32_t* row_slot_dev,
+                         int32_t* counts_dev, void* ws, size_t ws_bytes, void* stream);
+
+/* Encoding, second call: write the rows into their slots (from sp24_palette_analyze
+ * of the same w).  n_pal + n_verb must equal n; a slot outside [0, n_pal) or
+ * [0, n_verb) is skipped, never written.  Outputs as in sp24_palette_weight. */
+int sp24_palette_pack(const void* w_bf16, int64_t n, int64_t k, const uint8_t* palette_dev,
+                      const int32_t* row_slot_dev, int64_t n_pal, int64_t n_verb, uint8_t* sm_out,
+                      uint32_t* ix_out, int32_t* pal_rows_out, void* verb_out, int32_t* verb_rows_out,
+                      void* stream);
+
+/* Rebuild W [n, k] (bf16) from its encoded form, bit for bit.  Row numbers
+ * outside [0, n) are skipped. */
+int sp24_palette_decode(const sp24_palette_weight* pw, int64_t n, int64_t k, void* w_out_bf16, void* stream);
+
+/* Y = X . W^T (bf16 in, fp32 accumulation, bf16 out) with W in palette form.
+ *   m <= 16: the "direct palette" pipeline: the encoded rows stream from memory
+ *            and BF16 is rebuilt in registers right before the matrix
+ *            instructions; no workspace.
+ *   m > 16 : the "full decode" pipeline: W is rebuilt into the workspace, then
+ *            the dense BF16 GEMM (sp24_dense_gemm) runs on it.
+ *   x_bf16 [m, k]; y_bf16 [m, n]; k % 128 == 0; ws/ws_bytes:
+ *   sp24_workspace_size(SP24_OP_PALETTE_GEMM, 0, m, n, k). */
+int sp24_palette_gemm(int64_t m, int64_t n, int64_t k, const void* x_bf16, const sp24_palette_weight* pw,
+                      void* y_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by an op at a shape (0 if none; also 0 for invalid
  * arguments, which the op itself then rejects). */

@@ -27,7 +27,14 @@ Readings where the page is silent (each applied below and nowhere else):
     8g + t (t < 4) at bits [8t, 8t + 4), element 8g + 4 + t at bits
     [8t + 4, 8t + 8);
   * paletted and verbatim rows are stored compactly in ascending row order
-    with their row numbers; inputs must be finite.
+    with their row numbers; inputs must be finite;
+  * storage order in memory (``palette_store``): rows of each kind in blocks
+    of 16 (the last block padded), K in chunks of 512 (the last chunk T*128
+    values, T = 1..3, when K % 512 != 0); inside a (block, chunk) tile the
+    16-byte pieces are ordered [piece j][lane group q][row r16], where lane
+    group q holds K [32Tq, 32T(q+1)) of the chunk and piece j its j-th 16 bytes.
+    One 64-lane load then reads 1 KB of consecutive memory.  The format
+    needs K % 128 == 0.
 
 Every function is pinned in ``tests/test_oracle_palette.py``.
 """
@@ -115,10 +122,47 @@ def palette_decode(enc) -> np.ndarray:
     return w
 
 
+def _tile_order(row_bytes: np.ndarray, k: int, b32: int) -> np.ndarray:
+    """Storage order of compact rows [n, k/32 * b32] bytes (b32 bytes per 32 elements)."""
+    n = row_bytes.shape[0]
+    npad = (n + 15) // 16 * 16
+    width = k // 32 * b32
+    src = np.zeros((npad, width), dtype=np.uint8)
+    src[:n] = row_bytes.reshape(n, width)
+    out = np.zeros(npad * width, dtype=np.uint8)
+    units = k // 128
+    pos = 0
+    for b in range(npad // 16):
+        for c0 in range(0, units, 4):
+            t = min(4, units - c0)
+            base = c0 * 4 * b32                      # row byte offset of the chunk (4 x 32 values per unit)
+            span = t * b32                           # bytes of one lane group's K range (32t values)
+            for j in range(span // 16):
+                for q in range(4):
+                    for r16 in range(16):
+                        o = base + q * span + 16 * j
+                        out[pos:pos + 16] = src[16 * b + r16, o:o + 16]
+                        pos += 16
+    assert pos == out.size
+    return out
+
+
+def palette_store(enc):
+    """The encoded arrays in their storage order: (sign+mantissa bytes uint8, index words
+    uint32, verbatim rows uint16), each over its row count padded to a multiple of 16
+    (padding zero)."""
+    k = enc["k"]
+    assert k % 128 == 0
+    sm = _tile_order(np.asarray(enc["sm"], dtype=np.uint8), k, 32)
+    ix = _tile_order(np.ascontiguousarray(enc["ix"], dtype="<u4").view(np.uint8), k, 16).view("<u4")
+    verb = _tile_order(np.ascontiguousarray(enc["verb"], dtype="<u2").view(np.uint8), k, 64).view("<u2")
+    return sm, ix.astype(np.uint32), verb.astype(np.uint16)
+
+
 def encoded_bytes(enc) -> int:
     """Bytes of the encoded weight: palette, row lists, sign+mantissa, indices, verbatim rows."""
     n_p, n_v, k = len(enc["pal_rows"]), len(enc["verb_rows"]), enc["k"]
-    return 16 + 4 * (n_p + n_v) + n_p * k + n_p * k // 2 + 2 * n_v * k
+    return 16 + 4 * (n_p + n_v) + n_p * k + n_p * k // 2 + 2 * n_v * k   # unpadded
 
 
 def gemm_ref(x_bits: np.ndarray, w_bits: np.ndarray):

@@ -363,3 +363,61 @@ def test_int8_validation_and_plan():
     f = lib.sp24_dense_gemm
     assert f(2, 1, 1, 128, p(A), None, p(A + 0x1000), None, p(A + 0x2000), None, 0, None) == ENULL
     assert lib.sp24_workspace_size(sp.OP_GEMM_QX, 2, 1, 256, 256) == 0   # FP8 only
+
+
+def _pw(palette=A, n_pal=3, sm=A + 0x10000, ix=A + 0x20000, pal_rows=A + 0x30000, n_verb=1, verb=A + 0x40000,
+        verb_rows=A + 0x50000):
+    return sp._PaletteStruct(palette, n_pal, sm, ix, pal_rows, n_verb, verb, verb_rows)
+
+
+def test_palette_analyze_and_pack_validation():
+    n, k = 4, 128
+    need = lib.sp24_workspace_size(sp.OP_PALETTE_ANALYZE, 0, 0, n, k)
+    assert need >= 256 * 4 + 256 + n * 4
+    assert lib.sp24_workspace_size(sp.OP_PALETTE_ANALYZE, 0, 0, n, 12) == 0     # k % 8
+    an = lambda w=A, n=n, k=k, pal=A + 0x10000, slot=A + 0x20000, cnt=A + 0x30000, ws=A + 0x40000, wsb=need: \
+        lib.sp24_palette_analyze(p(w), n, k, p(pal), p(slot), p(cnt), p(ws), wsb, None)
+    assert an(w=None) == ENULL and an(pal=None) == ENULL and an(slot=None) == ENULL and an(cnt=None) == ENULL
+    assert an(n=0) == ESHAPE and an(k=12) == ESHAPE and an(k=0) == ESHAPE and an(k=64) == ESHAPE
+    assert an(w=A + 8) == EALIGN and an(pal=A + 0x10004) == EALIGN and an(slot=A + 0x20002) == EALIGN
+    assert an(ws=None) == EWS and an(wsb=need - 1) == EWS and an(ws=A + 0x40008) == EALIGN
+    assert an(pal=A + 0x100) == EALIAS                      # palette inside W (4 x 128 bf16 = 1 KB)
+    assert an(slot=A + 0x10000) == EALIAS                   # slots over the palette
+    pk = lambda w=A, n=n, k=k, pal=A + 0x10000, slot=A + 0x20000, npl=3, nvb=1, sm=A + 0x30000, ix=A + 0x40000, \
+        pr=A + 0x50000, vb=A + 0x60000, vr=A + 0x70000: lib.sp24_palette_pack(
+            p(w), n, k, p(pal), p(slot), npl, nvb, p(sm), p(ix), p(pr), p(vb), p(vr), None)
+    assert pk(npl=2) == ESHAPE and pk(npl=-1, nvb=5) == ESHAPE   # n_pal + n_verb == n
+    assert pk(sm=None) == ENULL and pk(vr=None) == ENULL
+    assert pk(w=A + 4) == EALIGN and pk(sm=A + 0x30008) == EALIGN and pk(pr=A + 0x50002) == EALIGN
+    assert pk(sm=A + 0x100) == EALIAS                        # codes over W
+    assert pk(ix=A + 0x30000 + 64) == EALIAS                 # indices over the codes (16 x 128 bytes)
+
+
+def test_palette_decode_and_gemm_validation():
+    n, k = 4, 128
+    d = lambda pw=None, n=n, k=k, out=A + 0x100000: lib.sp24_palette_decode(
+        ctypes.byref(pw if pw is not None else _pw()), n, k, p(out), None)
+    assert lib.sp24_palette_decode(None, n, k, p(A + 0x100000), None) == ENULL
+    assert d(out=None) == ENULL
+    assert d(pw=_pw(palette=None)) == ENULL
+    assert d(pw=_pw(n_pal=2)) == ESHAPE                      # rows do not add up to n
+    assert d(pw=_pw(sm=None)) == ENULL and d(pw=_pw(verb_rows=None)) == ENULL
+    assert d(pw=_pw(palette=A + 8)) == EALIGN and d(pw=_pw(ix=A + 0x20004)) == EALIGN
+    assert d(pw=_pw(pal_rows=A + 0x30002)) == EALIGN
+    assert d(k=12) == ESHAPE
+    assert d(out=A + 0x40000 + 64) == EALIAS                 # output over the verbatim rows
+    # n_pal == 0: its arrays may be NULL (the verbatim ones are still checked)
+    assert d(pw=_pw(n_pal=0, n_verb=4, sm=None, ix=None, pal_rows=None), out=A + 8) == EALIGN
+    g = lambda m=1, n=n, k=k, x=A + 0x200000, pw=None, y=A + 0x300000, ws=None, wsb=0: lib.sp24_palette_gemm(
+        m, n, k, p(x), ctypes.byref(pw if pw is not None else _pw()), p(y), p(ws), wsb, None)
+    assert g(x=None) == ENULL and g(y=None) == ENULL
+    assert g(k=64) == ESHAPE and g(m=0) == ESHAPE and g(pw=_pw(n_verb=3)) == ESHAPE
+    assert g(x=A + 0x200008) == EALIGN
+    assert g(y=A + 0x200000 + 64) == EALIAS                  # y over x
+    assert g(y=A + 0x10000) == EALIAS                        # y over the codes
+    # m <= 16 needs no workspace; larger m needs the rebuilt weight plus the dense GEMM's
+    assert lib.sp24_workspace_size(sp.OP_PALETTE_GEMM, 0, 16, 4096, 4096) == 0
+    big = lib.sp24_workspace_size(sp.OP_PALETTE_GEMM, 0, 17, 4096, 4096)
+    assert big >= 4096 * 4096 * 2
+    assert lib.sp24_workspace_size(sp.OP_PALETTE_GEMM, 0, 17, 4096, 4000) == 0   # k % 128
+    assert g(m=17, n=4, ws=None) == EWS

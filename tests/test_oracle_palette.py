@@ -109,3 +109,35 @@ def test_gemm_ref_against_triple_loop(rng):
             s = sum(float(xf[i, t]) * float(wf[j, t]) for t in range(16))
             a = sum(abs(float(xf[i, t]) * float(wf[j, t])) for t in range(16))
             assert abs(ref[i, j] - s) <= 1e-12 * a and abs(mag[i, j] - a) <= 1e-12 * a
+
+
+def test_storage_order_hand_example():
+    """One block of 16 rows, K = 128 (one chunk of T = 1): lane group q holds K [32q, 32q + 32);
+    piece j of (q, r16) sits at 16 * (64 j + 16 q + r16)."""
+    k = 128
+    sm = (np.arange(16 * k, dtype=np.int64) % 251).astype(np.uint8).reshape(16, k)
+    enc = {"k": k, "sm": sm, "ix": np.zeros((16, k // 8), np.uint32), "verb": np.zeros((0, k), np.uint16)}
+    st, _, _ = P.palette_store(enc)
+    for j in range(2):
+        for q in range(4):
+            for r in range(16):
+                o = 16 * (64 * j + 16 * q + r)
+                assert np.array_equal(st[o:o + 16], sm[r, 32 * q + 16 * j: 32 * q + 16 * j + 16])
+
+
+def test_storage_order_is_a_permutation_with_padding(rng):
+    """Every byte of every row appears once; padded rows are zero; K tails of 1-3 units."""
+    for n, k in ((5, 384), (16, 640), (33, 1536)):
+        sm = rng.integers(1, 256, size=(n, k)).astype(np.uint8)
+        ix = rng.integers(1, 2 ** 32, size=(n, k // 8), dtype=np.uint64).astype(np.uint32)
+        verb = rng.integers(1, 2 ** 16, size=(n, k)).astype(np.uint16)
+        st_sm, st_ix, st_v = P.palette_store({"k": k, "sm": sm, "ix": ix, "verb": verb})
+        npad = (n + 15) // 16 * 16
+        assert st_sm.size == npad * k and st_ix.size == npad * k // 8 and st_v.size == npad * k
+        assert np.array_equal(np.sort(st_sm[st_sm != 0]), np.sort(sm.ravel()))
+        assert np.array_equal(np.sort(st_ix[st_ix != 0]), np.sort(ix.ravel()))
+        assert np.array_equal(np.sort(st_v[st_v != 0]), np.sort(verb.ravel()))
+        assert (st_sm == 0).sum() == (npad - n) * k
+        # the first chunk of block 0: lane group 1, piece 0 of row 0 = row 0's K [32T, 32T + 16)
+        t = min(4, k // 128)
+        assert np.array_equal(st_sm[16 * 16:16 * 17], sm[0, 32 * t:32 * t + 16])
