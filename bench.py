@@ -560,7 +560,36 @@ def run_palette(args, torch, np, sp, W, ev, dev):
             "roofline": {"bound": "hbm", "achieved": up1["palette_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": up1["palette_GBs"] / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "pal_gemm_kernel, up-projection M=1"},
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_palette_baseline(W),
             "per_weight": out}
+
+
+def cpu_palette_baseline(W):
+    """The CPU oracle's per-call path for palette weights -- rebuild W from its encoded form
+    and the float64 product -- on the first 1024 rows of the up-projection weight at M=1
+    (encoding, a load-time step, is not timed), repeated for about 10 s."""
+    import numpy as np
+
+    from oracle import palette_ref as P
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wb = W.bf16_bits(W.up_weight()[:1024])
+    xb = W.bf16_bits(W.up_x(1))
+    enc = P.palette_encode(wb)
+    nbytes = P.encoded_bytes(enc) + xb.size * 2 + 1024 * 2
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        P.gemm_ref(xb, P.palette_decode(enc))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 200:
+            break
+    return {"value": nbytes * reps / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d call(s) on rows 0..1023 of the up-projection weight at M=1 (rebuild W from the "
+                      "palette form, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
 
 
 def run_layers(args, torch, np, sp, W, ev, dev):
