@@ -218,3 +218,44 @@ def test_gemm_int8_repeatable():
     y2 = sp.gemm(xq, qv, meta, x_scale=sx, w_scale=sw)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def _sampled_int8(x_cpu, w_cpu, what, n_rows=256, n_tokens=None, seed=0):
+    """Full-size INT8 run of the bench shapes; the oracle checks sampled W rows and tokens
+    (scales from every value: the per-tensor maximum survives 2:4 pruning)."""
+    sp = need_sp()
+    announce("gemm int8 sampled", what, tuple(x_cpu.shape), tuple(w_cpu.shape))
+    values, meta = sp.prune_compress(w_cpu.to(DEV))
+    qv, sw = sp.quant_int8(values)
+    xq, sx = sp.quant_int8(x_cpu.to(DEV))
+    y = sp.gemm(xq, qv, meta, x_scale=sx, w_scale=sw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    n, m, k = w_cpu.shape[0], x_cpu.shape[0], w_cpu.shape[1]
+    rows = np.unique(np.concatenate([np.sort(rng.choice(n, size=min(n_rows, n), replace=False)), [0, n - 1]]))
+    toks = np.arange(m) if n_tokens is None else np.unique(np.concatenate(
+        [np.sort(rng.choice(m, size=n_tokens, replace=False)), [0, m - 1]]))
+    wb, xb = W.bf16_bits(w_cpu), W.bf16_bits(x_cpu)
+    ov, om = O.prune_compress(wb[rows])
+    osw = O.int8_scale(wb)
+    oq, _ = O.quant_int8(ov, scale=osw)
+    osx = O.int8_scale(xb)
+    oxq, _ = O.quant_int8(xb[toks], scale=osx)
+    assert f32_bits(f32(sw)) == f32_bits(osw) and f32_bits(f32(sx)) == f32_bits(osx)
+    assert np.array_equal(i8(qv)[rows], oq)
+    assert np.array_equal(i8(xq)[toks], oxq)
+    assert np.array_equal(O.load_meta(u32(meta), n, k, rows), om)
+    ref, mag = O.gemm_ref(*O.sparse_operands_int8(oxq, osx, oq, om, osw, k))
+    yb = bits(y)[np.ix_(toks, rows)]
+    assert_within_tolerance(yb, ref, mag, what)
+    assert_exact_sum_bound(yb, ref, mag, what)
+
+
+def test_prefill_sampled_int8():
+    _sampled_int8(W.prefill_x(), W.prefill_weight(), "prefill int8", n_rows=256, n_tokens=256)
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_decode_sampled_int8(m):
+    _sampled_int8(W.up_x(m), W.up_weight(), "up int8 M=%d" % m, seed=m)
+    _sampled_int8(W.down_x(m), W.down_weight(), "down int8 M=%d" % m, seed=m + 1)
