@@ -55,6 +55,9 @@ struct PaletteArgs {
 constexpr int kPaletteWaves = 4;   // waves per workgroup of the small-m palette GEMM
 constexpr int kPaletteRb1MaxM = 4; // up to this m one 16-row block per workgroup ...
 constexpr int kPaletteRbWide = 2;  // ... above it this many blocks share a wave's X
+constexpr int kPaletteXlMaxM = 1;        // X in LDS for m up to this ...
+constexpr int kPaletteXLdsBytes = 61440;  // ... and X rows up to this size (with the
+                                          // 4 KB reduction buffer, within 64 KB per workgroup)
 constexpr int kPaletteMaxM = 16;   // largest m of the kernel that rebuilds BF16 in registers
 size_t palette_analyze_ws_bytes(int64_t n);
 hipError_t launch_palette_analyze(const uint16_t* w, int64_t n, int64_t k, uint8_t* palette, int32_t* slot,

@@ -275,18 +275,19 @@ __global__ __launch_bounds__(kPalThreads) void pal_decode_kernel(
 // lane % 16) uses the same map, so the sum over K is the product's.  The
 // accumulator (v_mfma_f32_16x16x32_bf16) is a tile of Y^T: lane l, register
 // j <-> row 4(l/16) + j, token l % 16.
-template <bool VERB, int T, int RB>
+template <bool VERB, int T, int RB, bool XL>
 struct PalChunk {
   // per lane and row block: paletted: 32T sign+mantissa bytes (2T vectors) and
-  // 4T index words (T vectors); verbatim: 32T bf16 (4T vectors); X: 32T bf16 (4T vectors)
+  // 4T index words (T vectors); verbatim: 32T bf16 (4T vectors); X: 32T bf16
+  // (4T vectors), unless X sits in LDS (XL)
   static constexpr int WV = VERB ? 4 * T : 2 * T;
   i32x4 wv[RB][WV];
   i32x4 iv[RB][VERB ? 1 : T];
-  i32x4 xv[4 * T];
+  i32x4 xv[XL ? 1 : 4 * T];
 };
 
-template <bool VERB, int T, int RB>
-__device__ __forceinline__ void pal_load(PalChunk<VERB, T, RB>& c, const uint8_t* __restrict__ wbase,
+template <bool VERB, int T, int RB, bool XL>
+__device__ __forceinline__ void pal_load(PalChunk<VERB, T, RB, XL>& c, const uint8_t* __restrict__ wbase,
                                          const uint8_t* __restrict__ ixbase, const uint16_t* __restrict__ x,
                                          int blk0, int last_blk, int chunk, int lane, int token, int kq, int M,
                                          int K) {
@@ -306,21 +307,31 @@ __device__ __forceinline__ void pal_load(PalChunk<VERB, T, RB>& c, const uint8_t
       for (int j = 0; j < T; ++j) c.iv[rb][j] = *reinterpret_cast<const i32x4*>(q + 1024 * j);
     }
   }
-  if (token < M) {
-    const uint16_t* xr = x + (int64_t)token * K + kq;
+  if constexpr (!XL) {
+    if (token < M) {
+      const uint16_t* xr = x + (int64_t)token * K + kq;
 #pragma unroll
-    for (int j = 0; j < 4 * T; ++j) c.xv[j] = *reinterpret_cast<const i32x4*>(xr + 8 * j);
-  } else {
+      for (int j = 0; j < 4 * T; ++j) c.xv[j] = *reinterpret_cast<const i32x4*>(xr + 8 * j);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4 * T; ++j) c.xv[j] = i32x4{0, 0, 0, 0};
+      for (int j = 0; j < 4 * T; ++j) c.xv[j] = i32x4{0, 0, 0, 0};
+    }
   }
 }
 
-template <bool VERB, int T, int RB>
-__device__ __forceinline__ void pal_mma(f32x4 (&acc)[RB], const PalChunk<VERB, T, RB>& c, uint32_t t0, uint32_t t1,
-                                        uint32_t t2, uint32_t t3) {
+// X in LDS (XL): row t of X at byte t * xstride; lanes of tokens >= M use zeros.
+template <bool VERB, int T, int RB, bool XL>
+__device__ __forceinline__ void pal_mma(f32x4 (&acc)[RB], const PalChunk<VERB, T, RB, XL>& c, uint32_t t0, uint32_t t1,
+                                        uint32_t t2, uint32_t t3, const uint8_t* xl, int kq, int token, int M) {
 #pragma unroll
   for (int j = 0; j < 4 * T; ++j) {  // instruction j: values [8j, 8j + 8) of the lane's range
+    i32x4 xb;
+    if constexpr (XL) {
+      xb = i32x4{0, 0, 0, 0};
+      if (token < M) xb = *reinterpret_cast<const i32x4*>(xl + 2 * (kq + 8 * j));
+    } else {
+      xb = c.xv[j];
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       i32x4 a;
@@ -331,49 +342,63 @@ __device__ __forceinline__ void pal_mma(f32x4 (&acc)[RB], const PalChunk<VERB, T
         const u32x2 smv = (j & 1) ? u32x2{(uint32_t)s[2], (uint32_t)s[3]} : u32x2{(uint32_t)s[0], (uint32_t)s[1]};
         a = rebuild8(smv, (uint32_t)c.iv[rb][j >> 2][j & 3], t0, t1, t2, t3);
       }
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, c.xv[j]), acc[rb], 0, 0, 0);
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, xb),
+                                                        acc[rb], 0, 0, 0);
     }
   }
 }
 
-template <bool VERB, int T, int RB>
+template <bool VERB, int T, int RB, bool XL>
 __device__ __forceinline__ void pal_chunk(f32x4 (&acc)[RB], const uint8_t* wbase, const uint8_t* ixbase,
-                                          const uint16_t* x, int blk0, int last_blk, int chunk, int lane, int token,
-                                          int M, int K, uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
-  PalChunk<VERB, T, RB> c;
-  pal_load<VERB, T, RB>(c, wbase, ixbase, x, blk0, last_blk, chunk, lane, token, chunk * 512 + 32 * T * (lane >> 4),
-                        M, K);
-  pal_mma<VERB, T, RB>(acc, c, t0, t1, t2, t3);
+                                          const uint16_t* x, const uint8_t* xl, int blk0, int last_blk, int chunk,
+                                          int lane, int token, int M, int K, uint32_t t0, uint32_t t1, uint32_t t2,
+                                          uint32_t t3) {
+  PalChunk<VERB, T, RB, XL> c;
+  const int kq = chunk * 512 + 32 * T * (lane >> 4);
+  pal_load<VERB, T, RB, XL>(c, wbase, ixbase, x, blk0, last_blk, chunk, lane, token, kq, M, K);
+  pal_mma<VERB, T, RB, XL>(acc, c, t0, t1, t2, t3, xl, kq, token, M);
 }
 
-template <bool VERB, int NW, int RB>
+template <bool VERB, int NW, int RB, bool XL>
 __device__ __forceinline__ void pal_rows_tile(f32x4 (&acc)[RB], const uint8_t* wbase, const uint8_t* ixbase,
-                                              const uint16_t* x, int blk0, int last_blk, int token, int wave,
-                                              int lane, int M, int K, uint32_t t0, uint32_t t1, uint32_t t2,
-                                              uint32_t t3) {
+                                              const uint16_t* x, const uint8_t* xl, int blk0, int last_blk, int token,
+                                              int wave, int lane, int M, int K, uint32_t t0, uint32_t t1,
+                                              uint32_t t2, uint32_t t3) {
   const int units = K / 128, full = units / 4, tail = units % 4;
-  // one chunk's loads in flight per wave; the waves of the CU's workgroups
-  // keep the memory system busy
-  for (int c = wave; c < full; c += NW)
-    pal_chunk<VERB, 4, RB>(acc, wbase, ixbase, x, blk0, last_blk, c, lane, token, M, K, t0, t1, t2, t3);
+  int c = wave;
+  if constexpr (XL) {
+    // X comes from LDS, so the registers hold two chunks of W: both loads in flight
+    for (; c + NW < full; c += 2 * NW) {
+      PalChunk<VERB, 4, RB, XL> a, b;
+      const int ka = c * 512 + 128 * (lane >> 4), kb = ka + NW * 512;
+      pal_load<VERB, 4, RB, XL>(a, wbase, ixbase, x, blk0, last_blk, c, lane, token, ka, M, K);
+      pal_load<VERB, 4, RB, XL>(b, wbase, ixbase, x, blk0, last_blk, c + NW, lane, token, kb, M, K);
+      pal_mma<VERB, 4, RB, XL>(acc, a, t0, t1, t2, t3, xl, ka, token, M);
+      pal_mma<VERB, 4, RB, XL>(acc, b, t0, t1, t2, t3, xl, kb, token, M);
+    }
+  }
+  // otherwise one chunk's loads in flight per wave; the waves of the CU's
+  // workgroups keep the memory system busy
+  for (; c < full; c += NW)
+    pal_chunk<VERB, 4, RB, XL>(acc, wbase, ixbase, x, xl, blk0, last_blk, c, lane, token, M, K, t0, t1, t2, t3);
   if (tail != 0 && wave == full % NW) {
     if (tail == 1)
-      pal_chunk<VERB, 1, RB>(acc, wbase, ixbase, x, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
+      pal_chunk<VERB, 1, RB, XL>(acc, wbase, ixbase, x, xl, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
     else if (tail == 2)
-      pal_chunk<VERB, 2, RB>(acc, wbase, ixbase, x, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
+      pal_chunk<VERB, 2, RB, XL>(acc, wbase, ixbase, x, xl, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
     else
-      pal_chunk<VERB, 3, RB>(acc, wbase, ixbase, x, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
+      pal_chunk<VERB, 3, RB, XL>(acc, wbase, ixbase, x, xl, blk0, last_blk, full, lane, token, M, K, t0, t1, t2, t3);
   }
 }
 
-template <int NW, int RB>
+template <int NW, int RB, bool XL>
 __global__ __launch_bounds__(NW * 64) void pal_gemm_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ palette, int n_pal, const uint8_t* __restrict__ sm,
     const uint32_t* __restrict__ ix, const int32_t* __restrict__ pal_rows, int n_verb,
     const uint16_t* __restrict__ verb, const int32_t* __restrict__ verb_rows, uint16_t* __restrict__ y, int M, int N,
     int K) {
   __shared__ float red[NW * RB * 256];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];  // XL: X [M, K] bf16, rows xstride apart
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gp = (n_pal + 16 * RB - 1) / (16 * RB);     // workgroups of paletted rows
   const bool verb_blk = (int)blockIdx.x >= gp;          // uniform per workgroup
@@ -383,16 +408,27 @@ __global__ __launch_bounds__(NW * 64) void pal_gemm_kernel(
   const int token = lane & 15;
   uint32_t t0, t1, t2, t3;
   load_palette(palette, t0, t1, t2, t3);
+  const int xstride = 2 * K + 64;  // bytes: consecutive tokens' rows start 16 banks apart
+  if constexpr (XL) {
+    const int vecs = K / 8;  // 16-byte vectors per row
+    for (int i = threadIdx.x; i < M * vecs; i += NW * 64) {
+      const int t = i / vecs, v = i - t * vecs;
+      *reinterpret_cast<i32x4*>(xlds + t * xstride + 16 * v) =
+          *reinterpret_cast<const i32x4*>(x + (int64_t)t * K + 8 * v);
+    }
+    __syncthreads();
+  }
+  const uint8_t* xl = xlds + (token < M ? token : 0) * xstride;
 
   f32x4 acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (verb_blk)
-    pal_rows_tile<true, NW, RB>(acc, reinterpret_cast<const uint8_t*>(verb), nullptr, x, blk0, last_blk, token, wave,
-                                lane, M, K, t0, t1, t2, t3);
+    pal_rows_tile<true, NW, RB, XL>(acc, reinterpret_cast<const uint8_t*>(verb), nullptr, x, xl, blk0, last_blk,
+                                    token, wave, lane, M, K, t0, t1, t2, t3);
   else
-    pal_rows_tile<false, NW, RB>(acc, sm, reinterpret_cast<const uint8_t*>(ix), x, blk0, last_blk, token, wave, lane,
-                                 M, K, t0, t1, t2, t3);
+    pal_rows_tile<false, NW, RB, XL>(acc, sm, reinterpret_cast<const uint8_t*>(ix), x, xl, blk0, last_blk, token,
+                                     wave, lane, M, K, t0, t1, t2, t3);
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -452,19 +488,26 @@ hipError_t launch_palette_decode(const PaletteArgs& p, int64_t n, int64_t k, uin
   return hipGetLastError();
 }
 
-template <int RB>
+template <int RB, bool XL>
 hipError_t launch_pal_gemm(const uint16_t* x, const PaletteArgs& p, uint16_t* y, int m, int n, int k, hipStream_t s) {
   const int64_t blocks = (p.n_pal + 16 * RB - 1) / (16 * RB) + (p.n_verb + 16 * RB - 1) / (16 * RB);
-  hipLaunchKernelGGL((pal_gemm_kernel<kPaletteWaves, RB>), dim3((int)blocks), dim3(kPaletteWaves * 64), 0, s, x,
-                     p.palette, (int)p.n_pal, p.sm, p.ix, p.pal_rows, (int)p.n_verb, p.verb, p.verb_rows, y, m, n,
+  const size_t lds = XL ? (size_t)m * (2 * k + 64) : 0;
+  hipLaunchKernelGGL((pal_gemm_kernel<kPaletteWaves, RB, XL>), dim3((int)blocks), dim3(kPaletteWaves * 64), lds, s,
+                     x, p.palette, (int)p.n_pal, p.sm, p.ix, p.pal_rows, (int)p.n_verb, p.verb, p.verb_rows, y, m, n,
                      k);
   return hipGetLastError();
 }
 
 hipError_t launch_palette_gemm_small(const uint16_t* x, const PaletteArgs& p, uint16_t* y, int m, int n, int k,
                                      hipStream_t s) {
-  // more tokens: more row blocks share a wave's X registers (X is re-read from L2 per workgroup)
-  return m <= kPaletteRb1MaxM ? launch_pal_gemm<1>(x, p, y, m, n, k, s) : launch_pal_gemm<kPaletteRbWide>(x, p, y, m, n, k, s);
+  // one token with a short enough X: X once per workgroup into LDS, and the registers
+  // free for two chunks of W in flight (measured faster at m = 1, slower at m = 4);
+  // more tokens: more row blocks share a wave's X registers (X is re-read from L2 per
+  // workgroup)
+  if (m <= kPaletteXlMaxM && (int64_t)m * (2 * k + 64) <= kPaletteXLdsBytes)
+    return launch_pal_gemm<1, true>(x, p, y, m, n, k, s);
+  return m <= kPaletteRb1MaxM ? launch_pal_gemm<1, false>(x, p, y, m, n, k, s)
+                              : launch_pal_gemm<kPaletteRbWide, false>(x, p, y, m, n, k, s);
 }
 
 }  // namespace sp24
