@@ -343,6 +343,11 @@ def main():
             per_m[m]["dense_GBs"] = db / t / 1e9
             per_m[m]["sparse_speedup_vs_dense"] = t / (per_m[m]["gemm_us"] / 1e6)
             del g
+            if kind == "fp8":
+                tv = vendor_dense_fp8(torch, ev, xin, wd_copies, bufs[m]["sx"], sw, m, bound)
+                if tv is not None:
+                    per_m[m]["vendor_dense_fp8_us"] = tv * 1e6
+                    per_m[m]["sparse_speedup_vs_vendor_dense"] = tv / (per_m[m]["gemm_us"] / 1e6)
         del wd_copies, wd
 
     if bound == "hbm":
@@ -392,6 +397,26 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out))
+
+
+def vendor_dense_fp8(torch, ev, xq, w_copies, sx, sw, m, bound):
+    """Reference only: the same dense FP8 product through torch._scaled_mm (hipBLASLt on
+    ROCm), X padded to 16 rows, back-to-back launches without graphs.  None if unavailable."""
+    try:
+        f8 = torch.float8_e4m3fn
+        mp = max(16, (m + 15) // 16 * 16)
+        xp = torch.zeros(mp, xq.shape[1], dtype=f8, device=xq.device)
+        xp[:m] = xq.view(f8)
+        ws = [w.view(f8) for w in w_copies]
+        fn = lambda i: torch._scaled_mm(xp, ws[i % len(ws)].t(), scale_a=sx.reshape(()), scale_b=sw.reshape(()),
+                                        out_dtype=torch.bfloat16)
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        reps = 8 * len(ws) if bound == "hbm" else 5
+        return ev.time(fn, reps) / reps
+    except Exception:  # pragma: no cover - depends on the torch build
+        return None
 
 
 def run_slide(args, torch, np, sp, W, ev, dev):
