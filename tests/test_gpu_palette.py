@@ -62,7 +62,8 @@ def test_encode_and_decode_bit_exact(kind, n, k):
 
 # (m, n, k, kind): m <= 16 -> registers; m > 16 -> rebuilt W + dense GEMM.  K chunks with
 # tails of 1, 2 and 3 units of 128 (640, 768, 384, 896, 256) and ragged row counts of both kinds.
-GEMM_CASES = [(1, 1000, 640, "gauss"), (3, 300, 768, "gauss"), (16, 37, 384, "gauss"), (5, 257, 896, "few"),
+GEMM_CASES = [(1, 1, 128, "gauss"), (16, 17, 512, "few"), (2, 1, 256, "allverb"),
+              (1, 1000, 640, "gauss"), (3, 300, 768, "gauss"), (16, 37, 384, "gauss"), (5, 257, 896, "few"),
               (2, 40, 256, "allverb"), (1, 4096, 4096, "gauss"), (17, 1000, 640, "gauss"),
               (64, 2048, 1024, "gauss"), (300, 700, 512, "few"), (1, 14336, 4096, "up")]
 
