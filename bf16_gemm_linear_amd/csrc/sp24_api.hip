@@ -196,6 +196,29 @@ Cfg skinny_cfg(int id) {
   return Cfg{1, 1, 8, 1};
 }
 
+// K split of the LDS-tiled kernel (256 x 256 tiles): 1 without a split, 0 when the
+// tiled kernel is not the plan, negative when a requested split is invalid.
+// K slices are whole steps (128 values for one-byte codes, 64 for bf16), an even
+// number of them (bf16 metadata steps come in pairs of words), at most 64 slices.
+// req >= 0: the split asked for through SP24_TILE (0: automatic); req < 0: the
+// automatic choice.  It takes the tiled kernel for m > 256 with at least 128 tiles,
+// and for 128 < m <= 256 (one tile of tokens) with at least 96 tiles, where it beats
+// the small-m kernels (measured at m = 256: gate+up 28672 x 4096, FP8 41 against
+// 43 us; BF16, whose 256-token stream configurations do not fit LDS, 65 us with K
+// split in two against 104 us).  Fewer tiles leave CUs idle and the small-m
+// kernels win (QKV, O, down of the same layer: 1.5-3x).
+int tiled_split(int dtype, bool sparse, int64_t m, int64_t n, int64_t k, int64_t tiles, int req) {
+  (void)n;
+  (void)sparse;
+  const int64_t steps = k / (dtype == SP24_BF16 ? 64 : 128);
+  auto valid = [&](int64_t s) { return s >= 1 && s <= 64 && steps % s == 0 && (s == 1 || (steps / s) % 2 == 0); };
+  if (req > 0) return valid(req) ? (int)req : -1;
+  if (req == 0) return 1;
+  if (m > 256 && tiles >= 128) return 1;
+  if (m > 128 && m <= 256 && tiles >= 96) return dtype == SP24_BF16 && valid(2) ? 2 : 1;
+  return 0;
+}
+
 }  // namespace
 
 int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out) {
@@ -225,19 +248,20 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     id = oid;
     sk = osk;
   }
-  if ((!forced && m > 256 && tiles >= 128) || (forced && id == kTiledConfig)) {
-    if (tiles > INT_MAX) return SP24_ERR_SHAPE;
+  const int tsk = tiled_split(dtype, op == SP24_OP_GEMM, m, n, k, tiles, forced && id == kTiledConfig ? sk : -1);
+  if ((!forced && tsk > 0) || (forced && id == kTiledConfig)) {
+    if (tiles > INT_MAX || tsk < 1) return SP24_ERR_SHAPE;
     out->kernel = SP24_KERNEL_TILED;
     out->tile_n = 256;
     out->tile_m = 256;
     out->waves = 8;
-    out->split_k = 1;
+    out->split_k = tsk;
     out->grid_x = (int)tiles;
-    out->grid_y = 1;
+    out->grid_y = tsk;
     out->grid_z = 1;
     out->config = kTiledConfig;
     out->batch = 1;
-    out->workspace_bytes = 0;
+    out->workspace_bytes = tsk > 1 ? (size_t)tsk * (size_t)m * (size_t)n * sizeof(float) : 0;
     return SP24_OK;
   }
   if (forced && id >= kStreamBase) {

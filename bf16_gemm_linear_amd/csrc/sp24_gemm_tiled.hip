@@ -120,9 +120,11 @@ struct Loader {
   int wave;  // wave-uniform (scalar)
   size_t mblock;  // metadata words per 128-K block of all N rows
 
+  // ks0: first K step of this workgroup's K slice (split-K; even, so that the
+  // metadata offset of bf16's 2-word steps stays whole blocks of 4 words)
   __device__ __forceinline__ Loader(const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
                                     const uint8_t* __restrict__ x, int n0, int m0, int N, int M,
-                                    int K, int wave_, int lane)
+                                    int K, int wave_, int lane, int ks0 = 0)
       : wave(wave_), mblock((size_t)N * 4) {
     const size_t wrow = SPARSE ? (size_t)(K / 2) * L::ESZ : (size_t)K * L::ESZ;
 #pragma unroll
@@ -145,6 +147,16 @@ struct Loader {
       const int p = (wave * S::X_INSTR + j) * 64 + lane, row = p / L::XP;
       const int m = min(m0 + row, M - 1);
       xp[j] = x + (size_t)m * xrow + 16 * swz16<L::XP>(row, p % L::XP);
+    }
+    if (ks0 != 0) {
+#pragma unroll
+      for (int j = 0; j < S::W_INSTR; ++j) wp[j] += (size_t)ks0 * L::WB;
+      if constexpr (SPARSE) {
+#pragma unroll
+        for (int j = 0; j < S::M_INSTR; ++j) mp[j] += meta_step(ks0);
+      }
+#pragma unroll
+      for (int j = 0; j < S::X_INSTR; ++j) xp[j] += (size_t)ks0 * L::XB;
     }
   }
 
@@ -353,11 +365,14 @@ __device__ __forceinline__ void inner_substeps(f32x16 (&acc)[TI][TJ], Frag<DT, S
   }
 }
 
-template <int DT, bool SPARSE>
+// PARTIAL (split-K): workgroup (tile, blockIdx.y) multiplies K steps
+// [blockIdx.y * slice_steps, +slice_steps) and writes its fp32 tile, unscaled, to
+// partial[blockIdx.y][m][n]; the reduction applies the scales.
+template <int DT, bool SPARSE, bool PARTIAL>
 __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-    int M, int N, int K, int xs_step) {
+    int M, int N, int K, int xs_step, float* __restrict__ partial, int slice_steps) {
   using L = TiledLayout<DT, SPARSE>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::LDS_BYTES];
 
@@ -399,8 +414,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
   // drain the ring; the explicit counter waits provide the ordering.
   constexpr int STAGES = L::STAGES, SUB = L::SUB;
   constexpr int PER_STEP = StageLoads<DT, SPARSE>::TOTAL;
-  const int nks = K / L::KS;
-  const Loader<DT, SPARSE> ld(w, meta, x, n0, m0, N, M, K, wave, lane);
+  const int nks = PARTIAL ? slice_steps : K / L::KS;
+  const Loader<DT, SPARSE> ld(w, meta, x, n0, m0, N, M, K, wave, lane, PARTIAL ? (int)blockIdx.y * slice_steps : 0);
 #pragma unroll
   for (int p = 0; p < STAGES; ++p)
     if (p < nks) ld.issue(lds + p * L::STAGE, p);
@@ -443,6 +458,40 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
   // 8-byte writes of a 32-row strip spread over the banks.
   constexpr int YS = L::YS;
   static_assert(BM * YS <= L::LDS_BYTES, "staged output tile fits");
+  if constexpr (PARTIAL) {
+    // fp32 partial tile straight from the accumulators: register 4g + e of tile
+    // (i, j) holds row ml, columns nl + e (e < 4)
+    if constexpr (DT == SP24_INT8)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = i32_bits_to_f32(acc[i][j][e]);
+    const int q = lane >> 5, c = lane & 31;
+    float* pz = partial + (size_t)blockIdx.y * M * N;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * (BM / WGM) + 32 * j + c;
+      if (m >= M) continue;
+      float* pr = pz + (size_t)m * N;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * (BN / WGN) + 32 * i + 8 * g + 4 * q;
+          const f32x4 v = f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          if ((N & 3) == 0 && n + 3 < N) {
+            *reinterpret_cast<f32x4*>(pr + n) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) pr[n + e] = v[e];
+          }
+        }
+    }
+    return;
+  }
   if constexpr (DT == SP24_INT8)
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -503,9 +552,15 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 
 template <int DT, bool SPARSE>
 hipError_t launch_tiled_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE>), dim3(p.grid_x), dim3(NT), 0, s,
-                     static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta,
-                     a.x_scale, a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step);
+  using L = TiledLayout<DT, SPARSE>;
+  if (p.split_k > 1)
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, true>), dim3(p.grid_x, p.split_k), dim3(NT), 0, s,
+                       static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
+                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.partial, a.k / L::KS / p.split_k);
+  else
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, false>), dim3(p.grid_x), dim3(NT), 0, s,
+                       static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
+                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, (float*)nullptr, 0);
   return hipGetLastError();
 }
 

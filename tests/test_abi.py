@@ -189,6 +189,20 @@ def test_plan_uses_tiled_kernel_for_prefill_only():
         assert sp.plan(sp.OP_GEMM, sp.FP8, m, 14336, 4096)["kernel"] != 1
 
 
+def test_plan_tiled_for_wide_layers_at_256_tokens():
+    # one tile of tokens and >= 96 tiles (gate+up of an 8B-class layer): the tiled kernel,
+    # BF16 with K split in two; narrower projections keep the small-m kernels
+    for m in (200, 256):
+        p8 = sp.plan(sp.OP_GEMM, sp.FP8, m, 28672, 4096)
+        p16 = sp.plan(sp.OP_GEMM, sp.BF16, m, 28672, 4096)
+        assert p8["kernel"] == 1 and p8["split_k"] == 1 and p8["workspace_bytes"] == 0
+        assert p16["kernel"] == 1 and p16["split_k"] == 2 and p16["grid_y"] == 2
+        assert p16["workspace_bytes"] == 2 * m * 28672 * 4
+    for m, n, k in ((256, 6144, 4096), (256, 4096, 4096), (256, 4096, 14336), (128, 28672, 4096),
+                    (129, 14336, 4096)):
+        assert sp.plan(sp.OP_GEMM, sp.BF16, m, n, k)["kernel"] == 2, (m, n, k)
+
+
 def test_plan_stream_rows_cover_every_cu_equally():
     # equal row ranges over all 256 CUs: 14336 rows as 512 ranges of 28 (two
     # workgroups per CU), 56 per CU at m = 64, 16 per CU for 4096 rows
@@ -421,3 +435,19 @@ def test_palette_decode_and_gemm_validation():
     assert big >= 4096 * 4096 * 2
     assert lib.sp24_workspace_size(sp.OP_PALETTE_GEMM, 0, 17, 4096, 4000) == 0   # k % 128
     assert g(m=17, n=4, ws=None) == EWS
+
+
+def test_tiled_split_k_plan(monkeypatch):
+    """The tiled kernel's K split (SP24_TILE="99,split"): whole, even numbers of K steps per
+    slice, the fp32 partials in the workspace; other splits are rejected."""
+    monkeypatch.setenv("SP24_TILE", "99,4")
+    pl = sp.plan(sp.OP_GEMM, sp.FP8, 256, 4096, 4096)
+    assert pl["kernel"] == 1 and pl["split_k"] == 4 and pl["grid_y"] == 4
+    assert pl["workspace_bytes"] == 4 * 256 * 4096 * 4
+    assert lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, 256, 4096, 4096) == pl["workspace_bytes"]
+    for dt, k, split in ((sp.FP8, 1024, 3), (sp.FP8, 1024, 8), (sp.BF16, 1024, 16), (sp.INT8, 384, 2)):
+        monkeypatch.setenv("SP24_TILE", "99,%d" % split)   # 8 steps of 128 in 3 or in 8 (odd), 16 of 64 in 16, 3 in 2
+        with pytest.raises(sp.Sp24Error):
+            sp.plan(sp.OP_GEMM, dt, 256, 512, k)
+    monkeypatch.setenv("SP24_TILE", "99,2")
+    assert sp.plan(sp.OP_GEMM, sp.BF16, 256, 512, 1024)["split_k"] == 2

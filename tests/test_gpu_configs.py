@@ -83,3 +83,13 @@ def test_skinny_config_k_tail(cid, fp8, dense):
     # ragged rows and tokens; K = 2 chunks of 512 + a tail of 384, split over 2 slices
     m, n, k = 16 * mb + 3, 16 * rb * 2 + 5, 1408
     _run("%d,2" % cid, m, n, k, fp8, dense, "skinny %d" % cid, seed=cid * 17 + 3)
+
+
+# The LDS-tiled kernel with its K split over the grid (fp32 partial tiles + the split-K
+# reduction): every operand type, ragged m and n, slices of 2 and more steps.
+@pytest.mark.parametrize("fp8,dense", VARIANTS)
+@pytest.mark.parametrize("m,n,k,sk", [(256, 1000, 1024, 2), (300, 520, 2048, 4), (17, 300, 1024, 4),
+                                      (256, 4096, 4096, 8)])
+def test_tiled_split_k(m, n, k, sk, fp8, dense):
+    _run("99,%d" % sk, m, n, k, fp8, dense, "tiled split-K %dx%dx%d/%d" % (m, n, k, sk), seed=m + n + k + sk)
+

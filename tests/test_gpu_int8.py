@@ -259,3 +259,15 @@ def test_prefill_sampled_int8():
 def test_decode_sampled_int8(m):
     _sampled_int8(W.up_x(m), W.up_weight(), "up int8 M=%d" % m, seed=m)
     _sampled_int8(W.down_x(m), W.down_weight(), "down int8 M=%d" % m, seed=m + 1)
+
+
+@pytest.mark.parametrize("m,n,k,sk", [(256, 1000, 1024, 2), (300, 520, 2048, 4)])
+def test_gemm_int8_tiled_split_k(m, n, k, sk):
+    """INT8 through the tiled kernel with its K split: per-slice int32 sums become fp32
+    partials, summed by the reduction in a fixed order."""
+    import os
+    os.environ["SP24_TILE"] = "99,%d" % sk
+    try:
+        test_gemm_int8_against_oracle(m, n, k)
+    finally:
+        os.environ.pop("SP24_TILE", None)
