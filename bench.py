@@ -128,7 +128,7 @@ class Events:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs on a single MI355X and has no "
               "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
