@@ -145,8 +145,11 @@ def main():
     quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
     code_t = torch.int8 if kind == "int8" else torch.uint8
     label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
-    if kind == "int8" and args.workload in ("slide", "layers", "palette"):
-        print("--dtype int8 is measured on the up, down and prefill workloads", file=sys.stderr)
+    if kind == "int8" and args.workload in ("layers", "palette"):
+        print("--dtype int8 is measured on the up, down, prefill and slide workloads", file=sys.stderr)
+        sys.exit(2)
+    if kind == "bf16" and args.workload == "slide":
+        print("the slide workload multiplies one-byte codes: --dtype fp8 or int8", file=sys.stderr)
         sys.exit(2)
     ev = Events(torch)
 
@@ -420,13 +423,19 @@ def vendor_dense_fp8(torch, ev, xq, w_copies, sx, sw, m, bound):
 
 
 def run_slide(args, torch, np, sp, W, ev, dev):
-    """SlideSparse 6:8 (N = 4) on the 2:4 path against the dense FP8 GEMM and the 2:4 GEMM of
-    the same shape: the decode up-projection (K=4096, N=14336, M=1/16/64) and the prefill
+    """SlideSparse 6:8 (N = 4) on the 2:4 path against the dense GEMM and the 2:4 GEMM of
+    the same shape and code type (FP8-E4M3, or INT8 W8A8 with --dtype int8): the decode up-projection (K=4096, N=14336, M=1/16/64) and the prefill
     GEMM (M=8192, K=8192, N=28672).  The 6:8 weight is expanded to K' = 1.5 K; its bound
     over dense is N/(N-1) = 4/3 in matrix work (the page's S_max), and the byte ratio at
     decode.  Weights: 0.02 N(0, 1) (prefill 0.01) drawn on the GPU (seeds 1 and 3); X from
     workloads/.  Decode rotates weight copies past the last-level cache."""
     n_pat = 4
+    i8 = args.dtype == "int8"
+    dt = sp.INT8 if i8 else sp.FP8
+    quant = sp.quant_int8 if i8 else sp.quant_fp8
+    quant_rows = sp.quant_int8_rows if i8 else sp.quant_fp8_rows
+    slide_quant = sp.slide_quant_int8_rows if i8 else sp.slide_quant_fp8_rows
+    tname = "INT8" if i8 else "FP8"
     shapes = [("up", m, 4096, 14336) for m in (1, 16, 64)] + [("prefill", 8192, 8192, 28672)]
     out = {}
     cache = {}
@@ -441,10 +450,10 @@ def run_slide(args, torch, np, sp, W, ev, dev):
             wp = sp.slide_prune_pack(w, n_pat)
             v68, m68 = sp.prune_compress(wp)
             del wp
-            q68, s68 = sp.quant_fp8(v68)
+            q68, s68 = quant(v68)
             v24, m24 = sp.prune_compress(w)
-            q24, s24 = sp.quant_fp8(v24)
-            qd, sd = sp.quant_fp8(w)
+            q24, s24 = quant(v24)
+            qd, sd = quant(w)
             del w, v68, v24
             b68 = q68.numel() + m68.numel() * 4
             b24 = q24.numel() + m24.numel() * 4
@@ -458,18 +467,18 @@ def run_slide(args, torch, np, sp, W, ev, dev):
                 s68=s68, s24=s24, sd=sd, b68=b68, b24=b24, bd=bd)
         c = cache[(k, n)]
         x = (W.up_x(m) if name == "up" else W.prefill_x()).to(dev)
-        xq68, sx68 = sp.slide_quant_fp8_rows(x, n_pat)
-        xq24, sx24 = sp.quant_fp8_rows(x)
+        xq68, sx68 = slide_quant(x, n_pat)
+        xq24, sx24 = quant_rows(x)
         y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        ws68 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, sp.FP8, m, n, kp)), dtype=torch.uint8, device=dev)
-        ws24 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)), dtype=torch.uint8, device=dev)
-        wsd = torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, sp.FP8, m, n, k)), dtype=torch.uint8,
+        ws68 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, m, n, kp)), dtype=torch.uint8, device=dev)
+        ws24 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, m, n, k)), dtype=torch.uint8, device=dev)
+        wsd = torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, dt, m, n, k)), dtype=torch.uint8,
                           device=dev)
         sxd = sx24[:1].contiguous()
         calls = {
             "slide_gemm": lambda i: sp.gemm_rows(xq68, c["w68"][i % len(c["w68"])][0], c["w68"][i % len(c["w68"])][1],
                                                  sx68, c["s68"], out=y, ws=ws68),
-            "slide_step": lambda i: (sp.slide_quant_fp8_rows(x, n_pat, out=xq68, scales=sx68),
+            "slide_step": lambda i: (slide_quant(x, n_pat, out=xq68, scales=sx68),
                                      sp.gemm_rows(xq68, c["w68"][i % len(c["w68"])][0], c["w68"][i % len(c["w68"])][1],
                                                   sx68, c["s68"], out=y, ws=ws68)),
             "sparse24_gemm": lambda i: sp.gemm_rows(xq24, c["w24"][i % len(c["w24"])][0],
@@ -508,10 +517,11 @@ def run_slide(args, torch, np, sp, W, ev, dev):
         })
         out["%s M=%d" % (name, m)] = res
     pre = out["prefill M=8192"]
-    return {"metric": "SlideSparse 6:8 FP8 GEMM (2:4 path over K' = 1.5 K): speedup over the dense FP8 GEMM",
+    return {"metric": "SlideSparse 6:8 %s GEMM (2:4 path over K' = 1.5 K): speedup over the dense %s GEMM"
+                      % (tname, tname),
             "value": pre["speedup_vs_dense"], "unit": "x (prefill, dense time / SlideSparse time)",
             "n_gpus": 1, "steps": None, "warmup": None, "ms_per_step": pre["slide_gemm_us"] / 1e3,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8" if i8 else "fp8_e4m3",
             "data": "synthetic (seeded)",
             "config": {"workload": "SlideSparse 6:8 (N=4): decode up-projection M=1/16/64 (K=4096, N=14336) and "
                                    "prefill 8192x28672x8192; per-token X scales, per-tensor W scale"},

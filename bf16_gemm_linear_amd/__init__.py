@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
-    "slide_prune_pack", "slide_quant_fp8_rows",
+    "slide_prune_pack", "slide_quant_fp8_rows", "slide_quant_int8_rows",
     "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
     "palette_encode", "palette_decode", "palette_gemm",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
@@ -75,6 +75,7 @@ _SIGS = {
     "sp24_quant_int8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_slide_prune_pack": [_vp, _i64, _i64, _int, _vp, _vp],
     "sp24_slide_quant_fp8_rows": [_vp, _i64, _i64, _int, _vp, _vp, _vp],
+    "sp24_slide_quant_int8_rows": [_vp, _i64, _i64, _int, _vp, _vp, _vp],
     "sp24_gemm_rows": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_workspace_size": [_int, _int, _i64, _i64, _i64],
     "sp24_palette_analyze": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -401,6 +402,24 @@ def slide_quant_fp8_rows(x: torch.Tensor, n_pat: int = 4, out: torch.Tensor | No
     _need(scales, "scales", torch.float32, 1, x.device)
     _check("sp24_slide_quant_fp8_rows", lib.sp24_slide_quant_fp8_rows(_ptr(x), m, k, n_pat, _ptr(out),
                                                                       _ptr(scales), _stream(x.device)))
+    return out, scales
+
+
+def slide_quant_int8_rows(x: torch.Tensor, n_pat: int = 4, out: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None):
+    """As slide_quant_fp8_rows with per-token INT8 codes -> (codes int8 [m, k (2N-2)/N],
+    scales fp32 [m], amax/127 per row)."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    kp = k // (2 * n_pat) * 4 * (n_pat - 1)
+    if out is None:
+        out = torch.empty(m, max(kp, 1), dtype=torch.int8, device=x.device)
+    _need(out, "out", torch.int8, 2, x.device)
+    if scales is None:
+        scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(scales, "scales", torch.float32, 1, x.device)
+    _check("sp24_slide_quant_int8_rows", lib.sp24_slide_quant_int8_rows(_ptr(x), m, k, n_pat, _ptr(out),
+                                                                        _ptr(scales), _stream(x.device)))
     return out, scales
 
 

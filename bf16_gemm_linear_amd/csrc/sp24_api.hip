@@ -643,8 +643,9 @@ int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, v
                 s);
 }
 
-int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
-                              float* scales_dev, void* stream) {
+namespace {
+int slide_quant_common(int dtype, const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
+                       float* scales_dev, void* stream) {
   if (!x_bf16 || !q_out || !scales_dev) return SP24_ERR_NULL;
   if (n_pat < 3 || n_pat > 8) return SP24_ERR_MODE;
   if (m < 1 || k < 8 || k % 8 != 0 || k % (2 * n_pat) != 0 || m > kMaxDim || k > kMaxDim ||
@@ -657,8 +658,20 @@ int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pa
       overlaps(scales_dev, sb, q_out, qb))
     return SP24_ERR_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return finish(launch_slide_quant_rows(static_cast<const uint16_t*>(x_bf16), m, k, n_pat, q_out, scales_dev, s),
-                s);
+  return finish(
+      launch_slide_quant_rows(dtype, static_cast<const uint16_t*>(x_bf16), m, k, n_pat, q_out, scales_dev, s), s);
+}
+}  // namespace
+
+int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
+                              float* scales_dev, void* stream) {
+  return slide_quant_common(SP24_FP8_E4M3, x_bf16, m, k, n_pat, q_out, scales_dev, stream);
+}
+
+int sp24_slide_quant_int8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, int8_t* q_out,
+                               float* scales_dev, void* stream) {
+  return slide_quant_common(SP24_INT8, x_bf16, m, k, n_pat, reinterpret_cast<uint8_t*>(q_out), scales_dev,
+                            stream);
 }
 
 int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, const float* x_scales_dev,

@@ -33,8 +33,9 @@ hipError_t launch_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_
 size_t quant_workspace_bytes(int64_t count);
 hipError_t launch_slide_prune_pack(const uint16_t* w, int64_t n, int64_t k, int np, uint16_t* out,
                                    hipStream_t s);
-hipError_t launch_slide_quant_rows(const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q, float* scales,
-                                   hipStream_t s);
+// dtype SP24_FP8_E4M3 or SP24_INT8
+hipError_t launch_slide_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q,
+                                   float* scales, hipStream_t s);
 // dtype SP24_FP8_E4M3 or SP24_INT8
 hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
                              hipStream_t s);

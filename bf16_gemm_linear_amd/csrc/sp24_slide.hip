@@ -96,9 +96,20 @@ __global__ __launch_bounds__(kThreads) void slide_prune_pack_kernel(const uint16
   }
 }
 
+// The 4 codes of one window (bf16 pairs d0, d1) for code type DT.
+template <int DT>
+__device__ __forceinline__ uint32_t qcast4(uint32_t d0, uint32_t d1, float s) {
+  if constexpr (DT == SP24_INT8)
+    return f32_to_i8(bf16_to_f32(d0 & 0xFFFFu) / s) | (f32_to_i8(bf16_to_f32(d0 >> 16) / s) << 8) |
+           (f32_to_i8(bf16_to_f32(d1 & 0xFFFFu) / s) << 16) | (f32_to_i8(bf16_to_f32(d1 >> 16) / s) << 24);
+  else
+    return f32x2_to_e4m3(bf16_to_f32(d0 & 0xFFFFu) / s, bf16_to_f32(d0 >> 16) / s) |
+           (f32x2_to_e4m3(bf16_to_f32(d1 & 0xFFFFu) / s, bf16_to_f32(d1 >> 16) / s) << 16);
+}
+
 // One workgroup per row: the row maximum, then the lifted codes, one window
 // (4 codes) per thread and step.
-template <int NP>
+template <int DT, int NP>
 __global__ __launch_bounds__(kThreads) void slide_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                                    int64_t k, uint8_t* __restrict__ q,
                                                                    float* __restrict__ scales) {
@@ -116,15 +127,13 @@ __global__ __launch_bounds__(kThreads) void slide_quant_rows_kernel(const uint16
 #pragma unroll
     for (int i = 0; i < kThreads / kWave; ++i) mk = max(mk, sh[i]);
     __syncthreads();
-    const float s = scale_from_key(mk);
+    const float s = qscale<DT>(mk);
     if (threadIdx.x == 0) scales[r] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + r * kp);
     for (int64_t v = threadIdx.x; v < nwin; v += kThreads) {
       const int64_t b = v / (NP - 1), j = v - b * (NP - 1);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(xr + b * BLK + 2 * j);  // 4-byte aligned
-      const uint32_t d0 = src[0], d1 = src[1];
-      qr[v] = f32x2_to_e4m3(bf16_to_f32(d0 & 0xFFFFu) / s, bf16_to_f32(d0 >> 16) / s) |
-              (f32x2_to_e4m3(bf16_to_f32(d1 & 0xFFFFu) / s, bf16_to_f32(d1 >> 16) / s) << 16);
+      qr[v] = qcast4<DT>(src[0], src[1], s);
     }
   }
 }
@@ -154,13 +163,19 @@ hipError_t launch_slide_prune_pack(const uint16_t* w, int64_t n, int64_t k, int 
   return hipGetLastError();
 }
 
-hipError_t launch_slide_quant_rows(const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q, float* scales,
-                                   hipStream_t s) {
+hipError_t launch_slide_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q,
+                                   float* scales, hipStream_t s) {
   const int blocks = (int)(m < 65536 ? m : 65536);
+  const bool i8 = dtype == SP24_INT8;
   switch (np) {
-#define SP24_SLIDE_QUANT(NP)                                                                                \
-  case NP:                                                                                                  \
-    hipLaunchKernelGGL(slide_quant_rows_kernel<NP>, dim3(blocks), dim3(kThreads), 0, s, x, m, k, q, scales); \
+#define SP24_SLIDE_QUANT(NP)                                                                                 \
+  case NP:                                                                                                   \
+    if (i8)                                                                                                  \
+      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_INT8, NP>), dim3(blocks), dim3(kThreads), 0, s, x, m, \
+                         k, q, scales);                                                                      \
+    else                                                                                                     \
+      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_FP8_E4M3, NP>), dim3(blocks), dim3(kThreads), 0, s, x, \
+                         m, k, q, scales);                                                                   \
     break;
     SP24_SLIDE_QUANT(3) SP24_SLIDE_QUANT(4) SP24_SLIDE_QUANT(5) SP24_SLIDE_QUANT(6) SP24_SLIDE_QUANT(7)
     SP24_SLIDE_QUANT(8)

@@ -238,6 +238,14 @@ int sp24_slide_prune_pack(const void* w_bf16, int64_t n, int64_t k, int n_pat, v
 int sp24_slide_quant_fp8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, uint8_t* q_out,
                               float* scales_dev, void* stream);
 
+/* The same lifting fused into per-token INT8 quantisation (the page's results
+ * are INT8 W8A8): the codes and scales_dev[r] = fp32(amax_r / 127) of
+ * sp24_quant_int8_rows, in the lifted order of sp24_slide_quant_fp8_rows.
+ * Multiply with sp24_gemm_rows(SP24_INT8, ...) on INT8 weights of W'.
+ *   Shapes, alignment and errors as sp24_slide_quant_fp8_rows. */
+int sp24_slide_quant_int8_rows(const void* x_bf16, int64_t m, int64_t k, int n_pat, int8_t* q_out,
+                               float* scales_dev, void* stream);
+
 /* Y = X . W^T as sp24_gemm with dtype SP24_FP8_E4M3 or SP24_INT8, except that
  * X carries one scale per row: y[r, :] = bf16_rne(acc[r, :] * fp32(x_scales_dev[r] * sw)).
  *   x [m, k] codes (from sp24_quant_fp8_rows / sp24_quant_int8_rows);

@@ -121,6 +121,18 @@ def assert_within_tolerance(y_bits: np.ndarray, ref: np.ndarray, mag: np.ndarray
             % (what, len(bad), ok.size, (int(i), int(j)), y[i, j], ref[i, j], mag[i, j], excess.max()))
 
 
+def assert_exact_sum_bound(y_bits, ref, mag, what):
+    """INT8 paths: the int32 sum is exact, so the only errors are the fp32 scale
+    product and the bf16 rounding of the output (2^-8 relative, with 2^-12 for
+    the scale product) plus fp32 underflow."""
+    y = O.bf16_to_f64(y_bits)
+    ok = np.abs(y - ref) <= 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -12) + 2.0 ** -20 * mag
+    if not ok.all():
+        i, j = np.argwhere(~ok)[0]
+        raise AssertionError("%s: %d outside the exact-sum bound; first at %s: y=%r ref=%r mag=%r"
+                             % (what, int((~ok).sum()), (int(i), int(j)), y[i, j], ref[i, j], mag[i, j]))
+
+
 def full_case(x_cpu, w_cpu, fp8, what, dense=False):
     """Whole pipeline on both sides; compare codes, scales and every output."""
     sp = need_sp()

@@ -349,13 +349,13 @@ def test_slide_validation():
     assert pk(k=60) == ESHAPE and pk(n=0) == ESHAPE
     assert pk(w=A + 4) == EALIGN
     assert pk(out=A + 0x100) == EALIAS
-    qz = lambda x=A, m=2, k=64, np_=4, q=A + 0x100000, s=A + 0x200000: lib.sp24_slide_quant_fp8_rows(
-        p(x), m, k, np_, p(q), p(s), None)
-    assert qz(x=None) == ENULL and qz(s=None) == ENULL
-    assert qz(np_=1) == EMODE
-    assert qz(k=60) == ESHAPE and qz(k=36, np_=3) == ESHAPE     # 36 % 8 != 0
-    assert qz(q=A + 8) == EALIGN
-    assert qz(s=A + 0x10) == EALIAS
+    for fn in (lib.sp24_slide_quant_fp8_rows, lib.sp24_slide_quant_int8_rows):
+        qz = lambda x=A, m=2, k=64, np_=4, q=A + 0x100000, s=A + 0x200000: fn(p(x), m, k, np_, p(q), p(s), None)
+        assert qz(x=None) == ENULL and qz(s=None) == ENULL
+        assert qz(np_=1) == EMODE
+        assert qz(k=60) == ESHAPE and qz(k=36, np_=3) == ESHAPE     # 36 % 8 != 0
+        assert qz(q=A + 8) == EALIGN
+        assert qz(s=A + 0x10) == EALIAS
 
 
 def test_int8_validation_and_plan():

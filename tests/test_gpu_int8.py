@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import DEV, announce, assert_within_tolerance, bits, f32, f32_bits, need_sp, u32
+from gpu_helpers import (DEV, announce, assert_exact_sum_bound, assert_within_tolerance, bits, f32, f32_bits,
+                         need_sp, u32)
 from oracle import sp24_ref as O
 
 pytestmark = pytest.mark.gpu
@@ -20,15 +21,6 @@ pytestmark = pytest.mark.gpu
 
 def i8(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.int8)
-
-
-def assert_exact_sum_bound(y_bits, ref, mag, what):
-    y = O.bf16_to_f64(y_bits)
-    ok = np.abs(y - ref) <= 2.0 ** -8 * np.abs(ref) * (1 + 2.0 ** -12) + 2.0 ** -20 * mag
-    if not ok.all():
-        i, j = np.argwhere(~ok)[0]
-        raise AssertionError("%s: %d outside the exact-sum bound; first at %s: y=%r ref=%r mag=%r"
-                             % (what, int((~ok).sum()), (int(i), int(j)), y[i, j], ref[i, j], mag[i, j]))
 
 
 # ---------------------------------------------------------------- quantisers

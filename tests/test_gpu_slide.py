@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import DEV, announce, assert_within_tolerance, bits, codes, f32, f32_bits, need_sp, u32
+from gpu_helpers import (DEV, announce, assert_exact_sum_bound, assert_within_tolerance, bits, codes, f32, f32_bits,
+                         need_sp, u32)
 from oracle import sp24_ref as O
 
 pytestmark = pytest.mark.gpu
@@ -72,3 +73,48 @@ def test_slide_gemm_matches_the_6_of_8_product(m, n, k):
     oxq, oxs = O.quant_fp8_rows(W.bf16_bits(x))
     ref, mag = O.gemm_ref(O.dequant_fp8_rows(oxq, oxs), O.dequant_fp8(wq, osw))
     assert_within_tolerance(bits(y), ref, mag, "slide %dx%dx%d" % (m, n, k))
+
+
+# ---------------------------------------------------------------- INT8 W8A8 (the page's precision)
+
+@pytest.mark.parametrize("m,k,n_pat", [(1, 4096, 4), (16, 14336, 4), (5, 96, 3), (3, 160, 5), (2, 256, 8)])
+def test_lift_quant_int8_bit_exact(m, k, n_pat):
+    sp = need_sp()
+    x = W.randn_bf16((m, k), seed=3 * m + k).float()
+    if m > 2:
+        x[1] *= 300.0
+        x[2] = 0.0                 # an all-zero token: scale 1, codes 0
+    x = x.to(torch.bfloat16)
+    announce("slide_quant_int8_rows", m, k, n_pat)
+    q, s = sp.slide_quant_int8_rows(x.to(DEV), n_pat)
+    torch.cuda.synchronize()
+    oq, os_ = O.quant_int8_rows(W.bf16_bits(x))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), O.slide_lift(oq, n_pat))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 14336, 4096), (16, 1024, 4096), (64, 2048, 2048), (512, 16384, 1024)])
+def test_slide_gemm_int8_matches_the_6_of_8_product(m, n, k):
+    sp = need_sp()
+    n_pat = 4
+    w = W.randn_bf16((n, k), seed=n + k + 2, std=0.02)
+    x = W.randn_bf16((m, k), seed=m + k + 3)
+    kp = k * (2 * n_pat - 2) // n_pat
+    announce("slide gemm int8", m, n, k, "K'", kp, "kernel", sp.plan(sp.OP_GEMM, sp.INT8, m, n, kp)["kernel"])
+    wp = sp.slide_prune_pack(w.to(DEV), n_pat)
+    values, meta = sp.prune_compress(wp)
+    qv, sw = sp.quant_int8(values)
+    xq, sx = sp.slide_quant_int8_rows(x.to(DEV), n_pat)
+    y = sp.gemm_rows(xq, qv, meta, sx, sw)
+    torch.cuda.synchronize()
+    # the reference over K: 6:8-pruned W with its per-tensor INT8 scale, X per token
+    wb = W.bf16_bits(w)
+    w68 = O.apply_mask(wb, O.slide_prune_mask(wb, n_pat))
+    wq, osw = O.quant_int8(w68)
+    assert f32_bits(f32(sw)) == f32_bits(osw)
+    oxq, oxs = O.quant_int8_rows(W.bf16_bits(x))
+    xs = oxs.astype(np.float64)[:, None] * oxq.astype(np.float64)
+    ref, mag = O.gemm_ref(xs, O.dequant_int8(wq, osw))
+    yb = bits(y)
+    assert_within_tolerance(yb, ref, mag, "slide int8 %dx%dx%d" % (m, n, k))
+    assert_exact_sum_bound(yb, ref, mag, "slide int8 %dx%dx%d" % (m, n, k))
