@@ -316,6 +316,28 @@ def main():
             reps = 200
             t = ev.time(lambda i: call_quant(m), reps) / reps
             per_m[m]["quant_x_us_eager"] = t * 1e6
+    if kind == "fp8" and bound == "hbm":
+        # quantise + GEMM in one call, per tensor (the step) and per token, graph-replayed
+        for m in Ms:
+            b = bufs[m]
+            xsr = torch.empty(m, dtype=torch.float32, device=dev)
+            wsr = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM_ROWS_QX, sp.FP8, m, N, K)), dtype=torch.uint8,
+                              device=dev)
+            calls = {"step_qx_us": lambda i: sp.gemm_qx(xs[m], wq_copies[i % R], meta_copies[i % R], sw,
+                                                        x_scale=b["sx"], out=b["y"], ws=b["qxws"]),
+                     "step_rows_qx_us": lambda i: sp.gemm_rows_qx(xs[m], wq_copies[i % R], meta_copies[i % R], sw,
+                                                                  x_scales=xsr, out=b["y"], ws=wsr)}
+            for key, fn in calls.items():
+                reps = R * 8
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(reps):
+                        fn(i)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                per_m[m][key] = ev.time(lambda i: g.replay(), 3) / 3 / reps * 1e6
+                del g
 
     # ---------------------------------------------------------------- dense baseline
     if not args.no_dense:
@@ -471,6 +493,8 @@ def run_slide(args, torch, np, sp, W, ev, dev):
         xq24, sx24 = quant_rows(x)
         y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
         ws68 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, m, n, kp)), dtype=torch.uint8, device=dev)
+        wsq68 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM_ROWS_QX, sp.FP8, m, n, kp)), dtype=torch.uint8,
+                            device=dev)
         ws24 = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, m, n, k)), dtype=torch.uint8, device=dev)
         wsd = torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, dt, m, n, k)), dtype=torch.uint8,
                           device=dev)
@@ -478,6 +502,9 @@ def run_slide(args, torch, np, sp, W, ev, dev):
         calls = {
             "slide_gemm": lambda i: sp.gemm_rows(xq68, c["w68"][i % len(c["w68"])][0], c["w68"][i % len(c["w68"])][1],
                                                  sx68, c["s68"], out=y, ws=ws68),
+            "slide_step_fused": (lambda i: sp.slide_gemm_qx(x, c["w68"][i % len(c["w68"])][0],
+                                                            c["w68"][i % len(c["w68"])][1], c["s68"], n_pat,
+                                                            x_scales=sx68, out=y, ws=wsq68)) if not i8 else None,
             "slide_step": lambda i: (slide_quant(x, n_pat, out=xq68, scales=sx68),
                                      sp.gemm_rows(xq68, c["w68"][i % len(c["w68"])][0], c["w68"][i % len(c["w68"])][1],
                                                   sx68, c["s68"], out=y, ws=ws68)),
@@ -488,6 +515,8 @@ def run_slide(args, torch, np, sp, W, ev, dev):
         }
         res = {}
         for key, fn in calls.items():
+            if fn is None:
+                continue
             nrep = 48 if name == "up" else 5
             fn(0)
             torch.cuda.synchronize()

@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
-    "slide_prune_pack", "slide_quant_fp8_rows", "slide_quant_int8_rows",
+    "slide_prune_pack", "slide_quant_fp8_rows", "slide_quant_int8_rows", "OP_GEMM_ROWS_QX", "gemm_rows_qx",
+    "slide_gemm_qx",
     "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
     "palette_encode", "palette_decode", "palette_gemm",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
@@ -34,6 +35,7 @@ __all__ = [
 BF16, FP8, INT8 = 0, 1, 2
 SCALE_DYNAMIC, SCALE_STATIC = 0, 1
 OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX, OP_PALETTE_ANALYZE, OP_PALETTE_GEMM = 0, 1, 2, 3, 4, 5
+OP_GEMM_ROWS_QX = 6
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsp24.so")
@@ -71,6 +73,8 @@ _SIGS = {
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_gemm_rows_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_slide_gemm_qx": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_quant_int8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_slide_prune_pack": [_vp, _i64, _i64, _int, _vp, _vp],
@@ -478,6 +482,57 @@ def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):
     _check("sp24_gemm_qx", lib.sp24_gemm_qx(m, n, k, _ptr(x), _ptr(x_scale), _ptr(values), _ptr(meta),
                                             _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
     return out, x_scale
+
+
+def _rows_qx_args(x, values, meta, w_scale, kp, x_scales, out):
+    _need(x, "x", torch.bfloat16, 2)
+    m = x.shape[0]
+    _need(values, "values", _CODE_T, 2, x.device)
+    n = values.shape[0]
+    if values.shape[1] * 2 != kp:
+        raise ValueError("compressed weight shapes do not match k=%d" % kp)
+    _need(meta, "meta", torch.int32, 1, x.device)
+    _meta_size(meta, n, kp)
+    _need(w_scale, "w_scale", torch.float32, None, x.device)
+    if x_scales is None:
+        x_scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(x_scales, "x_scales", torch.float32, 1, x.device)
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    return m, n, x_scales, out
+
+
+def gemm_rows_qx(x, values, meta, w_scale, x_scales=None, out=None, ws=None):
+    """Y = X . W^T with X [m, k] bf16 quantised per token inside the call (sp24_gemm_rows_qx):
+    returns (y [m, n] bf16, x_scales fp32 [m]), bit-identical to quant_fp8_rows followed by
+    gemm_rows."""
+    k = x.shape[1] if x.dim() == 2 else 0
+    m, n, x_scales, out = _rows_qx_args(x, values, meta, w_scale, k, x_scales, out)
+    nbytes = workspace_size(OP_GEMM_ROWS_QX, FP8, m, n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_gemm_rows_qx", lib.sp24_gemm_rows_qx(m, n, k, _ptr(x), _ptr(x_scales), _ptr(values), _ptr(meta),
+                                                      _ptr(w_scale), _ptr(out), _ptr(ws), nbytes,
+                                                      _stream(x.device)))
+    return out, x_scales
+
+
+def slide_gemm_qx(x, values, meta, w_scale, n_pat=4, x_scales=None, out=None, ws=None):
+    """SlideSparse per call in one call (sp24_slide_gemm_qx): X [m, k] bf16 lifted to the
+    windows and quantised per token, times the compressed E4M3 W' [n, k'/2] (k' = k (2N-2)/N);
+    returns (y [m, n] bf16, x_scales fp32 [m]), bit-identical to slide_quant_fp8_rows
+    followed by gemm_rows."""
+    k = x.shape[1] if x.dim() == 2 else 0
+    kp = k // (2 * n_pat) * 4 * (n_pat - 1) if 3 <= n_pat <= 8 else 0
+    m, n, x_scales, out = _rows_qx_args(x, values, meta, w_scale, kp, x_scales, out)
+    nbytes = workspace_size(OP_GEMM_ROWS_QX, FP8, m, n, kp)
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_slide_gemm_qx", lib.sp24_slide_gemm_qx(n_pat, m, n, k, _ptr(x), _ptr(x_scales), _ptr(values),
+                                                        _ptr(meta), _ptr(w_scale), _ptr(out), _ptr(ws), nbytes,
+                                                        _stream(x.device)))
+    return out, x_scales
 
 
 class PaletteWeight:

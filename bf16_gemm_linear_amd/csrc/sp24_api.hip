@@ -305,47 +305,47 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
 
 namespace {
 
-// X quantised inside the GEMM (sp24_gemm_qx): every workgroup of the sparse FP8
-// stream kernel reads all of X for the per-tensor scale, so X must be small
-// (M * K <= kQxMaxValues, 128 KB of bf16), and the codes of its tokens over its
-// K slice must fit the kStreamQxBytes region after the ring.
+// X quantised inside the GEMM (sp24_gemm_qx, sp24_gemm_rows_qx,
+// sp24_slide_gemm_qx): the sparse FP8 stream kernel holds the codes of a
+// workgroup's tokens over its K slice in the kStreamQxBytes region after the
+// ring.  With one scale per tensor every workgroup also reads all of X for it,
+// so X must be small (M * K <= kQxMaxValues, 128 KB of bf16); with one scale
+// per token a workgroup reads only its own tokens.
 constexpr int64_t kQxMaxValues = 65536;
 
-bool qx_fused(const sp24_plan& p, int64_t m, int64_t k) {
-  if (p.kernel != SP24_KERNEL_STREAM || m * k > kQxMaxValues) return false;
+bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
+  if (p.kernel != SP24_KERNEL_STREAM || (!rows && m * k > kQxMaxValues)) return false;
   int64_t room = -1;
   int ups = 0, bm = 0;
   switch (p.config - kStreamBase) {
-#define SP24_QX_ROOM(ID, RBW, RB, MW, KW, MB, U, SMAX)                                     \
-  case ID:                                                                           \
-    ups = (U) * (KW);                                                                \
-    bm = 16 * (MW) * (MB);                                                           \
-    if (stream_fits(SP24_FP8_E4M3, true, RBW, RB, MW, KW, MB, U, SMAX) &&               \
-        stream_ring_bytes(SP24_FP8_E4M3, true, RBW, RB, MW, KW, MB, U, SMAX, true) +     \
-                kStreamQxBytes + 64 <= kStreamLdsBytes)                                   \
-      room = kStreamQxBytes;                                                          \
+#define SP24_QX_ROOM(ID, RBW, RB, MW, KW, MB, U, SMAX)                               \
+  case ID:                                                                     \
+    ups = (U) * (KW);                                                          \
+    bm = 16 * (MW) * (MB);                                                     \
+    if (stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, rows)) room = kStreamQxBytes; \
     break;
     SP24_STREAM_CONFIGS(SP24_QX_ROOM)
 #undef SP24_QX_ROOM
     default: return false;
   }
-  const int64_t rows = m < bm ? m : bm;
-  return room >= 0 && rows * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
+  const int64_t rows_wg = m < bm ? m : bm;
+  return room >= 0 && rows_wg * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
 }
 
-// Workspace of sp24_gemm_qx: the GEMM's own, then (when X is not quantised
-// inside the kernel) the E4M3 codes of X and the quantiser's workspace.
+// Workspace of the quantising GEMMs: the GEMM's own, then (when X is not
+// quantised inside the kernel) the E4M3 codes of X and, per tensor, the
+// quantiser's workspace.  k is the GEMM's K (K' for SlideSparse).
 struct QxWorkspace {
   size_t gemm, codes, quant, total;
   bool fused;
 };
 
-QxWorkspace qx_workspace(const sp24_plan& p, int64_t m, int64_t k) {
+QxWorkspace qx_workspace(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
   QxWorkspace w;
   w.gemm = (p.workspace_bytes + 15) / 16 * 16;
-  w.fused = qx_fused(p, m, k);
+  w.fused = qx_fused(p, m, k, rows);
   w.codes = w.fused ? 0 : ((size_t)(m * k) + 15) / 16 * 16;
-  w.quant = w.fused ? 0 : quant_workspace_bytes(m * k);
+  w.quant = w.fused || rows ? 0 : quant_workspace_bytes(m * k);
   w.total = w.gemm + w.codes + w.quant;
   return w;
 }
@@ -465,9 +465,9 @@ size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k) {
   }
   if (op == SP24_OP_PALETTE_GEMM) return palette_gemm_ws(m, n, k).total;
   sp24_plan p;
-  if (op == SP24_OP_GEMM_QX) {
+  if (op == SP24_OP_GEMM_QX || op == SP24_OP_GEMM_ROWS_QX) {
     if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &p) != SP24_OK) return 0;
-    return qx_workspace(p, m, k).total;
+    return qx_workspace(p, m, k, op == SP24_OP_GEMM_ROWS_QX).total;
   }
   if (plan_gemm(op, dtype, m, n, k, &p) != SP24_OK) return 0;
   return p.workspace_bytes;
@@ -692,7 +692,7 @@ int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_s
   if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
     return SP24_ERR_ALIGN;
   if (((uintptr_t)x_scale_dev & 3u) || ((uintptr_t)w_scale_dev & 3u)) return SP24_ERR_ALIGN;
-  const QxWorkspace wsp = qx_workspace(p, m, k);
+  const QxWorkspace wsp = qx_workspace(p, m, k, false);
   if (wsp.total > 0) {
     if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
     if (!aligned16(ws)) return SP24_ERR_ALIGN;
@@ -735,6 +735,87 @@ int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_s
   a.x = codes;
   if (e == hipSuccess) e = launch_plan(a, p, s);
   return finish(e, s);
+}
+
+namespace {
+// sp24_gemm_rows_qx (lift = 0, xk = k) and sp24_slide_gemm_qx (lift = N, X rows
+// of xk values, the GEMM over k = K').
+int rows_qx_common(int lift, int64_t m, int64_t n, int64_t k, int64_t xk, const void* x_bf16,
+                   float* x_scales_dev, const void* w_values, const uint32_t* w_meta, const float* w_scale_dev,
+                   void* y_bf16, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_bf16 || !x_scales_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
+  sp24_plan p;
+  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  if (st != SP24_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
+    return SP24_ERR_ALIGN;
+  if (((uintptr_t)x_scales_dev & 3u) || ((uintptr_t)w_scale_dev & 3u)) return SP24_ERR_ALIGN;
+  const QxWorkspace wsp = qx_workspace(p, m, k, true);
+  if (wsp.total > 0) {
+    if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  }
+  const size_t xb = (size_t)m * xk * 2, yb = (size_t)m * n * 2, wb = (size_t)n * (k / 2);
+  const size_t mb = (size_t)n * (k / 32) * 4, sb = (size_t)m * 4;
+  const void* in[4] = {x_bf16, w_values, w_meta, w_scale_dev};
+  const size_t inb[4] = {xb, wb, mb, 4};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(y_bf16, yb, in[i], inb[i]) || overlaps(x_scales_dev, sb, in[i], inb[i]) ||
+        (wsp.total > 0 && overlaps(ws, wsp.total, in[i], inb[i])))
+      return SP24_ERR_ALIAS;
+  if (overlaps(y_bf16, yb, x_scales_dev, sb) ||
+      (wsp.total > 0 && (overlaps(ws, wsp.total, y_bf16, yb) || overlaps(ws, wsp.total, x_scales_dev, sb))))
+    return SP24_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  GemmArgs a;
+  a.dtype = SP24_FP8_E4M3;
+  a.sparse = true;
+  a.m = (int)m;
+  a.n = (int)n;
+  a.k = (int)k;
+  a.x_scale = x_scales_dev;  // one scale per row, also for the split-K reduction
+  a.x_scale_step = 1;
+  a.w = w_values;
+  a.meta = w_meta;
+  a.w_scale = w_scale_dev;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  a.partial = p.split_k > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  if (wsp.fused) {
+    a.x = nullptr;
+    a.x_bf16 = static_cast<const uint16_t*>(x_bf16);
+    a.x_scale_out = x_scales_dev;
+    a.x_rows = true;
+    a.x_lift = lift;
+    return finish(launch_plan(a, p, s), s);
+  }
+  uint8_t* codes = wsb + wsp.gemm;
+  hipError_t e = lift ? launch_slide_quant_rows(SP24_FP8_E4M3, static_cast<const uint16_t*>(x_bf16), m, xk, lift,
+                                                codes, x_scales_dev, s)
+                      : launch_quant_rows(SP24_FP8_E4M3, static_cast<const uint16_t*>(x_bf16), m, k, codes,
+                                          x_scales_dev, s);
+  a.x = codes;
+  if (e == hipSuccess) e = launch_plan(a, p, s);
+  return finish(e, s);
+}
+}  // namespace
+
+int sp24_gemm_rows_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scales_dev,
+                      const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return rows_qx_common(0, m, n, k, k, x_bf16, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16, ws, ws_bytes,
+                        stream);
+}
+
+int sp24_slide_gemm_qx(int n_pat, int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scales_dev,
+                       const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (n_pat < 3 || n_pat > 8) return SP24_ERR_MODE;
+  if (k < 8 || k % 8 != 0 || k % (2 * n_pat) != 0 || k > kMaxDim) return SP24_ERR_SHAPE;
+  const int64_t kp = k / (2 * n_pat) * 4 * (n_pat - 1);
+  return rows_qx_common(n_pat, m, n, kp, k, x_bf16, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16, ws,
+                        ws_bytes, stream);
 }
 
 int sp24_palette_analyze(const void* w_bf16, int64_t n, int64_t k, uint8_t* palette_dev, int32_t* row_slot_dev,

@@ -268,15 +268,20 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
   }
 }
 
-// QX: X is bf16 (xh) and quantised here with the per-tensor scale of the whole
-// of X, exactly as the quantiser does it (same key, scale and cast); block
-// (0, 0, 0) stores the scale to sx_out.
-template <class C, bool PARTIAL, bool QX>
+// QX: X is bf16 (xh) and quantised here, exactly as the quantisers do it (same
+// key, scale and cast).  Per tensor (QROWS false): the scale of the whole of
+// X; block (0, 0, 0) stores it to sx_out.  Per token (QROWS): each workgroup
+// reads only its own tokens, row r gets the scale of its own maximum, and the
+// blocks with blockIdx.x = blockIdx.z = 0 store their rows' scales to
+// sx_out[m].  X rows hold xk values; with lift = N (3..8) they are lifted to the
+// SlideSparse windows on the way into LDS (the GEMM's K is then K' = xk (2N-2)/N),
+// with lift = 0 they are taken as they are (xk = K).
+template <class C, bool PARTIAL, bool QX, bool QROWS = false>
 __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice,
-    const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step) {
+    const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step, int xk, int lift) {
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
   // QX: the X codes sit in an array of their own, so the compiler can tell its
@@ -287,7 +292,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   constexpr int LDS_QX = C::RING_QX + kStreamQxBytes > C::LDS ? C::LDS - kStreamQxBytes : C::RING_QX;
   __shared__ __attribute__((aligned(16))) uint8_t lds[QX ? LDS_QX : C::LDS];
   __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
-  __shared__ uint32_t wave_max[QX ? C::NW : 1];
+  // per tensor: each wave's largest key; per token: each row's largest key
+  __shared__ uint32_t wave_max[QX ? (QROWS ? C::BM : C::NW) : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -314,11 +320,83 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   // QX: take the scale from all of X and cast this workgroup's tokens over its
   // K slice into LDS (an array of kStreamQxBytes), piece p of a step's part of
   // row r in slot swz16(r, p) as a ring buffer would hold it.
+  // QX: the ring's first loads (W and metadata only) go out before the
+  // prologue, so they travel while X is read.  The prologue's first barrier
+  // waits for them (a workgroup barrier drains every load in flight), so no
+  // LDS-DMA load is in flight when the codes are written and the K loop's
+  // waits stay as they are without QX.
+  if constexpr (QX && QROWS) {  // the rows' maxima start at 0 (before any load is in flight)
+    if (threadIdx.x < C::BM) wave_max[threadIdx.x] = 0u;
+    __syncthreads();
+  }
+  if constexpr (QX) {
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nks) ld.issue(lds + p * STAGE, p);
+  }
   float sx = 1.0f;
   uint8_t* const xres = xcodes;
   const int mrows = min(C::BM, M - m0);
   const int xrs = (int)stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB);
-  if constexpr (QX) {
+  // the LDS slot of the code at K offset kk (within the slice) of token row rr
+  auto slot = [&](int rr, int kk) {
+    const int st = kk / C::XB, within = kk - st * C::XB;
+    return xres + rr * xrs + st * C::XB + 16 * swz16<C::PX>(rr, within / 16) + (within & 15);
+  };
+  if constexpr (QX && QROWS) {
+    const int tid = threadIdx.x;
+    const int vpr = xk / 8;                    // 8-value vectors per X row (xk % 8 == 0)
+    const int nv = mrows * vpr;                // this workgroup's tokens only
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xh + (size_t)m0 * xk);
+    uint32_t* row_key = wave_max;
+    constexpr int RV = 4;
+    const bool in_regs = nv <= RV * C::NT;
+    u32x4 xr[RV];
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const int i = tid + r * C::NT;
+        xr[r] = i < nv ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+        if (i < nv) atomicMax(&row_key[i / vpr], key_max8(xr[r]));
+      }
+    } else {
+      for (int i = tid; i < nv; i += C::NT) atomicMax(&row_key[i / vpr], key_max8(xv[i]));
+    }
+    __syncthreads();
+    if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.z == 0 && tid < mrows)
+      sx_out[m0 + tid] = scale_from_key(row_key[tid]);
+    const int k0 = u0 * 128, kslice = units_per_slice * 128;
+    // vector i: 8 codes at K offset kk of row rr, or (lifted) its 4 code pairs: pair
+    // P = kk/2 + t is pair j = P % N of block b = P / N, which window j (j <= N-2)
+    // takes at its positions 0, 1 and window j - 1 (j >= 1) at its positions 2, 3
+    auto cast_vec = [&](int i, u32x4 d) {
+      const int rr = i / vpr, kk = (i - rr * vpr) * 8;
+      const u32x2 c8 = cast8(d, scale_from_key(row_key[rr]));
+      if (lift == 0) {
+        const int kp = kk - k0;
+        if (kp >= 0 && kp < kslice) *reinterpret_cast<u32x2*>(slot(rr, kp)) = c8;
+        return;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint16_t c2 = (uint16_t)(c8[t >> 1] >> (16 * (t & 1)));
+        const int pr = kk / 2 + t, b = pr / lift, j = pr - b * lift;
+        const int base = b * 4 * (lift - 1) - k0;
+        int kp = base + 4 * j;
+        if (j <= lift - 2 && kp >= 0 && kp < kslice) *reinterpret_cast<uint16_t*>(slot(rr, kp)) = c2;
+        kp = base + 4 * (j - 1) + 2;
+        if (j >= 1 && kp >= 0 && kp < kslice) *reinterpret_cast<uint16_t*>(slot(rr, kp)) = c2;
+      }
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < RV; ++r)
+        if (tid + r * C::NT < nv) cast_vec(tid + r * C::NT, xr[r]);
+    } else {
+      for (int i = tid; i < nv; i += C::NT) cast_vec(i, xv[i]);
+    }
+    __syncthreads();  // the codes are in LDS for every wave
+  } else if constexpr (QX) {
     const int tid = threadIdx.x;
     const u32x4* xv = reinterpret_cast<const u32x4*>(xh);
     const int64_t nvec = (int64_t)M * K / 8;  // 8-value vectors of X (K % 8 == 0: none spans two rows)
@@ -353,11 +431,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     sx = scale_from_key(mk);
     if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *sx_out = sx;
     // codes of value kk (relative to the K slice) of token row rr
-    auto put = [&](int rr, int kk, u32x2 c8) {
-      const int st = kk / C::XB, within = kk - st * C::XB;
-      *reinterpret_cast<u32x2*>(xres + rr * xrs + st * C::XB + 16 * swz16<C::PX>(rr, within / 16) +
-                                (within & 15)) = c8;
-    };
+    auto put = [&](int rr, int kk, u32x2 c8) { *reinterpret_cast<u32x2*>(slot(rr, kk)) = c8; };
     const int k0 = u0 * 128;
     if (in_regs) {
 #pragma unroll
@@ -375,15 +449,14 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         put(rr, kk, cast8(*reinterpret_cast<const u32x4*>(xs0 + (size_t)rr * K + kk), sx));
       }
     }
-    __syncthreads();  // the codes are in LDS for every wave (no loads are in flight yet)
+    __syncthreads();  // the codes are in LDS for every wave
   }
 
-  // The ring's first loads go out after the QX prologue: ordinary LDS writes
-  // issued while LDS-DMA loads are in flight make the compiler wait for every
-  // load in flight before each later LDS read.
+  if constexpr (!QX) {
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nks) ld.issue(lds + p * STAGE, p);
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nks) ld.issue(lds + p * STAGE, p);
+  }
   for (int ks = 0; ks < nks; ++ks) {
     wait_later<QX ? C::MIN_PER_STEP_QX : C::MIN_PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
     __builtin_amdgcn_s_barrier();
@@ -456,7 +529,10 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         uint16_t* yr = y + (size_t)m * N;
         // FP8, INT8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
         float scale = 1.0f;
-        if constexpr (C::B8) scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
+        if constexpr (C::B8) {
+          if constexpr (QX && QROWS) scale = scale_from_key(wave_max[m - m0]) * w_scale[0];
+          else scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
+        }
         const uint32_t lo = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
         const uint32_t hi = f32_to_bf16_rne(v[2] * scale) | (f32_to_bf16_rne(v[3] * scale) << 16);
         if (n + 3 < n_end && (N & 3) == 0) {
@@ -485,19 +561,36 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
     const uint8_t* x = static_cast<const uint8_t*>(a.x);
     const uint8_t* w = static_cast<const uint8_t*>(a.w);
     if (a.x_bf16 != nullptr) {
-      if constexpr (DT == SP24_FP8_E4M3 && SPARSE && C::RING_QX + kStreamQxBytes + 64 <= kLdsBytes) {
+      if constexpr (DT == SP24_FP8_E4M3 && SPARSE && stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, false)) {
         // the X rows of a workgroup must fit the region after the ring
         const int64_t rows = a.m < C::BM ? a.m : C::BM;
         if (rows * stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB) > kStreamQxBytes)
           return hipErrorInvalidConfiguration;
-        if (p.split_k > 1)
+        const int xk = a.x_lift ? a.k / (4 * (a.x_lift - 1)) * (2 * a.x_lift) : a.k;
+        if (a.x_rows) {
+          if constexpr (stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, true)) {
+            if (p.split_k > 1)
+              hipLaunchKernelGGL((gemm_stream_kernel<C, true, true, true>), grid, block, 0, s, x, w, a.meta,
+                                 a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
+                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift);
+            else
+              hipLaunchKernelGGL((gemm_stream_kernel<C, false, true, true>), grid, block, 0, s, x, w, a.meta,
+                                 a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
+                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift);
+          } else {
+            return hipErrorInvalidConfiguration;
+          }
+        } else if (a.x_lift != 0) {
+          return hipErrorInvalidValue;  // lifting is per token only
+        } else if (p.split_k > 1) {
           hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0);
-        else
+                             a.x_scale_out, 0, a.k, 0);
+        } else {
           hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0);
+                             a.x_scale_out, 0, a.k, 0);
+        }
         return hipGetLastError();
       } else {
         return hipErrorInvalidConfiguration;
@@ -506,11 +599,11 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
     if (p.split_k > 1)
       hipLaunchKernelGGL((gemm_stream_kernel<C, true, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0);
     else
       hipLaunchKernelGGL((gemm_stream_kernel<C, false, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0);
     return hipGetLastError();
   }
 }

@@ -89,6 +89,10 @@ struct GemmArgs {
   float* x_scale_out = nullptr;
   // FP8: the scale of X row m is x_scale[m * x_scale_step] (0: one per tensor, 1: one per row)
   int x_scale_step = 0;
+  // with x_bf16: one scale per token (written to x_scale_out[m]) instead of one per
+  // tensor, and X rows lifted to the SlideSparse windows of N = x_lift (0: none)
+  bool x_rows = false;
+  int x_lift = 0;
 };
 // Small-m kernel configurations: X(id, row blocks of 16, token blocks of 16,
 // waves per workgroup, chunks of loads issued per batch).
@@ -185,6 +189,15 @@ constexpr int stream_ring_bytes(int dtype, bool sparse, int rbw, int rb, int mw,
   const int ring = stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) * stage;
   const int red = kw > 1 ? kw * rbw * mw * rb * mb * 1024 : 0;
   return ring > red ? ring : red;
+}
+// A stream configuration can quantise X itself (sparse FP8): its ring without X
+// rows, the kStreamQxBytes region and the per-wave (per tensor) or per-row (per
+// token) maxima fit the LDS.
+constexpr bool stream_qx_fits(int rbw, int rb, int mw, int kw, int mb, int u, int smax, bool rows) {
+  return stream_fits(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax) &&
+         stream_ring_bytes(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, true) + kStreamQxBytes + 64 +
+                 (rows ? 4 * 16 * mw * mb : 0) <=
+             kStreamLdsBytes;
 }
 // Row stride of the X rows a quantising stream kernel holds in LDS: its K
 // slice, plus 128 bytes when that keeps 128-byte steps (one unit per step) on

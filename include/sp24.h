@@ -96,7 +96,8 @@ typedef enum sp24_op {
   SP24_OP_DENSE_GEMM = 2, /* sp24_dense_gemm */
   SP24_OP_GEMM_QX = 3,    /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
   SP24_OP_PALETTE_ANALYZE = 4, /* sp24_palette_analyze (n = rows, k; m and dtype ignored) */
-  SP24_OP_PALETTE_GEMM = 5     /* sp24_palette_gemm (dtype ignored) */
+  SP24_OP_PALETTE_GEMM = 5,    /* sp24_palette_gemm (dtype ignored) */
+  SP24_OP_GEMM_ROWS_QX = 6     /* sp24_gemm_rows_qx; sp24_slide_gemm_qx with k = K' (dtype SP24_FP8_E4M3) */
 } sp24_op;
 
 typedef enum sp24_kernel {
@@ -276,6 +277,40 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
                  const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token FP8 quantisation fused into the sparse GEMM (the step left of the
+ * GEMM that the SlideSparse page fuses into its per-token quantisation, and
+ * the cookbook's FP8 activation step with one scale per token): exactly
+ * sp24_quant_fp8_rows(x_bf16, m, k, codes, x_scales_dev) followed by
+ * sp24_gemm_rows(SP24_FP8_E4M3, ..., codes, x_scales_dev, ...), bit for bit in
+ * y and in x_scales_dev, in one call.  When the plan's small-m kernel has room
+ * for its tokens' codes in LDS (decode shapes) each workgroup quantises its
+ * own tokens, so no codes go through memory and no quantiser is launched;
+ * otherwise the two steps run as two launches with the codes in the workspace.
+ *   x_bf16 in : [m, k] bf16;  x_scales_dev out: [m] fp32, amax_r/448 (1 for a
+ *   zero row);  w_values, w_meta, w_scale_dev, y_bf16 as for sp24_gemm_qx.
+ * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM_ROWS_QX,
+ * SP24_FP8_E4M3, m, n, k).  Shape limits, alignment and errors as
+ * sp24_gemm_qx; x_scales_dev may alias no other argument. */
+int sp24_gemm_rows_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scales_dev,
+                      const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* SlideSparse's per-call path in one call ("SlideSparse: Fast and Flexible
+ * (2N-2):2N Structured Sparsity", technical summary, section 2): exactly
+ * sp24_slide_quant_fp8_rows(x_bf16, m, k, n_pat, codes, x_scales_dev)
+ * followed by sp24_gemm_rows(SP24_FP8_E4M3, m, n, k', codes, ...), bit for
+ * bit, with k' = k (2N-2)/N and the weight W' of sp24_slide_prune_pack,
+ * compressed and quantised.  At decode shapes the lifting and the per-token
+ * quantisation both happen inside the GEMM kernel, as for sp24_gemm_rows_qx.
+ *   x_bf16 [m, k]; w_values [n, k'/2]; w_meta [n, k'/32]; y_bf16 [m, n].
+ *   n_pat = N in [3, 8] (SP24_ERR_MODE otherwise); k % 8 == 0 and
+ *   k % (2N) == 0; k' must meet sp24_gemm's limits.
+ * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM_ROWS_QX,
+ * SP24_FP8_E4M3, m, n, k').  Errors otherwise as sp24_gemm_rows_qx. */
+int sp24_slide_gemm_qx(int n_pat, int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scales_dev,
+                       const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Lossless BF16 exponent-palette weights (no sparsity).  The 8 exponent bits of

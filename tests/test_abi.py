@@ -299,6 +299,44 @@ def test_gemm_qx_validation():
     assert gemm_qx(ws=A + 0x500100) == EALIAS            # workspace over the output
 
 
+def rows_qx(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
+            wsc=A + 0x400000, y=A + 0x500000, ws=A + 0x600000, wsb=1 << 20, n_pat=None):
+    if n_pat is None:
+        return lib.sp24_gemm_rows_qx(m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), p(ws), wsb, None)
+    return lib.sp24_slide_gemm_qx(n_pat, m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), p(ws), wsb, None)
+
+
+def test_gemm_rows_qx_and_slide_gemm_qx_validation():
+    for n_pat, k in ((None, 256), (4, 1024), (3, 1536)):
+        for kw in ("x", "xs", "w", "meta", "wsc", "y"):
+            assert rows_qx(n_pat=n_pat, k=k, **{kw: None}) == ENULL, (n_pat, kw)
+        assert rows_qx(n_pat=n_pat, k=k, m=0) == ESHAPE
+        assert rows_qx(n_pat=n_pat, k=k, x=A + 8) == EALIGN
+        assert rows_qx(n_pat=n_pat, k=k, xs=A + 0x100002) == EALIGN
+        # the scales (8 x 4 bytes) may alias no input, not the output and not the workspace
+        assert rows_qx(n_pat=n_pat, k=k, xs=A + 0x100) == EALIAS
+        assert rows_qx(n_pat=n_pat, k=k, xs=A + 0x400000 - 16) == EALIAS   # over the weight scale
+        assert rows_qx(n_pat=n_pat, k=k, y=A + 0x200000) == EALIAS
+    assert rows_qx(k=96) == ESHAPE
+    assert rows_qx(n_pat=2, k=1024) == EMODE and rows_qx(n_pat=9, k=1024) == EMODE
+    assert rows_qx(n_pat=4, k=1020) == ESHAPE                  # k % 8 != 0
+    assert rows_qx(n_pat=4, k=192) == ESHAPE                   # K' = 288: not a multiple of 128
+    assert rows_qx(n_pat=3, k=1028) == ESHAPE                  # k % 6 != 0
+
+
+def test_gemm_rows_qx_workspace_rule():
+    ws_r = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM_ROWS_QX, sp.FP8, m, n, k)
+    ws_g = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)
+    # decode tokens whose codes fit the kernel's 16 KB: only the GEMM's own workspace
+    for m, n, k in ((1, 14336, 4096), (2, 14336, 4096), (4, 14336, 4096), (1, 14336, 6144), (1, 512, 24576)):
+        assert ws_r(m, n, k) == (ws_g(m, n, k) + 15) // 16 * 16, (m, n, k)
+    # otherwise the codes as well (the per-token quantiser needs no workspace of its own)
+    for m, n, k in ((16, 14336, 4096), (64, 14336, 4096), (3, 4096, 14336), (8192, 28672, 8192)):
+        assert ws_r(m, n, k) == (ws_g(m, n, k) + 15) // 16 * 16 + (m * k + 15) // 16 * 16, (m, n, k)
+    assert ws_r(1, 256, 96) == 0                              # invalid shape
+    assert lib.sp24_workspace_size(sp.OP_GEMM_ROWS_QX, sp.BF16, 1, 256, 256) == 0
+
+
 def test_gemm_qx_workspace_rule():
     ws_qx = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM_QX, sp.FP8, m, n, k)
     ws_g = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)

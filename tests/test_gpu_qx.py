@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import sp24_ref as O
 from gpu_helpers import (DEV, GpuWeight, OracleWeight, announce, assert_within_tolerance, bits, f32,
                          f32_bits, need_sp, oracle_ref, oracle_x)
 
@@ -87,3 +88,50 @@ def test_gemm_qx_repeated_calls_are_bitwise_stable():
     announce("gemm_qx repeated")
     ys = [bits(sp.gemm_qx(x, gw.qvalues, gw.meta, gw.scale)[0]) for _ in range(3)]
     assert all(np.array_equal(ys[0], yy) for yy in ys[1:])
+
+
+# ---------------------------------------------------------------- one scale per token
+
+def _fused_rows(sp, m, n, k):
+    g = sp.lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)
+    return sp.lib.sp24_workspace_size(sp.OP_GEMM_ROWS_QX, sp.FP8, m, n, k) == (g + 15) // 16 * 16
+
+
+@pytest.mark.parametrize("m,n,k,fused", SHAPES)
+def test_gemm_rows_qx_equals_quant_rows_then_gemm_rows(m, n, k, fused):
+    """sp24_gemm_rows_qx = sp24_quant_fp8_rows + sp24_gemm_rows bit for bit (Y and every row's
+    scale), fused into the stream kernel or not, and within the oracle's tolerance."""
+    sp = need_sp()
+    assert _fused_rows(sp, m, n, k) == fused
+    seed = 5 * m + 3 * n + k
+    x_cpu = W.randn_bf16((m, k), seed=seed).float()
+    if m > 2:
+        x_cpu[m // 2] *= 300.0        # an outlier token
+        x_cpu[m - 1] = 0.0            # an all-zero token: scale 1
+    x_cpu = x_cpu.to(torch.bfloat16)
+    w_cpu = W.randn_bf16((n, k), seed=seed + 1, std=0.02)
+    announce("gemm_rows_qx", m, n, k, "fused" if fused else "two launches")
+    gw = GpuWeight(w_cpu, True)
+    x = x_cpu.to(DEV)
+    y, sx = sp.gemm_rows_qx(x, gw.qvalues, gw.meta, gw.scale)
+    xq2, sx2 = sp.quant_fp8_rows(x)
+    y2 = sp.gemm_rows(xq2, gw.qvalues, gw.meta, sx2, gw.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(bits(y), bits(y2)), "differs from quant_rows + gemm_rows in %d outputs" % int(
+        (bits(y) != bits(y2)).sum())
+    ow = OracleWeight(W.bf16_bits(w_cpu), True)
+    oxq, oxs = O.quant_fp8_rows(W.bf16_bits(x_cpu))
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), oxs.view(np.uint32))
+    ref, mag = O.gemm_ref(*O.sparse_operands_fp8_rows(oxq, oxs, ow.qvalues, ow.meta, ow.scale, k))
+    assert_within_tolerance(bits(y), ref, mag, "gemm_rows_qx %dx%dx%d" % (m, n, k))
+
+
+def test_gemm_rows_qx_repeated_calls_are_bitwise_stable():
+    sp = need_sp()
+    gw = GpuWeight(W.up_weight(), True)
+    for m in (1, 2):
+        x = W.up_x(m).to(DEV)
+        announce("gemm_rows_qx repeated", m)
+        ys = [bits(sp.gemm_rows_qx(x, gw.qvalues, gw.meta, gw.scale)[0]) for _ in range(3)]
+        assert all(np.array_equal(ys[0], yy) for yy in ys[1:])

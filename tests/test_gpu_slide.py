@@ -118,3 +118,48 @@ def test_slide_gemm_int8_matches_the_6_of_8_product(m, n, k):
     yb = bits(y)
     assert_within_tolerance(yb, ref, mag, "slide int8 %dx%dx%d" % (m, n, k))
     assert_exact_sum_bound(yb, ref, mag, "slide int8 %dx%dx%d" % (m, n, k))
+
+
+# ---------------------------------------------------------------- lifting fused into the GEMM
+
+# (m, n, k, N, lifted inside the GEMM kernel): no split, split-K over 2/4/8 slices (slice
+# boundaries inside the lifted blocks), ragged rows, and shapes that take two launches
+SLIDE_QX = [(1, 14336, 4096, 4, True), (2, 14336, 4096, 4, True), (1, 1024, 6144, 3, True),
+            (3, 1000, 5120, 5, True), (1, 1024, 4096, 8, True), (2, 512, 16384, 4, True),
+            (1, 40, 8192, 4, True), (4, 300, 2560, 5, True),
+            (16, 1024, 4096, 4, False), (3, 1000, 1536, 4, False), (1, 4096, 14336, 4, False)]
+
+
+@pytest.mark.parametrize("m,n,k,n_pat,fused", SLIDE_QX)
+def test_slide_gemm_qx_equals_lift_quant_then_gemm_rows(m, n, k, n_pat, fused):
+    """sp24_slide_gemm_qx = sp24_slide_quant_fp8_rows + sp24_gemm_rows over K' bit for bit (Y
+    and every row's scale), and within the oracle's tolerance of the (2N-2):2N product."""
+    sp = need_sp()
+    kp = k // (2 * n_pat) * 4 * (n_pat - 1)
+    g = sp.lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, kp)
+    assert (sp.lib.sp24_workspace_size(sp.OP_GEMM_ROWS_QX, sp.FP8, m, n, kp) == (g + 15) // 16 * 16) == fused
+    w = W.randn_bf16((n, k), seed=n + k + n_pat, std=0.02)
+    x = W.randn_bf16((m, k), seed=m + k + 5).float()
+    if m > 2:
+        x[1] *= 300.0
+        x[m - 1] = 0.0
+    x = x.to(torch.bfloat16)
+    announce("slide_gemm_qx", m, n, k, "N", n_pat, "K'", kp, "fused" if fused else "two launches")
+    wp = sp.slide_prune_pack(w.to(DEV), n_pat)
+    values, meta = sp.prune_compress(wp)
+    qv, sw = sp.quant_fp8(values)
+    y, sx = sp.slide_gemm_qx(x.to(DEV), qv, meta, sw, n_pat)
+    xq2, sx2 = sp.slide_quant_fp8_rows(x.to(DEV), n_pat)
+    y2 = sp.gemm_rows(xq2, qv, meta, sx2, sw)
+    torch.cuda.synchronize()
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(bits(y), bits(y2)), "differs from lift + quant + gemm_rows in %d outputs" % int(
+        (bits(y) != bits(y2)).sum())
+    # the reference over K: the (2N-2):2N-pruned W, per-tensor W scale, per-token X scales
+    wb = W.bf16_bits(w)
+    wpr = O.apply_mask(wb, O.slide_prune_mask(wb, n_pat))
+    wq, osw = O.quant_fp8(wpr)
+    oxq, oxs = O.quant_fp8_rows(W.bf16_bits(x))
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), oxs.view(np.uint32))
+    ref, mag = O.gemm_ref(O.dequant_fp8_rows(oxq, oxs), O.dequant_fp8(wq, osw))
+    assert_within_tolerance(bits(y), ref, mag, "slide_gemm_qx %dx%dx%d N=%d" % (m, n, k, n_pat))
