@@ -146,6 +146,10 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 //  * m <= 16: X is negligible and W streams at the HBM rate; short row ranges
 //    want many waves along K (8 waves over 16 rows), ~30-64 rows per CU do
 //    best as two 8-wave workgroups per CU, longer ranges as 8 row blocks.
+//    BF16 (twice the bytes per step, so the two-workgroup ring no longer fits
+//    twice in a CU's LDS) does best there with one workgroup of 4 x 16 rows
+//    per CU (up-projection, 14336 x 4096: 15.7 against 16.3 us at m = 1, 15.8
+//    against 17.4 us at m = 16).
 //  * m <= 64: X (m*k bytes per workgroup, from L2 into LDS) costs as much as
 //    W's share when a CU has few rows, so few-row shapes take 32 tokens per
 //    workgroup (W read twice, the second time from cache), or, for long K, 64
@@ -154,7 +158,7 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 //    one workgroup with 8 waves along m, so that W streams once; long-K
 //    few-row shapes take 64 rows per workgroup and split K; the rest take
 //    64-token blocks.
-StreamChoice stream_default(int64_t m, int64_t n, int64_t k) {
+StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
   const int64_t rows_cu = (n + 255) / 256;
   auto rows_for = [&](int64_t shares, int64_t lo, int64_t hi) {
     int64_t r = ((n + shares - 1) / shares + 3) / 4 * 4;
@@ -162,7 +166,9 @@ StreamChoice stream_default(int64_t m, int64_t n, int64_t k) {
   };
   if (m <= 16) {
     if (rows_cu <= 16) return StreamChoice{k >= 8192 ? 5 : 4, 0};
-    if (rows_cu <= 64) return StreamChoice{15, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
+    if (rows_cu <= 64)
+      return dtype == SP24_BF16 && rows_cu > 32 ? StreamChoice{13, 0}
+                                                : StreamChoice{15, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
     return StreamChoice{9, 0};
   }
   if (m <= 32) {
@@ -272,7 +278,7 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   if (!forced) {
     // the choice for this shape, else (it does not fit this operand type, or K
     // does not split into its steps) the 64-token-block configurations
-    const StreamChoice d = stream_default(m, n, k);
+    const StreamChoice d = stream_default(dtype, m, n, k);
     if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
     const int64_t gy = (m + 63) / 64, shares = gy >= 256 ? 1 : 256 / gy;
     const int g = (n + shares - 1) / shares > 64 ? 12 : 3;
