@@ -189,6 +189,21 @@ def test_plan_uses_tiled_kernel_for_prefill_only():
         assert sp.plan(sp.OP_GEMM, sp.FP8, m, 14336, 4096)["kernel"] != 1
 
 
+def test_plan_decode_workgroups_per_cu_by_code_type():
+    # m <= 16 with 33-64 rows per CU: one-byte codes take two 8-wave workgroups per CU (512
+    # ranges of 28 rows), BF16 -- whose ring for that layout fits a CU's LDS only once --
+    # one workgroup of 4 x 16 rows per CU (256 ranges of 56 rows)
+    for m in (1, 4, 16):
+        for dt in (sp.FP8, sp.INT8):
+            p = sp.plan(sp.OP_GEMM, dt, m, 14336, 4096)
+            assert (p["kernel"], p["tile_n"], p["grid_x"], p["waves"]) == (2, 28, 512, 8), (m, dt, p)
+        p = sp.plan(sp.OP_GEMM, sp.BF16, m, 14336, 4096)
+        assert (p["kernel"], p["tile_n"], p["grid_x"], p["config"]) == (2, 56, 256, 113), (m, p)
+    # 17-32 rows per CU: one range per CU for every code type
+    for dt in (sp.FP8, sp.BF16):
+        assert sp.plan(sp.OP_GEMM, dt, 1, 6144, 4096)["grid_x"] == 256
+
+
 def test_plan_tiled_for_wide_layers_at_256_tokens():
     # one tile of tokens and >= 96 tiles (gate+up of an 8B-class layer): the tiled kernel,
     # BF16 with K split in two; narrower projections keep the small-m kernels
