@@ -1,33 +1,35 @@
 """Benchmark of the 2:4 sparse GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload up|down|prefill|layers]
+    python bench.py [--steps K] [--warmup W] [--workload all|up|down|prefill|layers|slide|palette]
 
-Default workload: the decode-shaped FP8 FFN up-projection (K=4096, N=14336) at
-M = 1, 16 and 64 tokens.  One step = one pass of the per-call path for each M:
-dynamic per-tensor E4M3 quantisation of X (sp24_quant_fp8) and the sparse GEMM
-(sp24_gemm, including any split-K reduction), on weights that were pruned,
-compressed and quantised once at load.  The load path (sp24_prune_compress and
-the weight quantisation) is timed separately and reported under "load_path".
-
---workload down: the down-projection (K=14336, N=4096) at the same M.
---workload prefill: the M=8192, K=8192, N=28672 GEMM (bound: matrix cores).
---workload layers: 32 layers x (QKV, O, gate+up, down) at M=256, 128 sequential
-sparse GEMMs per step (see run_layers).
---workload palette: lossless BF16 exponent-palette weights (no sparsity) against the
-dense BF16 GEMM at decode sizes (see run_palette).
+Default (--workload all): the whole metric, decode and prefill, in one JSON line.
+  * The headline step (value, ms_per_step, roofline, cpu_baseline) is the
+    decode-shaped FP8 FFN up-projection (K=4096, N=14336) at M = 1, 16 and 64
+    tokens: one step = sp24_gemm_qx for each M (dynamic per-tensor E4M3
+    quantisation of X and the sparse GEMM, including any split-K reduction) on
+    weights pruned, compressed and quantised once at load.
+  * "configs" holds every configuration of the metric, each with its own
+    roofline fraction, dense-MFMA baseline and per-call p50/p99:
+      up      -- the same up-projection per M (sparse GEMM, quantise + GEMM, dense
+                 MFMA, hipBLASLt's dense FP8 as a reference);
+      down    -- the down-projection (K=14336, N=4096) per M, which splits K;
+      prefill -- M=8192, K=8192, N=28672 (bound: matrix cores), with the CPU
+                 oracle timed on a slice;
+      layers  -- 32 layers x (QKV, O, gate+up, down) at M=256, 128 sequential
+                 sparse GEMMs per step, and the same sweep on dense MFMA.
+--workload up|down|prefill|layers prints the line of that configuration alone
+(the form the profiles are taken with); slide and palette measure the
+SlideSparse 6:8 and exponent-palette variants.
 --dtype int8: up, down or prefill with symmetric per-tensor INT8 codes (the
-cookbook's INT8 W8A8 recipe): a step is sp24_quant_int8 of X and the INT8
-sparse GEMM (exact int32 sums); the roofline peak is the dense INT8 MFMA rate.
+cookbook's INT8 W8A8 recipe); bf16: BF16 operands (no scales).
 
 Inputs are seeded synthetic tensors (workloads/) resident in HBM before the
-timed region.  Each call reads a different one of R weight copies (> 2x the
-256 MB last-level cache), so weight bytes come from HBM.  Steps are captured
-once per weight copy in HIP graphs and replayed; the graphs' outputs are
-checked bitwise against an eager run.
-
-Prints ONE JSON line with the metric, the roofline of the dominant kernel (the
-sparse GEMM, timed with HIP events on the stream it runs on), the dense-MFMA
-baseline of the same shapes, and the CPU oracle timed on the host.
+timed region.  At decode each call reads a different one of R weight copies
+(> 2x the 256 MB last-level cache), so weight bytes come from HBM.  Steps are
+captured once per weight copy in HIP graphs and replayed; the graphs' outputs
+are checked bitwise against an eager run.  Kernel times are HIP events on the
+stream the library launches on (torch's current stream); p50/p99 come from an
+event pair around each of many calls.
 """
 from __future__ import annotations
 
@@ -41,9 +43,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse GEMM TFLOP/s + GB/s and % of roofline vs dense MFMA, decode & prefill"
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (and INT8: 5.0 POP/s); SMFMAC's rate of nonzero MACs
-BF16_DENSE_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# MFMA peaks of MI355X from its unit counts and clock: 256 CUs x 2.4 GHz x dense flop per
+# clock per CU (FP8 and INT8 8192, BF16 4096).  SMFMAC performs as many nonzero
+# multiply-adds per clock as dense MFMA, so a 2:4 kernel is priced in nonzero MACs x 2 per
+# second against these, which equals dense-equivalent flops against twice these (the
+# sparse FP8 peak 10,066 TFLOP/s).
+N_CU, CLOCK_HZ = 256, 2.4e9
+FP8_DENSE_PEAK_TFLOPS = N_CU * 8192 * CLOCK_HZ / 1e12   # 5033.2 (INT8: the same in TOP/s)
+BF16_DENSE_PEAK_TFLOPS = N_CU * 4096 * CLOCK_HZ / 1e12  # 2516.6
+PEAK_SOURCE = "256 CUs x 2.4 GHz x 8192 (FP8/INT8) or 4096 (BF16) dense flop/clk/CU"
 LLC_BYTES = 256 << 20
 
 
@@ -52,10 +61,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="up", choices=["up", "down", "prefill", "layers", "slide", "palette"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "up", "down", "prefill", "layers", "slide", "palette"])
     ap.add_argument("--dtype", default="fp8", choices=["fp8", "int8", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-percentiles", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=0,
                     help="GEMM launches per M for the per-kernel timing (0: automatic)")
     return ap.parse_args()
@@ -107,6 +118,12 @@ def quant_bytes(m, k):
     return m * k * 2 + m * k + 4
 
 
+def n_copies(nbytes):
+    """Weight copies a decode call rotates over so that its weight comes from HBM."""
+    import math
+    return max(2, min(16, int(math.ceil(2.2 * LLC_BYTES / nbytes))))
+
+
 class Events:
     """HIP events on the current (torch) stream, which is the stream libsp24 launches on."""
 
@@ -124,6 +141,52 @@ class Events:
         e.synchronize()
         return s.elapsed_time(e) / 1e3  # seconds
 
+    def graph(self, fn, reps, replays=3):
+        """Mean seconds per call of fn(0) .. fn(reps - 1), captured once in a HIP graph and
+        replayed (launch-free back-to-back calls)."""
+        t = self.torch
+        fn(0)
+        t.cuda.synchronize()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        t.cuda.synchronize()
+        sec = self.time(lambda i: g.replay(), replays) / replays / reps
+        del g
+        return sec
+
+    def percentiles(self, fn, calls, warm=3):
+        """Per-call duration (us) from an event pair around each of `calls` calls: p50, p99,
+        mean.  A spin kernel first keeps the GPU busy so that the host enqueues every call
+        ahead of it and no launch gap falls inside a pair."""
+        t = self.torch
+        for i in range(warm):
+            fn(i)
+        t.cuda.synchronize()
+        pairs = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        t.cuda._sleep(20_000_000)
+        for i, (a, b) in enumerate(pairs):
+            a.record()
+            fn(i)
+            b.record()
+        t.cuda.synchronize()
+        d = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+        def pct(q):
+            return d[min(len(d) - 1, int(round(q * (len(d) - 1))))]
+        return {"p50_us": pct(0.50), "p90_us": pct(0.90), "p99_us": pct(0.99), "mean_us": sum(d) / len(d),
+                "calls": calls}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
 
 def main():
     args = parse()
@@ -140,44 +203,72 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kind = args.dtype
-    fp8 = kind != "bf16"  # one-byte codes with per-tensor scales: E4M3 or INT8
-    dt = {"fp8": sp.FP8, "int8": sp.INT8, "bf16": sp.BF16}[kind]
-    quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
-    code_t = torch.int8 if kind == "int8" else torch.uint8
-    label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
-    if kind == "int8" and args.workload in ("layers", "palette"):
+    if kind == "int8" and args.workload in ("layers", "palette", "all"):
         print("--dtype int8 is measured on the up, down, prefill and slide workloads", file=sys.stderr)
         sys.exit(2)
     if kind == "bf16" and args.workload == "slide":
         print("the slide workload multiplies one-byte codes: --dtype fp8 or int8", file=sys.stderr)
         sys.exit(2)
     ev = Events(torch)
+    ctx = (args, torch, np, sp, W, ev, dev)
 
-    # ---------------------------------------------------------------- workload
+    if args.workload == "slide":
+        print(json.dumps(run_slide(*ctx)))
+        return
+    if args.workload == "palette":
+        print(json.dumps(run_palette(*ctx)))
+        return
+    if args.workload == "layers":
+        print(json.dumps(layers_line(args, run_layers(*ctx))))
+        return
+    if args.workload == "prefill":
+        print(json.dumps(prefill_line(args, run_prefill(*ctx))))
+        return
     if args.workload in ("up", "down"):
-        spec = W.UP if args.workload == "up" else W.DOWN
-        K, N, Ms = spec["K"], spec["N"], list(spec["Ms"])
-        w_cpu = W.up_weight() if args.workload == "up" else W.down_weight()
-        xs_cpu = {m: (W.up_x(m) if args.workload == "up" else W.down_x(m)) for m in Ms}
-        desc = ("decode FFN %s-projection, 2:4 sparse %s, M=%s tokens, K=%d, N=%d"
-                % (args.workload, label,
-                   "/".join(map(str, Ms)), K, N))
-        bound = "hbm"
-    elif args.workload == "prefill":
-        K, N, Ms = W.PREFILL["K"], W.PREFILL["N"], [W.PREFILL["M"]]
-        w_cpu = W.prefill_weight()
-        xs_cpu = {Ms[0]: W.prefill_x()}
-        desc = "prefill GEMM, 2:4 sparse %s, M=%d, K=%d, N=%d" % (label, Ms[0], K, N)
-        bound = "mfma"
-    elif args.workload == "slide":
-        print(json.dumps(run_slide(args, torch, np, sp, W, ev, dev)))
+        print(json.dumps(decode_line(args, run_decode(*ctx, args.workload))))
         return
-    elif args.workload == "palette":
-        print(json.dumps(run_palette(args, torch, np, sp, W, ev, dev)))
-        return
-    else:
-        print(json.dumps(run_layers(args, torch, np, sp, W, ev, dev)))
-        return
+
+    # --workload all: the headline step, then every configuration of the metric
+    t_all = time.perf_counter()
+    up = run_decode(*ctx, "up")
+    out = decode_line(args, up)
+    torch.cuda.empty_cache()
+    down = run_decode(*ctx, "down", headline=False)
+    torch.cuda.empty_cache()
+    pre = run_prefill(*ctx)
+    torch.cuda.empty_cache()
+    lay = run_layers(*ctx)
+    torch.cuda.empty_cache()
+    out["config"]["workload"] = ("decode FFN up-projection, 2:4 sparse %s, M=1/16/64 tokens, K=4096, N=14336 "
+                                 "(headline step); every configuration of the metric under configs"
+                                 % up["label"])
+    out["configs"] = {
+        "up": config_summary_decode(up),
+        "down": config_summary_decode(down),
+        "prefill": config_summary_prefill(pre),
+        "layers": config_summary_layers(lay),
+    }
+    out["bench_wall_s"] = time.perf_counter() - t_all
+    print(json.dumps(out))
+
+
+# --------------------------------------------------------------------------- decode
+def run_decode(args, torch, np, sp, W, ev, dev, which, headline=True):
+    """The decode-shaped projection `which` ("up": K=4096, N=14336; "down": K=14336,
+    N=4096) at M = 1, 16, 64: load path, the per-call step in HIP graphs, every GEMM
+    alone, per-call percentiles, the dense-MFMA baseline and hipBLASLt's dense FP8."""
+    kind = args.dtype
+    fp8 = kind != "bf16"  # one-byte codes with per-tensor scales: E4M3 or INT8
+    dt = {"fp8": sp.FP8, "int8": sp.INT8, "bf16": sp.BF16}[kind]
+    quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
+    code_t = torch.int8 if kind == "int8" else torch.uint8
+    label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
+    spec = W.UP if which == "up" else W.DOWN
+    K, N, Ms = spec["K"], spec["N"], list(spec["Ms"])
+    w_cpu = W.up_weight() if which == "up" else W.down_weight()
+    xs_cpu = {m: (W.up_x(m) if which == "up" else W.down_x(m)) for m in Ms}
+    desc = ("decode FFN %s-projection, 2:4 sparse %s, M=%s tokens, K=%d, N=%d"
+            % (which, label, "/".join(map(str, Ms)), K, N))
 
     # ---------------------------------------------------------------- load path
     w = w_cpu.to(dev)
@@ -191,6 +282,7 @@ def main():
         qbuf = torch.empty_like(qv)
         quant(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC)
         t_wq = ev.time(lambda i: quant(values, scale=sw, out=qbuf, mode=sp.SCALE_DYNAMIC), 5) / 5
+        del qbuf
     else:
         t_wq = 0.0
     torch.cuda.synchronize()
@@ -203,8 +295,7 @@ def main():
     del w
 
     # weight copies, so that each call reads its weight from HBM
-    wbytes = qv.numel() * qv.element_size() + meta.numel() * 4
-    R = max(2, min(16, int(np.ceil(2.2 * LLC_BYTES / wbytes)))) if bound == "hbm" else 1
+    R = n_copies(qv.numel() * qv.element_size() + meta.numel() * 4)
     wq_copies = [qv] + [qv.clone() for _ in range(R - 1)]
     meta_copies = [meta] + [meta.clone() for _ in range(R - 1)]
 
@@ -256,7 +347,7 @@ def main():
     torch.cuda.synchronize()
     eager = {m: bufs[m]["y"].clone() for m in Ms}
 
-    # ---------------------------------------------------------------- graphs
+    # ---------------------------------------------------------------- graphs of the step
     graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -274,11 +365,13 @@ def main():
     def replay(i):
         graphs[i % n_graphs].replay()
 
-    for i in range(args.warmup):
+    steps = args.steps if headline else min(args.steps, 50)
+    warmup = args.warmup if headline else min(args.warmup, 5)
+    for i in range(warmup):
         replay(i)
     torch.cuda.synchronize()
-    t_steps = ev.time(replay, args.steps)
-    ms_per_step = t_steps / args.steps * 1e3
+    t_steps = ev.time(replay, steps)
+    ms_per_step = t_steps / steps * 1e3
 
     # graphs replayed many times must reproduce the eager outputs bitwise
     graphs[0].replay()
@@ -286,37 +379,32 @@ def main():
     for m in Ms:
         if not torch.equal(bufs[m]["y"].view(torch.int16), eager[m].view(torch.int16)):
             raise SystemExit("graph replay output differs from the eager run for M=%d" % m)
+    del graphs
 
     step_bytes = sum(gemm_bytes(m, N, K, fp8) + (quant_bytes(m, K) if fp8 else 0) for m in Ms)
     step_flops = sum(2 * m * N * K for m in Ms)          # dense-equivalent
-    value_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
 
-    # ---------------------------------------------------------------- dominant kernel
+    # ---------------------------------------------------------------- the sparse GEMM alone
     per_m = {}
     for m in Ms:
-        reps = args.kernel_reps or (R * 16 if bound == "hbm" else 5)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(reps):
-                call_gemm(m, i % R)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        t = ev.time(lambda i: g.replay(), 3) / 3 / reps
+        reps = args.kernel_reps or R * 16
+        t = ev.graph(lambda i: call_gemm(m, i % R), reps)
         gb = gemm_bytes(m, N, K, fp8)
         per_m[m] = {"gemm_us": t * 1e6, "GBs": gb / t / 1e9,
                     "hbm_frac": gb / t / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes": gb,
                     "tflops_dense_equiv": 2 * m * N * K / t / 1e12,
                     "tflops_effective": m * N * K / t / 1e12,
                     "plan": {k2: v for k2, v in bufs[m]["plan"].items()
-                             if k2 in ("tile_n", "tile_m", "waves", "split_k")}}
-        del g
+                             if k2 in ("kernel", "config", "tile_n", "tile_m", "waves", "split_k")}}
+        if not args.no_percentiles:
+            per_m[m]["gemm_call"] = ev.percentiles(lambda i: call_gemm(m, i % R), 400)
     for m in Ms:  # quantiser alone
         if fp8:
             reps = 200
             t = ev.time(lambda i: call_quant(m), reps) / reps
             per_m[m]["quant_x_us_eager"] = t * 1e6
-    if kind == "fp8" and bound == "hbm":
+    if kind == "fp8":
         # quantise + GEMM in one call, per tensor (the step) and per token, graph-replayed
         for m in Ms:
             b = bufs[m]
@@ -328,22 +416,15 @@ def main():
                      "step_rows_qx_us": lambda i: sp.gemm_rows_qx(xs[m], wq_copies[i % R], meta_copies[i % R], sw,
                                                                   x_scales=xsr, out=b["y"], ws=wsr)}
             for key, fn in calls.items():
-                reps = R * 8
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(reps):
-                        fn(i)
-                torch.cuda.synchronize()
-                g.replay()
-                torch.cuda.synchronize()
-                per_m[m][key] = ev.time(lambda i: g.replay(), 3) / 3 / reps * 1e6
-                del g
+                per_m[m][key] = ev.graph(fn, R * 8) * 1e6
+            per_m[m]["step_qx_over_gemm_us"] = per_m[m]["step_qx_us"] - per_m[m]["gemm_us"]
+            if not args.no_percentiles:
+                per_m[m]["step_qx_call"] = ev.percentiles(calls["step_qx_us"], 200)
 
     # ---------------------------------------------------------------- dense baseline
     if not args.no_dense:
         wd = sp.decompress(qv, meta, K)
-        Rd = max(2, min(16, int(np.ceil(2.2 * LLC_BYTES / (wd.numel() * wd.element_size()))))) \
-            if bound == "hbm" else 1
+        Rd = n_copies(wd.numel() * wd.element_size())
         wd_copies = [wd] + [wd.clone() for _ in range(Rd - 1)]
         for m in Ms:
             b = bufs[m]
@@ -355,73 +436,66 @@ def main():
             def dcall(i, m=m, xin=xin, yd=yd, dws=dws):
                 sp.dense_gemm(xin, wd_copies[i % Rd], x_scale=bufs[m].get("sx"), w_scale=sw, out=yd,
                               ws=dws)
-            reps = args.kernel_reps or (Rd * 16 if bound == "hbm" else 5)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(reps):
-                    dcall(i)
-            g.replay()
-            torch.cuda.synchronize()
-            t = ev.time(lambda i: g.replay(), 3) / 3 / reps
+            t = ev.graph(dcall, args.kernel_reps or Rd * 16)
             db = dense_bytes(m, N, K, fp8)
             per_m[m]["dense_gemm_us"] = t * 1e6
             per_m[m]["dense_GBs"] = db / t / 1e9
             per_m[m]["sparse_speedup_vs_dense"] = t / (per_m[m]["gemm_us"] / 1e6)
-            del g
             if kind == "fp8":
-                tv = vendor_dense_fp8(torch, ev, xin, wd_copies, bufs[m]["sx"], sw, m, bound)
+                tv = vendor_dense_fp8(torch, ev, xin, wd_copies, bufs[m]["sx"], sw, m, "hbm")
                 if tv is not None:
                     per_m[m]["vendor_dense_fp8_us"] = tv * 1e6
                     per_m[m]["sparse_speedup_vs_vendor_dense"] = tv / (per_m[m]["gemm_us"] / 1e6)
         del wd_copies, wd
 
-    if bound == "hbm":
-        tot_b = sum(gemm_bytes(m, N, K, fp8) for m in Ms)
-        tot_t = sum(per_m[m]["gemm_us"] for m in Ms) / 1e6
-        achieved = tot_b / tot_t / 1e9
-        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": counted_traffic(args.workload, "hbm") if kind == "fp8" else None,
-                    "kernel": "%s (sparse %s), mean over M=%s"
-                              % ("/".join(sorted({KERNEL_NAMES[bufs[m]["plan"]["kernel"]] for m in Ms})),
-                                 kind, "/".join(map(str, Ms)))}
-    else:
-        m = Ms[0]
-        eff = per_m[m]["tflops_effective"]
-        peak = FP8_DENSE_PEAK_TFLOPS if fp8 else BF16_DENSE_PEAK_TFLOPS
-        roofline = {"bound": "mfma", "achieved": eff, "peak": peak,
-                    "unit": "TOP/s" if kind == "int8" else "TFLOP/s",
-                    "frac": eff / peak,
-                    "traffic": counted_traffic(args.workload, "mfma") if kind == "fp8" else None,
-                    "kernel": "sparse GEMM, nonzero MACs x2 per second vs the dense %s MFMA peak"
-                              % kind.upper()}
-
-    # ---------------------------------------------------------------- CPU oracle baseline
+    tot_b = sum(gemm_bytes(m, N, K, fp8) for m in Ms)
+    tot_t = sum(per_m[m]["gemm_us"] for m in Ms) / 1e6
+    achieved = tot_b / tot_t / 1e9
+    kernels = "/".join(sorted({KERNEL_NAMES[bufs[m]["plan"]["kernel"]] for m in Ms}))
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": counted_traffic(which, "hbm") if kind == "fp8" else None,
+                "kernel": "%s (sparse %s), mean over M=%s" % (kernels, kind, "/".join(map(str, Ms))),
+                "per_unit": "values N*K/2*es + metadata N*K/8 + X M*K*es + Y 2*M*N bytes per launch"}
     cpu = None
-    if not args.no_cpu_baseline and bound == "hbm":
+    if not args.no_cpu_baseline and headline:
         cpu = cpu_baseline(w_cpu, xs_cpu, Ms, N, K, kind, step_bytes)
+    del wq_copies, meta_copies
+    return {"which": which, "kind": kind, "label": label, "desc": desc, "K": K, "N": N, "Ms": Ms, "R": R,
+            "steps": steps, "warmup": warmup, "ms_per_step": ms_per_step, "step_bytes": step_bytes,
+            "step_flops": step_flops, "per_m": per_m, "roofline": roofline, "cpu": cpu,
+            "load_path": load_path, "device": torch.cuda.get_device_name(dev)}
 
-    out = {
+
+def decode_line(args, d):
+    kind = d["kind"]
+    return {
         "metric": METRIC,
-        "value": value_gbs if bound == "hbm" else step_flops / 2 / (ms_per_step / 1e3) / 1e12,
-        "unit": "GB/s" if bound == "hbm" else ("TOP/s" if kind == "int8" else "TFLOP/s") + " (nonzero MACs x2)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "value": d["step_bytes"] / (d["ms_per_step"] / 1e3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": d["steps"], "warmup": d["warmup"], "ms_per_step": d["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"fp8": "fp8_e4m3", "int8": "int8", "bf16": "bf16"}[kind],
         "data": "synthetic (seeded, workloads/)",
-        "config": {"workload": desc, "M": Ms, "K": K, "N": N, "weight_copies": R,
+        "config": {"workload": d["desc"], "M": d["Ms"], "K": d["K"], "N": d["N"], "weight_copies": d["R"],
                    "step": {"fp8": "per M: sp24_gemm_qx (quantise X + sparse GEMM; one launch at M=1)",
                             "int8": "per M: sp24_quant_int8 + sparse INT8 GEMM",
                             "bf16": "per M: sparse GEMM"}[kind]},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "per_m": {str(m): per_m[m] for m in Ms},
-        "step_GB": step_bytes / 1e9,
-        "step_tflops_dense_equiv": step_flops / (ms_per_step / 1e3) / 1e12,
-        "load_path": load_path,
-        "device": torch.cuda.get_device_name(dev),
+        "roofline": d["roofline"],
+        "cpu_baseline": d["cpu"],
+        "per_m": {str(m): d["per_m"][m] for m in d["Ms"]},
+        "step_GB": d["step_bytes"] / 1e9,
+        "step_tflops_dense_equiv": d["step_flops"] / (d["ms_per_step"] / 1e3) / 1e12,
+        "load_path": d["load_path"],
+        "device": d["device"],
     }
-    print(json.dumps(out))
+
+
+def config_summary_decode(d):
+    return {"workload": d["desc"], "K": d["K"], "N": d["N"], "weight_copies": d["R"],
+            "roofline": d["roofline"],
+            "step_qx_GBs": d["step_bytes"] / (d["ms_per_step"] / 1e3) / 1e9 if d["kind"] == "fp8" else None,
+            "per_m": {str(m): d["per_m"][m] for m in d["Ms"]}}
 
 
 def vendor_dense_fp8(torch, ev, xq, w_copies, sx, sw, m, bound):
@@ -442,6 +516,145 @@ def vendor_dense_fp8(torch, ev, xq, w_copies, sx, sw, m, bound):
         return ev.time(fn, reps) / reps
     except Exception:  # pragma: no cover - depends on the torch build
         return None
+
+
+# --------------------------------------------------------------------------- prefill
+def run_prefill(args, torch, np, sp, W, ev, dev):
+    """The prefill-shaped GEMM M=8192, K=8192, N=28672 (bound: matrix cores): the sparse
+    GEMM alone (mean and per-call percentiles), quantise + GEMM, the dense-MFMA baseline,
+    hipBLASLt's dense FP8, and the CPU oracle on a slice."""
+    kind = args.dtype
+    fp8 = kind != "bf16"
+    dt = {"fp8": sp.FP8, "int8": sp.INT8, "bf16": sp.BF16}[kind]
+    quant = sp.quant_int8 if kind == "int8" else sp.quant_fp8
+    label = {"fp8": "FP8-E4M3 (per-tensor scales)", "int8": "INT8 W8A8 (per-tensor scales)", "bf16": "BF16"}[kind]
+    M, K, N = W.PREFILL["M"], W.PREFILL["K"], W.PREFILL["N"]
+    w_cpu, x_cpu = W.prefill_weight(), W.prefill_x()
+    w, x = w_cpu.to(dev), x_cpu.to(dev)
+    values, meta = sp.prune_compress(w)
+    del w
+    if fp8:
+        qv, sw = quant(values)
+        xq, sx = quant(x)
+    else:
+        qv, sw, xq, sx = values, None, x, None
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    gws = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM, dt, M, N, K)), dtype=torch.uint8, device=dev)
+    plan = sp.plan(sp.OP_GEMM, dt, M, N, K)
+
+    def call(i):
+        sp.gemm(xq, qv, meta, x_scale=sx, w_scale=sw, out=y, ws=gws)
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    reps = 20
+    t = ev.time(call, reps) / reps
+    flops = 2.0 * M * N * K
+    peak = FP8_DENSE_PEAK_TFLOPS if fp8 else BF16_DENSE_PEAK_TFLOPS
+    res = {"gemm_ms": t * 1e3, "tflops_dense_equiv": flops / t / 1e12, "tflops_effective": flops / 2 / t / 1e12,
+           "frac_of_sparse_peak": flops / 2 / t / 1e12 / peak,
+           "GBs": gemm_bytes(M, N, K, fp8) / t / 1e9,
+           "plan": {k2: v for k2, v in plan.items() if k2 in ("kernel", "config", "tile_n", "tile_m", "waves",
+                                                              "split_k")}}
+    if not args.no_percentiles:
+        res["gemm_call"] = ev.percentiles(call, 40)
+    if kind == "fp8":  # the per-call step: quantise X (two launches at this size) + GEMM
+        sxs = torch.empty(1, dtype=torch.float32, device=dev)
+        qws = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM_QX, sp.FP8, M, N, K)), dtype=torch.uint8,
+                          device=dev)
+        fn = lambda i: sp.gemm_qx(x, qv, meta, sw, x_scale=sxs, out=y, ws=qws)
+        fn(0)
+        torch.cuda.synchronize()
+        res["step_qx_ms"] = ev.time(fn, 10) / 10 * 1e3
+        del qws
+    if not args.no_dense:
+        wd = sp.decompress(qv, meta, K)
+        dws = torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, dt, M, N, K)), dtype=torch.uint8, device=dev)
+        dcall = lambda i: sp.dense_gemm(xq, wd, x_scale=sx, w_scale=sw, out=y, ws=dws)
+        for i in range(2):
+            dcall(i)
+        torch.cuda.synchronize()
+        td = ev.time(dcall, 10) / 10
+        res.update({"dense_gemm_ms": td * 1e3, "dense_tflops": flops / td / 1e12,
+                    "dense_frac_of_dense_peak": flops / td / 1e12 / peak,
+                    "sparse_speedup_vs_dense": td / t})
+        if kind == "fp8":
+            tv = vendor_dense_fp8(torch, ev, xq, [wd], sx, sw, M, "mfma")
+            if tv is not None:
+                res["vendor_dense_fp8_ms"] = tv * 1e3
+                res["sparse_speedup_vs_vendor_dense"] = tv / t
+        del wd, dws
+    eff = res["tflops_effective"]
+    roofline = {"bound": "mfma", "achieved": eff, "peak": peak,
+                "unit": "TOP/s" if kind == "int8" else "TFLOP/s", "frac": eff / peak,
+                "traffic": counted_traffic("prefill", "mfma") if kind == "fp8" else None,
+                "kernel": "%s (sparse %s): nonzero MACs x 2 per second against the dense %s MFMA peak (%s); "
+                          "equals dense-equivalent flops against twice that peak"
+                          % (KERNEL_NAMES[plan["kernel"]], kind, kind.upper(), PEAK_SOURCE),
+                "per_unit": "M*N*K nonzero multiply-adds (2*M*N*K dense-equivalent flops) per launch"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_prefill_baseline(w_cpu, x_cpu, kind)
+    del qv, meta, xq, y, gws
+    return {"kind": kind, "label": label, "M": M, "K": K, "N": N, "res": res, "roofline": roofline, "cpu": cpu,
+            "desc": "prefill GEMM, 2:4 sparse %s, M=%d, K=%d, N=%d" % (label, M, K, N),
+            "device": torch.cuda.get_device_name(dev)}
+
+
+def prefill_line(args, p):
+    kind, r = p["kind"], p["res"]
+    return {
+        "metric": METRIC,
+        "value": r["tflops_effective"],
+        "unit": ("TOP/s" if kind == "int8" else "TFLOP/s") + " (nonzero MACs x2)",
+        "n_gpus": 1, "steps": 20, "warmup": 3, "ms_per_step": r["gemm_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp8": "fp8_e4m3", "int8": "int8", "bf16": "bf16"}[kind],
+        "data": "synthetic (seeded, workloads/)",
+        "config": {"workload": p["desc"], "M": p["M"], "K": p["K"], "N": p["N"], "step": "sparse GEMM"},
+        "roofline": p["roofline"], "cpu_baseline": p["cpu"], "prefill": r, "device": p["device"],
+    }
+
+
+def config_summary_prefill(p):
+    return {"workload": p["desc"], "M": p["M"], "K": p["K"], "N": p["N"], "roofline": p["roofline"],
+            "cpu_baseline": p["cpu"], **p["res"]}
+
+
+def cpu_prefill_baseline(w_cpu, x_cpu, kind):
+    """The CPU oracle's per-call path on a slice of the prefill GEMM: rows 0..255 of W
+    (pruned, compressed and quantised at load, not timed) against tokens 0..511 of X
+    (quantise X, decompress W, float64 product and magnitude sum), repeated for about 8 s;
+    reported as dense-equivalent TFLOP/s of the slice."""
+    import workloads as W
+    from oracle import sp24_ref as O
+    wb = W.bf16_bits(w_cpu[:256])
+    xb = W.bf16_bits(x_cpu[:512])
+    K = wb.shape[1]
+    v, meta = O.prune_compress(wb)
+    if kind == "fp8":
+        vq, sw = O.quant_fp8(v)
+    elif kind == "int8":
+        vq, sw = O.quant_int8(v)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if kind == "fp8":
+            xq, sx = O.quant_fp8(xb)
+            O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, K))
+        elif kind == "int8":
+            xq, sx = O.quant_int8(xb)
+            O.gemm_ref(*O.sparse_operands_int8(xq, sx, vq, meta, sw, K))
+        else:
+            O.gemm_ref(*O.sparse_operands_bf16(xb, v, meta, K))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 8.0 or reps >= 50:
+            break
+    flops = 2.0 * 512 * 256 * K
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(blas_threads()),
+            "kind": "oracle",
+            "sample": "%d call(s) of a 512-token x 256-row slice of the prefill GEMM (K=%d: quantise X, "
+                      "decompress W, float64 product and magnitude sum), %.1f s wall" % (reps, K, el)}
 
 
 def run_slide(args, torch, np, sp, W, ev, dev):
@@ -656,14 +869,19 @@ def cpu_palette_baseline(W):
                       "palette form, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
 
 
+
+
+# --------------------------------------------------------------------------- layer sweep
 def run_layers(args, torch, np, sp, W, ev, dev):
     """Layer sweep: 32 layers x (QKV, O, gate+up, down) of a Llama-3-8B-sized block at 256
     tokens, 128 sequential sparse GEMMs per step on weights pruned, compressed and (FP8)
-    quantised once at load.  Weights are drawn on the GPU from seeded generators (seed
+    quantised once at load, and the same 128 products on dense MFMA over the decompressed
+    pruned weights.  Weights are drawn on the GPU from seeded generators (seed
     5000 + 4*layer + projection, 0.02 * N(0, 1)); the two inputs X [256, 4096] ~ N(0, 1) and
     [256, 14336] ~ SiLU(N(0, 1)) come from workloads/ and are quantised once.  The whole
     sweep (4.4 GB of FP8 weights) exceeds the last-level cache, so no weight copies."""
-    fp8 = args.dtype == "fp8"
+    kind = "fp8" if args.dtype == "fp8" or args.workload == "all" else args.dtype
+    fp8 = kind == "fp8"
     dt = sp.FP8 if fp8 else sp.BF16
     M, L = W.LAYER_M, W.N_LAYERS
     projs = W.LAYER_PROJS
@@ -718,25 +936,21 @@ def run_layers(args, torch, np, sp, W, ev, dev):
     with torch.cuda.graph(graph):
         sweep()
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    warmup = min(args.warmup, 10)
+    for _ in range(warmup):
         graph.replay()
-    steps = max(1, min(args.steps, 50))
+    steps = max(1, min(args.steps, 30))
     t = ev.time(lambda i: graph.replay(), steps) / steps
     graph.replay()
     torch.cuda.synchronize()
     for p in range(len(projs)):
         if not torch.equal(ys[p].view(torch.int16), eager[p].view(torch.int16)):
             raise SystemExit("graph replay output differs from the eager run for %s" % projs[p][0])
+    del graph
 
     per_proj, tot_b, tot_t = {}, 0, 0.0
     for p, (name, k, n) in enumerate(projs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for layer in range(L):
-                call(layer, p)
-        g.replay()
-        torch.cuda.synchronize()
-        tp = ev.time(lambda i: g.replay(), 5) / 5 / L
+        tp = ev.graph(lambda i: call(i % L, p), L, replays=5)
         b = gemm_bytes(M, n, k, fp8)
         tot_b += b * L
         tot_t += tp * L
@@ -745,46 +959,76 @@ def run_layers(args, torch, np, sp, W, ev, dev):
                           "tflops_dense_equiv": 2 * M * n * k / tp / 1e12,
                           "plan": {k2: v for k2, v in plans[p].items()
                                    if k2 in ("kernel", "config", "tile_n", "tile_m", "waves", "split_k")}}
-        del g
     sweep_bytes = sum(gemm_bytes(M, n, k, fp8) for _, k, n in projs) * L
+
+    dense = None
+    if not args.no_dense:
+        # the same products on dense MFMA over the decompressed pruned weights
+        wd = [[sp.decompress(wts[layer][p][0], wts[layer][p][1], projs[p][1]) for p in range(len(projs))]
+              for layer in range(L)]
+        dws = [torch.empty(max(16, sp.workspace_size(sp.OP_DENSE_GEMM, dt, M, n, k)), dtype=torch.uint8,
+                           device=dev) for _, k, n in projs]
+
+        def dcall(layer, p):
+            _, k, _ = projs[p]
+            sp.dense_gemm(xq[k], wd[layer][p], x_scale=sx[k], w_scale=wts[layer][p][2], out=ys[p], ws=dws[p])
+
+        def dsweep():
+            for layer in range(L):
+                for p in range(len(projs)):
+                    dcall(layer, p)
+        dt_sweep = ev.graph(lambda i: dsweep(), 1, replays=max(3, min(args.steps, 20)))
+        dense = {"sweep_ms": dt_sweep * 1e3, "sparse_speedup_vs_dense": dt_sweep / t,
+                 "GBs": sum(dense_bytes(M, n, k, fp8) for _, k, n in projs) * L / dt_sweep / 1e9}
+        for p, (name, k, n) in enumerate(projs):
+            tp = ev.graph(lambda i: dcall(i % L, p), L, replays=5)
+            per_proj[name]["dense_gemm_us"] = tp * 1e6
+            per_proj[name]["sparse_speedup_vs_dense"] = tp / (per_proj[name]["gemm_us"] / 1e6)
+        del wd, dws
     achieved = tot_b / tot_t / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_layer_baseline(W, fp8, gemm_bytes(M, 4096, 4096, fp8))
+    label = "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16"
+    return {"kind": kind, "M": M, "L": L, "projs": projs, "steps": steps, "warmup": warmup, "t": t,
+            "sweep_bytes": sweep_bytes, "per_proj": per_proj, "dense": dense, "cpu": cpu, "load_s": load_s,
+            "desc": "layer sweep: %d layers x QKV/O/gate+up/down, M=%d tokens, 2:4 sparse %s" % (L, M, label),
+            "flops": sum(2 * M * n * k for _, k, n in projs) * L,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "%s (sparse %s), all 128 calls" % (
+                             "/".join(sorted({KERNEL_NAMES[pl["kernel"]] for pl in plans})), kind),
+                         "per_unit": "values N*K/2*es + metadata N*K/8 + X M*K*es + Y 2*M*N bytes per launch"},
+            "device": torch.cuda.get_device_name(dev)}
+
+
+def layers_line(args, d):
     return {
         "metric": METRIC,
-        "value": sweep_bytes / t / 1e9, "unit": "GB/s",
-        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": t * 1e3,
+        "value": d["sweep_bytes"] / d["t"] / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": d["steps"], "warmup": d["warmup"], "ms_per_step": d["t"] * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "dtype": "fp8_e4m3" if d["kind"] == "fp8" else "bf16",
         "data": "synthetic (seeded; weights drawn on the GPU, inputs from workloads/)",
-        "config": {"workload": "layer sweep: %d layers x QKV/O/gate+up/down, M=%d tokens, 2:4 sparse %s"
-                               % (L, M, "FP8-E4M3 (per-tensor scales)" if fp8 else "BF16"),
-                   "M": M, "layers": L, "projections": [list(pr) for pr in projs],
+        "config": {"workload": d["desc"], "M": d["M"], "layers": d["L"], "projections": [list(pr) for pr in d["projs"]],
                    "step": "128 sequential sparse GEMMs (X quantised once)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "%s (sparse %s), all 128 calls" % (
-                         "/".join(sorted({KERNEL_NAMES[pl["kernel"]] for pl in plans})),
-                         "fp8" if fp8 else "bf16")},
-        "cpu_baseline": cpu,
-        "per_projection": per_proj,
-        "sweep_GB": sweep_bytes / 1e9,
-        "sweep_tflops_dense_equiv": sum(2 * M * n * k for _, k, n in projs) * L / t / 1e12,
-        "load_path": {"generate_prune_compress_quantise_s": load_s},
-        "device": torch.cuda.get_device_name(dev),
+        "roofline": d["roofline"], "cpu_baseline": d["cpu"], "per_projection": d["per_proj"],
+        "dense_sweep": d["dense"], "sweep_GB": d["sweep_bytes"] / 1e9,
+        "sweep_tflops_dense_equiv": d["flops"] / d["t"] / 1e12,
+        "load_path": {"generate_prune_compress_quantise_s": d["load_s"]}, "device": d["device"],
     }
+
+
+def config_summary_layers(d):
+    return {"workload": d["desc"], "sweep_ms": d["t"] * 1e3, "sweep_GBs": d["sweep_bytes"] / d["t"] / 1e9,
+            "roofline": d["roofline"], "dense_sweep": d["dense"], "cpu_baseline": d["cpu"],
+            "sweep_tflops_dense_equiv": d["flops"] / d["t"] / 1e12, "per_projection": d["per_proj"]}
 
 
 def cpu_layer_baseline(W, fp8, call_bytes):
     """The CPU oracle on one call of the sweep (layer 0's O projection, 256 x 4096 x 4096),
-    repeated for about 10 s."""
+    repeated for about 5 s."""
     from oracle import sp24_ref as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     wb = W.bf16_bits(W.layer_weight(0, 1))
     xb = W.bf16_bits(W.layer_x(4096))
     v, meta = O.prune_compress(wb)
@@ -799,9 +1043,9 @@ def cpu_layer_baseline(W, fp8, call_bytes):
             O.gemm_ref(*O.sparse_operands_bf16(xb, v, meta, 4096))
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 20:
+        if el > 5.0 or reps >= 20:
             break
-    return {"value": call_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(threads),
+    return {"value": call_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(blas_threads()),
             "kind": "oracle",
             "sample": "%d call(s) of layer 0's O projection (256 x 4096 x 4096: quantise X, "
                       "decompress W, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
@@ -809,16 +1053,10 @@ def cpu_layer_baseline(W, fp8, call_bytes):
 
 def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, kind, step_bytes):
     """The CPU oracle's per-call path on the same inputs: quantise X and the float64
-    product over the decompressed weight, one full step (all M) per repetition."""
-    import numpy as np
-
+    product over the decompressed weight, one full step (all M) per repetition, for
+    about 8 s."""
     import workloads as W
     from oracle import sp24_ref as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     wb = W.bf16_bits(w_cpu)
     v, meta = O.prune_compress(wb)            # load path, not timed
     if kind == "fp8":
@@ -831,17 +1069,17 @@ def cpu_baseline(w_cpu, xs_cpu, Ms, N, K, kind, step_bytes):
         for m in Ms:
             if kind == "fp8":
                 xq, sx = O.quant_fp8(xb[m])
-                ref, mag = O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, K))
+                O.gemm_ref(*O.sparse_operands_fp8(xq, sx, vq, meta, sw, K))
             elif kind == "int8":
                 xq, sx = O.quant_int8(xb[m])
-                ref, mag = O.gemm_ref(*O.sparse_operands_int8(xq, sx, vq, meta, sw, K))
+                O.gemm_ref(*O.sparse_operands_int8(xq, sx, vq, meta, sw, K))
             else:
-                ref, mag = O.gemm_ref(*O.sparse_operands_bf16(xb[m], v, meta, K))
+                O.gemm_ref(*O.sparse_operands_bf16(xb[m], v, meta, K))
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 20:
+        if el > 8.0 or reps >= 20:
             break
-    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(threads),
+    return {"value": step_bytes * reps / el / 1e9, "unit": "GB/s", "cores": int(blas_threads()),
             "kind": "oracle",
             "sample": "%d full step(s) of the same workload (quantise X, decompress W, float64 "
                       "product and magnitude sum for M=%s), %.1f s wall" % (

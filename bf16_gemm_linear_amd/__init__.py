@@ -145,6 +145,12 @@ def _need(t, name, dtype=None, ndim=None, device=None):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _need_scalar(t, name):
+    """A per-tensor scale: at least one fp32 value (the kernels read element 0)."""
+    if t.numel() < 1:
+        raise ValueError("%s must hold at least one value" % name)
+
+
 _FP8_T = torch.float8_e4m3fn
 _CODE_T = (torch.uint8, torch.float8_e4m3fn)
 _ANY_T = (torch.bfloat16, torch.int8) + _CODE_T
@@ -259,6 +265,7 @@ def quant_fp8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Ten
             raise ValueError("static mode needs a scale")
         scale = torch.empty(1, dtype=torch.float32, device=x.device)
     _need(scale, "scale", torch.float32, None, x.device)
+    _need_scalar(scale, "scale")
     nbytes = workspace_size(OP_QUANT, BF16, count, 1, 1) if mode == SCALE_DYNAMIC else 0
     ws = _workspace(nbytes, x.device, ws)
     _check("sp24_quant_fp8",
@@ -285,6 +292,7 @@ def quant_int8(x: torch.Tensor, scale: torch.Tensor | None = None, out: torch.Te
             raise ValueError("static mode needs a scale")
         scale = torch.empty(1, dtype=torch.float32, device=x.device)
     _need(scale, "scale", torch.float32, None, x.device)
+    _need_scalar(scale, "scale")
     nbytes = workspace_size(OP_QUANT, BF16, count, 1, 1) if mode == SCALE_DYNAMIC else 0
     ws = _workspace(nbytes, x.device, ws)
     _check("sp24_quant_int8",
@@ -311,6 +319,8 @@ def _gemm(sparse, x, w, meta, x_scale, w_scale, out, ws):
             raise ValueError("FP8 and INT8 operands need x_scale and w_scale")
         _need(x_scale, "x_scale", torch.float32, None, x.device)
         _need(w_scale, "w_scale", torch.float32, None, x.device)
+        _need_scalar(x_scale, "x_scale")
+        _need_scalar(w_scale, "w_scale")
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2, x.device)
@@ -444,6 +454,7 @@ def gemm_rows(x, values, meta, x_scales, w_scale, out=None, ws=None):
     if x_scales.numel() != m:
         raise ValueError("x_scales must hold %d values" % m)
     _need(w_scale, "w_scale", torch.float32, None, x.device)
+    _need_scalar(w_scale, "w_scale")
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2, x.device)
@@ -469,9 +480,11 @@ def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):
     _need(meta, "meta", torch.int32, 1, x.device)
     _meta_size(meta, n, k)
     _need(w_scale, "w_scale", torch.float32, None, x.device)
+    _need_scalar(w_scale, "w_scale")
     if x_scale is None:
         x_scale = torch.empty(1, dtype=torch.float32, device=x.device)
     _need(x_scale, "x_scale", torch.float32, None, x.device)
+    _need_scalar(x_scale, "x_scale")
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2, x.device)
@@ -494,9 +507,12 @@ def _rows_qx_args(x, values, meta, w_scale, kp, x_scales, out):
     _need(meta, "meta", torch.int32, 1, x.device)
     _meta_size(meta, n, kp)
     _need(w_scale, "w_scale", torch.float32, None, x.device)
+    _need_scalar(w_scale, "w_scale")
     if x_scales is None:
         x_scales = torch.empty(m, dtype=torch.float32, device=x.device)
     _need(x_scales, "x_scales", torch.float32, 1, x.device)
+    if x_scales.numel() != m:  # the kernels write one scale per row
+        raise ValueError("x_scales must hold %d values" % m)
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2, x.device)

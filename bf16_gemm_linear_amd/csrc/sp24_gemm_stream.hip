@@ -286,10 +286,11 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
   // QX: the X codes sit in an array of their own, so the compiler can tell its
   // reads from the LDS-DMA writes into the ring (it would otherwise wait for
-  // every load in flight before each step's reads); and the two take at least
-  // the LDS of the same configuration without QX, so that as many workgroups
-  // share a CU (the host sizes the grid for that occupancy).
-  constexpr int LDS_QX = C::RING_QX + kStreamQxBytes > C::LDS ? C::LDS - kStreamQxBytes : C::RING_QX;
+  // every load in flight before each step's reads).  The ring array holds the
+  // ring without X rows and the reduction of the KW partial tiles
+  // (stream_ring_bytes with qx); it is never smaller than that.
+  constexpr int LDS_QX = C::RING_QX;
+  static_assert(!QX || LDS_QX + kStreamQxBytes <= kLdsBytes, "quantising ring and X codes fit the LDS");
   __shared__ __attribute__((aligned(16))) uint8_t lds[QX ? LDS_QX : C::LDS];
   __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
   // per tensor: each wave's largest key; per token: each row's largest key
