@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
-    "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "quant_fp8_rows", "gemm_rows",
+    "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "gemm_qx_noalloc", "NOALLOC_SCRATCH_BYTES", "quant_fp8_rows", "gemm_rows",
     "slide_prune_pack", "slide_quant_fp8_rows", "slide_quant_int8_rows", "OP_GEMM_ROWS_QX", "gemm_rows_qx",
     "slide_gemm_qx",
     "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
@@ -73,6 +73,7 @@ _SIGS = {
     "sp24_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_dense_gemm": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_gemm_qx_noalloc": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "sp24_gemm_rows_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_slide_gemm_qx": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
@@ -495,6 +496,35 @@ def gemm_qx(x, values, meta, w_scale, x_scale=None, out=None, ws=None):
     _check("sp24_gemm_qx", lib.sp24_gemm_qx(m, n, k, _ptr(x), _ptr(x_scale), _ptr(values), _ptr(meta),
                                             _ptr(w_scale), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
     return out, x_scale
+
+
+def gemm_qx_noalloc(x, values, meta, w_scale, x_scale, out):
+    """gemm_qx with the library's own per-GPU scratch array instead of a workspace
+    (sp24_gemm_qx_noalloc): the call allocates nothing, so x_scale (fp32[1]) and out
+    ([m, n] bf16) must be given.  Bit-identical to gemm_qx.  Calls that may overlap on one
+    GPU race on the scratch array; calls on one stream are ordered and safe."""
+    _need(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    _need(values, "values", _CODE_T, 2, x.device)
+    n = values.shape[0]
+    if values.shape[1] * 2 != k:
+        raise ValueError("compressed weight shapes do not match k=%d" % k)
+    _need(meta, "meta", torch.int32, 1, x.device)
+    _meta_size(meta, n, k)
+    _need(w_scale, "w_scale", torch.float32, None, x.device)
+    _need_scalar(w_scale, "w_scale")
+    _need(x_scale, "x_scale", torch.float32, None, x.device)
+    _need_scalar(x_scale, "x_scale")
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    _check("sp24_gemm_qx_noalloc", lib.sp24_gemm_qx_noalloc(m, n, k, _ptr(x), _ptr(x_scale), _ptr(values),
+                                                            _ptr(meta), _ptr(w_scale), _ptr(out),
+                                                            _stream(x.device)))
+    return out, x_scale
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SP24_NOALLOC_SCRATCH_BYTES (include/sp24.h)
 
 
 def _rows_qx_args(x, values, meta, w_scale, kp, x_scales, out):

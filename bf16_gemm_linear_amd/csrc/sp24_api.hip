@@ -9,6 +9,9 @@
 // outside the table is never silently sent to a dense kernel: every accepted
 // shape runs the sparse kernels and every rejected one returns an error.
 #include <limits.h>
+
+#include <atomic>
+#include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -429,6 +432,100 @@ PaletteArgs palette_args(const sp24_palette_weight* pw) {
   return a;
 }
 
+// Scratch memory of sp24_gemm_qx_noalloc, for callers that cannot allocate:
+// one array per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is a stand-in, not a device
+// address): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kScratchBytes = SP24_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address (the first call on a device looks it up).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return SP24_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SP24_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SP24_OK;
+}
+
+// sp24_gemm_qx (the caller's workspace) and sp24_gemm_qx_noalloc (use_scratch:
+// this device's scratch array).  Every argument is checked before the first
+// HIP call; with use_scratch the first HIP call is the scratch lookup.
+int gemm_qx_common(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
+                   const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                   void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
+  if (!x_bf16 || !x_scale_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
+  sp24_plan p;
+  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  if (st != SP24_OK) return st;
+  if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
+    return SP24_ERR_ALIGN;
+  if (((uintptr_t)x_scale_dev & 3u) || ((uintptr_t)w_scale_dev & 3u)) return SP24_ERR_ALIGN;
+  const QxWorkspace wsp = qx_workspace(p, m, k, false);
+  if (use_scratch) {
+    if (wsp.total > kScratchBytes) return SP24_ERR_WORKSPACE;
+  } else if (wsp.total > 0) {
+    if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  }
+  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 2, wb = (size_t)n * (k / 2);
+  const size_t mb = (size_t)n * (k / 32) * 4;
+  const void* in[4] = {x_bf16, w_values, w_meta, w_scale_dev};
+  const size_t inb[4] = {xb, wb, mb, 4};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(y_bf16, yb, in[i], inb[i]) || overlaps(x_scale_dev, 4, in[i], inb[i]) ||
+        (!use_scratch && wsp.total > 0 && overlaps(ws, wsp.total, in[i], inb[i])))
+      return SP24_ERR_ALIAS;
+  if (overlaps(y_bf16, yb, x_scale_dev, 4) ||
+      (!use_scratch && wsp.total > 0 &&
+       (overlaps(ws, wsp.total, y_bf16, yb) || overlaps(ws, wsp.total, x_scale_dev, 4))))
+    return SP24_ERR_ALIAS;
+  if (use_scratch && wsp.total > 0) {
+    const int st2 = scratch_of_current_device(&ws);
+    if (st2 != SP24_OK) return st2;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  GemmArgs a;
+  a.dtype = SP24_FP8_E4M3;
+  a.sparse = true;
+  a.m = (int)m;
+  a.n = (int)n;
+  a.k = (int)k;
+  a.x_scale = x_scale_dev;
+  a.w = w_values;
+  a.meta = w_meta;
+  a.w_scale = w_scale_dev;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  a.partial = p.split_k > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
+  if (wsp.fused) {
+    a.x = nullptr;
+    a.x_bf16 = static_cast<const uint16_t*>(x_bf16);
+    a.x_scale_out = x_scale_dev;
+    return finish(launch_plan(a, p, s), s);
+  }
+  uint8_t* codes = wsb + wsp.gemm;
+  hipError_t e = launch_quant(SP24_FP8_E4M3, static_cast<const uint16_t*>(x_bf16), m * k, codes,
+                              x_scale_dev, SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
+  a.x = codes;
+  if (e == hipSuccess) e = launch_plan(a, p, s);
+  return finish(e, s);
+}
+
 }  // namespace
 
 }  // namespace sp24
@@ -691,56 +788,15 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
                  const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                  void* ws, size_t ws_bytes, void* stream) {
-  if (!x_bf16 || !x_scale_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
-  sp24_plan p;
-  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
-  if (st != SP24_OK) return st;
-  if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
-    return SP24_ERR_ALIGN;
-  if (((uintptr_t)x_scale_dev & 3u) || ((uintptr_t)w_scale_dev & 3u)) return SP24_ERR_ALIGN;
-  const QxWorkspace wsp = qx_workspace(p, m, k, false);
-  if (wsp.total > 0) {
-    if (ws == nullptr || ws_bytes < wsp.total) return SP24_ERR_WORKSPACE;
-    if (!aligned16(ws)) return SP24_ERR_ALIGN;
-  }
-  const size_t xb = (size_t)m * k * 2, yb = (size_t)m * n * 2, wb = (size_t)n * (k / 2);
-  const size_t mb = (size_t)n * (k / 32) * 4;
-  const void* in[4] = {x_bf16, w_values, w_meta, w_scale_dev};
-  const size_t inb[4] = {xb, wb, mb, 4};
-  for (int i = 0; i < 4; ++i)
-    if (overlaps(y_bf16, yb, in[i], inb[i]) || overlaps(x_scale_dev, 4, in[i], inb[i]) ||
-        (wsp.total > 0 && overlaps(ws, wsp.total, in[i], inb[i])))
-      return SP24_ERR_ALIAS;
-  if (overlaps(y_bf16, yb, x_scale_dev, 4) ||
-      (wsp.total > 0 && (overlaps(ws, wsp.total, y_bf16, yb) || overlaps(ws, wsp.total, x_scale_dev, 4))))
-    return SP24_ERR_ALIAS;
+  return gemm_qx_common(m, n, k, x_bf16, x_scale_dev, w_values, w_meta, w_scale_dev, y_bf16, ws, ws_bytes,
+                        false, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* wsb = static_cast<uint8_t*>(ws);
-  GemmArgs a;
-  a.dtype = SP24_FP8_E4M3;
-  a.sparse = true;
-  a.m = (int)m;
-  a.n = (int)n;
-  a.k = (int)k;
-  a.x_scale = x_scale_dev;
-  a.w = w_values;
-  a.meta = w_meta;
-  a.w_scale = w_scale_dev;
-  a.y = static_cast<uint16_t*>(y_bf16);
-  a.partial = p.split_k > 1 ? reinterpret_cast<float*>(wsb) : nullptr;
-  if (wsp.fused) {
-    a.x = nullptr;
-    a.x_bf16 = static_cast<const uint16_t*>(x_bf16);
-    a.x_scale_out = x_scale_dev;
-    return finish(launch_plan(a, p, s), s);
-  }
-  uint8_t* codes = wsb + wsp.gemm;
-  hipError_t e = launch_quant(SP24_FP8_E4M3, static_cast<const uint16_t*>(x_bf16), m * k, codes,
-                              x_scale_dev, SP24_SCALE_DYNAMIC, wsp.quant > 0 ? codes + wsp.codes : nullptr, s);
-  a.x = codes;
-  if (e == hipSuccess) e = launch_plan(a, p, s);
-  return finish(e, s);
+int sp24_gemm_qx_noalloc(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
+                         const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                         void* stream) {
+  return gemm_qx_common(m, n, k, x_bf16, x_scale_dev, w_values, w_meta, w_scale_dev, y_bf16, nullptr, 0, true,
+                        stream);
 }
 
 namespace {

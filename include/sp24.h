@@ -28,7 +28,9 @@
  * Conventions shared by every entry point
  *   - All tensors are dense, contiguous, row-major device buffers owned by the
  *     caller.  The library never allocates or frees device memory and keeps no
- *     mutable global state; calls are reentrant.
+ *     mutable global state; calls are reentrant.  The one exception is
+ *     sp24_gemm_qx_noalloc, whose scratch memory is a fixed array per GPU (see
+ *     there).
  *   - W is [n, k] (the nn.Linear weight layout), X is [m, k], Y is [m, n].
  *   - bf16 buffers hold IEEE bfloat16 bit patterns; FP8 buffers hold OCP
  *     E4M3FN byte codes (bias 7, max 448, NaN = 0x7F/0xFF, no infinities);
@@ -277,6 +279,33 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
                  const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the scratch array that sp24_gemm_qx_noalloc keeps on each GPU. */
+#define SP24_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* sp24_gemm_qx without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The result is bit for bit that of sp24_gemm_qx with
+ * the same arguments (the same kernels run).  The workspace sp24_gemm_qx would
+ * need (split-K partial sums, the E4M3 codes of X when they go through memory,
+ * the quantiser's partial maxima) lives instead in one static array of
+ * SP24_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
+ * from the first kernel launch until the process ends.  The call allocates and
+ * frees nothing, and nothing in the array has to start at zero: every byte a
+ * call reads there it wrote first.
+ *   Arguments, layouts, shape limits, alignment and errors as sp24_gemm_qx,
+ *   minus ws/ws_bytes.  SP24_ERR_WORKSPACE when sp24_workspace_size(
+ *   SP24_OP_GEMM_QX, SP24_FP8_E4M3, m, n, k) exceeds SP24_NOALLOC_SCRATCH_BYTES
+ *   (decode shapes fit; an 8192-token prefill does not).  The stream must belong
+ *   to the current device: the array used is the current device's.
+ *   The first call on a device looks the array's address up (a HIP runtime
+ *   query; make that first call outside graph capture) and keeps it.
+ *   Every call on one GPU shares that GPU's array: calls that may run at the
+ *   same time on one GPU (different streams, or threads without ordering) race
+ *   on it and give wrong results; calls ordered on one stream are safe. */
+int sp24_gemm_qx_noalloc(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
+                         const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
+                         void* stream);
 
 /* Per-token FP8 quantisation fused into the sparse GEMM (the step left of the
  * GEMM that the SlideSparse page fuses into its per-token quantisation, and

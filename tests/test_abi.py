@@ -314,6 +314,33 @@ def test_gemm_qx_validation():
     assert gemm_qx(ws=A + 0x500100) == EALIAS            # workspace over the output
 
 
+def gemm_qx_noalloc(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
+                    wsc=A + 0x400000, y=A + 0x500000):
+    return lib.sp24_gemm_qx_noalloc(m, n, k, p(x), p(xs), p(w), p(meta), p(wsc), p(y), None)
+
+
+def test_gemm_qx_noalloc_validation():
+    """The allocation-free variant checks its arguments as sp24_gemm_qx does, before any HIP
+    call, and rejects shapes whose workspace would exceed its per-GPU scratch array."""
+    for kw in ("x", "xs", "w", "meta", "wsc", "y"):
+        assert gemm_qx_noalloc(**{kw: None}) == ENULL, kw
+    assert gemm_qx_noalloc(m=0) == ESHAPE
+    assert gemm_qx_noalloc(k=96) == ESHAPE
+    assert gemm_qx_noalloc(x=A + 8) == EALIGN
+    assert gemm_qx_noalloc(xs=A + 0x100002) == EALIGN
+    assert gemm_qx_noalloc(xs=A + 0x100) == EALIAS
+    assert gemm_qx_noalloc(y=A + 0x200000) == EALIAS
+    ws_qx = lambda m, n, k: lib.sp24_workspace_size(sp.OP_GEMM_QX, sp.FP8, m, n, k)
+    assert sp.NOALLOC_SCRATCH_BYTES == 32 << 20
+    # decode shapes fit the scratch array; an 8192-token prefill does not and is refused
+    for m, n, k in ((1, 14336, 4096), (64, 14336, 4096), (64, 4096, 14336), (256, 28672, 4096)):
+        assert ws_qx(m, n, k) <= sp.NOALLOC_SCRATCH_BYTES, (m, n, k)
+    m, n, k = 8192, 28672, 8192
+    assert ws_qx(m, n, k) > sp.NOALLOC_SCRATCH_BYTES
+    assert gemm_qx_noalloc(m=m, n=n, k=k, x=A, xs=A + (1 << 28), w=A + (2 << 28), meta=A + (4 << 28),
+                           wsc=A + (6 << 28), y=A + (8 << 28)) == EWS
+
+
 def rows_qx(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
             wsc=A + 0x400000, y=A + 0x500000, ws=A + 0x600000, wsb=1 << 20, n_pat=None):
     if n_pat is None:
