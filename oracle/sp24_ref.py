@@ -380,6 +380,65 @@ def dequant_fp8_rows(codes: np.ndarray, scales) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Finer FP8 scales: one scale per group of consecutive values of a row.  The
+# research-roadmap page ("La Densite Dynamique et les Noyaux Non Structures",
+# quantisation under extreme sparsity) recommends per-channel or per-group
+# scales for outlier-heavy layers.  No page fixes the details; the readings:
+#   * a group is `group` consecutive values of one row; each group is quantised
+#     exactly as quant_fp8 would quantise it alone (s = fp32(amax / 448), 1 for
+#     an all-zero group; codes by IEEE float32 division and round to nearest
+#     even);
+#   * X [M, K] takes groups along K; the weight takes them along its compressed
+#     rows [N, K/2], group/2 kept values for a group of K values (the kept values
+#     of K positions [group*g, group*(g+1)) are compressed columns
+#     [group/2*g, group/2*(g+1)));
+#   * one group per row is per-token X and per-output-channel W;
+#   * the product is sum_k (s_x[m, k // group] dec(qx)) (s_w[n, k // group] dec(qw)),
+#     which the float64 reference below takes as written.
+# ----------------------------------------------------------------------------
+
+
+def fp8_group_scales(v_bits: np.ndarray, group: int) -> np.ndarray:
+    """Dynamic scales of each group of ``group`` consecutive values of every row of
+    ``v [R, C]``: ``fp32(amax / 448)`` per group, 1 for an all-zero group.
+    Returns float32 ``[R, C // group]``."""
+    v = np.asarray(v_bits, dtype=np.uint16)
+    rows, cols = v.shape
+    if group < 1 or cols % group:
+        raise ValueError("the row length must be a multiple of the group")
+    amax = np.max(np.abs(bf16_to_f32(v)).reshape(rows, cols // group, group), axis=2).astype(np.float32)
+    return np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
+
+
+def quant_fp8_groups(v_bits: np.ndarray, group: int):
+    """Quantise ``v [R, C]`` (bfloat16 bits) with one dynamic scale per group of
+    ``group`` consecutive values of a row: every group exactly as :func:`quant_fp8`
+    would quantise it alone.  Returns (codes uint8 ``[R, C]``, scales float32
+    ``[R, C // group]``)."""
+    v = np.asarray(v_bits, dtype=np.uint16)
+    scales = fp8_group_scales(v, group)
+    t = bf16_to_f32(v) / np.repeat(scales, group, axis=1)
+    assert t.dtype == np.float32
+    return e4m3_encode(t), scales
+
+
+def dequant_fp8_groups(codes: np.ndarray, scales, group: int) -> np.ndarray:
+    """float64 values ``scales[r, c // group] * decode(code[r, c])``."""
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return np.repeat(s, group, axis=1) * e4m3_decode(codes)
+
+
+def sparse_operands_fp8_groups(xq, x_scales, wq_values, meta, w_scales, k: int, group: int):
+    """Dense float64 operands of the FP8 path with group scales: X ``[M, K]`` codes with
+    ``x_scales [M, K // group]``; W compressed codes ``[N, K/2]`` with ``w_scales
+    [N, K // group]`` (each over group/2 kept values), decompressed to ``[N, K]``
+    (dropped positions are code 0, i.e. +0) and scaled by the group of their K position."""
+    x_hat = dequant_fp8_groups(xq, x_scales, group)
+    w_hat = dequant_fp8_groups(decompress(wq_values, meta, k), w_scales, group)
+    return x_hat, w_hat
+
+
+# ----------------------------------------------------------------------------
 # Reference product Y = X . W^T (float64) and its magnitude sum
 # ----------------------------------------------------------------------------
 
