@@ -25,7 +25,7 @@ __all__ = [
     "BF16", "FP8", "INT8", "SCALE_DYNAMIC", "SCALE_STATIC", "OP_GEMM", "OP_QUANT", "OP_DENSE_GEMM", "OP_GEMM_QX",
     "Sp24Error", "lib", "lib_path", "version", "gemm_qx", "gemm_qx_noalloc", "NOALLOC_SCRATCH_BYTES", "quant_fp8_rows", "gemm_rows",
     "slide_prune_pack", "slide_quant_fp8_rows", "slide_quant_int8_rows", "OP_GEMM_ROWS_QX", "gemm_rows_qx",
-    "slide_gemm_qx",
+    "slide_gemm_qx", "OP_GEMM_GROUPS", "quant_fp8_groups", "gemm_groups",
     "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
     "palette_encode", "palette_decode", "palette_gemm",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
@@ -36,6 +36,7 @@ BF16, FP8, INT8 = 0, 1, 2
 SCALE_DYNAMIC, SCALE_STATIC = 0, 1
 OP_GEMM, OP_QUANT, OP_DENSE_GEMM, OP_GEMM_QX, OP_PALETTE_ANALYZE, OP_PALETTE_GEMM = 0, 1, 2, 3, 4, 5
 OP_GEMM_ROWS_QX = 6
+OP_GEMM_GROUPS = 7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libsp24.so")
@@ -75,6 +76,8 @@ _SIGS = {
     "sp24_gemm_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_gemm_qx_noalloc": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "sp24_gemm_rows_qx": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "sp24_quant_fp8_groups": [_vp, _i64, _i64, _i64, _vp, _vp, _vp],
+    "sp24_gemm_groups": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_slide_gemm_qx": [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "sp24_quant_fp8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
     "sp24_quant_int8_rows": [_vp, _i64, _i64, _vp, _vp, _vp],
@@ -525,6 +528,62 @@ def gemm_qx_noalloc(x, values, meta, w_scale, x_scale, out):
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # SP24_NOALLOC_SCRATCH_BYTES (include/sp24.h)
+
+
+def quant_fp8_groups(x: torch.Tensor, group: int, out: torch.Tensor | None = None,
+                     scales: torch.Tensor | None = None):
+    """E4M3 codes of a bf16 [rows, cols] with one dynamic scale per group of `group`
+    consecutive values of a row -> (codes uint8 [rows, cols], scales fp32 [rows, cols/group]).
+    For X use the GEMM's group along k; for compressed weights [n, k/2] use group/2."""
+    _need(x, "x", torch.bfloat16, 2)
+    rows, cols = x.shape
+    if group < 8 or group % 8 or cols % group:
+        raise ValueError("group must be a multiple of 8 that divides the row length %d" % cols)
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    _need(out, "out", _CODE_T, 2, x.device)
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError("out must be [%d, %d]" % (rows, cols))
+    if scales is None:
+        scales = torch.empty(rows, cols // group, dtype=torch.float32, device=x.device)
+    _need(scales, "scales", torch.float32, None, x.device)
+    if scales.numel() != rows * (cols // group):
+        raise ValueError("scales must hold %d values" % (rows * (cols // group)))
+    _check("sp24_quant_fp8_groups", lib.sp24_quant_fp8_groups(_ptr(x), rows, cols, group, _ptr(out), _ptr(scales),
+                                                              _stream(x.device)))
+    return out, scales
+
+
+def gemm_groups(x, x_scales, values, meta, w_scales, group, out=None, ws=None):
+    """Y = X . W^T with E4M3 codes and one scale per group of `group` values of k: X [m, k]
+    with x_scales [m, k/group], compressed W codes [n, k/2] with w_scales [n, k/group]
+    (quantised in groups of group/2 compressed values); group == k is per-token X and
+    per-output-channel W.  bf16 output [m, n]."""
+    _need(x, "x", _CODE_T, 2)
+    m, k = x.shape
+    _need(values, "values", _CODE_T, 2, x.device)
+    n = values.shape[0]
+    if values.shape[1] * 2 != k:
+        raise ValueError("compressed weight shapes do not match k=%d" % k)
+    _need(meta, "meta", torch.int32, 1, x.device)
+    _meta_size(meta, n, k)
+    if group < 128 or group % 128 or k % group:
+        raise ValueError("group must be a multiple of 128 that divides k=%d" % k)
+    ng = k // group
+    _need(x_scales, "x_scales", torch.float32, None, x.device)
+    _need(w_scales, "w_scales", torch.float32, None, x.device)
+    if x_scales.numel() != m * ng or w_scales.numel() != n * ng:
+        raise ValueError("x_scales must hold %d values and w_scales %d" % (m * ng, n * ng))
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2, x.device)
+    if out.shape != (m, n):
+        raise ValueError("out must be [%d, %d]" % (m, n))
+    nbytes = workspace_size(OP_GEMM_GROUPS, FP8, m, n, k)
+    ws = _workspace(nbytes, x.device, ws)
+    _check("sp24_gemm_groups", lib.sp24_gemm_groups(m, n, k, group, _ptr(x), _ptr(x_scales), _ptr(values), _ptr(meta),
+                                                    _ptr(w_scales), _ptr(out), _ptr(ws), nbytes, _stream(x.device)))
+    return out
 
 
 def _rows_qx_args(x, values, meta, w_scale, kp, x_scales, out):

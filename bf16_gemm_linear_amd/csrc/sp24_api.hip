@@ -85,6 +85,7 @@ struct StreamShape {
 struct StreamChoice {
   int id;
   int64_t rows;
+  int split_k = 0;  // 0: automatic
 };
 
 StreamShape stream_shape(int id) {
@@ -147,8 +148,10 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 // every configuration on the decode shapes of a Llama-3-8B-sized layer on
 // MI355X:
 //  * m <= 16: X is negligible and W streams at the HBM rate; short row ranges
-//    want many waves along K (8 waves over 16 rows), ~30-64 rows per CU do
-//    best as two 8-wave workgroups per CU, longer ranges as 8 row blocks.
+//    want many waves along K (4 waves over 16 rows), ~30-64 rows per CU do
+//    best as two 8-wave workgroups per CU at m <= 8 and as one workgroup of 4
+//    row blocks x 32 tokens at 8 < m <= 16 (up-projection at m = 16: 8.65
+//    against 9.2 us), longer ranges as 8 row blocks.
 //    BF16 (twice the bytes per step, so the two-workgroup ring no longer fits
 //    twice in a CU's LDS) does best there with one workgroup of 4 x 16 rows
 //    per CU (up-projection, 14336 x 4096: 15.7 against 16.3 us at m = 1, 15.8
@@ -158,9 +161,11 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 //    workgroup (W read twice, the second time from cache), or, for long K, 64
 //    rows per workgroup with K split over 4 workgroups.
 //  * m <= 256: wide shapes (more than 64 rows per CU) keep all 256 tokens in
-//    one workgroup with 8 waves along m, so that W streams once; long-K
-//    few-row shapes take 64 rows per workgroup and split K; the rest take
-//    64-token blocks.
+//    one workgroup with 8 waves along m, so that W streams once (gate+up,
+//    28672 x 4096 at m = 256, FP8: 38.5 us against 40.6 us for the tiled
+//    kernel); long-K few-row shapes take 128 rows x 128 tokens per workgroup
+//    with K split in 4 (down-projection 4096 x 14336: 27.0 against 29.5 us
+//    for 64 rows x 256 tokens); the rest take 64-token blocks.
 StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
   const int64_t rows_cu = (n + 255) / 256;
   auto rows_for = [&](int64_t shares, int64_t lo, int64_t hi) {
@@ -168,10 +173,12 @@ StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
     return r < lo ? lo : (r > hi ? hi : r);
   };
   if (m <= 16) {
-    if (rows_cu <= 16) return StreamChoice{k >= 8192 ? 5 : 4, 0};
-    if (rows_cu <= 64)
-      return dtype == SP24_BF16 && rows_cu > 32 ? StreamChoice{13, 0}
-                                                : StreamChoice{15, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
+    if (rows_cu <= 16) return StreamChoice{4, 0};
+    if (rows_cu <= 64) {
+      if (dtype == SP24_BF16) return rows_cu > 32 ? StreamChoice{13, 0} : StreamChoice{15, rows_for(256, 16, 32)};
+      if (m > 8 && rows_cu > 32) return StreamChoice{10, rows_for(256, 16, 64)};
+      return StreamChoice{15, rows_for(rows_cu <= 32 ? 256 : 512, 16, 32)};
+    }
     return StreamChoice{9, 0};
   }
   if (m <= 32) {
@@ -188,7 +195,7 @@ StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
   if (m <= 256) {
     // 256 tokens per workgroup (8 waves along m): W is streamed once
     if (rows_cu > 64) return StreamChoice{22, 0};
-    if (rows_cu <= 16 && k >= 8192) return StreamChoice{24, 64};
+    if (rows_cu <= 16 && k >= 8192) return StreamChoice{25, 128, 4};
   }
   const int64_t gy = (m + 63) / 64;
   const int64_t shares = gy >= 256 ? 1 : 256 / gy;
@@ -211,11 +218,12 @@ Cfg skinny_cfg(int id) {
 // number of them (bf16 metadata steps come in pairs of words), at most 64 slices.
 // req >= 0: the split asked for through SP24_TILE (0: automatic); req < 0: the
 // automatic choice.  It takes the tiled kernel for m > 256 with at least 128 tiles,
-// and for 128 < m <= 256 (one tile of tokens) with at least 96 tiles, where it beats
-// the small-m kernels (measured at m = 256: gate+up 28672 x 4096, FP8 41 against
-// 43 us; BF16, whose 256-token stream configurations do not fit LDS, 65 us with K
-// split in two against 104 us).  Fewer tiles leave CUs idle and the small-m
-// kernels win (QKV, O, down of the same layer: 1.5-3x).
+// and for BF16 at 128 < m <= 256 (one tile of tokens) with at least 96 tiles, where
+// the 256-token stream configurations do not fit the LDS with two-byte operands
+// (gate+up 28672 x 4096 at m = 256: 65 us with K split in two against 104 us for
+// 64-token blocks).  One-byte codes keep the stream kernel there (FP8 gate+up: 38.5
+// us against 40.6 us for the tiled kernel).  Fewer tiles leave CUs idle and the
+// small-m kernels win (QKV, O, down of the same layer: 1.5-3x).
 int tiled_split(int dtype, bool sparse, int64_t m, int64_t n, int64_t k, int64_t tiles, int req) {
   (void)n;
   (void)sparse;
@@ -224,7 +232,7 @@ int tiled_split(int dtype, bool sparse, int64_t m, int64_t n, int64_t k, int64_t
   if (req > 0) return valid(req) ? (int)req : -1;
   if (req == 0) return 1;
   if (m > 256 && tiles >= 128) return 1;
-  if (m > 128 && m <= 256 && tiles >= 96) return dtype == SP24_BF16 && valid(2) ? 2 : 1;
+  if (m > 128 && m <= 256 && tiles >= 96 && dtype == SP24_BF16) return valid(2) ? 2 : 1;
   return 0;
 }
 
@@ -282,7 +290,7 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     // the choice for this shape, else (it does not fit this operand type, or K
     // does not split into its steps) the 64-token-block configurations
     const StreamChoice d = stream_default(dtype, m, n, k);
-    if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, 0, (int)d.rows, m, n, k, out)) return SP24_OK;
+    if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, d.split_k, (int)d.rows, m, n, k, out)) return SP24_OK;
     const int64_t gy = (m + 63) / 64, shares = gy >= 256 ? 1 : 256 / gy;
     const int g = (n + shares - 1) / shares > 64 ? 12 : 3;
     if (m > 64 && plan_stream(g, dtype, op == SP24_OP_GEMM, 0, 0, m, n, k, out)) return SP24_OK;
@@ -313,6 +321,36 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
 }
 
 namespace {
+
+// Plan of sp24_gemm_groups with group scales finer than one per row (group < k):
+// the sparse FP8 stream kernel with its table of group scales (stream_gs_fits),
+// sized for 128-K groups, so that one plan (and one workspace size) serves every
+// group: the default stream configuration of the shape when it is a stream plan
+// that fits, else the 64-token, 128-row configuration of one unit per step
+// (config 12, which takes any k % 128 == 0); K is split further while the scales
+// of a slice, (rows + tokens) * units * 4 bytes, exceed the table.
+int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
+  sp24_plan p;
+  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  if (st != SP24_OK) return st;
+  const int64_t units = k / 128;
+  auto fits = [&](int id) {
+    const StreamShape c = stream_shape(id);
+    return stream_gs_fits(c.rbw, c.rb, c.mw, c.kw, c.mb, c.u, c.smax);
+  };
+  const int ids[2] = {p.kernel == SP24_KERNEL_STREAM ? p.config - kStreamBase : -1, 12};
+  for (int id : ids) {
+    if (id < 0 || !fits(id)) continue;
+    const StreamShape c = stream_shape(id);
+    const int64_t ups = (int64_t)c.u * c.kw, table = 16 * (c.rbw * c.rb + c.mw * c.mb) * 4;
+    const int rows = id == ids[0] ? p.tile_n : 0;
+    int sk = id == ids[0] ? p.split_k : 1;
+    while (table * (units / sk) > kStreamGsBytes && units % (2 * sk * ups) == 0 && sk < 64) sk *= 2;
+    if (table * (units / sk) > kStreamGsBytes) continue;
+    if (plan_stream(id, SP24_FP8_E4M3, true, sk, rows, m, n, k, out)) return SP24_OK;
+  }
+  return SP24_ERR_SHAPE;
+}
 
 // X quantised inside the GEMM (sp24_gemm_qx, sp24_gemm_rows_qx,
 // sp24_slide_gemm_qx): the sparse FP8 stream kernel holds the codes of a
@@ -567,6 +605,14 @@ size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k) {
     return palette_analyze_ws_bytes(n);
   }
   if (op == SP24_OP_PALETTE_GEMM) return palette_gemm_ws(m, n, k).total;
+  if (op == SP24_OP_GEMM_GROUPS) {
+    // the larger of the two plans: one group per row (plan_gemm), finer groups (plan_groups)
+    sp24_plan a, b;
+    if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &a) != SP24_OK ||
+        plan_groups(m, n, k, &b) != SP24_OK)
+      return 0;
+    return a.workspace_bytes > b.workspace_bytes ? a.workspace_bytes : b.workspace_bytes;
+  }
   sp24_plan p;
   if (op == SP24_OP_GEMM_QX || op == SP24_OP_GEMM_ROWS_QX) {
     if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &p) != SP24_OK) return 0;
@@ -878,6 +924,78 @@ int sp24_slide_gemm_qx(int n_pat, int64_t m, int64_t n, int64_t k, const void* x
   const int64_t kp = k / (2 * n_pat) * 4 * (n_pat - 1);
   return rows_qx_common(n_pat, m, n, kp, k, x_bf16, x_scales_dev, w_values, w_meta, w_scale_dev, y_bf16, ws,
                         ws_bytes, stream);
+}
+
+int sp24_quant_fp8_groups(const void* x_bf16, int64_t rows, int64_t cols, int64_t group, uint8_t* q_out,
+                          float* scales_dev, void* stream) {
+  if (!x_bf16 || !q_out || !scales_dev) return SP24_ERR_NULL;
+  if (rows < 1 || cols < 8 || group < 8 || group % 8 != 0 || cols % group != 0 || rows > kMaxDim || cols > kMaxDim ||
+      rows * cols > ((int64_t)1 << 40))
+    return SP24_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(q_out) || ((uintptr_t)scales_dev & 3u)) return SP24_ERR_ALIGN;
+  const size_t xb = (size_t)rows * cols * 2, qb = (size_t)rows * cols, sb = (size_t)rows * (cols / group) * 4;
+  if (overlaps(q_out, qb, x_bf16, xb) || overlaps(scales_dev, sb, x_bf16, xb) || overlaps(scales_dev, sb, q_out, qb))
+    return SP24_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_quant_groups(static_cast<const uint16_t*>(x_bf16), rows, cols, group, q_out, scales_dev, s), s);
+}
+
+int sp24_gemm_groups(int64_t m, int64_t n, int64_t k, int64_t group, const void* x, const float* x_scales_dev,
+                     const void* w_values, const uint32_t* w_meta, const float* w_scales_dev, void* y_bf16, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!x || !x_scales_dev || !w_values || !w_meta || !w_scales_dev || !y_bf16) return SP24_ERR_NULL;
+  if (group < 128 || group % 128 != 0 || k % group != 0) return SP24_ERR_SHAPE;
+  const bool per_row = group == k;  // per-token X and per-output-channel W scales
+  sp24_plan p;
+  int st = per_row ? plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p) : plan_groups(m, n, k, &p);
+  if (st != SP24_OK) return st;
+  const int64_t ng = k / group, gu = group / 128;
+  if (!per_row) {  // K slices must hold whole groups (a finer plan than the 128-K one splits less)
+    while (p.split_k > 1 && (k / 128 / p.split_k) % gu != 0) {
+      p.split_k /= 2;
+      p.grid_z = p.split_k;
+    }
+    if (p.split_k == 1) p.workspace_bytes = 0;
+  }
+  if (!aligned16(x) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16)) return SP24_ERR_ALIGN;
+  if (((uintptr_t)x_scales_dev & 3u) || ((uintptr_t)w_scales_dev & 3u)) return SP24_ERR_ALIGN;
+  const size_t need = p.split_k > 1 ? (size_t)p.split_k * m * n * 4 : 0;
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return SP24_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SP24_ERR_ALIGN;
+  }
+  const size_t xb = (size_t)m * k, yb = (size_t)m * n * 2, wb = (size_t)n * (k / 2), mb = (size_t)n * (k / 32) * 4;
+  const size_t xsb = (size_t)m * ng * 4, wsb = (size_t)n * ng * 4;
+  const void* in[6] = {x, w_values, w_meta, x_scales_dev, w_scales_dev, nullptr};
+  const size_t inb[6] = {xb, wb, mb, xsb, wsb, 0};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(y_bf16, yb, in[i], inb[i]) || (need > 0 && overlaps(ws, need, in[i], inb[i]))) return SP24_ERR_ALIAS;
+  if (need > 0 && overlaps(ws, need, y_bf16, yb)) return SP24_ERR_ALIAS;
+
+  GemmArgs a;
+  a.dtype = SP24_FP8_E4M3;
+  a.sparse = true;
+  a.m = (int)m;
+  a.n = (int)n;
+  a.k = (int)k;
+  a.x = x;
+  a.w = w_values;
+  a.meta = w_meta;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  a.partial = p.split_k > 1 ? static_cast<float*>(ws) : nullptr;
+  if (per_row) {
+    a.x_scale = x_scales_dev;
+    a.x_scale_step = 1;
+    a.w_scale = w_scales_dev;
+    a.w_scale_step = 1;
+  } else {
+    a.x_gscale = x_scales_dev;
+    a.w_gscale = w_scales_dev;
+    a.group_units = (int)gu;
+    a.n_groups = (int)ng;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(launch_plan(a, p, s), s);
 }
 
 int sp24_palette_analyze(const void* w_bf16, int64_t n, int64_t k, uint8_t* palette_dev, int32_t* row_slot_dev,

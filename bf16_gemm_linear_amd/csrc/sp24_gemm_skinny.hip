@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
     const uint32_t* __restrict__ meta, const float* __restrict__ x_scale,
     const float* __restrict__ w_scale, uint16_t* __restrict__ y, float* __restrict__ partial,
-    int M, int N, int K, int xs_step) {
+    int M, int N, int K, int xs_step, int ws_step) {
   constexpr int TILE = RB * MB * 256;  // floats per wave tile
   __shared__ float red[NW * TILE];
 
@@ -275,8 +275,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
         partial[((size_t)blockIdx.z * M + m) * N + n] = s;
       else
       {
-        // FP8, INT8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
-        const float scale = DT != SP24_BF16 ? x_scale[(size_t)m * xs_step] * w_scale[0] : 1.0f;
+        // FP8, INT8: fp32(sx * sw) with the scales of X row m and W row n (one per
+        // tensor: step 0)
+        const float scale = DT != SP24_BF16 ? x_scale[(size_t)m * xs_step] * w_scale[(size_t)n * ws_step] : 1.0f;
         y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(s * scale);
       }
     }
@@ -290,10 +291,12 @@ hipError_t launch_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   const uint8_t* w = static_cast<const uint8_t*>(a.w);
   if (p.split_k > 1)
     hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, true>), grid, block, 0, s,
-                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step);
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step,
+                       a.w_scale_step);
   else
     hipLaunchKernelGGL((gemm_skinny_kernel<DT, SPARSE, RB, MB, NW, BATCH, false>), grid, block, 0, s,
-                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step);
+                       x, w, a.meta, a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, a.x_scale_step,
+                       a.w_scale_step);
   return hipGetLastError();
 }
 

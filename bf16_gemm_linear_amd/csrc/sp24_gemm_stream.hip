@@ -46,7 +46,10 @@ namespace {
 
 constexpr int kLdsBytes = kStreamLdsBytes;
 
-template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, int SMAX>
+// BUDGET: LDS bytes the ring may take (less than the LDS when the kernel keeps a
+// table of group scales beside it).
+template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, int SMAX,
+          int BUDGET = kStreamLdsBytes>
 struct StreamCfg {
   static constexpr int DT_ = DT, RBW_ = RBW, RB_ = RB, MW_ = MW, KW_ = KW, MB_ = MB, U_ = U;
   static constexpr bool SPARSE_ = SPARSE;
@@ -64,8 +67,11 @@ struct StreamCfg {
   static constexpr int PXU = XU / 16, PWU = WU / 16;      // ... per unit
   static constexpr int W_OFF = 0, M_OFF = BN * WB, X_OFF = M_OFF + BN * MWD * 4;
   static constexpr int STAGE = X_OFF + BM * XB;           // bytes per LDS buffer
-  static constexpr int STAGES = stream_stages(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX);
-  static constexpr bool FITS = stream_fits(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX);
+  static constexpr int STAGES = stream_stages(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, BUDGET);
+  static constexpr bool FITS = stream_fits(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, BUDGET);
+  // 16-byte operand pieces per lane per unit: A (per row block), B (per token block)
+  static constexpr int AP = SPARSE ? (B8 ? 1 : 2) : (B8 ? 2 : 4);
+  static constexpr int BP = B8 ? 2 : 4;
   // load instructions per step: 1 KB (dwordx4) for values and X, 256 B (dword) for metadata
   static constexpr int W_TOT = BN * WB / 1024, M_TOT = BN * MWD / 64, X_TOT = BM * XB / 1024;
   static constexpr int W_PER = (W_TOT + NW - 1) / NW, M_PER = (M_TOT + NW - 1) / NW,
@@ -75,11 +81,12 @@ struct StreamCfg {
   static constexpr int RED = KW > 1 ? KW * RBW * MW * RB * MB * 1024 : 0;  // epilogue LDS bytes
   static constexpr int LDS = STAGES * STAGE > RED ? STAGES * STAGE : RED;
   static_assert(STAGE == stream_stage_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U), "one stage formula");
-  static_assert(!FITS || (STAGES >= 2 && LDS <= kLdsBytes), "LDS budget");
+  static_assert(!FITS || (STAGES >= 2 && LDS <= kLdsBytes && STAGES * STAGE <= BUDGET), "LDS budget");
   static_assert(W_TOT * 1024 == BN * WB && X_TOT * 1024 == BM * XB && M_TOT * 64 == BN * MWD,
                 "whole load instructions");
   static_assert(!FITS || MIN_PER_STEP * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(LDS == stream_ring_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, false), "one LDS formula");
+  static_assert(LDS == stream_ring_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, false, BUDGET),
+                "one LDS formula");
   // X quantised by the kernel (QX): ring buffers without X rows, the X rows of
   // the workgroup's tokens and K slice after RING_QX
   static constexpr int STAGE_QX = X_OFF;
@@ -169,103 +176,156 @@ __device__ __forceinline__ i32x4 lds16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
 
+// 16-byte piece (within its 128-K unit) that B operand piece e of lane group q
+// takes from a token's row: sparse one-byte codes, run e: bytes [64e + 16q, +16);
+// sparse bf16, instruction h = e >> 1, run hb = e & 1: K 64hb + 32(q>>1) + 16h +
+// 8(q&1); dense one-byte codes: bytes [32q + 16e, +16); dense bf16: K [32e + 8q, +8).
+template <class C>
+__device__ __forceinline__ int b_piece(int e, int q) {
+  if constexpr (C::SPARSE_ && C::B8) return 4 * e + q;
+  else if constexpr (C::SPARSE_) return 8 * (e & 1) + 4 * (q >> 1) + 2 * (e >> 1) + (q & 1);
+  else if constexpr (C::B8) return 2 * q + e;
+  else return 4 * e + q;
+}
+
+// Operands of units kg*U .. kg*U + U - 1 of one step from LDS: A (W) and index
+// words for the RB row blocks of row group rg, from the step's ring buffer; B
+// (X) for the MB token blocks of token group mg, from X rows at xs + min(r,
+// xlast) * xstride (a ring buffer: xs = buf + X_OFF, xstride = XB; resident X:
+// the step's part of each row).
+template <class C>
+struct StreamOperands {
+  i32x4 a[C::U_][C::RB_][C::AP];
+  uint32_t ix[C::U_][C::RB_];
+  i32x4 b[C::U_][C::MB_][C::BP];
+
+  __device__ __forceinline__ void read(const uint8_t* __restrict__ buf, const uint8_t* __restrict__ xs,
+                                       int xstride, int xlast, int rg, int mg, int kg, int lane) {
+    constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
+    constexpr bool B8 = C::B8, SPARSE = C::SPARSE_;
+    const int q = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = kg * U + u;  // unit within the step
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int wrow = 16 * (RB * rg + rb) + r;
+        const uint8_t* wr = buf + C::W_OFF + wrow * C::WB;
+#pragma unroll
+        for (int e = 0; e < C::AP; ++e) {
+          int c;
+          if constexpr (SPARSE && B8) c = v * C::PWU + q;                  // K [32q, +32)
+          else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
+          else if constexpr (B8) c = v * C::PWU + 2 * q + e;               // K [32q, +32)
+          else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
+          a[u][rb][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
+        }
+        if constexpr (SPARSE)
+          ix[u][rb] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MWD * 4 +
+                                                         4 * swzm<C::MWD>(wrow, 4 * v + q));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int xrow = min(16 * (MB * mg + mb) + r, xlast);
+        const uint8_t* xr = xs + xrow * xstride;
+#pragma unroll
+        for (int e = 0; e < C::BP; ++e)
+          b[u][mb][e] = lds16(xr + 16 * swz16<C::PX>(xrow, v * C::PXU + b_piece<C>(e, q)));
+      }
+    }
+  }
+};
+
+// The matrix instruction(s) of unit u for row block rb and token block mb: c += W x X.
+template <class C>
+__device__ __forceinline__ void stream_mfma_one(f32x4& c, const StreamOperands<C>& o, int u, int rb, int mb) {
+  constexpr bool B8 = C::B8, I8 = C::I8, SPARSE = C::SPARSE_;
+  if constexpr (SPARSE && I8) {
+    c = __builtin_bit_cast(f32x4, __builtin_amdgcn_smfmac_i32_16x16x128_i8(
+                                      o.a[u][rb][0], cat8(o.b[u][mb][0], o.b[u][mb][1]),
+                                      __builtin_bit_cast(i32x4, c), (int)o.ix[u][rb], 0, 0));
+  } else if constexpr (SPARSE && B8) {
+    c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(o.a[u][rb][0], cat8(o.b[u][mb][0], o.b[u][mb][1]), c,
+                                                      (int)o.ix[u][rb], 0, 0);
+  } else if constexpr (SPARSE) {
+    c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+        __builtin_bit_cast(bf16x8, o.a[u][rb][0]), __builtin_bit_cast(bf16x16, cat8(o.b[u][mb][0], o.b[u][mb][1])),
+        c, (int)o.ix[u][rb], 0, 0);
+    c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+        __builtin_bit_cast(bf16x8, o.a[u][rb][1]), __builtin_bit_cast(bf16x16, cat8(o.b[u][mb][2], o.b[u][mb][3])),
+        c, (int)o.ix[u][rb], 0, 1);
+  } else if constexpr (I8) {
+    // dense INT8: two instructions of K=64 over the lane group's 32 bytes
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      c = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[u][rb][e], o.b[u][mb][e],
+                                                                          __builtin_bit_cast(i32x4, c), 0, 0, 0));
+  } else if constexpr (B8) {
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat8(o.a[u][rb][0], o.a[u][rb][1]),
+                                                         cat8(o.b[u][mb][0], o.b[u][mb][1]), c, 0, 0, 0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, o.a[u][rb][e]),
+                                                  __builtin_bit_cast(bf16x8, o.b[u][mb][e]), c, 0, 0, 0);
+  }
+}
+
 // Units kg*U .. kg*U + U - 1 of one step for the RB row blocks of row group
 // rg and the MB token blocks of token group mg.  All LDS reads of the step
 // are issued before its matrix instructions.
-// X rows of the step: row r at xs + min(r, xlast) * xstride (a ring buffer:
-// xs = buf + X_OFF, xstride = XB; resident X: the step's part of each row).
 template <class C>
 __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
                                            const uint8_t* __restrict__ xs, int xstride, int xlast,
                                            int rg, int mg, int kg, int lane) {
-  constexpr int MB = C::MB_, U = C::U_, RB = C::RB_;
-  constexpr bool B8 = C::B8, I8 = C::I8, SPARSE = C::SPARSE_;
+  StreamOperands<C> o;
+  o.read(buf, xs, xstride, xlast, rg, mg, kg, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < C::U_; ++u)
+#pragma unroll
+    for (int rb = 0; rb < C::RB_; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < C::MB_; ++mb) stream_mfma_one<C>(acc[rb][mb], o, u, rb, mb);
+}
+
+// The same with group scales (sparse FP8): each unit's products go to a fresh
+// partial tile, which is added to the accumulator times fp32(sx * sw) of its
+// group: sw of the lane's four W rows from tw ([group][row], rows of the
+// workgroup), sx of its token from tx ([group][token]).  `unit0` is the index of
+// the step's first unit within the workgroup's K slice.
+template <class C>
+__device__ __forceinline__ void stream_mma_gs(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
+                                              const uint8_t* __restrict__ xs, int xstride, int xlast, int rg,
+                                              int mg, int kg, int lane, const float* __restrict__ tw,
+                                              const float* __restrict__ tx, int unit0, int group_units) {
+  static_assert(C::SPARSE_ && C::DT_ == SP24_FP8_E4M3, "group scales: sparse FP8");
+  StreamOperands<C> o;
+  o.read(buf, xs, xstride, xlast, rg, mg, kg, lane);
   const int q = lane >> 4, r = lane & 15;
-  // A: sparse fp8 1 piece, sparse bf16 2, dense fp8 2, dense bf16 4 per unit
-  constexpr int AP = SPARSE ? (B8 ? 1 : 2) : (B8 ? 2 : 4);
-  // B: sparse fp8 2 pieces, sparse bf16 4, dense fp8 2, dense bf16 4 per unit and token block
-  constexpr int BP = B8 ? 2 : 4;
-  i32x4 a[U][RB][AP];
-  uint32_t ix[U][RB];
-  i32x4 b[U][MB][BP];
+  f32x4 sw[C::U_][C::RB_];
+  float sx[C::U_][C::MB_];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int v = kg * U + u;  // unit within the step
+  for (int u = 0; u < C::U_; ++u) {
+    const int g = (unit0 + kg * C::U_ + u) / group_units;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int wrow = 16 * (RB * rg + rb) + r;
-      const uint8_t* wr = buf + C::W_OFF + wrow * C::WB;
+    for (int rb = 0; rb < C::RB_; ++rb)
+      sw[u][rb] = *reinterpret_cast<const f32x4*>(tw + g * C::BN + 16 * (C::RB_ * rg + rb) + 4 * q);
 #pragma unroll
-      for (int e = 0; e < AP; ++e) {
-        int c;
-        if constexpr (SPARSE && B8) c = v * C::PWU + q;                  // K [32q, +32)
-        else if constexpr (SPARSE) c = v * C::PWU + 2 * q + e;           // e-th 16 K of [32q, +32)
-        else if constexpr (B8) c = v * C::PWU + 2 * q + e;               // K [32q, +32)
-        else c = v * C::PWU + 4 * e + q;                                 // K [32e + 8q, +8)
-        a[u][rb][e] = lds16(wr + 16 * swz16<C::PW>(wrow, c));
-      }
-      if constexpr (SPARSE)
-        ix[u][rb] = *reinterpret_cast<const uint32_t*>(buf + C::M_OFF + wrow * C::MWD * 4 +
-                                                       4 * swzm<C::MWD>(wrow, 4 * v + q));
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int xrow = min(16 * (MB * mg + mb) + r, xlast);
-      const uint8_t* xr = xs + xrow * xstride;
-#pragma unroll
-      for (int e = 0; e < BP; ++e) {
-        int c;
-        if constexpr (SPARSE && B8) c = v * C::PXU + 4 * e + q;  // run e: bytes [64e + 16q, +16)
-        else if constexpr (SPARSE) {
-          // instruction h = e >> 1, run hb = e & 1: K 64hb + 32(q>>1) + 16h + 8(q&1)
-          const int h = e >> 1, hb = e & 1;
-          c = v * C::PXU + 8 * hb + 4 * (q >> 1) + 2 * h + (q & 1);
-        } else if constexpr (B8) c = v * C::PXU + 2 * q + e;
-        else c = v * C::PXU + 4 * e + q;
-        b[u][mb][e] = lds16(xr + 16 * swz16<C::PX>(xrow, c));
-      }
-    }
+    for (int mb = 0; mb < C::MB_; ++mb) sx[u][mb] = tx[g * C::BM + 16 * (C::MB_ * mg + mb) + r];
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = 0; u < C::U_; ++u)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < C::RB_; ++rb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        f32x4& c = acc[rb][mb];
-        if constexpr (SPARSE && I8) {
-          c = __builtin_bit_cast(f32x4, __builtin_amdgcn_smfmac_i32_16x16x128_i8(
-                                            a[u][rb][0], cat8(b[u][mb][0], b[u][mb][1]),
-                                            __builtin_bit_cast(i32x4, c), (int)ix[u][rb], 0, 0));
-        } else if constexpr (SPARSE && B8) {
-          c = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[u][rb][0], cat8(b[u][mb][0], b[u][mb][1]), c,
-                                                            (int)ix[u][rb], 0, 0);
-        } else if constexpr (SPARSE) {
-          c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-              __builtin_bit_cast(bf16x8, a[u][rb][0]),
-              __builtin_bit_cast(bf16x16, cat8(b[u][mb][0], b[u][mb][1])), c, (int)ix[u][rb], 0, 0);
-          c = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-              __builtin_bit_cast(bf16x8, a[u][rb][1]),
-              __builtin_bit_cast(bf16x16, cat8(b[u][mb][2], b[u][mb][3])), c, (int)ix[u][rb], 0, 1);
-        } else if constexpr (I8) {
-          // dense INT8: two instructions of K=64 over the lane group's 32 bytes
+      for (int mb = 0; mb < C::MB_; ++mb) {
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+        stream_mfma_one<C>(t, o, u, rb, mb);
 #pragma unroll
-          for (int e = 0; e < 2; ++e)
-            c = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                                              a[u][rb][e], b[u][mb][e], __builtin_bit_cast(i32x4, c), 0, 0, 0));
-        } else if constexpr (B8) {
-          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              cat8(a[u][rb][0], a[u][rb][1]), cat8(b[u][mb][0], b[u][mb][1]), c, 0, 0, 0, 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][rb][e]),
-                                                        __builtin_bit_cast(bf16x8, b[u][mb][e]), c, 0, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) acc[rb][mb][i] += t[i] * (sx[u][mb] * sw[u][rb][i]);
       }
-    }
-  }
 }
 
 // QX: X is bf16 (xh) and quantised here, exactly as the quantisers do it (same
@@ -276,12 +336,21 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
 // sx_out[m].  X rows hold xk values; with lift = N (3..8) they are lifted to the
 // SlideSparse windows on the way into LDS (the GEMM's K is then K' = xk (2N-2)/N),
 // with lift = 0 they are taken as they are (xk = K).
-template <class C, bool PARTIAL, bool QX, bool QROWS = false>
+//
+// GS (group scales, sparse FP8, X codes given): X row m and W row n carry one
+// scale per group of group_units units of 128 K (x_gscale [M, n_groups],
+// w_gscale [N, n_groups]).  The scales of the workgroup's rows and tokens for its
+// K slice are loaded once into an LDS table beside the ring; every unit's
+// products are added to the accumulator times fp32(sx * sw) of its group, so the
+// epilogue applies no scale.  Otherwise W row n's scale is w_scale[n * ws_step].
+template <class C, bool PARTIAL, bool QX, bool QROWS = false, bool GS = false>
 __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice,
-    const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step, int xk, int lift) {
+    const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step, int xk, int lift, int ws_step,
+    const float* __restrict__ x_gscale, const float* __restrict__ w_gscale, int group_units, int n_groups) {
+  static_assert(!(GS && QX), "group scales take X codes");
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
   // QX: the X codes sit in an array of their own, so the compiler can tell its
@@ -295,6 +364,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
   // per tensor: each wave's largest key; per token: each row's largest key
   __shared__ uint32_t wave_max[QX ? (QROWS ? C::BM : C::NW) : 1];
+  // GS: the group scales of this workgroup's rows ([group][row]) and tokens ([group][token])
+  __shared__ __attribute__((aligned(16))) float gstab[GS ? kStreamGsBytes / 4 : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -453,6 +524,21 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     __syncthreads();  // the codes are in LDS for every wave
   }
 
+  if constexpr (GS) {
+    // the group scales of the K slice, before any ring load is in flight (the host
+    // keeps slices whole groups and the table within kStreamGsBytes)
+    const int gslice = units_per_slice / group_units, g0 = u0 / group_units;
+    for (int e = threadIdx.x; e < gslice * C::BN; e += C::NT) {
+      const int g = e / C::BN, row = e - g * C::BN;
+      gstab[e] = w_gscale[(size_t)min(n0 + row, n_end - 1) * n_groups + g0 + g];
+    }
+    float* tx = gstab + gslice * C::BN;
+    for (int e = threadIdx.x; e < gslice * C::BM; e += C::NT) {
+      const int g = e / C::BM, tok = e - g * C::BM;
+      tx[e] = x_gscale[(size_t)min(m0 + tok, M - 1) * n_groups + g0 + g];
+    }
+    __syncthreads();
+  }
   if constexpr (!QX) {
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
@@ -467,6 +553,9 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const uint8_t* buf = lds + (ks % STAGES) * STAGE;
     if constexpr (QX)
       stream_mma<C>(acc, buf, xres + ks * C::XB, xrs, mrows - 1, rg, mg, kg, lane);
+    else if constexpr (GS)
+      stream_mma_gs<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane, gstab,
+                       gstab + (units_per_slice / group_units) * C::BN, ks * C::UPS, group_units);
     else
       stream_mma<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
   }
@@ -528,14 +617,18 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         }
       } else {
         uint16_t* yr = y + (size_t)m * N;
-        // FP8, INT8: fp32(sx * sw) with the scale of X row m (one per tensor: xs_step = 0)
-        float scale = 1.0f;
-        if constexpr (C::B8) {
-          if constexpr (QX && QROWS) scale = scale_from_key(wave_max[m - m0]) * w_scale[0];
-          else scale = (QX ? sx : x_scale[(size_t)m * xs_step]) * w_scale[0];
+        // FP8, INT8: fp32(sx * sw) with the scales of X row m and W row n + e (one per
+        // tensor: step 0); GS: the group scales are applied already
+        float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (C::B8 && !GS) {
+          float sxm;
+          if constexpr (QX && QROWS) sxm = scale_from_key(wave_max[m - m0]);
+          else sxm = QX ? sx : x_scale[(size_t)m * xs_step];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] = sxm * w_scale[(size_t)min(n + e, n_end - 1) * ws_step];
         }
-        const uint32_t lo = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[2] * scale) | (f32_to_bf16_rne(v[3] * scale) << 16);
+        const uint32_t lo = f32_to_bf16_rne(v[0] * sc[0]) | (f32_to_bf16_rne(v[1] * sc[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2] * sc[2]) | (f32_to_bf16_rne(v[3] * sc[3]) << 16);
         if (n + 3 < n_end && (N & 3) == 0) {
           *reinterpret_cast<u32x2*>(yr + n) = u32x2{lo, hi};
         } else {
@@ -573,11 +666,13 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
             if (p.split_k > 1)
               hipLaunchKernelGGL((gemm_stream_kernel<C, true, true, true>), grid, block, 0, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
-                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift);
+                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
             else
               hipLaunchKernelGGL((gemm_stream_kernel<C, false, true, true>), grid, block, 0, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
-                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift);
+                                 units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
           } else {
             return hipErrorInvalidConfiguration;
           }
@@ -586,12 +681,37 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
         } else if (p.split_k > 1) {
           hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0, a.k, 0);
+                             a.x_scale_out, 0, a.k, 0,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
         } else {
           hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0, a.k, 0);
+                             a.x_scale_out, 0, a.k, 0,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
         }
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidConfiguration;
+      }
+    }
+    if (a.group_units > 0) {
+      // group scales: the same configuration with its ring inside kStreamGsBudget
+      if constexpr (DT == SP24_FP8_E4M3 && SPARSE && stream_gs_fits(RBW, RB, MW, KW, MB, U, SMAX)) {
+        using CG = StreamCfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, kStreamGsBudget>;
+        const int64_t gslice = units_per_slice / a.group_units;
+        if (units_per_slice % a.group_units != 0 || gslice * (CG::BN + CG::BM) * 4 > kStreamGsBytes ||
+            a.x_gscale == nullptr || a.w_gscale == nullptr)
+          return hipErrorInvalidConfiguration;
+        if (p.split_k > 1)
+          hipLaunchKernelGGL((gemm_stream_kernel<CG, true, false, false, true>), grid, block, 0, s, x, w, a.meta,
+                             a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
+                             (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
+                             a.group_units, a.n_groups);
+        else
+          hipLaunchKernelGGL((gemm_stream_kernel<CG, false, false, false, true>), grid, block, 0, s, x, w, a.meta,
+                             a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
+                             (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
+                             a.group_units, a.n_groups);
         return hipGetLastError();
       } else {
         return hipErrorInvalidConfiguration;
@@ -600,11 +720,13 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
     if (p.split_k > 1)
       hipLaunchKernelGGL((gemm_stream_kernel<C, true, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
     else
       hipLaunchKernelGGL((gemm_stream_kernel<C, false, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
-                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0);
+                         (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0,
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
     return hipGetLastError();
   }
 }

@@ -372,7 +372,7 @@ template <int DT, bool SPARSE, bool PARTIAL>
 __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
-    int M, int N, int K, int xs_step, float* __restrict__ partial, int slice_steps) {
+    int M, int N, int K, int xs_step, int ws_step, float* __restrict__ partial, int slice_steps) {
   using L = TiledLayout<DT, SPARSE>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::LDS_BYTES];
 
@@ -507,20 +507,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int ml = wm * (BM / WGM) + 32 * j + c;
-      // FP8, INT8: fp32(sx * sw) with the scale of X row m0 + ml (one per tensor: xs_step = 0;
-      // rows past M are staged but never stored)
-      float scale = 1.0f;
-      if constexpr (DT != SP24_BF16) scale = x_scale[(size_t)min(m0 + ml, M - 1) * xs_step] * w_scale[0];
+      // FP8, INT8: fp32(sx * sw) with the scales of X row m0 + ml and W row n (one per
+      // tensor: step 0; rows past M or N are staged but never stored)
+      float sx = 1.0f;
+      if constexpr (DT != SP24_BF16) sx = x_scale[(size_t)min(m0 + ml, M - 1) * xs_step];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           // accumulator registers 4g..4g+3 hold columns nl .. nl+3 of row ml
           const int nl = wn * (BN / WGN) + 32 * i + 8 * g + 4 * q;
-          const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * g + 0] * scale) |
-                              (f32_to_bf16_rne(acc[i][j][4 * g + 1] * scale) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * g + 2] * scale) |
-                              (f32_to_bf16_rne(acc[i][j][4 * g + 3] * scale) << 16);
+          float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (DT != SP24_BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = sx * w_scale[(size_t)min(n0 + nl + e, N - 1) * ws_step];
+          }
+          const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * g + 0] * sc[0]) |
+                              (f32_to_bf16_rne(acc[i][j][4 * g + 1] * sc[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[i][j][4 * g + 2] * sc[2]) |
+                              (f32_to_bf16_rne(acc[i][j][4 * g + 3] * sc[3]) << 16);
           *reinterpret_cast<u32x2*>(lds + ml * YS + nl * 2) = u32x2{lo, hi};
         }
       }
@@ -556,11 +561,12 @@ hipError_t launch_tiled_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s)
   if (p.split_k > 1)
     hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, true>), dim3(p.grid_x, p.split_k), dim3(NT), 0, s,
                        static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
-                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.partial, a.k / L::KS / p.split_k);
+                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.w_scale_step, a.partial,
+                       a.k / L::KS / p.split_k);
   else
     hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, false>), dim3(p.grid_x), dim3(NT), 0, s,
                        static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
-                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, (float*)nullptr, 0);
+                       a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.w_scale_step, (float*)nullptr, 0);
   return hipGetLastError();
 }
 

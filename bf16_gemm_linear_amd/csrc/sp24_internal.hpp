@@ -41,6 +41,9 @@ hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k,
                              hipStream_t s);
 hipError_t launch_quant(int dtype, const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,
                         void* ws, hipStream_t s);
+// E4M3 codes with one scale per group of `group` values of a row ([rows, cols], cols % group == 0)
+hipError_t launch_quant_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t group, uint8_t* q,
+                               float* scales, hipStream_t s);
 
 // sp24_palette.hip: the encoded exponent-palette weight (device pointers)
 struct PaletteArgs {
@@ -89,6 +92,16 @@ struct GemmArgs {
   float* x_scale_out = nullptr;
   // FP8: the scale of X row m is x_scale[m * x_scale_step] (0: one per tensor, 1: one per row)
   int x_scale_step = 0;
+  // FP8: the scale of W row n is w_scale[n * w_scale_step] (0: one per tensor, 1: one per row)
+  int w_scale_step = 0;
+  // FP8 with scales per group of group_units units of 128 K (stream kernel only): X row m
+  // and W row n carry n_groups scales each, x_gscale[m * n_groups + g] and
+  // w_gscale[n * n_groups + g]; the kernel applies them to each unit's partial sums, so
+  // the epilogue and the split-K reduction apply none (x_scale and w_scale unused)
+  const float* x_gscale = nullptr;
+  const float* w_gscale = nullptr;
+  int group_units = 0;
+  int n_groups = 0;
   // with x_bf16: one scale per token (written to x_scale_out[m]) instead of one per
   // tensor, and X rows lifted to the SlideSparse windows of N = x_lift (0: none)
   bool x_rows = false;
@@ -168,27 +181,41 @@ constexpr int stream_stage_bytes(int dtype, bool sparse, int rbw, int rb, int mw
   const int wb = ups * (sparse ? 64 : 128) * esz, mwords = sparse ? ups * 4 : 0, xb = ups * 128 * esz;
   return 16 * rbw * rb * (wb + 4 * mwords) + 16 * mw * mb * xb;
 }
+// budget: LDS bytes the ring may take (less than the whole LDS when the kernel
+// keeps a table of group scales beside it).
 constexpr int stream_stages(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
-                            int smax) {
-  const int fit = kStreamLdsBytes / stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u);
+                            int smax, int budget = kStreamLdsBytes) {
+  const int fit = budget / stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u);
   return smax < fit ? smax : fit;
 }
 constexpr bool stream_fits(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
-                           int smax) {
-  return stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) >= 2;
+                           int smax, int budget = kStreamLdsBytes) {
+  return stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax, budget) >= 2;
 }
 // LDS bytes of a stream configuration below anything else: its ring or the
 // reduction of the KW partial tiles, whichever is larger.  With qx (X
 // quantised by the kernel itself and held in LDS) the ring buffers hold W and
 // metadata only; the X rows live after these bytes.
 constexpr int stream_ring_bytes(int dtype, bool sparse, int rbw, int rb, int mw, int kw, int mb, int u,
-                                int smax, bool qx) {
+                                int smax, bool qx, int budget = kStreamLdsBytes) {
   const int esz = dtype == SP24_BF16 ? 2 : 1;
   const int stage = stream_stage_bytes(dtype, sparse, rbw, rb, mw, kw, mb, u) -
                     (qx ? 16 * mw * mb * u * kw * 128 * esz : 0);
-  const int ring = stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax) * stage;
+  const int ring = stream_stages(dtype, sparse, rbw, rb, mw, kw, mb, u, smax, budget) * stage;
   const int red = kw > 1 ? kw * rbw * mw * rb * mb * 1024 : 0;
   return ring > red ? ring : red;
+}
+// Group scales (sp24_gemm_groups): the sparse FP8 stream kernel keeps the scales
+// of its rows and tokens for its whole K slice in an LDS table of kStreamGsBytes
+// beside its ring, as [group][row] and [group][token] fp32 arrays: (rows of the
+// configuration + tokens of the configuration) * groups of the slice * 4 bytes
+// must fit.  The ring then gets the rest of the LDS.
+constexpr int kStreamGsBytes = 32768;
+constexpr int kStreamGsBudget = kStreamLdsBytes - kStreamGsBytes;
+constexpr bool stream_gs_fits(int rbw, int rb, int mw, int kw, int mb, int u, int smax) {
+  return stream_fits(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, kStreamGsBudget) &&
+         stream_ring_bytes(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, false, kStreamGsBudget) <=
+             kStreamGsBudget;
 }
 // A stream configuration can quantise X itself (sparse FP8): its ring without X
 // rows, the kStreamQxBytes region and the per-wave (per tensor) or per-row (per

@@ -172,6 +172,54 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __
   }
 }
 
+// Per-group scales: each group of `group` consecutive values of a row of X [m, k]
+// (k % group == 0, group % 8 == 0) gets s = fp32(amax_group / 448) (1 for a zero
+// group) and its codes as the per-tensor quantiser would give the group alone --
+// the per-channel or per-group scales the research-roadmap page ("La Densite
+// Dynamique et les Noyaux Non Structures", quantisation under extreme sparsity)
+// recommends.  A segment of S lanes (S a power of two up to 64 that divides the
+// group's vector count, group / 8) takes one group: each lane V = group / 8 / S
+// vectors, the maximum over the segment by shuffles, then the cast.  Up to
+// kGroupRegVecs vectors per lane stay in registers between the two.
+constexpr int kGroupRegVecs = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_groups_kernel(const uint16_t* __restrict__ x, int64_t ngroups,
+                                                                int64_t group, int seg, uint8_t* __restrict__ q,
+                                                                float* __restrict__ scales) {
+  const int64_t vpg = group / 8;     // 8-value vectors per group
+  const int per = (int)(vpg / seg);  // vectors per lane
+  const int lseg = threadIdx.x % seg;
+  const int64_t segs = (int64_t)gridDim.x * (kThreads / seg);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  u32x2* qv = reinterpret_cast<u32x2*>(q);
+  for (int64_t g = (int64_t)blockIdx.x * (kThreads / seg) + threadIdx.x / seg; g < ngroups; g += segs) {
+    const int64_t base = g * vpg + lseg;  // vector j of this lane: base + j * seg
+    u32x4 v[kGroupRegVecs];
+    uint32_t mk = 0;
+    if (per <= kGroupRegVecs) {
+#pragma unroll
+      for (int j = 0; j < kGroupRegVecs; ++j)
+        if (j < per) {
+          v[j] = xv[base + (int64_t)j * seg];
+          mk = max(mk, key_max8(v[j]));
+        }
+    } else {
+      for (int j = 0; j < per; ++j) mk = max(mk, key_max8(xv[base + (int64_t)j * seg]));
+    }
+    for (int off = 1; off < seg; off <<= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
+    const float s = qscale<DT>(mk);
+    if (lseg == 0) scales[g] = s;
+    if (per <= kGroupRegVecs) {
+#pragma unroll
+      for (int j = 0; j < kGroupRegVecs; ++j)
+        if (j < per) qv[base + (int64_t)j * seg] = qcast8<DT>(v[j], s);
+    } else {
+      for (int j = 0; j < per; ++j) qv[base + (int64_t)j * seg] = qcast8<DT>(xv[base + (int64_t)j * seg], s);
+    }
+  }
+}
+
 int n_partials(int64_t count) {
   int64_t g = (count / 8 + kThreads * 4 - 1) / (kThreads * 4);  // >= 4 vectors per thread
   if (g > kMaxPartials) g = kMaxPartials;
@@ -230,6 +278,18 @@ hipError_t launch_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k,
                              hipStream_t s) {
   return dtype == SP24_INT8 ? launch_quant_rows_dt<SP24_INT8>(x, m, k, q, scales, s)
                             : launch_quant_rows_dt<SP24_FP8_E4M3>(x, m, k, q, scales, s);
+}
+
+hipError_t launch_quant_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t group, uint8_t* q,
+                               float* scales, hipStream_t s) {
+  const int64_t vpg = group / 8, ngroups = rows * (cols / group);
+  int seg = 1;
+  while (seg < 64 && vpg % (2 * seg) == 0) seg *= 2;  // segments never straddle a wave
+  int64_t blocks = (ngroups + kThreads / seg - 1) / (kThreads / seg);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quant_groups_kernel<SP24_FP8_E4M3>, dim3((int)blocks), dim3(kThreads), 0, s, x, ngroups, group,
+                     seg, q, scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant(int dtype, const uint16_t* x, int64_t count, uint8_t* q, float* scale, int mode,

@@ -1,6 +1,7 @@
 // Split-K reduction: y[m, n] = bf16_rne((sum over slices z in order of
 // partial[z, m, n]) * scale), scale = fp32(sx * sw) for FP8 and INT8 (sx per tensor or
-// per X row).  The fixed slice order makes the result bitwise
+// per X row, sw per tensor or per W row), 1 for BF16 and for partial sums that carry
+// their group scales already.  The fixed slice order makes the result bitwise
 // reproducible.
 #include "sp24_common.hpp"
 #include "sp24_internal.hpp"
@@ -12,10 +13,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             int splits, int64_t mn, int64_t n,
                                                             const float* __restrict__ x_scale,
                                                             const float* __restrict__ w_scale, int xs_step,
-                                                            uint16_t* __restrict__ y) {
-  // FP8, INT8: fp32(sx * sw), sx the scale of X row i / n (one per tensor: xs_step = 0)
+                                                            int ws_step, uint16_t* __restrict__ y) {
+  // FP8, INT8: fp32(sx * sw), sx the scale of X row i / n and sw that of W row i % n
+  // (one per tensor: step 0)
   const float s0 = x_scale != nullptr ? x_scale[0] * w_scale[0] : 1.0f;
-  auto scale_of = [&](int64_t i) { return xs_step == 0 ? s0 : x_scale[i / n] * w_scale[0]; };
+  auto scale_of = [&](int64_t i) {
+    if (x_scale == nullptr || (xs_step == 0 && ws_step == 0)) return s0;
+    return x_scale[(i / n) * xs_step] * w_scale[(i % n) * ws_step];
+  };
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t nvec = (mn % 4 == 0) ? mn / 4 : 0;  // 16-byte loads need every slice aligned
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
@@ -39,10 +44,11 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s) {
   int64_t blocks = (mn / 4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
-  const bool scaled = a.dtype != SP24_BF16;  // E4M3 and INT8 carry scales
+  // E4M3 and INT8 carry scales, unless the partial sums were scaled per group already
+  const bool scaled = a.dtype != SP24_BF16 && a.group_units == 0;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((int)blocks), dim3(256), 0, s, a.partial, split_k, mn,
                      (int64_t)a.n, scaled ? a.x_scale : nullptr, scaled ? a.w_scale : nullptr, a.x_scale_step,
-                     a.y);
+                     a.w_scale_step, a.y);
   return hipGetLastError();
 }
 

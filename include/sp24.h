@@ -99,7 +99,8 @@ typedef enum sp24_op {
   SP24_OP_GEMM_QX = 3,    /* sp24_gemm_qx (dtype SP24_FP8_E4M3) */
   SP24_OP_PALETTE_ANALYZE = 4, /* sp24_palette_analyze (n = rows, k; m and dtype ignored) */
   SP24_OP_PALETTE_GEMM = 5,    /* sp24_palette_gemm (dtype ignored) */
-  SP24_OP_GEMM_ROWS_QX = 6     /* sp24_gemm_rows_qx; sp24_slide_gemm_qx with k = K' (dtype SP24_FP8_E4M3) */
+  SP24_OP_GEMM_ROWS_QX = 6,    /* sp24_gemm_rows_qx; sp24_slide_gemm_qx with k = K' (dtype SP24_FP8_E4M3) */
+  SP24_OP_GEMM_GROUPS = 7      /* sp24_gemm_groups, any group (dtype SP24_FP8_E4M3) */
 } sp24_op;
 
 typedef enum sp24_kernel {
@@ -279,6 +280,50 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
 int sp24_gemm_qx(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x_scale_dev,
                  const void* w_values, const uint32_t* w_meta, const float* w_scale_dev, void* y_bf16,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Finer FP8 scales: per output channel of W and per group of K.  The research-
+ * roadmap page ("La Densite Dynamique et les Noyaux Non Structures ...",
+ * quantisation under extreme sparsity) recommends per-channel or per-group
+ * scales for outlier-heavy layers; this library's reading of them:
+ *   - a group is `group` consecutive values of one row, quantised exactly as
+ *     sp24_quant_fp8 would quantise those values alone (dynamic scale
+ *     fp32(amax / 448), 1 for an all-zero group);
+ *   - X [m, k] is quantised in groups along k; W in groups of its compressed
+ *     values [n, k/2], group/2 of them for a group of k (the kept values of k
+ *     positions [group*g, group*(g+1)) are compressed columns [group/2*g,
+ *     group/2*(g+1)));
+ *   - group == k is per-token X and per-output-channel W scales.
+ * ------------------------------------------------------------------------- */
+
+/* E4M3 codes of a bf16 [rows, cols] with one dynamic scale per group of `group`
+ * consecutive values of a row.
+ *   x_bf16 in : [rows, cols] bf16;  q_out out: [rows, cols] E4M3 codes;
+ *   scales_dev out: [rows, cols/group] fp32, scale of group g of row r at
+ *   scales_dev[r * (cols/group) + g].
+ *   group % 8 == 0, cols % group == 0.  No workspace, no host synchronisation. */
+int sp24_quant_fp8_groups(const void* x_bf16, int64_t rows, int64_t cols, int64_t group, uint8_t* q_out,
+                          float* scales_dev, void* stream);
+
+/* Y = X . W^T with FP8 codes carrying one scale per group of `group` values of k:
+ *   y[r, c] = bf16_rne( sum over groups g of P_g * fp32(x_scales[r, g] * w_scales[c, g]) ),
+ *   P_g the fp32 sum of the products of group g (k in [group*g, group*(g+1))).
+ *   x [m, k] E4M3 codes, x_scales_dev [m, k/group]; w_values [n, k/2] E4M3 codes of
+ *   the compressed weight quantised in groups of group/2 (sp24_quant_fp8_groups),
+ *   w_scales_dev [n, k/group]; w_meta as for sp24_gemm; y_bf16 [m, n].
+ *   group % 128 == 0 and k % group == 0.  group == k (per-token X, per-output-channel
+ *   W) runs the plan of sp24_gemm with the two scale vectors applied in the
+ *   epilogue; smaller groups run the small-m stream kernel at every m, which
+ *   keeps the scales of its rows, tokens and K slice in LDS and scales each 128-K
+ *   unit's partial product (the large-m kernel has no room for a second set of
+ *   accumulators, so prefill shapes with groups are slower than with one scale
+ *   per row).
+ * ws/ws_bytes: at least sp24_workspace_size(SP24_OP_GEMM_GROUPS, SP24_FP8_E4M3, m,
+ * n, k) (the same for every group).  Shape limits, alignment (scales: 4 bytes) and
+ * errors as sp24_gemm. */
+int sp24_gemm_groups(int64_t m, int64_t n, int64_t k, int64_t group, const void* x, const float* x_scales_dev,
+                     const void* w_values, const uint32_t* w_meta, const float* w_scales_dev, void* y_bf16,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of the scratch array that sp24_gemm_qx_noalloc keeps on each GPU. */
 #define SP24_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)

@@ -191,12 +191,14 @@ def test_plan_uses_tiled_kernel_for_prefill_only():
 
 def test_plan_decode_workgroups_per_cu_by_code_type():
     # m <= 16 with 33-64 rows per CU: one-byte codes take two 8-wave workgroups per CU (512
-    # ranges of 28 rows), BF16 -- whose ring for that layout fits a CU's LDS only once --
-    # one workgroup of 4 x 16 rows per CU (256 ranges of 56 rows)
-    for m in (1, 4, 16):
+    # ranges of 28 rows) up to m = 8 and one workgroup of 4 row blocks x 32 tokens above
+    # (256 ranges of 56 rows); BF16 -- whose ring for the two-workgroup layout fits a CU's
+    # LDS only once -- one workgroup of 4 x 16 rows per CU (256 ranges of 56 rows)
+    for m in (1, 4, 8, 16):
         for dt in (sp.FP8, sp.INT8):
             p = sp.plan(sp.OP_GEMM, dt, m, 14336, 4096)
-            assert (p["kernel"], p["tile_n"], p["grid_x"], p["waves"]) == (2, 28, 512, 8), (m, dt, p)
+            want = (2, 28, 512, 8) if m <= 8 else (2, 56, 256, 4)
+            assert (p["kernel"], p["tile_n"], p["grid_x"], p["waves"]) == want, (m, dt, p)
         p = sp.plan(sp.OP_GEMM, sp.BF16, m, 14336, 4096)
         assert (p["kernel"], p["tile_n"], p["grid_x"], p["config"]) == (2, 56, 256, 113), (m, p)
     # 17-32 rows per CU: one range per CU for every code type
@@ -205,12 +207,14 @@ def test_plan_decode_workgroups_per_cu_by_code_type():
 
 
 def test_plan_tiled_for_wide_layers_at_256_tokens():
-    # one tile of tokens and >= 96 tiles (gate+up of an 8B-class layer): the tiled kernel,
-    # BF16 with K split in two; narrower projections keep the small-m kernels
+    # one tile of tokens and >= 96 tiles (gate+up of an 8B-class layer): BF16 takes the
+    # tiled kernel with K split in two (its 256-token stream configurations do not fit
+    # LDS); one-byte codes keep all 256 tokens in one stream workgroup (W streamed once);
+    # narrower projections keep the small-m kernels
     for m in (200, 256):
         p8 = sp.plan(sp.OP_GEMM, sp.FP8, m, 28672, 4096)
         p16 = sp.plan(sp.OP_GEMM, sp.BF16, m, 28672, 4096)
-        assert p8["kernel"] == 1 and p8["split_k"] == 1 and p8["workspace_bytes"] == 0
+        assert p8["kernel"] == 2 and p8["config"] == 122 and p8["split_k"] == 1 and p8["workspace_bytes"] == 0
         assert p16["kernel"] == 1 and p16["split_k"] == 2 and p16["grid_y"] == 2
         assert p16["workspace_bytes"] == 2 * m * 28672 * 4
     for m, n, k in ((256, 6144, 4096), (256, 4096, 4096), (256, 4096, 14336), (128, 28672, 4096),
@@ -339,6 +343,36 @@ def test_gemm_qx_noalloc_validation():
     assert ws_qx(m, n, k) > sp.NOALLOC_SCRATCH_BYTES
     assert gemm_qx_noalloc(m=m, n=n, k=k, x=A, xs=A + (1 << 28), w=A + (2 << 28), meta=A + (4 << 28),
                            wsc=A + (6 << 28), y=A + (8 << 28)) == EWS
+
+
+def test_groups_validation():
+    """sp24_quant_fp8_groups and sp24_gemm_groups check their arguments before any HIP call."""
+    qg = lambda x=A, r=4, c=256, g=128, q=A + 0x100000, s=A + 0x200000: lib.sp24_quant_fp8_groups(
+        p(x), r, c, g, p(q), p(s), None)
+    assert qg(x=None) == ENULL and qg(s=None) == ENULL
+    assert qg(g=12) == ESHAPE and qg(c=200) == ESHAPE and qg(r=0) == ESHAPE and qg(g=0) == ESHAPE
+    assert qg(x=A + 8) == EALIGN and qg(s=A + 0x200002) == EALIGN
+    assert qg(s=A + 0x100) == EALIAS                       # the scales inside X
+    gg = lambda m=8, n=256, k=256, g=128, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000, \
+        ws_=A + 0x400000, y=A + 0x500000, ws=None, wsb=0: lib.sp24_gemm_groups(
+            m, n, k, g, p(x), p(xs), p(w), p(meta), p(ws_), p(y), p(ws), wsb, None)
+    for kw in ("x", "xs", "w", "meta", "ws_", "y"):
+        assert gg(**{kw: None}) == ENULL, kw
+    assert gg(g=64) == ESHAPE and gg(g=384) == ESHAPE and gg(k=96, g=96) == ESHAPE
+    assert gg(x=A + 8) == EALIGN and gg(xs=A + 0x100002) == EALIGN
+    assert gg(y=A + 0x200000) == EALIAS                     # output over the weights
+    assert gg(y=A + 0x100000) == EALIAS                     # output over the X scales
+    # a split-K plan without its workspace is refused
+    m, n, k = 64, 4096, 14336
+    need = lib.sp24_workspace_size(sp.OP_GEMM_GROUPS, sp.FP8, m, n, k)
+    assert need > 0
+    assert gg(m=m, n=n, k=k, x=A, xs=A + (1 << 24), w=A + (2 << 24), meta=A + (4 << 26), ws_=A + (5 << 26),
+              y=A + (6 << 26)) == EWS
+    assert lib.sp24_workspace_size(sp.OP_GEMM_GROUPS, sp.BF16, m, n, k) == 0
+    # the workspace covers the finer-group plan and the one-group (sp24_gemm) plan
+    for m, n, k in ((1, 14336, 4096), (64, 14336, 4096), (16, 4096, 14336), (8192, 28672, 8192)):
+        assert lib.sp24_workspace_size(sp.OP_GEMM_GROUPS, sp.FP8, m, n, k) >= \
+            lib.sp24_workspace_size(sp.OP_GEMM, sp.FP8, m, n, k)
 
 
 def rows_qx(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
