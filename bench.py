@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "up", "down", "prefill", "layers", "slide", "palette"])
+                    choices=["all", "up", "down", "prefill", "layers", "slide", "palette", "groups"])
     ap.add_argument("--dtype", default="fp8", choices=["fp8", "int8", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -218,6 +218,10 @@ def main():
     if args.workload == "palette":
         print(json.dumps(run_palette(*ctx)))
         return
+    if args.workload == "groups":
+        print(json.dumps({"metric": "FP8 sparse GEMM with group scales: time against per-tensor scales",
+                          "n_gpus": 1, "data": "synthetic (seeded, workloads/)", **run_groups(*ctx)}))
+        return
     if args.workload == "layers":
         print(json.dumps(layers_line(args, run_layers(*ctx))))
         return
@@ -239,6 +243,7 @@ def main():
     torch.cuda.empty_cache()
     lay = run_layers(*ctx)
     torch.cuda.empty_cache()
+    grp = run_groups(*ctx)
     out["config"]["workload"] = ("decode FFN up-projection, 2:4 sparse %s, M=1/16/64 tokens, K=4096, N=14336 "
                                  "(headline step); every configuration of the metric under configs"
                                  % up["label"])
@@ -247,6 +252,8 @@ def main():
         "down": config_summary_decode(down),
         "prefill": config_summary_prefill(pre),
         "layers": config_summary_layers(lay),
+        "groups": {"workload": "FP8 with one scale per 128-K group and per output channel (sp24_gemm_groups) "
+                               "against per-tensor scales, decode up/down M=1/16/64 and prefill", **grp},
     }
     out["bench_wall_s"] = time.perf_counter() - t_all
     print(json.dumps(out))
@@ -869,6 +876,79 @@ def cpu_palette_baseline(W):
                       "palette form, float64 product and magnitude sum), %.1f s wall" % (reps, el)}
 
 
+
+
+# --------------------------------------------------------------------------- group scales
+def run_groups(args, torch, np, sp, W, ev, dev):
+    """FP8 with finer scales (sp24_gemm_groups) against the per-tensor sparse GEMM of the
+    same shape: 128-K groups and one group per row (per-token X, per-output-channel W), at
+    the decode up- and down-projection (M = 1/16/64, weight copies rotated past the
+    last-level cache, HIP graphs) and at prefill (M=8192, K=8192, N=28672).  The codes and
+    scales come from sp24_quant_fp8_groups (X in groups along K, the compressed weight in
+    groups of group/2 kept values)."""
+    out = {}
+    cases = [("up", W.up_weight, W.up_x, W.UP), ("down", W.down_weight, W.down_x, W.DOWN)]
+    for name, wf, xf, spec in cases:
+        K, N = spec["K"], spec["N"]
+        w = wf().to(dev)
+        values, meta = sp.prune_compress(w)
+        del w
+        qv, sw = sp.quant_fp8(values)
+        forms = {g: sp.quant_fp8_groups(values, g // 2) for g in (128, K)}
+        del values
+        R = n_copies(qv.numel() + meta.numel() * 4)
+        metas = [meta] + [meta.clone() for _ in range(R - 1)]
+        qvs = [qv] + [qv.clone() for _ in range(R - 1)]
+        gq = {g: [f] + [(f[0].clone(), f[1].clone()) for _ in range(R - 1)] for g, f in forms.items()}
+        res = {}
+        for m in spec["Ms"]:
+            x = xf(m).to(dev)
+            xq, sx = sp.quant_fp8(x)
+            y = torch.empty(m, N, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM_GROUPS, sp.FP8, m, N, K)), dtype=torch.uint8,
+                             device=dev)
+            r = {"per_tensor_us": ev.graph(lambda i: sp.gemm(xq, qvs[i % R], metas[i % R], x_scale=sx, w_scale=sw,
+                                                             out=y, ws=ws), R * 8) * 1e6}
+            for g, label in ((128, "group128_us"), (K, "per_channel_us")):
+                gx, gs = sp.quant_fp8_groups(x, g)
+                r[label] = ev.graph(lambda i: sp.gemm_groups(gx, gs, gq[g][i % R][0], metas[i % R], gq[g][i % R][1], g,
+                                                             out=y, ws=ws), R * 8) * 1e6
+            gb = gemm_bytes(m, N, K, True)
+            r["group128_GBs"] = (gb + N * K // 128 * 4 + m * K // 128 * 4) / r["group128_us"] / 1e3
+            r["group128_over_per_tensor"] = r["group128_us"] / r["per_tensor_us"]
+            res[str(m)] = r
+        out[name] = res
+        del qvs, metas, gq, forms, qv, meta
+        torch.cuda.empty_cache()
+    # prefill: one call each, eager
+    M, K, N = W.PREFILL["M"], W.PREFILL["K"], W.PREFILL["N"]
+    w = W.prefill_weight().to(dev)
+    values, meta = sp.prune_compress(w)
+    del w
+    x = W.prefill_x().to(dev)
+    qv, sw = sp.quant_fp8(values)
+    xq, sx = sp.quant_fp8(x)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, sp.workspace_size(sp.OP_GEMM_GROUPS, sp.FP8, M, N, K)), dtype=torch.uint8, device=dev)
+    pre = {}
+    fn = lambda i: sp.gemm(xq, qv, meta, x_scale=sx, w_scale=sw, out=y, ws=ws)
+    fn(0)
+    torch.cuda.synchronize()
+    pre["per_tensor_ms"] = ev.time(fn, 5) / 5 * 1e3
+    for g, label in ((K, "per_channel_ms"), (128, "group128_ms")):
+        gw, gws = sp.quant_fp8_groups(values, g // 2)
+        gx, gxs = sp.quant_fp8_groups(x, g)
+        fn = lambda i: sp.gemm_groups(gx, gxs, gw, meta, gws, g, out=y, ws=ws)
+        fn(0)
+        torch.cuda.synchronize()
+        reps = 5 if g == K else 2
+        pre[label] = ev.time(fn, reps) / reps * 1e3
+        pre[label.replace("_ms", "_tflops_dense_equiv")] = 2.0 * M * N * K / (pre[label] / 1e3) / 1e12
+        del gw, gws, gx, gxs
+    out["prefill"] = pre
+    del qv, meta, values, x, xq, y, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 # --------------------------------------------------------------------------- layer sweep

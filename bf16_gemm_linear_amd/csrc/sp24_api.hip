@@ -326,9 +326,11 @@ namespace {
 // the sparse FP8 stream kernel with its table of group scales (stream_gs_fits),
 // sized for 128-K groups, so that one plan (and one workspace size) serves every
 // group: the default stream configuration of the shape when it is a stream plan
-// that fits, else the 64-token, 128-row configuration of one unit per step
-// (config 12, which takes any k % 128 == 0); K is split further while the scales
-// of a slice, (rows + tokens) * units * 4 bytes, exceed the table.
+// that fits and holds at most 8 tiles per wave (two sets of unscaled tiles are
+// kept besides the accumulators), else the 64-token, 128-row configuration of one
+// unit per step (config 12, which takes any k % 128 == 0); K is split further
+// while the scales of a slice, (rows + tokens) * units * 4 bytes, exceed the
+// table.
 int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
   sp24_plan p;
   int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
@@ -336,7 +338,7 @@ int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
   const int64_t units = k / 128;
   auto fits = [&](int id) {
     const StreamShape c = stream_shape(id);
-    return stream_gs_fits(c.rbw, c.rb, c.mw, c.kw, c.mb, c.u, c.smax);
+    return stream_gs_fits(c.rbw, c.rb, c.mw, c.kw, c.mb, c.u, c.smax) && c.u * c.rb * c.mb <= 8;
   };
   const int ids[2] = {p.kernel == SP24_KERNEL_STREAM ? p.config - kStreamBase : -1, 12};
   for (int id : ids) {

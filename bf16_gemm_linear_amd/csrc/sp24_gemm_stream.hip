@@ -289,19 +289,48 @@ __device__ __forceinline__ void stream_mma(f32x4 (&acc)[C::RB_][C::MB_], const u
       for (int mb = 0; mb < C::MB_; ++mb) stream_mfma_one<C>(acc[rb][mb], o, u, rb, mb);
 }
 
-// The same with group scales (sparse FP8): each unit's products go to a fresh
-// partial tile, which is added to the accumulator times fp32(sx * sw) of its
-// group: sw of the lane's four W rows from tw ([group][row], rows of the
-// workgroup), sx of its token from tx ([group][token]).  `unit0` is the index of
-// the step's first unit within the workgroup's K slice.
+// Group scales (sparse FP8): the products of every unit of a step go to fresh
+// tiles t; each tile is added to the accumulator times fp32(sx * sw) of its
+// unit's group (sw of the lane's four W rows from tw, [group][row] over the
+// workgroup's rows; sx of its token from tx, [group][token]).
 template <class C>
-__device__ __forceinline__ void stream_mma_gs(f32x4 (&acc)[C::RB_][C::MB_], const uint8_t* __restrict__ buf,
-                                              const uint8_t* __restrict__ xs, int xstride, int xlast, int rg,
-                                              int mg, int kg, int lane, const float* __restrict__ tw,
-                                              const float* __restrict__ tx, int unit0, int group_units) {
+struct GsTiles {
+  f32x4 t[C::U_][C::RB_][C::MB_];
+  f32x4 s[C::U_][C::RB_][C::MB_];  // the scale of each element of t
+
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int u = 0; u < C::U_; ++u)
+#pragma unroll
+      for (int rb = 0; rb < C::RB_; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < C::MB_; ++mb) t[u][rb][mb] = s[u][rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // acc += t * s, unit by unit in order
+  __device__ __forceinline__ void fold(f32x4 (&acc)[C::RB_][C::MB_]) const {
+#pragma unroll
+    for (int u = 0; u < C::U_; ++u)
+#pragma unroll
+      for (int rb = 0; rb < C::RB_; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < C::MB_; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][mb][i] += t[u][rb][mb][i] * s[u][rb][mb][i];
+  }
+};
+
+// One step with group scales: the step's products into `cur` (with their scales),
+// then the previous step's tiles `prev` folded into the accumulator while the
+// matrix instructions run.  `unit0` is the step's first unit within the K slice.
+template <class C>
+__device__ __forceinline__ void stream_gs_step(GsTiles<C>& cur, const GsTiles<C>& prev, f32x4 (&acc)[C::RB_][C::MB_],
+                                               const uint8_t* __restrict__ buf, int rg, int mg, int kg, int lane,
+                                               const float* __restrict__ tw, const float* __restrict__ tx, int unit0,
+                                               int group_units) {
   static_assert(C::SPARSE_ && C::DT_ == SP24_FP8_E4M3, "group scales: sparse FP8");
   StreamOperands<C> o;
-  o.read(buf, xs, xstride, xlast, rg, mg, kg, lane);
+  o.read(buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
   const int q = lane >> 4, r = lane & 15;
   f32x4 sw[C::U_][C::RB_];
   float sx[C::U_][C::MB_];
@@ -321,11 +350,18 @@ __device__ __forceinline__ void stream_mma_gs(f32x4 (&acc)[C::RB_][C::MB_], cons
     for (int rb = 0; rb < C::RB_; ++rb)
 #pragma unroll
       for (int mb = 0; mb < C::MB_; ++mb) {
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-        stream_mfma_one<C>(t, o, u, rb, mb);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][mb][i] += t[i] * (sx[u][mb] * sw[u][rb][i]);
+        cur.t[u][rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        stream_mfma_one<C>(cur.t[u][rb][mb], o, u, rb, mb);
       }
+  prev.fold(acc);
+#pragma unroll
+  for (int u = 0; u < C::U_; ++u)
+#pragma unroll
+    for (int rb = 0; rb < C::RB_; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < C::MB_; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur.s[u][rb][mb][i] = sx[u][mb] * sw[u][rb][i];
 }
 
 // QX: X is bf16 (xh) and quantised here, exactly as the quantisers do it (same
@@ -364,8 +400,9 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
   // per tensor: each wave's largest key; per token: each row's largest key
   __shared__ uint32_t wave_max[QX ? (QROWS ? C::BM : C::NW) : 1];
-  // GS: the group scales of this workgroup's rows ([group][row]) and tokens ([group][token])
-  __shared__ __attribute__((aligned(16))) float gstab[GS ? kStreamGsBytes / 4 : 4];
+  // GS: the group scales of this workgroup's rows ([group][row]) and tokens ([group][token]),
+  // in dynamic LDS sized by the host for the K slice (at most kStreamGsBytes)
+  extern __shared__ __attribute__((aligned(16))) float gstab[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -544,20 +581,44 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     for (int p = 0; p < STAGES - 1; ++p)
       if (p < nks) ld.issue(lds + p * STAGE, p);
   }
-  for (int ks = 0; ks < nks; ++ks) {
+  // The top of step ks: this wave's loads of the step have landed and every wave
+  // is done with the buffer the loads of step ks + STAGES - 1 go to; returns the
+  // step's buffer.
+  auto ring_step = [&](int ks) {
     wait_later<QX ? C::MIN_PER_STEP_QX : C::MIN_PER_STEP, STAGES - 2>(min(nks - 1 - ks, STAGES - 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // LDS reads stay after the barrier
     const int nxt = ks + STAGES - 1;
     if (nxt < nks) ld.issue(lds + (nxt % STAGES) * STAGE, nxt);
-    const uint8_t* buf = lds + (ks % STAGES) * STAGE;
-    if constexpr (QX)
-      stream_mma<C>(acc, buf, xres + ks * C::XB, xrs, mrows - 1, rg, mg, kg, lane);
-    else if constexpr (GS)
-      stream_mma_gs<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane, gstab,
-                       gstab + (units_per_slice / group_units) * C::BN, ks * C::UPS, group_units);
-    else
-      stream_mma<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
+    return static_cast<const uint8_t*>(lds + (ks % STAGES) * STAGE);
+  };
+  if constexpr (GS) {
+    // Each step's products go to fresh tiles, which are scaled and added one step
+    // later, so that the matrix instructions of step ks + 1 run while the vector
+    // unit folds step ks (two sets of tiles, the loop taken two steps at a time).
+    const float* tx = gstab + (units_per_slice / group_units) * C::BN;
+    GsTiles<C> t0, t1;
+    t1.clear();
+    int ks = 0;
+    for (; ks + 1 < nks; ks += 2) {
+      stream_gs_step<C>(t0, t1, acc, ring_step(ks), rg, mg, kg, lane, gstab, tx, ks * C::UPS, group_units);
+      stream_gs_step<C>(t1, t0, acc, ring_step(ks + 1), rg, mg, kg, lane, gstab, tx, (ks + 1) * C::UPS,
+                        group_units);
+    }
+    if (ks < nks) {
+      stream_gs_step<C>(t0, t1, acc, ring_step(ks), rg, mg, kg, lane, gstab, tx, ks * C::UPS, group_units);
+      t0.fold(acc);
+    } else {
+      t1.fold(acc);
+    }
+  } else {
+    for (int ks = 0; ks < nks; ++ks) {
+      const uint8_t* buf = ring_step(ks);
+      if constexpr (QX)
+        stream_mma<C>(acc, buf, xres + ks * C::XB, xrs, mrows - 1, rg, mg, kg, lane);
+      else
+        stream_mma<C>(acc, buf, buf + C::X_OFF, C::XB, C::BM - 1, rg, mg, kg, lane);
+    }
   }
 
   if constexpr (C::I8)
@@ -702,13 +763,14 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
         if (units_per_slice % a.group_units != 0 || gslice * (CG::BN + CG::BM) * 4 > kStreamGsBytes ||
             a.x_gscale == nullptr || a.w_gscale == nullptr)
           return hipErrorInvalidConfiguration;
+        const size_t tab = (size_t)gslice * (CG::BN + CG::BM) * 4;  // dynamic LDS: the scale table
         if (p.split_k > 1)
-          hipLaunchKernelGGL((gemm_stream_kernel<CG, true, false, false, true>), grid, block, 0, s, x, w, a.meta,
+          hipLaunchKernelGGL((gemm_stream_kernel<CG, true, false, false, true>), grid, block, tab, s, x, w, a.meta,
                              a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                              (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
                              a.group_units, a.n_groups);
         else
-          hipLaunchKernelGGL((gemm_stream_kernel<CG, false, false, false, true>), grid, block, 0, s, x, w, a.meta,
+          hipLaunchKernelGGL((gemm_stream_kernel<CG, false, false, false, true>), grid, block, tab, s, x, w, a.meta,
                              a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                              (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
                              a.group_units, a.n_groups);
