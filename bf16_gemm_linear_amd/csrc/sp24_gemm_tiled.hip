@@ -519,8 +519,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
           const int nl = wn * (BN / WGN) + 32 * i + 8 * g + 4 * q;
           float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
           if constexpr (DT != SP24_BF16) {
+            if (ws_step == 0) {  // one W scale per tensor: the common case, one product per row
+              sc[0] = sc[1] = sc[2] = sc[3] = sx * w_scale[0];
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sc[e] = sx * w_scale[(size_t)min(n0 + nl + e, N - 1) * ws_step];
+              for (int e = 0; e < 4; ++e) sc[e] = sx * w_scale[(size_t)min(n0 + nl + e, N - 1) * ws_step];
+            }
           }
           const uint32_t lo = f32_to_bf16_rne(acc[i][j][4 * g + 0] * sc[0]) |
                               (f32_to_bf16_rne(acc[i][j][4 * g + 1] * sc[1]) << 16);

@@ -6,7 +6,7 @@
         and each stream-kernel configuration spelled out
     python -m bf16_gemm_linear_amd.profile_summary traffic WORKLOAD FETCH_DIR WRITE_DIR COPY_FETCH_DIR \
             COPY_WRITE_DIR COPY_BYTES KERNEL_SUBSTRING [KERNEL_SUBSTRING ...]
-        HBM bytes per launch of the kernels whose names contain one of the substrings, from
+        HBM bytes per launch of the kernels whose names contain every one of the substrings, from
         a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what the counter reads for a
         copy of COPY_BYTES bytes (FETCH_SIZE and WRITE_SIZE are in KiB per dispatch), and
         the machine-readable traffic record bench.py reads (tied to the hash of the
@@ -59,10 +59,10 @@ def _rows(pattern, d):
 
 
 def short_name(name):
-    """Kernel name without the namespaces and the argument list."""
-    name = re.sub(r"\(.*\)$", "", name)
+    """Kernel name without the return type, the namespaces and the argument list."""
     name = name.replace("sp24::(anonymous namespace)::", "").replace("sp24::", "")
-    return name.strip()
+    name = re.sub(r"\([^()]*\)\s*$", "", name.strip())
+    return re.sub(r"^void\s+", "", name).strip()
 
 
 def describe_stream(name):
@@ -109,7 +109,7 @@ def trace(d):
             print("- `%s`: %s" % (k, describe_stream(k)))
 
 
-def _counter(d, counter, subs):
+def _counter(d, counter, subs, every=False):
     rows = _rows("*counter_collection.csv", d)
     per = {}
     for r in rows:
@@ -117,7 +117,7 @@ def _counter(d, counter, subs):
         if name != counter:
             continue
         k = short_name(r.get("Kernel_Name") or r["Kernel-Name"])
-        if subs and not any(s in k for s in subs):
+        if subs and not (all if every else any)(s in k for s in subs):
             continue
         disp = r.get("Dispatch_Id") or r.get("Dispatch-Id") or r.get("Correlation_Id")
         per.setdefault(k, {}).setdefault(disp, 0.0)
@@ -141,8 +141,8 @@ def traffic(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, 
     cw = _counter(cwrite_dir, "WRITE_SIZE", ["copy"])
     fscale = copy_kib / statistics.mean(next(iter(cf.values())))
     wscale = copy_kib / statistics.mean(next(iter(cw.values())))
-    f = _counter(fetch_dir, "FETCH_SIZE", subs)
-    w = _counter(write_dir, "WRITE_SIZE", subs)
+    f = _counter(fetch_dir, "FETCH_SIZE", subs, every=True)
+    w = _counter(write_dir, "WRITE_SIZE", subs, every=True)
     print("Copy of %d bytes: FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f." % (copy_bytes, fscale, wscale))
     print()
     print("| kernel | launches | fetched MB / launch | written MB / launch |")
