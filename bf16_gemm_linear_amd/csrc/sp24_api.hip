@@ -356,11 +356,18 @@ int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
 
 // X quantised inside the GEMM (sp24_gemm_qx, sp24_gemm_rows_qx,
 // sp24_slide_gemm_qx): the sparse FP8 stream kernel holds the codes of a
-// workgroup's tokens over its K slice in the kStreamQxBytes region after the
-// ring.  With one scale per tensor every workgroup also reads all of X for it,
-// so X must be small (M * K <= kQxMaxValues, 128 KB of bf16); with one scale
-// per token a workgroup reads only its own tokens.
+// workgroup's tokens over its K slice in dynamic LDS after its ring, as much as
+// the ring leaves (stream_qx_room).  With one scale per tensor every workgroup
+// also reads all of X for it, so X must be small (M * K <= kQxMaxValues, 128 KB
+// of bf16); with one scale per token a workgroup reads only its own tokens.
+// Every workgroup casts all of its tokens' K slice, so the cast (an IEEE
+// division per value) is repeated by every workgroup along n: it is fused only
+// while that is at most kQxMaxWgValues values per workgroup (one token over
+// K = 14336, four over K = 4096).  Measured on MI355X, the up-projection
+// 14336 x 4096 at m = 16 (65536 values per workgroup): 24.5 us fused against
+// 13.4 us for the one-launch quantiser followed by the GEMM.
 constexpr int64_t kQxMaxValues = 65536;
+constexpr int64_t kQxMaxWgValues = 16384;
 
 bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
   if (p.kernel != SP24_KERNEL_STREAM || (!rows && m * k > kQxMaxValues)) return false;
@@ -371,14 +378,15 @@ bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
   case ID:                                                                     \
     ups = (U) * (KW);                                                          \
     bm = 16 * (MW) * (MB);                                                     \
-    if (stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, rows)) room = kStreamQxBytes; \
+    if (stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, rows)) room = stream_qx_room(RBW, RB, MW, KW, MB, U, SMAX, rows); \
     break;
     SP24_STREAM_CONFIGS(SP24_QX_ROOM)
 #undef SP24_QX_ROOM
     default: return false;
   }
   const int64_t rows_wg = m < bm ? m : bm;
-  return room >= 0 && rows_wg * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
+  return room >= 0 && rows_wg * (k / p.split_k) <= kQxMaxWgValues &&
+         rows_wg * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
 }
 
 // Workspace of the quantising GEMMs: the GEMM's own, then (when X is not

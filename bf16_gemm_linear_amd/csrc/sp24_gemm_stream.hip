@@ -45,6 +45,17 @@ namespace sp24 {
 namespace {
 
 constexpr int kLdsBytes = kStreamLdsBytes;
+// Quantising kernels (QX): a workgroup holds up to this many values of X in
+// registers from the maximum to the cast (8-value vectors, spread over its
+// threads: 4 per thread with 512 threads, 8 with 256; one token over K = 14336),
+// so that X is read once; larger X is read twice, four loads at a time.  More
+// per thread would cost the two-workgroup configurations their occupancy
+// (128 VGPRs).
+constexpr int kQxRegValues = 16384;
+template <class C>
+constexpr int qx_reg_vecs() {
+  return kQxRegValues / 8 / C::NT > 0 ? kQxRegValues / 8 / C::NT : 1;
+}
 
 // BUDGET: LDS bytes the ring may take (less than the LDS when the kernel keeps a
 // table of group scales beside it).
@@ -389,20 +400,22 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   static_assert(!(GS && QX), "group scales take X codes");
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
-  // QX: the X codes sit in an array of their own, so the compiler can tell its
-  // reads from the LDS-DMA writes into the ring (it would otherwise wait for
+  // QX: the X codes sit in an array of their own (dynamic LDS, sized by the
+  // host: the workgroup's rows times the row stride), so the compiler can tell
+  // its reads from the LDS-DMA writes into the ring (it would otherwise wait for
   // every load in flight before each step's reads).  The ring array holds the
   // ring without X rows and the reduction of the KW partial tiles
   // (stream_ring_bytes with qx); it is never smaller than that.
   constexpr int LDS_QX = C::RING_QX;
-  static_assert(!QX || LDS_QX + kStreamQxBytes <= kLdsBytes, "quantising ring and X codes fit the LDS");
   __shared__ __attribute__((aligned(16))) uint8_t lds[QX ? LDS_QX : C::LDS];
-  __shared__ __attribute__((aligned(16))) uint8_t xcodes[QX ? kStreamQxBytes : 16];
   // per tensor: each wave's largest key; per token: each row's largest key
   __shared__ uint32_t wave_max[QX ? (QROWS ? C::BM : C::NW) : 1];
-  // GS: the group scales of this workgroup's rows ([group][row]) and tokens ([group][token]),
-  // in dynamic LDS sized by the host for the K slice (at most kStreamGsBytes)
-  extern __shared__ __attribute__((aligned(16))) float gstab[];
+  // dynamic LDS, sized by the host: QX, the X codes; GS, the group scales of this
+  // workgroup's rows ([group][row]) and tokens ([group][token]) for the K slice (at
+  // most kStreamGsBytes)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  float* const gstab = reinterpret_cast<float*>(dyn_lds);
+  uint8_t* const xcodes = dyn_lds;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   const StreamLoader<C, QX> ld(w, meta, x, n0, n_end - 1, m0, M, N, K, u0, wave, lane);
 
   // QX: take the scale from all of X and cast this workgroup's tokens over its
-  // K slice into LDS (an array of kStreamQxBytes), piece p of a step's part of
+  // K slice into LDS (the dynamic array), piece p of a step's part of
   // row r in slot swz16(r, p) as a ring buffer would hold it.
   // QX: the ring's first loads (W and metadata only) go out before the
   // prologue, so they travel while X is read.  The prologue's first barrier
@@ -458,7 +471,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const int nv = mrows * vpr;                // this workgroup's tokens only
     const u32x4* xv = reinterpret_cast<const u32x4*>(xh + (size_t)m0 * xk);
     uint32_t* row_key = wave_max;
-    constexpr int RV = 4;
+    constexpr int RV = qx_reg_vecs<C>();
     const bool in_regs = nv <= RV * C::NT;
     u32x4 xr[RV];
     if (in_regs) {
@@ -469,7 +482,15 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         if (i < nv) atomicMax(&row_key[i / vpr], key_max8(xr[r]));
       }
     } else {
-      for (int i = tid; i < nv; i += C::NT) atomicMax(&row_key[i / vpr], key_max8(xv[i]));
+      int i = tid;
+      for (; i + 3 * C::NT < nv; i += 4 * C::NT) {  // four loads in flight
+        const u32x4 a = xv[i], b = xv[i + C::NT], c = xv[i + 2 * C::NT], d = xv[i + 3 * C::NT];
+        atomicMax(&row_key[i / vpr], key_max8(a));
+        atomicMax(&row_key[(i + C::NT) / vpr], key_max8(b));
+        atomicMax(&row_key[(i + 2 * C::NT) / vpr], key_max8(c));
+        atomicMax(&row_key[(i + 3 * C::NT) / vpr], key_max8(d));
+      }
+      for (; i < nv; i += C::NT) atomicMax(&row_key[i / vpr], key_max8(xv[i]));
     }
     __syncthreads();
     if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.z == 0 && tid < mrows)
@@ -502,7 +523,15 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       for (int r = 0; r < RV; ++r)
         if (tid + r * C::NT < nv) cast_vec(tid + r * C::NT, xr[r]);
     } else {
-      for (int i = tid; i < nv; i += C::NT) cast_vec(i, xv[i]);
+      int i = tid;
+      for (; i + 3 * C::NT < nv; i += 4 * C::NT) {  // four loads in flight
+        const u32x4 a = xv[i], b = xv[i + C::NT], c = xv[i + 2 * C::NT], d = xv[i + 3 * C::NT];
+        cast_vec(i, a);
+        cast_vec(i + C::NT, b);
+        cast_vec(i + 2 * C::NT, c);
+        cast_vec(i + 3 * C::NT, d);
+      }
+      for (; i < nv; i += C::NT) cast_vec(i, xv[i]);
     }
     __syncthreads();  // the codes are in LDS for every wave
   } else if constexpr (QX) {
@@ -512,15 +541,15 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const int kslice = units_per_slice * 128;
     // small X (every decode token at once): each thread keeps its vectors in
     // registers from the maximum to the cast, one pass over global memory
-    constexpr int RV = 4;
+    constexpr int RV = qx_reg_vecs<C>();
     const bool in_regs = nvec <= (int64_t)RV * C::NT;
     u32x4 xr[RV];
     uint32_t mk = 0;
-    if (in_regs) {
+    if (in_regs) {  // nvec <= RV * NT: 32-bit indices
 #pragma unroll
       for (int r = 0; r < RV; ++r) {
-        const int64_t i = tid + (int64_t)r * C::NT;
-        xr[r] = i < nvec ? xv[i] : u32x4{0u, 0u, 0u, 0u};
+        const int i = tid + r * C::NT;
+        xr[r] = i < (int)nvec ? xv[i] : u32x4{0u, 0u, 0u, 0u};
         mk = max(mk, key_max8(xr[r]));
       }
     } else {
@@ -545,18 +574,32 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     if (in_regs) {
 #pragma unroll
       for (int r = 0; r < RV; ++r) {
-        const int64_t i = tid + (int64_t)r * C::NT;
-        if (i >= nvec) continue;
-        const int row = (int)(8 * i / K), kk = (int)(8 * i - (int64_t)row * K) - k0;
+        const int i = tid + r * C::NT;
+        if (i >= (int)nvec) continue;
+        const int row = 8 * i / K, kk = 8 * i - row * K - k0;
         if (row >= m0 && row < m0 + mrows && kk >= 0 && kk < kslice) put(row - m0, kk, cast8(xr[r], sx));
       }
     } else {
       const int vpr = kslice / 8;  // 8-value vectors per row of the slice
       const uint16_t* xs0 = xh + (size_t)m0 * K + k0;
-      for (int v = tid; v < mrows * vpr; v += C::NT) {
-        const int rr = v / vpr, kk = (v - rr * vpr) * 8;
-        put(rr, kk, cast8(*reinterpret_cast<const u32x4*>(xs0 + (size_t)rr * K + kk), sx));
+      auto src = [&](int v) {
+        const int rr = v / vpr;
+        return reinterpret_cast<const u32x4*>(xs0 + (size_t)rr * K + (v - rr * vpr) * 8);
+      };
+      auto put_vec = [&](int v, u32x4 d) {
+        const int rr = v / vpr;
+        put(rr, (v - rr * vpr) * 8, cast8(d, sx));
+      };
+      const int nv = mrows * vpr;
+      int v = tid;
+      for (; v + 3 * C::NT < nv; v += 4 * C::NT) {  // four loads in flight
+        const u32x4 a = *src(v), b = *src(v + C::NT), c = *src(v + 2 * C::NT), d = *src(v + 3 * C::NT);
+        put_vec(v, a);
+        put_vec(v + C::NT, b);
+        put_vec(v + 2 * C::NT, c);
+        put_vec(v + 3 * C::NT, d);
       }
+      for (; v < nv; v += C::NT) put_vec(v, *src(v));
     }
     __syncthreads();  // the codes are in LDS for every wave
   }
@@ -717,20 +760,22 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
     const uint8_t* w = static_cast<const uint8_t*>(a.w);
     if (a.x_bf16 != nullptr) {
       if constexpr (DT == SP24_FP8_E4M3 && SPARSE && stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, false)) {
-        // the X rows of a workgroup must fit the region after the ring
+        // the X rows of a workgroup (dynamic LDS) must fit what the ring leaves
         const int64_t rows = a.m < C::BM ? a.m : C::BM;
-        if (rows * stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB) > kStreamQxBytes)
+        const int64_t xbytes = rows * stream_qx_row_bytes((int64_t)units_per_slice * 128, C::XB);
+        if (xbytes > stream_qx_room(RBW, RB, MW, KW, MB, U, SMAX, a.x_rows != 0))
           return hipErrorInvalidConfiguration;
+        const size_t dyn = (size_t)xbytes;
         const int xk = a.x_lift ? a.k / (4 * (a.x_lift - 1)) * (2 * a.x_lift) : a.k;
         if (a.x_rows) {
           if constexpr (stream_qx_fits(RBW, RB, MW, KW, MB, U, SMAX, true)) {
             if (p.split_k > 1)
-              hipLaunchKernelGGL((gemm_stream_kernel<C, true, true, true>), grid, block, 0, s, x, w, a.meta,
+              hipLaunchKernelGGL((gemm_stream_kernel<C, true, true, true>), grid, block, dyn, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
                                  units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
                              a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
             else
-              hipLaunchKernelGGL((gemm_stream_kernel<C, false, true, true>), grid, block, 0, s, x, w, a.meta,
+              hipLaunchKernelGGL((gemm_stream_kernel<C, false, true, true>), grid, block, dyn, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
                                  units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
                              a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
@@ -740,12 +785,12 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
         } else if (a.x_lift != 0) {
           return hipErrorInvalidValue;  // lifting is per token only
         } else if (p.split_k > 1) {
-          hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+          hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, dyn, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
                              a.x_scale_out, 0, a.k, 0,
                              a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
         } else {
-          hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, 0, s, x, w, a.meta, a.x_scale,
+          hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, dyn, s, x, w, a.meta, a.x_scale,
                              a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
                              a.x_scale_out, 0, a.k, 0,
                              a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);

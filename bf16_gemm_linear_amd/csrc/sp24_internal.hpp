@@ -164,14 +164,17 @@ constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
   X(24, 1, 4, 8, 1, 2, 1, 3)         \
   X(25, 2, 4, 4, 1, 2, 1, 3)         \
   X(26, 1, 2, 8, 1, 2, 1, 4)         \
-  X(27, 1, 4, 4, 2, 4, 1, 2)
-constexpr int kStreamConfigs = 28;
+  X(27, 1, 4, 4, 2, 4, 1, 2)         \
+  X(28, 8, 1, 1, 1, 4, 1, 8)
+constexpr int kStreamConfigs = 29;
 constexpr int kStreamBase = 100;
 constexpr int kStreamLdsBytes = 160 * 1024;
-// A stream kernel that quantises X itself holds its tokens' X codes in a
-// region of kStreamQxBytes after its ring (M * K-slice bytes must fit: M = 1
-// decode), small enough to keep the configuration's occupancy.
-constexpr int kStreamQxBytes = 16384;
+// A stream kernel that quantises X itself holds its tokens' X codes for its K
+// slice in dynamic LDS after its ring, sized per launch (rows * row bytes), so
+// that a small region (M = 1) keeps the configuration's occupancy and a large
+// one (M = 16 over K = 4096: 66 KB) takes what the ring leaves.  A
+// configuration is a quantising one when at least kStreamQxMinBytes are left.
+constexpr int kStreamQxMinBytes = 16384;
 
 // Bytes of one LDS buffer of a stream configuration: W values and metadata of
 // 16 * rbw * rb rows plus 16 * mw * mb X rows, for u * kw units of 128 K.
@@ -217,14 +220,18 @@ constexpr bool stream_gs_fits(int rbw, int rb, int mw, int kw, int mb, int u, in
          stream_ring_bytes(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, false, kStreamGsBudget) <=
              kStreamGsBudget;
 }
-// A stream configuration can quantise X itself (sparse FP8): its ring without X
-// rows, the kStreamQxBytes region and the per-wave (per tensor) or per-row (per
-// token) maxima fit the LDS.
+// LDS bytes a quantising stream configuration (sparse FP8) leaves for its X
+// codes: the LDS less its ring without X rows, the per-wave (per tensor) or
+// per-row (per token) maxima and 256 bytes for the alignment of the static
+// arrays; a configuration can quantise X itself when that is at least
+// kStreamQxMinBytes.
+constexpr int stream_qx_room(int rbw, int rb, int mw, int kw, int mb, int u, int smax, bool rows) {
+  return kStreamLdsBytes - stream_ring_bytes(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, true) - 64 -
+         (rows ? 4 * 16 * mw * mb : 0) - 256;
+}
 constexpr bool stream_qx_fits(int rbw, int rb, int mw, int kw, int mb, int u, int smax, bool rows) {
   return stream_fits(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax) &&
-         stream_ring_bytes(SP24_FP8_E4M3, true, rbw, rb, mw, kw, mb, u, smax, true) + kStreamQxBytes + 64 +
-                 (rows ? 4 * 16 * mw * mb : 0) <=
-             kStreamLdsBytes;
+         stream_qx_room(rbw, rb, mw, kw, mb, u, smax, rows) >= kStreamQxMinBytes;
 }
 // Row stride of the X rows a quantising stream kernel holds in LDS: its K
 // slice, plus 128 bytes when that keeps 128-byte steps (one unit per step) on

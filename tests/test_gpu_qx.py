@@ -22,8 +22,10 @@ SHAPES = [(1, 14336, 4096, True), (1, 4096, 14336, True),
           (1, 1024, 16384, True),       # split-K over 4 slices
           (16, 40, 4096, True),         # split-K over 8 slices, 3 workgroups of rows
           (40, 4096, 512, True),        # two token groups of 32 rows (the second ragged)
-          (2, 512, 16384, True),        # split-K over 8 slices, two tokens
-          (16, 14336, 4096, False),     # 16 tokens over all of K: more codes than the kernel holds
+          (2, 512, 16384, True),        # split-K over 8 slices, two tokens; X read twice (4 waves)
+          (4, 14336, 4096, True),       # 4 tokens over all of K, X in registers
+          (16, 14336, 4096, False),     # 16 tokens over all of K: too many values to cast per workgroup
+          (4, 4096, 14336, False),
           (5, 300, 640, False),         # small-m kernel without LDS: two launches
           (64, 14336, 4096, False),     # X too large to quantise in every workgroup
           (16, 4096, 14336, False)]

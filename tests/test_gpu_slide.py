@@ -127,7 +127,8 @@ def test_slide_gemm_int8_matches_the_6_of_8_product(m, n, k):
 SLIDE_QX = [(1, 14336, 4096, 4, True), (2, 14336, 4096, 4, True), (1, 1024, 6144, 3, True),
             (3, 1000, 5120, 5, True), (1, 1024, 4096, 8, True), (2, 512, 16384, 4, True),
             (1, 40, 8192, 4, True), (4, 300, 2560, 5, True),
-            (16, 1024, 4096, 4, False), (3, 1000, 1536, 4, False), (1, 4096, 14336, 4, False)]
+            (16, 1024, 4096, 4, False), (3, 1000, 1536, 4, False), (1, 4096, 14336, 4, False),
+            (64, 2048, 4096, 4, False)]
 
 
 @pytest.mark.parametrize("m,n,k,n_pat,fused", SLIDE_QX)
