@@ -13,7 +13,11 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: large CPU work (full-size workloads)")
 
 
-@pytest.fixture(scope="session")
-def rng():
+@pytest.fixture
+def rng(request):
+    """A generator of its own for every test, seeded from the test's name, so that its
+    data do not depend on which tests ran before it (or on the worker under xdist)."""
+    import zlib
+
     import numpy as np
-    return np.random.default_rng(12345)
+    return np.random.default_rng(zlib.crc32(request.node.nodeid.encode()))
