@@ -61,8 +61,13 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t* 
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   uint32_t m = 0;
-  for (int64_t i = t0; i < nvec; i += stride) m = max(m, key_max8(*(xv + i)));
-  for (int64_t i = nvec * 8 + t0; i < count; i += stride) m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+  int64_t i = t0;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight
+    const u32x4 a = xv[i], b = xv[i + stride], c = xv[i + 2 * stride], d = xv[i + 3 * stride];
+    m = max(m, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+  }
+  for (; i < nvec; i += stride) m = max(m, key_max8(*(xv + i)));
+  for (int64_t j = nvec * 8 + t0; j < count; j += stride) m = max(m, (uint32_t)(x[j] & 0x7FFFu));
   m = block_max<kThreads>(m, sh);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
@@ -89,8 +94,16 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x2* qv = reinterpret_cast<u32x2*>(q);
-  for (int64_t i = t0; i < nvec; i += stride) qv[i] = qcast8<DT>(*(xv + i), s);
-  for (int64_t i = nvec * 8 + t0; i < count; i += stride) q[i] = qcast1<DT>(x[i], s);
+  int64_t i = t0;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {  // four loads in flight
+    const u32x4 a = xv[i], b = xv[i + stride], c = xv[i + 2 * stride], d = xv[i + 3 * stride];
+    qv[i] = qcast8<DT>(a, s);
+    qv[i + stride] = qcast8<DT>(b, s);
+    qv[i + 2 * stride] = qcast8<DT>(c, s);
+    qv[i + 3 * stride] = qcast8<DT>(d, s);
+  }
+  for (; i < nvec; i += stride) qv[i] = qcast8<DT>(*(xv + i), s);
+  for (int64_t j = nvec * 8 + t0; j < count; j += stride) q[j] = qcast1<DT>(x[j], s);
 }
 
 // Small tensors in one launch: workgroup b takes amax over the whole tensor,
@@ -108,6 +121,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
   if (dynamic) {
     uint32_t m = 0;
     int i = threadIdx.x;
+    for (; i + 7 * kFusedThreads < nvec; i += 8 * kFusedThreads) {  // eight loads in flight
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = xv[i + j * kFusedThreads];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = max(m, key_max8(v[j]));
+    }
     for (; i + 3 * kFusedThreads < nvec; i += 4 * kFusedThreads) {  // four loads in flight
       const u32x4 a = xv[i], b = xv[i + kFusedThreads], c = xv[i + 2 * kFusedThreads],
                   d = xv[i + 3 * kFusedThreads];
@@ -220,8 +240,10 @@ __global__ __launch_bounds__(kThreads) void quant_groups_kernel(const uint16_t* 
   }
 }
 
+// Workgroups of the maximum pass: one 8-value vector per thread up to
+// kMaxPartials workgroups (each thread's loads are all in flight at once)
 int n_partials(int64_t count) {
-  int64_t g = (count / 8 + kThreads * 4 - 1) / (kThreads * 4);  // >= 4 vectors per thread
+  int64_t g = (count / 8 + kThreads - 1) / kThreads;
   if (g > kMaxPartials) g = kMaxPartials;
   if (g < 1) g = 1;
   return (int)g;
@@ -254,7 +276,9 @@ hipError_t launch_quant_dt(const uint16_t* x, int64_t count, uint8_t* q, float* 
                        dynamic ? 1 : 0);
     return hipGetLastError();
   }
-  int64_t cast_blocks = (count / 8 + kThreads * 2 - 1) / (kThreads * 2);
+  // one vector per thread up to 2048 workgroups: the division of every value is the
+  // costly part, spread over as many CUs as there are vectors
+  int64_t cast_blocks = (count / 8 + kThreads - 1) / kThreads;
   if (cast_blocks > 256 * 8) cast_blocks = 256 * 8;
   if (cast_blocks < 1) cast_blocks = 1;
   if (!dynamic) {
