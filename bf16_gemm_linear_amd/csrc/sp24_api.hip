@@ -65,7 +65,7 @@ bool tile_override(int* cfg, int* sk, int* rows) {
   int a, b, r = 0;
   const int got = sscanf(v, "%d,%d,%d", &a, &b, &r);
   if (got < 2) return false;
-  const bool known = (a >= 0 && a < kSkinnyConfigs) || a == kTiledConfig ||
+  const bool known = (a >= 0 && a < kSkinnyConfigs) || a == kTiledConfig || a == kTiled128Config ||
                      (a >= kStreamBase && a < kStreamBase + kStreamConfigs);
   if (!known || b < 0 || b > 64 || r < 0) return false;
   *cfg = a;
@@ -224,6 +224,8 @@ Cfg skinny_cfg(int id) {
 // 64-token blocks).  One-byte codes keep the stream kernel there (FP8 gate+up: 38.5
 // us against 40.6 us for the tiled kernel).  Fewer tiles leave CUs idle and the
 // small-m kernels win (QKV, O, down of the same layer: 1.5-3x).
+constexpr int64_t kTiled128MinTiles = 192;
+
 int tiled_split(int dtype, bool sparse, int64_t m, int64_t n, int64_t k, int64_t tiles, int req) {
   (void)n;
   (void)sparse;
@@ -247,8 +249,15 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     return SP24_ERR_SHAPE;
   if (dtype == SP24_INT8 && k > kMaxKInt8) return SP24_ERR_SHAPE;
 
-  // Large m with enough 256 x 256 tiles to fill the chip: LDS-tiled kernel.
+  // Large m with enough 256 x 256 tiles to fill the chip: LDS-tiled kernel.  One
+  // tile of tokens (128 < m <= 256) over a wide layer with one-byte codes: the same
+  // kernel with 128-row tiles when those number at least kTiled128MinTiles (gate+up
+  // 28672 x 4096 at m = 256, FP8: 34.4 us for 224 tiles of 128 rows against 43.8 us
+  // for the stream kernel with all 256 tokens per workgroup and 40.6 us for 112
+  // tiles of 256 rows); narrower layers keep the stream kernel (QKV, O and down of
+  // the same layer: 22-33 us with 128-row tiles against 11.6-28 us).
   const int64_t tiles = ((n + 255) / 256) * ((m + 255) / 256);
+  const int64_t tiles128 = ((n + 127) / 128) * ((m + 255) / 256);
   int id, sk = 0;
   if (m <= 16) {
     id = n >= 8192 ? 5 : 1;
@@ -265,18 +274,26 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
     id = oid;
     sk = osk;
   }
-  const int tsk = tiled_split(dtype, op == SP24_OP_GEMM, m, n, k, tiles, forced && id == kTiledConfig ? sk : -1);
-  if ((!forced && tsk > 0) || (forced && id == kTiledConfig)) {
-    if (tiles > INT_MAX || tsk < 1) return SP24_ERR_SHAPE;
+  const bool one_byte = dtype != SP24_BF16;
+  const bool auto128 = !forced && one_byte && m > 128 && m <= 256 && tiles128 >= kTiled128MinTiles;
+  const bool use128 = auto128 || (forced && id == kTiled128Config);
+  if (use128 && !one_byte) return SP24_ERR_SHAPE;
+  const bool tiled_req = forced && (id == kTiledConfig || id == kTiled128Config);
+  const int tsk = auto128 ? 1
+                          : tiled_split(dtype, op == SP24_OP_GEMM, m, n, k, use128 ? tiles128 : tiles,
+                                        tiled_req ? sk : -1);
+  if ((!forced && tsk > 0) || tiled_req) {
+    const int64_t t = use128 ? tiles128 : tiles;
+    if (t > INT_MAX || tsk < 1) return SP24_ERR_SHAPE;
     out->kernel = SP24_KERNEL_TILED;
-    out->tile_n = 256;
+    out->tile_n = use128 ? 128 : 256;
     out->tile_m = 256;
     out->waves = 8;
     out->split_k = tsk;
-    out->grid_x = (int)tiles;
+    out->grid_x = (int)t;
     out->grid_y = tsk;
     out->grid_z = 1;
-    out->config = kTiledConfig;
+    out->config = use128 ? kTiled128Config : kTiledConfig;
     out->batch = 1;
     out->workspace_bytes = tsk > 1 ? (size_t)tsk * (size_t)m * (size_t)n * sizeof(float) : 0;
     return SP24_OK;
@@ -408,7 +425,8 @@ QxWorkspace qx_workspace(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
 }
 
 hipError_t launch_plan(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
-  hipError_t e = p.kernel == SP24_KERNEL_TILED    ? launch_gemm_tiled(a, p, s)
+  hipError_t e = p.kernel == SP24_KERNEL_TILED    ? (p.tile_n == 128 ? launch_gemm_tiled128(a, p, s)
+                                                                     : launch_gemm_tiled(a, p, s))
                  : p.kernel == SP24_KERNEL_STREAM ? launch_gemm_stream(a, p, s)
                                                   : launch_gemm_skinny(a, p, s);
   if (e == hipSuccess && p.split_k > 1) e = launch_splitk_reduce(a, p.split_k, s);

@@ -44,7 +44,15 @@
 namespace sp24 {
 namespace {
 
-constexpr int BN = 256, BM = 256;  // tile rows of W and of X
+// Tile rows of W and of X.  This file is also compiled with SP24_TILED_BN = 128
+// (sp24_gemm_tiled128.hip, one-byte codes only): 128 W rows x 256 tokens per
+// workgroup, so that a one-token-tile product of a wide layer (gate+up at m = 256:
+// 224 tiles) fills the chip.
+#ifndef SP24_TILED_BN
+#define SP24_TILED_BN 256
+#define SP24_TILED_LAUNCH launch_gemm_tiled
+#endif
+constexpr int BN = SP24_TILED_BN, BM = 256;
 constexpr int WGN = 2, WGM = 4;     // waves along n and along m
 constexpr int NWAVES = WGN * WGM, NT = NWAVES * 64;
 constexpr int TI = BN / WGN / 32;   // 32-row instruction tiles per wave along n
@@ -576,13 +584,18 @@ hipError_t launch_tiled_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
+hipError_t SP24_TILED_LAUNCH(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   if (a.dtype == SP24_FP8_E4M3)
     return a.sparse ? launch_tiled_dt<SP24_FP8_E4M3, true>(a, p, s)
                     : launch_tiled_dt<SP24_FP8_E4M3, false>(a, p, s);
   if (a.dtype == SP24_INT8)
     return a.sparse ? launch_tiled_dt<SP24_INT8, true>(a, p, s) : launch_tiled_dt<SP24_INT8, false>(a, p, s);
+#if SP24_TILED_BN == 256
   return a.sparse ? launch_tiled_dt<SP24_BF16, true>(a, p, s) : launch_tiled_dt<SP24_BF16, false>(a, p, s);
+#else
+  // bf16 metadata steps (two words per row) do not split over 8 waves at 128 rows
+  return hipErrorInvalidConfiguration;
+#endif
 }
 
 }  // namespace sp24

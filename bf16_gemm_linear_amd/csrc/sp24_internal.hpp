@@ -129,7 +129,8 @@ struct GemmArgs {
   X(16, 1, 2, 8, 1)            \
   X(17, 2, 4, 8, 1)
 constexpr int kSkinnyConfigs = 18;
-constexpr int kTiledConfig = 99;  // config id of the LDS-tiled large-m kernel
+constexpr int kTiledConfig = 99;     // config id of the LDS-tiled large-m kernel (256 x 256 tiles)
+constexpr int kTiled128Config = 98;  // the same kernel with 128 W rows x 256 tokens (one-byte codes)
 
 // Small-m LDS-ring kernel configurations (config id = kStreamBase + id):
 // X(id, waves along n, row blocks of 16 per wave, waves along m, waves along
@@ -243,6 +244,7 @@ constexpr int64_t stream_qx_row_bytes(int64_t k_slice, int step_bytes) {
 hipError_t launch_gemm_skinny(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_gemm_stream(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
+hipError_t launch_gemm_tiled128(const GemmArgs& a, const sp24_plan& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& a, int split_k, hipStream_t s);
 
 // host plan (sp24_plan.cpp logic lives in sp24_api.hip)

@@ -152,9 +152,11 @@ def test_plan_table_shapes():
         for op in (sp.OP_GEMM, sp.OP_DENSE_GEMM):
             for m, n, k in shapes:
                 pl = sp.plan(op, dt, m, n, k)
-                if pl["kernel"] == 1:   # LDS-tiled: one workgroup per 256 x 256 tile
-                    assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (256, 256, 8, 1)
-                    assert pl["grid_x"] == -(-n // 256) * -(-m // 256)
+                if pl["kernel"] == 1:   # LDS-tiled: one workgroup per 256 x 256 (or 128 x 256) tile
+                    tn = 128 if pl["config"] == 98 else 256
+                    assert pl["config"] in (98, 99) and (tn == 256 or dt != sp.BF16)
+                    assert (pl["tile_n"], pl["tile_m"], pl["waves"], pl["split_k"]) == (tn, 256, 8, 1)
+                    assert pl["grid_x"] == -(-n // tn) * -(-m // 256)
                     continue
                 if pl["kernel"] == 2:   # LDS ring: one range of rows per workgroup
                     rbw, rb, mw, kw, mb, u, smax = stream[pl["config"]]
@@ -209,14 +211,26 @@ def test_plan_decode_workgroups_per_cu_by_code_type():
 def test_plan_tiled_for_wide_layers_at_256_tokens():
     # one tile of tokens and >= 96 tiles (gate+up of an 8B-class layer): BF16 takes the
     # tiled kernel with K split in two (its 256-token stream configurations do not fit
-    # LDS); one-byte codes keep all 256 tokens in one stream workgroup (W streamed once);
-    # narrower projections keep the small-m kernels
+    # LDS); one-byte codes take the tiled kernel with 128-row tiles (224 of them, no
+    # split); narrower projections keep the small-m kernels
     for m in (200, 256):
-        p8 = sp.plan(sp.OP_GEMM, sp.FP8, m, 28672, 4096)
+        for dt in (sp.FP8, sp.INT8):
+            p8 = sp.plan(sp.OP_GEMM, dt, m, 28672, 4096)
+            assert (p8["kernel"], p8["config"], p8["tile_n"], p8["tile_m"]) == (1, 98, 128, 256)
+            assert p8["grid_x"] == 224 and p8["split_k"] == 1 and p8["workspace_bytes"] == 0
         p16 = sp.plan(sp.OP_GEMM, sp.BF16, m, 28672, 4096)
-        assert p8["kernel"] == 2 and p8["config"] == 122 and p8["split_k"] == 1 and p8["workspace_bytes"] == 0
-        assert p16["kernel"] == 1 and p16["split_k"] == 2 and p16["grid_y"] == 2
+        assert p16["kernel"] == 1 and p16["config"] == 99 and p16["split_k"] == 2 and p16["grid_y"] == 2
         assert p16["workspace_bytes"] == 2 * m * 28672 * 4
+    for m, n, k in ((256, 6144, 4096), (256, 4096, 4096), (256, 4096, 14336), (128, 28672, 4096)):
+        assert sp.plan(sp.OP_GEMM, sp.FP8, m, n, k)["kernel"] == 2, (m, n, k)
+    os.environ["SP24_TILE"] = "98,2"
+    try:
+        with pytest.raises(sp.Sp24Error):   # 128-row tiles take one-byte codes only
+            sp.plan(sp.OP_GEMM, sp.BF16, 256, 1024, 1024)
+        p = sp.plan(sp.OP_GEMM, sp.FP8, 300, 1000, 1024)
+        assert (p["config"], p["tile_n"], p["grid_x"], p["split_k"]) == (98, 128, 8 * 2, 2)
+    finally:
+        os.environ.pop("SP24_TILE", None)
     for m, n, k in ((256, 6144, 4096), (256, 4096, 4096), (256, 4096, 14336), (128, 28672, 4096),
                     (129, 14336, 4096)):
         assert sp.plan(sp.OP_GEMM, sp.BF16, m, n, k)["kernel"] == 2, (m, n, k)

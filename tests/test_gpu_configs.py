@@ -93,3 +93,11 @@ def test_skinny_config_k_tail(cid, fp8, dense):
 def test_tiled_split_k(m, n, k, sk, fp8, dense):
     _run("99,%d" % sk, m, n, k, fp8, dense, "tiled split-K %dx%dx%d/%d" % (m, n, k, sk), seed=m + n + k + sk)
 
+
+# The tiled kernel with 128-row tiles (one-byte codes), with and without its K split:
+# ragged m and n, one and several tiles of tokens.
+@pytest.mark.parametrize("fp8,dense", [v for v in VARIANTS if v[0]])
+@pytest.mark.parametrize("m,n,k,sk", [(256, 1000, 1024, 1), (200, 300, 2048, 1), (300, 520, 2048, 2),
+                                      (17, 130, 1024, 4), (256, 4096, 4096, 1)])
+def test_tiled128(m, n, k, sk, fp8, dense):
+    _run("98,%d" % sk, m, n, k, fp8, dense, "tiled 128 rows %dx%dx%d/%d" % (m, n, k, sk), seed=m + n + k + 7 * sk)
