@@ -79,6 +79,10 @@ KERNEL_SOURCES = {  # the dominant kernel's sources and the plan that picks its 
                                 "sp24_internal.hpp", "sp24_api.hip")],
     "mfma": [_CSRC + f for f in ("sp24_gemm_tiled.hip", "sp24_dma.hpp", "sp24_common.hpp",
                                  "sp24_internal.hpp", "sp24_api.hip")],
+    # the layer sweep: stream and tiled kernels (both tile shapes) and the split-K reduction
+    "sweep": [_CSRC + f for f in ("sp24_gemm_stream.hip", "sp24_gemm_tiled.hip", "sp24_gemm_tiled128.hip",
+                                  "sp24_reduce.hip", "sp24_dma.hpp", "sp24_common.hpp", "sp24_internal.hpp",
+                                  "sp24_api.hip")],
 }
 
 
@@ -1075,7 +1079,8 @@ def run_layers(args, torch, np, sp, W, ev, dev):
             "desc": "layer sweep: %d layers x QKV/O/gate+up/down, M=%d tokens, 2:4 sparse %s" % (L, M, label),
             "flops": sum(2 * M * n * k for _, k, n in projs) * L,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": counted_traffic("layers", "sweep") if kind == "fp8" else None,
                          "kernel": "%s (sparse %s), all 128 calls" % (
                              "/".join(sorted({KERNEL_NAMES[pl["kernel"]] for pl in plans})), kind),
                          "per_unit": "values N*K/2*es + metadata N*K/8 + X M*K*es + Y 2*M*N bytes per launch"},

@@ -11,7 +11,7 @@
         copy of COPY_BYTES bytes (FETCH_SIZE and WRITE_SIZE are in KiB per dispatch), and
         the machine-readable traffic record bench.py reads (tied to the hash of the
         sources of the kernel family: the stream kernel for up/down, the tiled one for
-        prefill)
+        prefill, both with the split-K reduction for the layer sweep)
     python -m bf16_gemm_linear_amd.profile_summary counters DIR [KERNEL_SUBSTRING ...]
         mean, min and max per dispatch of every counter of a `--pmc` run, per kernel
 
@@ -36,7 +36,11 @@ SOURCES = {
                                "sp24_api.hip")],
     "mfma": [CSRC + f for f in ("sp24_gemm_tiled.hip", "sp24_dma.hpp", "sp24_common.hpp", "sp24_internal.hpp",
                                 "sp24_api.hip")],
+    "sweep": [CSRC + f for f in ("sp24_gemm_stream.hip", "sp24_gemm_tiled.hip", "sp24_gemm_tiled128.hip",
+                                 "sp24_reduce.hip", "sp24_dma.hpp", "sp24_common.hpp", "sp24_internal.hpp",
+                                 "sp24_api.hip")],
 }
+BOUND = {"prefill": "mfma", "layers": "sweep"}  # the source set of each workload's record (else "hbm")
 DT_NAMES = {"0": "BF16", "1": "FP8", "2": "INT8"}
 
 
@@ -155,7 +159,7 @@ def traffic(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, 
         nk = len(f.get(k, []))
         tot += (fb + wb) * nk
         n += nk
-    bound = "mfma" if workload == "prefill" else "hbm"
+    bound = BOUND.get(workload, "hbm")
     rec = {"workload": workload, "kernel_source_sha256": source_hash(bound), "traffic_bytes_per_launch": tot / n,
            "fetch_scale": fscale, "write_scale": wscale}
     print()
