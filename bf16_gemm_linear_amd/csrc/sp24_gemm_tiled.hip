@@ -376,11 +376,14 @@ __device__ __forceinline__ void inner_substeps(f32x16 (&acc)[TI][TJ], Frag<DT, S
 // PARTIAL (split-K): workgroup (tile, blockIdx.y) multiplies K steps
 // [blockIdx.y * slice_steps, +slice_steps) and writes its fp32 tile, unscaled, to
 // partial[blockIdx.y][m][n]; the reduction applies the scales.
-template <int DT, bool SPARSE, bool PARTIAL>
+// ROWS: the tile's W rows (BN), part of the kernel's name so that traces tell the
+// two tile shapes apart.
+template <int DT, bool SPARSE, bool PARTIAL, int ROWS>
 __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ w, const uint32_t* __restrict__ meta,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     int M, int N, int K, int xs_step, int ws_step, float* __restrict__ partial, int slice_steps) {
+  static_assert(ROWS == BN, "the tile rows of this build");
   using L = TiledLayout<DT, SPARSE>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::LDS_BYTES];
 
@@ -571,12 +574,12 @@ template <int DT, bool SPARSE>
 hipError_t launch_tiled_dt(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   using L = TiledLayout<DT, SPARSE>;
   if (p.split_k > 1)
-    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, true>), dim3(p.grid_x, p.split_k), dim3(NT), 0, s,
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, true, BN>), dim3(p.grid_x, p.split_k), dim3(NT), 0, s,
                        static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
                        a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.w_scale_step, a.partial,
                        a.k / L::KS / p.split_k);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, false>), dim3(p.grid_x), dim3(NT), 0, s,
+    hipLaunchKernelGGL((gemm_tiled_kernel<DT, SPARSE, false, BN>), dim3(p.grid_x), dim3(NT), 0, s,
                        static_cast<const uint8_t*>(a.x), static_cast<const uint8_t*>(a.w), a.meta, a.x_scale,
                        a.w_scale, a.y, a.m, a.n, a.k, a.x_scale_step, a.w_scale_step, (float*)nullptr, 0);
   return hipGetLastError();

@@ -69,11 +69,22 @@ def short_name(name):
     return re.sub(r"^void\s+", "", name).strip()
 
 
-def describe_stream(name):
-    """Words for StreamCfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX[, BUDGET]>."""
-    m = re.search(r"StreamCfg<(\d+), (true|false), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)", name)
+def describe_tiled(name):
+    """Words for gemm_tiled_kernel<DT, SPARSE, PARTIAL, ROWS>."""
+    m = re.search(r"gemm_tiled_kernel<(\d+), (true|false), (true|false), (\d+)>", name)
     if not m:
         return None
+    dt, sparse, partial, rows = m.groups()
+    return ("%s %s; %s W rows x 256 tokens per workgroup, 8 waves of %s x 64 outputs, 32 x 32 instructions%s"
+            % (DT_NAMES.get(dt, dt), "sparse" if sparse == "true" else "dense", rows, int(rows) // 2,
+               "; K split over the grid (fp32 partial tiles)" if partial == "true" else ""))
+
+
+def describe_stream(name):
+    """Words for StreamCfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX[, BUDGET]> (or a tiled kernel)."""
+    m = re.search(r"StreamCfg<(\d+), (true|false), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)", name)
+    if not m:
+        return describe_tiled(name)
     dt, sparse, rbw, rb, mw, kw, mb, u, smax = m.groups()
     rbw, rb, mw, kw, mb, u, smax = map(int, (rbw, rb, mw, kw, mb, u, smax))
     return ("%s %s; %d waves = %d along the rows x %d along the tokens x %d along K; each wave %d row "
