@@ -147,7 +147,7 @@ def counters(d, subs):
     print("|---|---|---|---|---|---|")
     for c in names:
         for k, v in sorted(_counter(d, c, subs).items()):
-            print("| `%s` | %s | %d | %.6g | %.6g | %.6g |" % (k, c, len(v), statistics.mean(v), min(v), max(v)))
+            print("| `%s` | %s | %d | %.10g | %.10g | %.10g |" % (k, c, len(v), statistics.mean(v), min(v), max(v)))
 
 
 def traffic(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, subs):
