@@ -266,10 +266,11 @@ int sp24_gemm_rows(int dtype, int64_t m, int64_t n, int64_t k, const void* x, co
  * *x_scale_dev, in one call.  The per-tensor scale follows the cookbook's
  * dynamic FP8 scaling ("Deploying 2:4 Sparsity with FP8 on Hopper", pipeline
  * step 3); the quantisation happens inside the GEMM kernel when X is small
- * (m*k <= 65536 values and the plan's small-m kernel has room for its tokens'
- * codes in LDS: decode shapes), which saves the quantiser's launch and the
- * round trip of the codes through memory; otherwise the two steps run as two
- * launches with the codes in the workspace.
+ * (m*k <= 65536 values, the plan's small-m kernel has room for its tokens'
+ * codes in LDS and each of its workgroups casts at most 16384 values: every
+ * workgroup repeats the cast of its tokens), which saves the quantiser's launch
+ * and the round trip of the codes through memory; otherwise the two steps run
+ * as two launches with the codes in the workspace.
  *   x_bf16      in : [m, k] bf16
  *   x_scale_dev out: fp32, the scale amax(|x|)/448 (1 when x is all zero)
  *   w_values    in : [n, k/2] E4M3 codes; w_meta as for sp24_gemm;
