@@ -29,7 +29,7 @@ __all__ = [
     "quant_int8", "quant_int8_rows", "OP_PALETTE_ANALYZE", "OP_PALETTE_GEMM", "PaletteWeight",
     "palette_encode", "palette_decode", "palette_gemm",
     "prune_compress", "decompress", "quant_fp8", "gemm", "dense_gemm", "workspace_size", "plan",
-    "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read",
+    "probe_mfma_layout", "probe_mfma_rate", "probe_copy", "probe_read", "probe_ring",
 ]
 
 BF16, FP8, INT8 = 0, 1, 2
@@ -98,6 +98,7 @@ _SIGS = {
     "sp24_probe_copy": [_vp, _vp, _sz, _vp],
     "sp24_probe_read": [_vp, _sz, _vp, _vp],
     "sp24_probe_read_blocks": [],
+    "sp24_probe_ring": [_int, _int, _int, _int, _vp, _sz, _vp, _sz, _int, _int, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
     try:
@@ -766,6 +767,23 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor):
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst too small")
     _check("sp24_probe_copy", lib.sp24_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+
+
+def probe_ring(w_kb: int, x_kb: int, stages: int, barrier: bool, w: torch.Tensor, w_stride: int,
+               x: torch.Tensor, blocks: int, steps: int, out: torch.Tensor):
+    """The GEMM rings' load path without arithmetic (sp24_probe_ring): workgroup b
+    reads steps * w_kb KB at w + b * w_stride; x holds one region per XCD (its
+    bytes / 8 a power of two)."""
+    _need(w, "w")
+    _need(x, "x", None, None, w.device)
+    _need(out, "out", torch.int32, None, w.device)
+    if out.numel() < blocks:
+        raise ValueError("out too small")
+    if w_kb > 0 and w.numel() * w.element_size() < (blocks - 1) * w_stride + steps * w_kb * 1024:
+        raise ValueError("w too small")
+    _check("sp24_probe_ring",
+           lib.sp24_probe_ring(w_kb, x_kb, stages, 1 if barrier else 0, _ptr(w), w_stride, _ptr(x),
+                               x.numel() * x.element_size(), blocks, steps, _ptr(out), _stream(w.device)))
 
 
 def probe_read(src: torch.Tensor, out: torch.Tensor):

@@ -9,6 +9,7 @@
 
 #include "../../include/sp24_probe.h"
 #include "sp24_common.hpp"
+#include "sp24_dma.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -195,6 +196,50 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   if (threadIdx.x == 0) out[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
 }
 
+// The load path of the LDS-ring GEMM kernels without their arithmetic: a ring of
+// S LDS buffers; per step a workgroup of 8 waves loads WKB KB of W (its own
+// region, read once) and XKB KB of X (a region per XCD, re-read, so L2-resident)
+// with global_load_lds, 16 bytes a lane, W first.  Each wave waits for its loads
+// of step ks, then (BAR) the workgroup synchronises, and the loads of step
+// ks + S - 1 go out, as in the GEMM kernels' rings.
+constexpr int kRingWaves = 8;
+
+template <int WKB, int XKB, int S, bool BAR>
+__global__ __launch_bounds__(kRingWaves * 64) void ring_kernel(const uint8_t* __restrict__ w, int64_t w_stride,
+                                                                const uint8_t* __restrict__ x, int64_t x_region,
+                                                                int steps, uint32_t* __restrict__ out) {
+  constexpr int PER = (WKB + XKB) / kRingWaves;
+  static_assert((WKB + XKB) % kRingWaves == 0 && PER >= 1, "whole loads per wave");
+  static_assert(PER * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * (WKB + XKB) * 1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint8_t* wp = w + (int64_t)blockIdx.x * w_stride + lane * 16;
+  const uint8_t* xp = x + (int64_t)(blockIdx.x % 8) * x_region + lane * 16;
+  auto issue = [&](int ks) {
+    uint8_t* buf = lds + (ks % S) * (WKB + XKB) * 1024;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int g = j * kRingWaves + wave;  // load g of the step
+      if (g < WKB) dma16(wp + ((int64_t)ks * WKB + g) * 1024, buf + g * 1024);
+      else dma16(xp + ((((int64_t)ks * XKB + (g - WKB)) * 1024) & (x_region - 1)), buf + g * 1024);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < steps) issue(p);
+  uint32_t acc = 0;
+  for (int ks = 0; ks < steps; ++ks) {
+    const int left = steps - 1 - ks;
+    wait_later<PER, S - 2>(left < S - 2 ? left : S - 2);
+    if constexpr (BAR) __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ks + S - 1 < steps) issue(ks + S - 1);
+    acc ^= *reinterpret_cast<const uint32_t*>(lds + (ks % S) * (WKB + XKB) * 1024 + wave * 1024 + lane * 16);
+  }
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, 64);
+  if (threadIdx.x == 0) out[blockIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace sp24
 
@@ -260,6 +305,30 @@ int sp24_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
 }
 
 int sp24_probe_read_blocks(void) { return kReadBlocks; }
+
+int sp24_probe_ring(int w_kb, int x_kb, int stages, int barrier, const void* w, size_t w_stride, const void* x,
+                    size_t x_bytes, int blocks, int steps, uint32_t* out, void* stream) {
+  if (!out || (w_kb > 0 && !w) || (x_kb > 0 && !x)) return SP24_ERR_NULL;
+  if (blocks < 1 || blocks > 65536 || steps < 1) return SP24_ERR_SHAPE;
+  if (w_kb > 0 && w_stride < (size_t)steps * w_kb * 1024) return SP24_ERR_SHAPE;
+  const size_t x_region = x_bytes / 8;  // one region per XCD: a power of two of at least one step
+  if (x_kb > 0 && (x_bytes % 8 != 0 || x_region < (size_t)x_kb * 1024 || (x_region & (x_region - 1)) != 0))
+    return SP24_ERR_SHAPE;
+  if ((((uintptr_t)w | (uintptr_t)x | (uintptr_t)out | w_stride) & 15u) != 0) return SP24_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* pw = static_cast<const uint8_t*>(w);
+  const uint8_t* px = static_cast<const uint8_t*>(x);
+  const dim3 g(blocks), blk(kRingWaves * 64);
+  const int64_t ws = (int64_t)w_stride, xr = (int64_t)(x_region > 0 ? x_region : 1024);
+#define SP24_RING_CASE(WKB, XKB, S, BAR)                                                                  \
+  if (w_kb == WKB && x_kb == XKB && stages == S && (barrier != 0) == BAR) {                              \
+    hipLaunchKernelGGL((ring_kernel<WKB, XKB, S, BAR>), g, blk, 0, s, pw, ws, px, xr, steps, out);        \
+    return hipGetLastError() == hipSuccess ? SP24_OK : SP24_ERR_HIP;                                      \
+  }
+  SP24_PROBE_RING_SHAPES(SP24_RING_CASE)
+#undef SP24_RING_CASE
+  return SP24_ERR_MODE;
+}
 
 int sp24_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
   if (!src || !out) return SP24_ERR_NULL;

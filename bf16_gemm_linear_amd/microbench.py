@@ -9,6 +9,14 @@ Prints one JSON object:
   * mfma_tflops[variant]: sp24_probe_mfma_rate with every SIMD busy, in
     dense-equivalent flops per second (sparse variants count the full K), and
     the implied clock assuming the instruction's nominal cycle count.
+
+    python -m bf16_gemm_linear_amd.microbench --ring
+
+Prints one JSON object with the load path of the LDS-ring GEMM kernels
+(sp24_probe_ring, one workgroup of 8 waves per CU, 128 steps): per shape (KB of
+W and of X per step, buffers, barrier) the time of one launch (best of 5) and
+the KB per microsecond per CU, W streamed from HBM (1 GB in all, a fresh part
+per launch), X from L2.
 """
 from __future__ import annotations
 
@@ -85,7 +93,39 @@ def mfma_rate(variant, cus):
     return name, tflops, clock_ghz
 
 
+RING_SHAPES = [(8, 16, 4, True), (8, 16, 4, False), (8, 16, 6, True), (8, 0, 4, True), (24, 0, 4, True),
+               (0, 16, 4, True), (0, 24, 4, True)]
+
+
+def ring(cus):
+    steps, w_stride = 128, 4 << 20
+    w = torch.empty(cus * w_stride, dtype=torch.uint8, device="cuda")
+    x = torch.empty(8 * (256 << 10), dtype=torch.uint8, device="cuda")
+    w.fill_(1)
+    x.fill_(1)
+    out = torch.empty(cus, dtype=torch.int32, device="cuda")
+    res = {}
+    for w_kb, x_kb, stages, bar in RING_SHAPES:
+        per = steps * max(w_kb, 1) << 10  # W bytes of one launch per workgroup
+        parts = w_stride // per            # each launch reads a fresh part of every region
+
+        def launch(i):
+            wv = w[(i % parts) * per:]
+            sp.probe_ring(w_kb, x_kb, stages, bar, wv, w_stride, x, cus, steps, out)
+        launch(0)
+        t = min(_time(launch, 1) for _ in range(5))
+        per_cu = steps * (w_kb + x_kb) / (t * 1e6)  # KB per microsecond per CU
+        key = "W%d_X%d_S%d_%s" % (w_kb, x_kb, stages, "bar" if bar else "nobar")
+        res[key] = {"us": t * 1e6, "KB_per_us_per_CU": per_cu,
+                    "W_TBs": cus * steps * w_kb * 1024 / t / 1e12}
+    return res
+
+
 def main():
+    if "--ring" in sys.argv:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        print(json.dumps({"ring": ring(cus), "compute_units": cus}))
+        return
     if "--copy-only" in sys.argv:  # reference kernel of known traffic, for counter scaling
         gbs, t = hbm_copy(256 << 20)
         print(json.dumps({"copy_bytes_read": 256 << 20, "copy_bytes_written": 256 << 20,

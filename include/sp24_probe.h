@@ -64,6 +64,34 @@ int sp24_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int sp24_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 int sp24_probe_read_blocks(void);
 
+/* The load path of the LDS-ring GEMM kernels without their arithmetic.
+ * `blocks` workgroups of 8 waves walk `steps` steps of a ring of `stages` LDS
+ * buffers of (w_kb + x_kb) KB.  Per step workgroup b loads w_kb KB of W, the
+ * step's next bytes of its own region w + b * w_stride (each byte once: when
+ * blocks * w_stride exceeds the last-level cache, W streams from HBM), and x_kb
+ * KB of X from the region x + (b % 8) * x_bytes / 8, wrapping (re-read by the
+ * workgroups of each XCD, so L2-resident), with global_load_lds (16 bytes a
+ * lane, W first).  Each wave waits for its loads of a step; with barrier != 0
+ * the workgroup then synchronises (the GEMM kernels' ring); then the loads of
+ * step + stages - 1 go out.  One checksum word per workgroup goes to out[b]
+ * (out holds >= blocks words).  The caller times the launch.
+ *   w: blocks * w_stride bytes, w_stride >= steps * w_kb KB, a multiple of 16;
+ *   x: x_bytes, x_bytes / 8 a power of two >= x_kb KB (unused when x_kb = 0).
+ * (w_kb, x_kb, stages, barrier) must be one of SP24_PROBE_RING_SHAPES (else
+ * SP24_ERR_MODE): the stream kernel's mix at M = 64 (8 KB of W values and 16 KB
+ * of X per step, four buffers) with and without the barrier and with six
+ * buffers, and W or X alone. */
+#define SP24_PROBE_RING_SHAPES(X) \
+  X(8, 16, 4, true)               \
+  X(8, 16, 4, false)              \
+  X(8, 16, 6, true)               \
+  X(8, 0, 4, true)                \
+  X(24, 0, 4, true)               \
+  X(0, 16, 4, true)               \
+  X(0, 24, 4, true)
+int sp24_probe_ring(int w_kb, int x_kb, int stages, int barrier, const void* w, size_t w_stride, const void* x,
+                    size_t x_bytes, int blocks, int steps, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -310,6 +310,18 @@ def test_probe_validation():
     assert lib.sp24_probe_copy(p(A), p(A + 4096), 65, None) == ESHAPE
     assert lib.sp24_probe_read(p(A), 0, p(A + 4096), None) == ESHAPE
     assert lib.sp24_probe_read_blocks() > 0
+    # ring probe: arguments checked before any HIP call; shapes outside the built set
+    ring = lambda wkb, xkb, st, bar, w=A, ws=64 << 10, x=A + (1 << 24), xb=2 << 20, blocks=4, steps=8, out=A + (1 << 25): \
+        lib.sp24_probe_ring(wkb, xkb, st, bar, p(w), ws, p(x), xb, blocks, steps, p(out), None)
+    assert ring(8, 16, 4, 1, out=0) == ENULL
+    assert ring(8, 16, 4, 1, w=0) == ENULL
+    assert ring(8, 16, 4, 1, blocks=0) == ESHAPE
+    assert ring(8, 16, 4, 1, ws=8 * 8 * 1024 - 16) == ESHAPE      # region shorter than steps * w_kb KB
+    assert ring(8, 16, 4, 1, xb=3 << 20) == ESHAPE                 # x bytes / 8 not a power of two
+    assert ring(8, 16, 4, 1, xb=8 * 8 * 1024) == ESHAPE            # region below one step of X
+    assert ring(8, 16, 4, 1, ws=(64 << 10) + 8) == EALIGN
+    assert ring(16, 16, 4, 1, ws=128 << 10) == EMODE               # not one of SP24_PROBE_RING_SHAPES
+    assert ring(8, 16, 5, 1) == EMODE
 
 
 def gemm_qx(m=8, n=256, k=256, x=A, xs=A + 0x100000, w=A + 0x200000, meta=A + 0x300000,
