@@ -166,7 +166,12 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 //    kernel); long-K few-row shapes take 128 rows x 128 tokens per workgroup
 //    with K split in 4 (down-projection 4096 x 14336: 27.0 against 29.5 us
 //    for 64 rows x 256 tokens); the rest take 64-token blocks.
-StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
+//  * Sparse one-byte codes at m <= 256 with 128-row workgroups step two units
+//    of K at a time (W in 128-byte row pieces; one unit moves 64-byte halves of
+//    a line, which the load path takes at half the rate): QKV 6144 x 4096 at
+//    m = 256 15.0 against 16.3 us, down 4096 x 14336 26.4 against 27.4 us.
+StreamChoice stream_default(int dtype, bool sparse, int64_t m, int64_t n, int64_t k) {
+  const bool two_units = sparse && dtype != SP24_BF16;
   const int64_t rows_cu = (n + 255) / 256;
   auto rows_for = [&](int64_t shares, int64_t lo, int64_t hi) {
     int64_t r = ((n + shares - 1) / shares + 3) / 4 * 4;
@@ -195,13 +200,15 @@ StreamChoice stream_default(int dtype, int64_t m, int64_t n, int64_t k) {
   if (m <= 256) {
     // 256 tokens per workgroup (8 waves along m): W is streamed once
     if (rows_cu > 64) return StreamChoice{22, 0};
-    if (rows_cu <= 16 && k >= 8192) return StreamChoice{25, 128, 4};
+    if (rows_cu <= 16 && k >= 8192) return StreamChoice{two_units ? 30 : 25, 128, 4};
   }
-  // 64-token blocks: more than 64 rows per share take 128-row workgroups with an
-  // 8-buffer ring (QKV 6144 x 4096 at m = 256: 15.5 against 16.5 us with 3 buffers)
+  // 64-token blocks: more than 64 rows per share take 128-row workgroups, with an
+  // 8-buffer ring for one unit per step (QKV 6144 x 4096 at m = 256: 15.5 against
+  // 16.5 us with 3 buffers)
   const int64_t gy = (m + 63) / 64;
   const int64_t shares = gy >= 256 ? 1 : 256 / gy;
-  return StreamChoice{(n + shares - 1) / shares > 64 ? 28 : 3, 0};
+  if ((n + shares - 1) / shares > 64) return StreamChoice{two_units ? 29 : 28, 0};
+  return StreamChoice{3, 0};
 }
 
 Cfg skinny_cfg(int id) {
@@ -308,7 +315,7 @@ int plan_gemm(int op, int dtype, int64_t m, int64_t n, int64_t k, sp24_plan* out
   if (!forced) {
     // the choice for this shape, else (it does not fit this operand type, or K
     // does not split into its steps) the 64-token-block configurations
-    const StreamChoice d = stream_default(dtype, m, n, k);
+    const StreamChoice d = stream_default(dtype, op == SP24_OP_GEMM, m, n, k);
     if (plan_stream(d.id, dtype, op == SP24_OP_GEMM, d.split_k, (int)d.rows, m, n, k, out)) return SP24_OK;
     const int64_t gy = (m + 63) / 64, shares = gy >= 256 ? 1 : 256 / gy;
     const int g = (n + shares - 1) / shares > 64 ? 12 : 3;

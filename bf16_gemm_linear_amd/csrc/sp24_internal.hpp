@@ -166,8 +166,10 @@ constexpr int kTiled128Config = 98;  // the same kernel with 128 W rows x 256 to
   X(25, 2, 4, 4, 1, 2, 1, 3)         \
   X(26, 1, 2, 8, 1, 2, 1, 4)         \
   X(27, 1, 4, 4, 2, 4, 1, 2)         \
-  X(28, 8, 1, 1, 1, 4, 1, 8)
-constexpr int kStreamConfigs = 29;
+  X(28, 8, 1, 1, 1, 4, 1, 8)         \
+  X(29, 8, 1, 1, 1, 4, 2, 3)         \
+  X(30, 2, 4, 4, 1, 2, 2, 3)
+constexpr int kStreamConfigs = 31;
 constexpr int kStreamBase = 100;
 constexpr int kStreamLdsBytes = 160 * 1024;
 // A stream kernel that quantises X itself holds its tokens' X codes for its K
