@@ -36,6 +36,8 @@
 // LDS rows are XOR-swizzled in 16-byte pieces so that the 16 rows read by one
 // instruction fall on distinct bank groups; the LDS-DMA load writes lane i's
 // bytes to slot i, so the swizzle is applied on the global side.
+#include <atomic>
+
 #include "sp24_common.hpp"
 #include "sp24_dma.hpp"
 #include "sp24_fp8.hpp"
@@ -104,6 +106,28 @@ struct StreamCfg {
   static constexpr int RING_QX = stream_ring_bytes(DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX, true);
   static constexpr int MIN_PER_STEP_QX = W_TOT / NW + M_TOT / NW;
 };
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [LO, HI].
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vm_range<LO, MID>(n);
+    else wait_vm_range<MID + 1, HI>(n);
+  }
+}
+
+// Workgroup barrier for LDS data only: this wave's LDS accesses are done
+// (lgkmcnt 0), then a bare s_barrier; vector-memory loads in flight (the ring's
+// LDS-DMA loads) stay in flight, where __syncthreads() would wait for them.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Metadata words (MW per row): the 16 rows x 4 words of one read land on 64
 // distinct banks.
@@ -396,7 +420,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const float* __restrict__ x_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ y,
     float* __restrict__ partial, int M, int N, int K, int rows_per_wg, int units_per_slice,
     const uint16_t* __restrict__ xh, float* __restrict__ sx_out, int xs_step, int xk, int lift, int ws_step,
-    const float* __restrict__ x_gscale, const float* __restrict__ w_gscale, int group_units, int n_groups) {
+    const float* __restrict__ x_gscale, const float* __restrict__ w_gscale, int group_units, int n_groups,
+    int x_stage) {
   static_assert(!(GS && QX), "group scales take X codes");
   constexpr int MB = C::MB_, RB = C::RB_, RBW = C::RBW_, KW = C::KW_, STAGES = C::STAGES;
   constexpr int STAGE = QX ? C::STAGE_QX : C::STAGE;
@@ -415,7 +440,10 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   // most kStreamGsBytes)
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   float* const gstab = reinterpret_cast<float*>(dyn_lds);
-  uint8_t* const xcodes = dyn_lds;
+  // QX per tensor with x_stage > 0: all of X (bf16, x_stage = 2 M K bytes) is staged
+  // in dyn_lds[0, x_stage) and the codes follow it
+  if constexpr (!QX || QROWS) x_stage = 0;
+  uint8_t* const xcodes = dyn_lds + x_stage;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar
@@ -443,13 +471,35 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   // K slice into LDS (the dynamic array), piece p of a step's part of
   // row r in slot swz16(r, p) as a ring buffer would hold it.
   // QX: the ring's first loads (W and metadata only) go out before the
-  // prologue, so they travel while X is read.  The prologue's first barrier
-  // waits for them (a workgroup barrier drains every load in flight), so no
-  // LDS-DMA load is in flight when the codes are written and the K loop's
-  // waits stay as they are without QX.
+  // prologue, so they travel while X is read.  Loads complete in issue order,
+  // so X loaded into registers after them is usable only once they have
+  // landed, and the prologue's __syncthreads() waits for every load in
+  // flight: the first steps of W arrive before the prologue ends and the ring
+  // refills from empty after it.  With x_stage (per tensor, X small enough and
+  // the LDS to hold it without losing a workgroup per CU) X goes into LDS by
+  // LDS-DMA before the ring's loads: the wave waits for its own X loads only
+  // (the ring's loads, issued after them, may stay in flight), and the
+  // prologue's barriers wait for LDS accesses only, so W streams on while X is
+  // reduced and cast.
   if constexpr (QX && QROWS) {  // the rows' maxima start at 0 (before any load is in flight)
     if (threadIdx.x < C::BM) wave_max[threadIdx.x] = 0u;
     __syncthreads();
+  }
+  int ring_prologue_loads = 0;  // this wave's ring loads issued after its X staging loads
+  if constexpr (QX && !QROWS) {
+    if (x_stage > 0) {
+      const int nvec = M * K / 8, ninstr = (nvec + 63) / 64;  // M K <= kQxRegValues (host)
+      for (int g = wave; g < ninstr; g += C::NW) {
+        const int i = g * 64 + lane;
+        if (i < nvec) dma16(xh + (size_t)i * 8, dyn_lds + g * 1024);
+      }
+      int per = 0;
+#pragma unroll
+      for (int j = 0; j < C::W_PER; ++j) per += (j * C::NW + wave < C::W_TOT) ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < C::M_PER; ++j) per += (j * C::NW + wave < C::M_TOT) ? 1 : 0;
+      ring_prologue_loads = per * min(STAGES - 1, nks);
+    }
   }
   if constexpr (QX) {
 #pragma unroll
@@ -545,7 +595,19 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     const bool in_regs = nvec <= (int64_t)RV * C::NT;
     u32x4 xr[RV];
     uint32_t mk = 0;
-    if (in_regs) {  // nvec <= RV * NT: 32-bit indices
+    if (x_stage > 0) {  // in_regs holds (the host stages only X of at most kQxRegValues values)
+      // this wave's staging loads have landed (more than 63 ring loads after them:
+      // waiting for 63 still implies them); the barrier makes every wave's visible
+      wait_vm_range<0, 63>(min(ring_prologue_loads, 63));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < RV; ++r) {
+        const int i = tid + r * C::NT;
+        xr[r] = i < (int)nvec ? *reinterpret_cast<const u32x4*>(dyn_lds + (size_t)i * 16) : u32x4{0u, 0u, 0u, 0u};
+        mk = max(mk, key_max8(xr[r]));
+      }
+    } else if (in_regs) {  // nvec <= RV * NT: 32-bit indices
 #pragma unroll
       for (int r = 0; r < RV; ++r) {
         const int i = tid + r * C::NT;
@@ -563,7 +625,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
     if (lane == 0) wave_max[wave] = mk;
-    __syncthreads();
+    if (x_stage > 0) lds_barrier();
+    else __syncthreads();
 #pragma unroll
     for (int g = 0; g < C::NW; ++g) mk = max(mk, wave_max[g]);
     sx = scale_from_key(mk);
@@ -601,7 +664,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       }
       for (; v < nv; v += C::NT) put_vec(v, *src(v));
     }
-    __syncthreads();  // the codes are in LDS for every wave
+    if (x_stage > 0) lds_barrier();  // the codes are in LDS for every wave
+    else __syncthreads();
   }
 
   if constexpr (GS) {
@@ -746,6 +810,26 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   }
 }
 
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Rounds of workgroups a launch of `grid` workgroups of `lds` bytes each runs in,
+// as far as the LDS decides how many a CU holds.
+int64_t lds_rounds(int64_t grid, int64_t lds) {
+  const int64_t per_cu = kStreamLdsBytes / (lds > 0 ? lds : 1);
+  const int64_t at_once = (per_cu > 0 ? per_cu : 1) * device_cus();
+  return (grid + at_once - 1) / at_once;
+}
+
 template <int DT, bool SPARSE, int RBW, int RB, int MW, int KW, int MB, int U, int SMAX>
 hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t s) {
   using C = StreamCfg<DT, SPARSE, RBW, RB, MW, KW, MB, U, SMAX>;
@@ -773,27 +857,39 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
               hipLaunchKernelGGL((gemm_stream_kernel<C, true, true, true>), grid, block, dyn, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
                                  units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, 0);
             else
               hipLaunchKernelGGL((gemm_stream_kernel<C, false, true, true>), grid, block, dyn, s, x, w, a.meta,
                                  a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n,
                                  units_per_slice, a.x_bf16, a.x_scale_out, 0, xk, a.x_lift,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, 0);
           } else {
             return hipErrorInvalidConfiguration;
           }
         } else if (a.x_lift != 0) {
           return hipErrorInvalidValue;  // lifting is per token only
-        } else if (p.split_k > 1) {
-          hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, dyn, s, x, w, a.meta, a.x_scale,
-                             a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0, a.k, 0,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
         } else {
-          hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, dyn, s, x, w, a.meta, a.x_scale,
-                             a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
-                             a.x_scale_out, 0, a.k, 0,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
+          // stage X (bf16) in LDS ahead of the codes when it is small enough to stay in
+          // registers from the maximum to the cast, fits what the ring leaves, and adds
+          // no round of workgroups (the LDS per workgroup can lower how many a CU holds)
+          const int64_t stage = 2 * (int64_t)a.m * a.k;
+          const int64_t base = kStreamLdsBytes - stream_qx_room(RBW, RB, MW, KW, MB, U, SMAX, false) + xbytes;
+          const int64_t grid_n = (int64_t)p.grid_x * p.grid_y * p.grid_z;
+          const bool staged = (int64_t)a.m * a.k <= (int64_t)kQxRegValues &&
+                              xbytes + stage <= stream_qx_room(RBW, RB, MW, KW, MB, U, SMAX, false) &&
+                              lds_rounds(grid_n, base + stage) == lds_rounds(grid_n, base);
+          const int xst = staged ? (int)stage : 0;
+          const size_t dyn2 = dyn + (size_t)xst;
+          if (p.split_k > 1)
+            hipLaunchKernelGGL((gemm_stream_kernel<C, true, true>), grid, block, dyn2, s, x, w, a.meta, a.x_scale,
+                               a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
+                               a.x_scale_out, 0, a.k, 0,
+                               a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, xst);
+          else
+            hipLaunchKernelGGL((gemm_stream_kernel<C, false, true>), grid, block, dyn2, s, x, w, a.meta, a.x_scale,
+                               a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice, a.x_bf16,
+                               a.x_scale_out, 0, a.k, 0,
+                               a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, xst);
         }
         return hipGetLastError();
       } else {
@@ -813,12 +909,12 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
           hipLaunchKernelGGL((gemm_stream_kernel<CG, true, false, false, true>), grid, block, tab, s, x, w, a.meta,
                              a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                              (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
-                             a.group_units, a.n_groups);
+                             a.group_units, a.n_groups, 0);
         else
           hipLaunchKernelGGL((gemm_stream_kernel<CG, false, false, false, true>), grid, block, tab, s, x, w, a.meta,
                              a.x_scale, a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                              (const uint16_t*)nullptr, (float*)nullptr, 0, a.k, 0, 0, a.x_gscale, a.w_gscale,
-                             a.group_units, a.n_groups);
+                             a.group_units, a.n_groups, 0);
         return hipGetLastError();
       } else {
         return hipErrorInvalidConfiguration;
@@ -828,12 +924,12 @@ hipError_t launch_stream_cfg(const GemmArgs& a, const sp24_plan& p, hipStream_t 
       hipLaunchKernelGGL((gemm_stream_kernel<C, true, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                          (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, 0);
     else
       hipLaunchKernelGGL((gemm_stream_kernel<C, false, false>), grid, block, 0, s, x, w, a.meta, a.x_scale,
                          a.w_scale, a.y, a.partial, a.m, a.n, a.k, p.tile_n, units_per_slice,
                          (const uint16_t*)nullptr, (float*)nullptr, a.x_scale_step, a.k, 0,
-                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0);
+                             a.w_scale_step, (const float*)nullptr, (const float*)nullptr, 0, 0, 0);
     return hipGetLastError();
   }
 }
