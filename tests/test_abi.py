@@ -236,6 +236,23 @@ def test_plan_tiled_for_wide_layers_at_256_tokens():
         assert sp.plan(sp.OP_GEMM, sp.BF16, m, n, k)["kernel"] == 2, (m, n, k)
 
 
+def test_plan_two_units_per_step_for_sparse_one_byte_codes_at_256_tokens():
+    # 128-row workgroups at m = 256 step two units of K (W in whole 128-byte lines) for
+    # sparse FP8 / INT8; BF16 (twice the bytes per step) and the dense baseline keep one unit
+    for dt in (sp.FP8, sp.INT8):
+        qkv = sp.plan(sp.OP_GEMM, dt, 256, 6144, 4096)
+        assert (qkv["kernel"], qkv["config"], qkv["tile_n"], qkv["tile_m"], qkv["batch"]) == (2, 129, 96, 64, 2)
+        assert (qkv["grid_x"], qkv["grid_y"], qkv["split_k"]) == (64, 4, 1)
+        down = sp.plan(sp.OP_GEMM, dt, 256, 4096, 14336)
+        assert (down["kernel"], down["config"], down["tile_n"], down["tile_m"], down["batch"]) == (2, 130, 128, 128, 2)
+        assert (down["grid_x"], down["grid_y"], down["split_k"]) == (32, 2, 4)
+        assert down["workspace_bytes"] == 4 * 256 * 4096 * 4
+        assert sp.plan(sp.OP_DENSE_GEMM, dt, 256, 6144, 4096)["config"] == 128
+        assert sp.plan(sp.OP_DENSE_GEMM, dt, 256, 4096, 14336)["config"] == 125
+    assert sp.plan(sp.OP_GEMM, sp.BF16, 256, 6144, 4096)["config"] == 128
+    assert sp.plan(sp.OP_GEMM, sp.BF16, 256, 4096, 14336)["config"] == 125
+
+
 def test_plan_stream_rows_cover_every_cu_equally():
     # equal row ranges over all 256 CUs: 14336 rows as 512 ranges of 28 (two
     # workgroups per CU), 56 per CU at m = 64, 16 per CU for 4096 rows
