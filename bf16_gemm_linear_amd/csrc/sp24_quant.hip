@@ -150,20 +150,26 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
   if (blockIdx.x == gridDim.x - 1 && tail < count) q[tail] = qcast1<DT>(x[tail], s);
 }
 
-// Per-row (per-token) scales: workgroup b quantises rows b, b + gridDim.x, ...
-// of X [m, k] (k % 8 == 0), each with s_r = fp32(amax_r / 448) (1 for a zero
-// row).  A row of up to kRowRegVecs * kThreads vectors stays in registers from
-// the maximum to the cast (k <= 8192: one pass over global memory).
+// Per-row (per-token) scales: X [m, k] (k % 8 == 0), row r with s_r = fp32(amax_r /
+// 448) (1 for a zero row).  Workgroup (c, b) takes the maximum over the whole of rows
+// b, b + gridDim.y, ... and casts chunk c (chunk_vecs 8-value vectors) of each: a
+// few rows are cast by many workgroups (the division per value is the costly part;
+// one CU per row takes ~2 us for 14336 values), each reading its rows' maximum from
+// L2.  A row of up to kRowRegVecs * kThreads vectors cast by one workgroup stays in
+// registers from the maximum to the cast (one pass over global memory).
 constexpr int kRowRegVecs = 4;
+constexpr int kRowMinChunkVecs = 64;  // vectors a workgroup casts at least when a row is split
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                               int64_t k, uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales) {
+                                                              float* __restrict__ scales, int64_t chunk_vecs) {
   __shared__ uint32_t sh[kThreads / kWave];
   const int64_t nvec = k / 8;
-  const bool in_regs = nvec <= (int64_t)kRowRegVecs * kThreads;
-  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+  const bool whole = chunk_vecs >= nvec;  // one workgroup per row (gridDim.x == 1)
+  const bool in_regs = whole && nvec <= (int64_t)kRowRegVecs * kThreads;
+  const int64_t c0 = (int64_t)blockIdx.x * chunk_vecs, c1 = min(nvec, c0 + chunk_vecs);
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
     const u32x4* xv = reinterpret_cast<const u32x4*>(x + r * k);
     u32x2* qv = reinterpret_cast<u32x2*>(q + r * k);
     u32x4 v[kRowRegVecs];
@@ -176,10 +182,15 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __
         mk = max(mk, key_max8(v[j]));
       }
     } else {
-      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
+      int64_t i = threadIdx.x;
+      for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {  // four loads in flight
+        const u32x4 a = xv[i], b = xv[i + kThreads], c = xv[i + 2 * kThreads], d = xv[i + 3 * kThreads];
+        mk = max(mk, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+      }
+      for (; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
     }
     const float s = qscale<DT>(block_max<kThreads>(mk, sh));
-    if (threadIdx.x == 0) scales[r] = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kRowRegVecs; ++j) {
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __
         if (i < nvec) qv[i] = qcast8<DT>(v[j], s);
       }
     } else {
-      for (int64_t i = threadIdx.x; i < nvec; i += kThreads) qv[i] = qcast8<DT>(xv[i], s);
+      for (int64_t i = c0 + threadIdx.x; i < c1; i += kThreads) qv[i] = qcast8<DT>(xv[i], s);
     }
   }
 }
@@ -261,8 +272,17 @@ namespace {
 template <int DT>
 hipError_t launch_quant_rows_dt(const uint16_t* x, int64_t m, int64_t k, uint8_t* q, float* scales,
                                 hipStream_t s) {
-  const int64_t blocks = m < 65536 ? m : 65536;
-  hipLaunchKernelGGL(quant_rows_kernel<DT>, dim3((int)blocks), dim3(kThreads), 0, s, x, m, k, q, scales);
+  // rows over grid.y; each row's cast split over grid.x so that few rows still fill
+  // about 256 workgroups (chunks of at least kRowMinChunkVecs vectors)
+  const int64_t rows = m < 65535 ? m : 65535, nvec = k / 8;
+  int64_t splits = 256 / rows;
+  const int64_t most = nvec / kRowMinChunkVecs;
+  if (splits > most) splits = most;
+  if (splits < 1) splits = 1;
+  const int64_t chunk = (nvec + splits - 1) / splits;
+  splits = (nvec + chunk - 1) / chunk;
+  hipLaunchKernelGGL(quant_rows_kernel<DT>, dim3((int)splits, (int)rows), dim3(kThreads), 0, s, x, m, k, q, scales,
+                     chunk);
   return hipGetLastError();
 }
 
