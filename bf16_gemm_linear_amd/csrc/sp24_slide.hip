@@ -107,30 +107,38 @@ __device__ __forceinline__ uint32_t qcast4(uint32_t d0, uint32_t d1, float s) {
            (f32x2_to_e4m3(bf16_to_f32(d1 & 0xFFFFu) / s, bf16_to_f32(d1 >> 16) / s) << 16);
 }
 
-// One workgroup per row: the row maximum, then the lifted codes, one window
-// (4 codes) per thread and step.
+// Workgroup (c, b) takes the maximum over the whole of rows b, b + gridDim.y, ...
+// and writes chunk c (chunk_win windows of 4 codes, one window per thread and step)
+// of each row's lifted codes: a few rows are quantised by many workgroups (the
+// division per value is the costly part), each reading its rows' maximum from L2.
 template <int DT, int NP>
 __global__ __launch_bounds__(kThreads) void slide_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                                    int64_t k, uint8_t* __restrict__ q,
-                                                                   float* __restrict__ scales) {
+                                                                   float* __restrict__ scales, int64_t chunk_win) {
   constexpr int BLK = 2 * NP, GRP = 4 * (NP - 1);
   __shared__ uint32_t sh[kThreads / kWave];
   const int64_t nvec = k / 8, nwin = k / BLK * (NP - 1), kp = k / BLK * GRP;
-  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+  const int64_t w0 = (int64_t)blockIdx.x * chunk_win, w1 = min(nwin, w0 + chunk_win);
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
     const uint16_t* xr = x + r * k;
     const u32x4* xv = reinterpret_cast<const u32x4*>(xr);
     uint32_t mk = 0;
-    for (int64_t i = threadIdx.x; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
+    int64_t i = threadIdx.x;
+    for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {  // four loads in flight
+      const u32x4 a = xv[i], b = xv[i + kThreads], c = xv[i + 2 * kThreads], d = xv[i + 3 * kThreads];
+      mk = max(mk, max(max(key_max8(a), key_max8(b)), max(key_max8(c), key_max8(d))));
+    }
+    for (; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
     mk = wave_max_u32(mk);
     if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = mk;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kThreads / kWave; ++i) mk = max(mk, sh[i]);
+    for (int j = 0; j < kThreads / kWave; ++j) mk = max(mk, sh[j]);
     __syncthreads();
     const float s = qscale<DT>(mk);
-    if (threadIdx.x == 0) scales[r] = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + r * kp);
-    for (int64_t v = threadIdx.x; v < nwin; v += kThreads) {
+    for (int64_t v = w0 + threadIdx.x; v < w1; v += kThreads) {
       const int64_t b = v / (NP - 1), j = v - b * (NP - 1);
       const uint32_t* src = reinterpret_cast<const uint32_t*>(xr + b * BLK + 2 * j);  // 4-byte aligned
       qr[v] = qcast4<DT>(src[0], src[1], s);
@@ -165,17 +173,25 @@ hipError_t launch_slide_prune_pack(const uint16_t* w, int64_t n, int64_t k, int 
 
 hipError_t launch_slide_quant_rows(int dtype, const uint16_t* x, int64_t m, int64_t k, int np, uint8_t* q,
                                    float* scales, hipStream_t s) {
-  const int blocks = (int)(m < 65536 ? m : 65536);
+  // rows over grid.y; each row's windows split over grid.x so that few rows still fill
+  // about 256 workgroups (at least 256 windows each)
+  const int64_t rows = m < 65535 ? m : 65535, nwin = k / (2 * np) * (np - 1);
+  int64_t splits = 256 / rows;
+  const int64_t most = nwin / 256;
+  if (splits > most) splits = most;
+  if (splits < 1) splits = 1;
+  const int64_t chunk = (nwin + splits - 1) / splits;
+  const dim3 blocks((unsigned)((nwin + chunk - 1) / chunk), (unsigned)rows);
   const bool i8 = dtype == SP24_INT8;
   switch (np) {
 #define SP24_SLIDE_QUANT(NP)                                                                                 \
   case NP:                                                                                                   \
     if (i8)                                                                                                  \
-      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_INT8, NP>), dim3(blocks), dim3(kThreads), 0, s, x, m, \
-                         k, q, scales);                                                                      \
+      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_INT8, NP>), blocks, dim3(kThreads), 0, s, x, m,       \
+                         k, q, scales, chunk);                                                               \
     else                                                                                                     \
-      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_FP8_E4M3, NP>), dim3(blocks), dim3(kThreads), 0, s, x, \
-                         m, k, q, scales);                                                                   \
+      hipLaunchKernelGGL((slide_quant_rows_kernel<SP24_FP8_E4M3, NP>), blocks, dim3(kThreads), 0, s, x,       \
+                         m, k, q, scales, chunk);                                                            \
     break;
     SP24_SLIDE_QUANT(3) SP24_SLIDE_QUANT(4) SP24_SLIDE_QUANT(5) SP24_SLIDE_QUANT(6) SP24_SLIDE_QUANT(7)
     SP24_SLIDE_QUANT(8)
