@@ -395,6 +395,14 @@ int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
 constexpr int64_t kQxMaxValues = 65536;
 constexpr int64_t kQxMaxWgValues = 16384;
 
+// SP24_QX_FUSE=<values> replaces kQxMaxWgValues (tuning and tests only).
+int64_t qx_max_wg_values() {
+  const char* v = getenv("SP24_QX_FUSE");
+  long long x = 0;
+  if (v != nullptr && sscanf(v, "%lld", &x) == 1 && x >= 0 && x <= kQxMaxValues * 4) return x;
+  return kQxMaxWgValues;
+}
+
 bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
   if (p.kernel != SP24_KERNEL_STREAM || (!rows && m * k > kQxMaxValues)) return false;
   int64_t room = -1;
@@ -411,7 +419,7 @@ bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
     default: return false;
   }
   const int64_t rows_wg = m < bm ? m : bm;
-  return room >= 0 && rows_wg * (k / p.split_k) <= kQxMaxWgValues &&
+  return room >= 0 && rows_wg * (k / p.split_k) <= qx_max_wg_values() &&
          rows_wg * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
 }
 

@@ -435,6 +435,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[QX ? LDS_QX : C::LDS];
   // per tensor: each wave's largest key; per token: each row's largest key
   __shared__ uint32_t wave_max[QX ? (QROWS ? C::BM : C::NW) : 1];
+  // per token: each row's scale and the reciprocal of its divisor (QDiv)
+  __shared__ float row_sr[QX && QROWS ? 2 * C::BM : 1];
   // dynamic LDS, sized by the host: QX, the X codes; GS, the group scales of this
   // workgroup's rows ([group][row]) and tokens ([group][token]) for the K slice (at
   // most kStreamGsBytes)
@@ -543,15 +545,20 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       for (; i < nv; i += C::NT) atomicMax(&row_key[i / vpr], key_max8(xv[i]));
     }
     __syncthreads();
-    if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.z == 0 && tid < mrows)
-      sx_out[m0 + tid] = scale_from_key(row_key[tid]);
+    if (tid < mrows) {
+      const QDiv d = qdiv<SP24_FP8_E4M3>(row_key[tid]);
+      row_sr[2 * tid] = d.s;
+      row_sr[2 * tid + 1] = d.r;
+      if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.z == 0) sx_out[m0 + tid] = d.s;
+    }
+    __syncthreads();
     const int k0 = u0 * 128, kslice = units_per_slice * 128;
     // vector i: 8 codes at K offset kk of row rr, or (lifted) its 4 code pairs: pair
     // P = kk/2 + t is pair j = P % N of block b = P / N, which window j (j <= N-2)
     // takes at its positions 0, 1 and window j - 1 (j >= 1) at its positions 2, 3
     auto cast_vec = [&](int i, u32x4 d) {
       const int rr = i / vpr, kk = (i - rr * vpr) * 8;
-      const u32x2 c8 = cast8(d, scale_from_key(row_key[rr]));
+      const u32x2 c8 = cast8(d, qdiv_from(row_sr[2 * rr], row_sr[2 * rr + 1]));
       if (lift == 0) {
         const int kp = kk - k0;
         if (kp >= 0 && kp < kslice) *reinterpret_cast<u32x2*>(slot(rr, kp)) = c8;
@@ -629,7 +636,8 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
     else __syncthreads();
 #pragma unroll
     for (int g = 0; g < C::NW; ++g) mk = max(mk, wave_max[g]);
-    sx = scale_from_key(mk);
+    const QDiv sxd = qdiv<SP24_FP8_E4M3>(mk);
+    sx = sxd.s;
     if (sx_out != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *sx_out = sx;
     // codes of value kk (relative to the K slice) of token row rr
     auto put = [&](int rr, int kk, u32x2 c8) { *reinterpret_cast<u32x2*>(slot(rr, kk)) = c8; };
@@ -640,7 +648,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
         const int i = tid + r * C::NT;
         if (i >= (int)nvec) continue;
         const int row = 8 * i / K, kk = 8 * i - row * K - k0;
-        if (row >= m0 && row < m0 + mrows && kk >= 0 && kk < kslice) put(row - m0, kk, cast8(xr[r], sx));
+        if (row >= m0 && row < m0 + mrows && kk >= 0 && kk < kslice) put(row - m0, kk, cast8(xr[r], sxd));
       }
     } else {
       const int vpr = kslice / 8;  // 8-value vectors per row of the slice
@@ -651,7 +659,7 @@ __global__ __launch_bounds__(C::NT) void gemm_stream_kernel(
       };
       auto put_vec = [&](int v, u32x4 d) {
         const int rr = v / vpr;
-        put(rr, (v - rr * vpr) * 8, cast8(d, sx));
+        put(rr, (v - rr * vpr) * 8, cast8(d, sxd));
       };
       const int nv = mrows * vpr;
       int v = tid;

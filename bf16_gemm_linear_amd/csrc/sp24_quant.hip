@@ -79,15 +79,15 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
                                                         const uint32_t* __restrict__ partial,
                                                         int npartial) {
   __shared__ uint32_t sh[kThreads / kWave];
-  float s;
+  QDiv s;
   if (partial != nullptr) {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < npartial; i += kThreads) m = max(m, partial[i]);
     m = block_max<kThreads>(m, sh);
-    s = qscale<DT>(m);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+    s = qdiv<DT>(m);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s.s;
   } else {
-    s = *scale;
+    s = qdiv_static(*scale);
   }
   const int64_t nvec = count / 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
   __shared__ uint32_t sh[kFusedThreads / kWave];
   const int nvec = (int)(count / 8);
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  float s;
+  QDiv s;
   if (dynamic) {
     uint32_t m = 0;
     int i = threadIdx.x;
@@ -137,10 +137,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
     const int tail = nvec * 8 + threadIdx.x;
     if (tail < count) m = max(m, (uint32_t)(x[tail] & 0x7FFFu));
     m = block_max<kFusedThreads>(m, sh);
-    s = qscale<DT>(m);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+    s = qdiv<DT>(m);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s.s;
   } else {
-    s = *scale;
+    s = qdiv_static(*scale);
   }
   const int v0 = blockIdx.x * (kFusedSlice / 8);
   const int v1 = min(nvec, v0 + kFusedSlice / 8);
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __
       }
       for (; i < nvec; i += kThreads) mk = max(mk, key_max8(xv[i]));
     }
-    const float s = qscale<DT>(block_max<kThreads>(mk, sh));
-    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s;
+    const QDiv s = qdiv<DT>(block_max<kThreads>(mk, sh));
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s.s;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kRowRegVecs; ++j) {
@@ -239,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void quant_groups_kernel(const uint16_t* 
       for (int j = 0; j < per; ++j) mk = max(mk, key_max8(xv[base + (int64_t)j * seg]));
     }
     for (int off = 1; off < seg; off <<= 1) mk = max(mk, (uint32_t)__shfl_xor((int)mk, off, 64));
-    const float s = qscale<DT>(mk);
-    if (lseg == 0) scales[g] = s;
+    const QDiv s = qdiv<DT>(mk);
+    if (lseg == 0) scales[g] = s.s;
     if (per <= kGroupRegVecs) {
 #pragma unroll
       for (int j = 0; j < kGroupRegVecs; ++j)

@@ -98,13 +98,13 @@ __global__ __launch_bounds__(kThreads) void slide_prune_pack_kernel(const uint16
 
 // The 4 codes of one window (bf16 pairs d0, d1) for code type DT.
 template <int DT>
-__device__ __forceinline__ uint32_t qcast4(uint32_t d0, uint32_t d1, float s) {
+__device__ __forceinline__ uint32_t qcast4(uint32_t d0, uint32_t d1, const QDiv& s) {
+  const float v0 = qdiv_apply(bf16_to_f32(d0 & 0xFFFFu), s), v1 = qdiv_apply(bf16_to_f32(d0 >> 16), s);
+  const float v2 = qdiv_apply(bf16_to_f32(d1 & 0xFFFFu), s), v3 = qdiv_apply(bf16_to_f32(d1 >> 16), s);
   if constexpr (DT == SP24_INT8)
-    return f32_to_i8(bf16_to_f32(d0 & 0xFFFFu) / s) | (f32_to_i8(bf16_to_f32(d0 >> 16) / s) << 8) |
-           (f32_to_i8(bf16_to_f32(d1 & 0xFFFFu) / s) << 16) | (f32_to_i8(bf16_to_f32(d1 >> 16) / s) << 24);
+    return f32_to_i8(v0) | (f32_to_i8(v1) << 8) | (f32_to_i8(v2) << 16) | (f32_to_i8(v3) << 24);
   else
-    return f32x2_to_e4m3(bf16_to_f32(d0 & 0xFFFFu) / s, bf16_to_f32(d0 >> 16) / s) |
-           (f32x2_to_e4m3(bf16_to_f32(d1 & 0xFFFFu) / s, bf16_to_f32(d1 >> 16) / s) << 16);
+    return f32x2_to_e4m3(v0, v1) | (f32x2_to_e4m3(v2, v3) << 16);
 }
 
 // Workgroup (c, b) takes the maximum over the whole of rows b, b + gridDim.y, ...
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(kThreads) void slide_quant_rows_kernel(const uint16
 #pragma unroll
     for (int j = 0; j < kThreads / kWave; ++j) mk = max(mk, sh[j]);
     __syncthreads();
-    const float s = qscale<DT>(mk);
-    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s;
+    const QDiv s = qdiv<DT>(mk);
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[r] = s.s;
     uint32_t* qr = reinterpret_cast<uint32_t*>(q + r * kp);
     for (int64_t v = w0 + threadIdx.x; v < w1; v += kThreads) {
       const int64_t b = v / (NP - 1), j = v - b * (NP - 1);

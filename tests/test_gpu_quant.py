@@ -101,3 +101,34 @@ def test_static_saturation():
     want, _ = O.quant_fp8(xb, scale=np.float32(0.5))
     assert np.array_equal(got, want)
     assert list(got[2:6]) == [0x7E, 0xFE, 0x7E, 0xFE]
+
+
+def _keys_spanning_the_divisor_routes():
+    # largest magnitudes around the key 0x2000 (2^-63) below which the quantisers
+    # divide, the extremes, and a spread of ordinary ones
+    keys = [0x0001, 0x0080, 0x1FFF, 0x2000, 0x2001, 0x3F80, 0x43E0, 0x4380, 0x7F7F, 0x7F7E]
+    keys += [int(k) for k in np.random.default_rng(5).integers(0x2000, 0x7F7F, size=22)]
+    return keys
+
+
+@pytest.mark.parametrize("dt", ["fp8", "int8"])
+def test_dynamic_every_pattern_below_each_maximum(dt):
+    """Dynamic per-tensor scales on every bf16 pattern of magnitude <= amax, for maxima
+    on both sides of the key where the quantisers switch from the IEEE division to the
+    reciprocal with one exact-residual correction: codes and scale bit-exact."""
+    sp = need_sp()
+    quant, oquant = (sp.quant_fp8, O.quant_fp8) if dt == "fp8" else (sp.quant_int8, O.quant_int8)
+    b = np.arange(65536, dtype=np.uint32)
+    for key in _keys_spanning_the_divisor_routes():
+        xb = b[(b & 0x7FFF) <= key].astype(np.uint16)
+        announce("quant dynamic every pattern below key", dt, hex(key), xb.size)
+        x = W.bits_to_bf16(xb).to(DEV)
+        q, s = quant(x)
+        torch.cuda.synchronize()
+        want, ws = oquant(xb)
+        want = want.view(np.uint8)
+        assert f32_bits(f32(s)) == f32_bits(ws), "key %#06x: scale differs" % key
+        got = codes(q)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, "key %#06x: %d codes differ, first x bits %#06x got %#04x want %#04x" % (
+            key, bad.size, int(xb[bad[0]]), int(got[bad[0]]), int(want[bad[0]]))
