@@ -386,12 +386,13 @@ int plan_groups(int64_t m, int64_t n, int64_t k, sp24_plan* out) {
 // the ring leaves (stream_qx_room).  With one scale per tensor every workgroup
 // also reads all of X for it, so X must be small (M * K <= kQxMaxValues, 128 KB
 // of bf16); with one scale per token a workgroup reads only its own tokens.
-// Every workgroup casts all of its tokens' K slice, so the cast (an IEEE
-// division per value) is repeated by every workgroup along n: it is fused only
-// while that is at most kQxMaxWgValues values per workgroup (one token over
-// K = 14336, four over K = 4096).  Measured on MI355X, the up-projection
-// 14336 x 4096 at m = 16 (65536 values per workgroup): 24.5 us fused against
-// 13.4 us for the one-launch quantiser followed by the GEMM.
+// Every workgroup reads and casts all of its tokens' K slice, repeated by every
+// workgroup along n: it is fused only while that is at most kQxMaxWgValues
+// values per workgroup (one token over K = 14336, four over K = 4096).
+// Measured on MI355X, the up-projection 14336 x 4096 at m = 16 (65536 values
+// per workgroup): 21.0 us fused against 12.9 us for the one-launch quantiser
+// followed by the GEMM (the reading of X twice per workgroup, not the cast,
+// sets the fused time).
 constexpr int64_t kQxMaxValues = 65536;
 constexpr int64_t kQxMaxWgValues = 16384;
 

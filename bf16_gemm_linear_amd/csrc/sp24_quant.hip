@@ -12,9 +12,10 @@
 // (bits & 0x7FFF), which order finite bf16 magnitudes exactly.
 //   small tensors (<= kFusedMax values): one launch; every workgroup takes
 //                   amax over the whole tensor (at most 256 KB, from L2) and
-//                   casts its own slice of kFusedSlice values, so the division
-//                   (the costly part) is spread over the CUs while the
-//                   reduction needs no second launch (a launch costs ~2 us);
+//                   casts its own slice of kFusedSlice values, so the cast is
+//                   spread over the CUs while the reduction needs no second
+//                   launch (a launch costs ~2 us; 16K-value slices on 1024
+//                   threads, a quarter of the workgroups, measured slower);
 //   larger tensors: kernel 1 writes one partial maximum per workgroup into the
 //                   workspace; kernel 2 re-reduces those partials in every
 //                   workgroup (a few KB from L2), stores the scale from
@@ -153,8 +154,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_quant_kernel(const uint16
 // Per-row (per-token) scales: X [m, k] (k % 8 == 0), row r with s_r = fp32(amax_r /
 // 448) (1 for a zero row).  Workgroup (c, b) takes the maximum over the whole of rows
 // b, b + gridDim.y, ... and casts chunk c (chunk_vecs 8-value vectors) of each: a
-// few rows are cast by many workgroups (the division per value is the costly part;
-// one CU per row takes ~2 us for 14336 values), each reading its rows' maximum from
+// few rows are cast by many workgroups (with the IEEE division per value one CU per
+// row took ~2 us for 14336 values), each reading its rows' maximum from
 // L2.  A row of up to kRowRegVecs * kThreads vectors cast by one workgroup stays in
 // registers from the maximum to the cast (one pass over global memory).
 constexpr int kRowRegVecs = 4;
@@ -296,8 +297,8 @@ hipError_t launch_quant_dt(const uint16_t* x, int64_t count, uint8_t* q, float* 
                        dynamic ? 1 : 0);
     return hipGetLastError();
   }
-  // one vector per thread up to 2048 workgroups: the division of every value is the
-  // costly part, spread over as many CUs as there are vectors
+  // one vector per thread up to 2048 workgroups: the cast is spread over as many CUs
+  // as there are vectors
   int64_t cast_blocks = (count / 8 + kThreads - 1) / kThreads;
   if (cast_blocks > 256 * 8) cast_blocks = 256 * 8;
   if (cast_blocks < 1) cast_blocks = 1;

@@ -109,8 +109,8 @@ __device__ __forceinline__ uint32_t qcast4(uint32_t d0, uint32_t d1, const QDiv&
 
 // Workgroup (c, b) takes the maximum over the whole of rows b, b + gridDim.y, ...
 // and writes chunk c (chunk_win windows of 4 codes, one window per thread and step)
-// of each row's lifted codes: a few rows are quantised by many workgroups (the
-// division per value is the costly part), each reading its rows' maximum from L2.
+// of each row's lifted codes: a few rows are quantised by many workgroups, each
+// reading its rows' maximum from L2.
 template <int DT, int NP>
 __global__ __launch_bounds__(kThreads) void slide_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                                    int64_t k, uint8_t* __restrict__ q,
