@@ -148,7 +148,10 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 // every configuration on the decode shapes of a Llama-3-8B-sized layer on
 // MI355X:
 //  * m <= 16: X is negligible and W streams at the HBM rate; short row ranges
-//    want many waves along K (4 waves over 16 rows), ~30-64 rows per CU do
+//    want many waves along K (4 waves over 16 rows; 8 for sparse one-byte codes,
+//    whose fused quantising prologue then casts on twice the waves: down-
+//    projection 4096 x 14336 quantise + GEMM at m = 1 10.3 against 11.3 us, the
+//    GEMM alone 8.7 against 8.8-9.0 us), ~30-64 rows per CU do
 //    best as two 8-wave workgroups per CU at m <= 8 and as one workgroup of 4
 //    row blocks x 32 tokens at 8 < m <= 16 (up-projection at m = 16: 8.65
 //    against 9.2 us), longer ranges as 8 row blocks.
@@ -178,7 +181,7 @@ StreamChoice stream_default(int dtype, bool sparse, int64_t m, int64_t n, int64_
     return r < lo ? lo : (r > hi ? hi : r);
   };
   if (m <= 16) {
-    if (rows_cu <= 16) return StreamChoice{4, 0};
+    if (rows_cu <= 16) return two_units ? StreamChoice{5, 0} : StreamChoice{4, 0};
     if (rows_cu <= 64) {
       if (dtype == SP24_BF16) return rows_cu > 32 ? StreamChoice{13, 0} : StreamChoice{15, rows_for(256, 16, 32)};
       if (m > 8 && rows_cu > 32) return StreamChoice{10, rows_for(256, 16, 64)};
