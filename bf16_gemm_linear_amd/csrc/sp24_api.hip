@@ -148,10 +148,9 @@ bool plan_stream(int id, int dtype, bool sparse, int sk_req, int rows_req, int64
 // every configuration on the decode shapes of a Llama-3-8B-sized layer on
 // MI355X:
 //  * m <= 16: X is negligible and W streams at the HBM rate; short row ranges
-//    want many waves along K (4 waves over 16 rows; 8 for sparse one-byte codes,
-//    whose fused quantising prologue then casts on twice the waves: down-
-//    projection 4096 x 14336 quantise + GEMM at m = 1 10.3 against 11.3 us, the
-//    GEMM alone 8.7 against 8.8-9.0 us), ~30-64 rows per CU do
+//    want many waves along K (4 waves over 16 rows: down-projection 4096 x 14336
+//    at m = 1 / 16 8.3 / 10.2 against 8.6 / 10.8 us with 8; the calls that
+//    quantise X inside the kernel take 8, plan_qx below), ~30-64 rows per CU do
 //    best as two 8-wave workgroups per CU at m <= 8 and as one workgroup of 4
 //    row blocks x 32 tokens at 8 < m <= 16 (up-projection at m = 16: 8.65
 //    against 9.2 us), longer ranges as 8 row blocks.
@@ -181,7 +180,7 @@ StreamChoice stream_default(int dtype, bool sparse, int64_t m, int64_t n, int64_
     return r < lo ? lo : (r > hi ? hi : r);
   };
   if (m <= 16) {
-    if (rows_cu <= 16) return two_units ? StreamChoice{5, 0} : StreamChoice{4, 0};
+    if (rows_cu <= 16) return StreamChoice{4, 0};
     if (rows_cu <= 64) {
       if (dtype == SP24_BF16) return rows_cu > 32 ? StreamChoice{13, 0} : StreamChoice{15, rows_for(256, 16, 32)};
       if (m > 8 && rows_cu > 32) return StreamChoice{10, rows_for(256, 16, 64)};
@@ -427,6 +426,27 @@ bool qx_fused(const sp24_plan& p, int64_t m, int64_t k, bool rows) {
          rows_wg * stream_qx_row_bytes(k / p.split_k, ups * 128) <= room;
 }
 
+// The plan of the calls that quantise X (sp24_gemm_qx, sp24_gemm_rows_qx,
+// sp24_slide_gemm_qx): plan_gemm's, except that the 16-row, 4-K-wave plan of few
+// rows per CU (config 104) becomes its 8-K-wave form (config 105) when X is then
+// quantised inside the kernel: the prologue's cast runs on twice the waves
+// (down-projection 4096 x 14336 at m = 1: 10.2 against 10.6 us per tensor),
+// while the GEMM on codes is faster with 4.  A plan forced through SP24_TILE is
+// kept as it is.
+int plan_qx(int64_t m, int64_t n, int64_t k, bool rows, sp24_plan* out) {
+  const int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, out);
+  int cfg, sk, orows;
+  if (st != SP24_OK || out->kernel != SP24_KERNEL_STREAM || out->config != kStreamBase + 4 ||
+      tile_override(&cfg, &sk, &orows))
+    return st;
+  sp24_plan q;
+  memset(&q, 0, sizeof(q));
+  if (plan_stream(5, SP24_FP8_E4M3, true, out->split_k, 0, m, n, k, &q) && q.split_k == out->split_k &&
+      q.workspace_bytes == out->workspace_bytes && qx_fused(q, m, k, rows))
+    *out = q;
+  return SP24_OK;
+}
+
 // Workspace of the quantising GEMMs: the GEMM's own, then (when X is not
 // quantised inside the kernel) the E4M3 codes of X and, per tensor, the
 // quantiser's workspace.  k is the GEMM's K (K' for SlideSparse).
@@ -556,7 +576,7 @@ int gemm_qx_common(int64_t m, int64_t n, int64_t k, const void* x_bf16, float* x
                    void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
   if (!x_bf16 || !x_scale_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
   sp24_plan p;
-  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  int st = plan_qx(m, n, k, false, &p);
   if (st != SP24_OK) return st;
   if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
     return SP24_ERR_ALIGN;
@@ -664,7 +684,7 @@ size_t sp24_workspace_size(int op, int dtype, int64_t m, int64_t n, int64_t k) {
   }
   sp24_plan p;
   if (op == SP24_OP_GEMM_QX || op == SP24_OP_GEMM_ROWS_QX) {
-    if (dtype != SP24_FP8_E4M3 || plan_gemm(SP24_OP_GEMM, dtype, m, n, k, &p) != SP24_OK) return 0;
+    if (dtype != SP24_FP8_E4M3 || plan_qx(m, n, k, op == SP24_OP_GEMM_ROWS_QX, &p) != SP24_OK) return 0;
     return qx_workspace(p, m, k, op == SP24_OP_GEMM_ROWS_QX).total;
   }
   if (plan_gemm(op, dtype, m, n, k, &p) != SP24_OK) return 0;
@@ -902,7 +922,7 @@ int rows_qx_common(int lift, int64_t m, int64_t n, int64_t k, int64_t xk, const 
                    void* y_bf16, void* ws, size_t ws_bytes, void* stream) {
   if (!x_bf16 || !x_scales_dev || !w_values || !w_meta || !w_scale_dev || !y_bf16) return SP24_ERR_NULL;
   sp24_plan p;
-  int st = plan_gemm(SP24_OP_GEMM, SP24_FP8_E4M3, m, n, k, &p);
+  int st = plan_qx(m, n, k, true, &p);
   if (st != SP24_OK) return st;
   if (!aligned16(x_bf16) || !aligned16(w_values) || !aligned16(w_meta) || !aligned16(y_bf16))
     return SP24_ERR_ALIGN;

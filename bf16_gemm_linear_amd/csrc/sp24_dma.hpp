@@ -13,6 +13,15 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
+// The same with the non-temporal hint (data read once, streamed past the caches).
+__device__ __forceinline__ void dma16_nt(const void* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 2);
+}
+__device__ __forceinline__ void dma4_nt(const void* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 2);
+}
 __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds_dst, 4, 0, 0);

@@ -190,13 +190,13 @@ struct StreamLoader {
     for (int j = 0; j < C::W_PER; ++j) {
       const int g = j * C::NW + wave;
       if (C::W_TOT % C::NW == 0 || g < C::W_TOT)
-        dma16(wp[j] + (size_t)ks * C::WB, buf + C::W_OFF + g * 1024);
+        dma16_nt(wp[j] + (size_t)ks * C::WB, buf + C::W_OFF + g * 1024);
     }
 #pragma unroll
     for (int j = 0; j < C::M_PER; ++j) {
       const int g = j * C::NW + wave;
       if (C::M_TOT % C::NW == 0 || g < C::M_TOT)
-        dma4(mp[j] + (size_t)ks * mstep, buf + C::M_OFF + g * 256);
+        dma4_nt(mp[j] + (size_t)ks * mstep, buf + C::M_OFF + g * 256);
     }
 #pragma unroll
     for (int j = 0; j < (QX ? 0 : C::X_PER); ++j) {

@@ -208,17 +208,16 @@ def test_plan_decode_workgroups_per_cu_by_code_type():
         assert sp.plan(sp.OP_GEMM, dt, 1, 6144, 4096)["grid_x"] == 256
 
 
-def test_plan_few_rows_per_cu_takes_eight_k_waves_for_sparse_one_byte_codes():
+def test_plan_few_rows_per_cu_takes_one_row_block_and_four_k_waves():
     # m <= 16 with at most 16 rows per CU (the down-projection, N = 4096): one 16-row block
-    # per workgroup, 256 ranges; sparse FP8 / INT8 walk K with 8 waves (config 105), BF16
-    # and the dense baseline with 4 (config 104)
+    # per workgroup, 256 ranges, 4 waves along K (config 104) for every code type and the
+    # dense baseline (the calls that quantise X inside the kernel use 8, config 105)
     for m in (1, 16):
-        for dt in (sp.FP8, sp.INT8):
+        for dt in (sp.FP8, sp.INT8, sp.BF16):
             p = sp.plan(sp.OP_GEMM, dt, m, 4096, 14336)
             assert (p["kernel"], p["config"], p["tile_n"], p["grid_x"], p["waves"], p["split_k"]) == \
-                (2, 105, 16, 256, 8, 1), (m, dt, p)
+                (2, 104, 16, 256, 4, 1), (m, dt, p)
             assert sp.plan(sp.OP_DENSE_GEMM, dt, m, 4096, 14336)["config"] == 104
-        assert sp.plan(sp.OP_GEMM, sp.BF16, m, 4096, 14336)["config"] == 104
 
 
 def test_plan_tiled_for_wide_layers_at_256_tokens():
