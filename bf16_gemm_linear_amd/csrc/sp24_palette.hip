@@ -286,6 +286,8 @@ struct PalChunk {
   i32x4 xv[XL ? 1 : 4 * T];
 };
 
+// The encoded rows are read once per call: their loads carry the non-temporal hint
+// (up-projection at m = 1: 18.0 against 19.6 us, down 24.7 against 28.4 us).
 template <bool VERB, int T, int RB, bool XL>
 __device__ __forceinline__ void pal_load(PalChunk<VERB, T, RB, XL>& c, const uint8_t* __restrict__ wbase,
                                          const uint8_t* __restrict__ ixbase, const uint16_t* __restrict__ x,
@@ -297,14 +299,14 @@ __device__ __forceinline__ void pal_load(PalChunk<VERB, T, RB, XL>& c, const uin
     if constexpr (VERB) {  // 64 bytes per 32 values: tile of 16 rows x 512 values = 16 KB
       const uint8_t* p = wbase + blk * 32 * K + (int64_t)chunk * 16384 + 16 * lane;
 #pragma unroll
-      for (int j = 0; j < 4 * T; ++j) c.wv[rb][j] = *reinterpret_cast<const i32x4*>(p + 1024 * j);
+      for (int j = 0; j < 4 * T; ++j) c.wv[rb][j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p + 1024 * j));
     } else {               // sign+mantissa: 32 bytes per 32 values; indices: 16 bytes per 32 values
       const uint8_t* p = wbase + blk * 16 * K + (int64_t)chunk * 8192 + 16 * lane;
 #pragma unroll
-      for (int j = 0; j < 2 * T; ++j) c.wv[rb][j] = *reinterpret_cast<const i32x4*>(p + 1024 * j);
+      for (int j = 0; j < 2 * T; ++j) c.wv[rb][j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p + 1024 * j));
       const uint8_t* q = ixbase + blk * 8 * K + (int64_t)chunk * 4096 + 16 * lane;
 #pragma unroll
-      for (int j = 0; j < T; ++j) c.iv[rb][j] = *reinterpret_cast<const i32x4*>(q + 1024 * j);
+      for (int j = 0; j < T; ++j) c.iv[rb][j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(q + 1024 * j));
     }
   }
   if constexpr (!XL) {
