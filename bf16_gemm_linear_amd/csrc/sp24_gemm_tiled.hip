@@ -561,7 +561,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tiled_kernel(
     if (m >= M) continue;
     uint16_t* yr = y + (size_t)m * N;
     if (vec) {
-      *reinterpret_cast<u32x4*>(yr + n) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(yr + n));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
