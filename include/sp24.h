@@ -156,8 +156,10 @@ int sp24_check_meta(const uint32_t* meta, int64_t n, int64_t k, uint32_t* bad_de
  *        *scale_dev = fp32(amax / 448) (1.0 if amax == 0), written by the
  *        device (no host synchronisation); needs a workspace.
  *   mode SP24_SCALE_STATIC : *scale_dev is read, not written; no workspace.
- *   Each value: q = e4m3_rne(clamp(fp32(x / s), -448, 448)) with an IEEE
- *   float32 division (values beyond the range saturate to +-448).
+ *   Each value: q = e4m3_rne(clamp(fp32(x / s), -448, 448)) with the IEEE
+ *   float32 quotient (values beyond the range saturate to +-448); with a dynamic
+ *   scale and amax >= 2^-63 the kernels form it as x * fp32(1/s) plus one
+ *   exact-residual correction, which gives the same code for every bf16 x.
  *   x_bf16 in: [count] bf16; q_out out: [count] bytes; scale_dev: one fp32 on
  *   the device.  count >= 1.  ws/ws_bytes: sp24_workspace_size(SP24_OP_QUANT, ...). */
 int sp24_quant_fp8(const void* x_bf16, int64_t count, uint8_t* q_out, float* scale_dev, int mode,
