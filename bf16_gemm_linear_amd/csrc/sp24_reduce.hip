@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     if constexpr (SPLITS > 0) {
       f32x4 p[SPLITS];
 #pragma unroll
-      for (int z = 0; z < SPLITS; ++z) p[z] = *reinterpret_cast<const f32x4*>(partial + z * mn + 4 * i);
+      for (int z = 0; z < SPLITS; ++z) p[z] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(partial + z * mn + 4 * i));
       s = p[0];
 #pragma unroll
       for (int z = 1; z < SPLITS; ++z) s += p[z];
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
     u32x2 o{f32_to_bf16_rne(s[0] * scale_of(4 * i)) | (f32_to_bf16_rne(s[1] * scale_of(4 * i + 1)) << 16),
             f32_to_bf16_rne(s[2] * scale_of(4 * i + 2)) | (f32_to_bf16_rne(s[3] * scale_of(4 * i + 3)) << 16)};
-    *reinterpret_cast<u32x2*>(y + 4 * i) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(y + 4 * i));
   }
   for (int64_t i = nvec * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
     float s = partial[i];
